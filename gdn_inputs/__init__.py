@@ -1,0 +1,276 @@
+"""Seeded synthetic inputs for tree-verified Gated DeltaNet layers.
+
+This module is shared by the oracle-side tests and the GPU path. It holds no
+arithmetic of the method itself: it only draws trees, per-node vectors, gates,
+states and accepted nodes, and rounds the drawn values to the storage dtype.
+
+Workload shapes follow the pages:
+  * the Qwen3.5-9B GDN layer shape, 24 GDN layers x 16 key heads x a 128x128
+    state (rainlin-top "Qwen3.5 tree spec", section 6 "overhead analysis",
+    memory part);
+  * the k=2/d=2 tree with nodes root,A,B,C,D,E,F and the accepted path
+    root->A->C (same page, section 4 "Fork/Checkpoint" and section 5
+    "dual use of checkpoints");
+  * k-ary trees of 7/15/40 nodes (same page, section 6 table and section 8);
+  * per-level branching lists such as [2,2,1,1] (anrans handbook
+    "speculative" chapter, "implementation" section and exercise 1).
+
+Value distributions (q,k ~ N(0,1) then L2-normalised, v ~ N(0,1),
+alpha ~ U(0.9,1), beta = sigmoid(N(0,1)), S0 ~ N(0, 0.1^2)) are the synthetic
+recipe of the five workload configurations this library is measured on.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "CONFIGS", "Workload", "kary_parents", "chain_parents", "branching_parents",
+    "random_tree_parents", "make_workload", "make_config", "round_to_bf16",
+    "bf16_bits", "bf16_bits_to_f32", "path_to_root", "pick_accepted",
+]
+
+# ---------------------------------------------------------------------------
+# bf16 rounding (storage format only): round-to-nearest-even of an fp32 value
+# to its upper 16 bits, as the bf16 format defines it.
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 array -> uint16 bf16 bit patterns, round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    out = r.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to bf16 and widened back to fp32 (exact)."""
+    return bf16_bits_to_f32(bf16_bits(x))
+
+
+# ---------------------------------------------------------------------------
+# Tree shapes. Every tree is a parents list in topological order: node 0 is
+# the root with parent -1, and every other node's parent has a smaller index.
+# ---------------------------------------------------------------------------
+
+
+def kary_parents(k: int, d: int) -> List[int]:
+    """Complete k-ary tree of depth d (root = depth 0) in BFS order."""
+    n = sum(k ** i for i in range(d + 1))
+    return [-1] + [(i - 1) // k for i in range(1, n)]
+
+
+def chain_parents(n: int) -> List[int]:
+    return [-1] + list(range(n - 1))
+
+
+def branching_parents(branching: Sequence[int]) -> List[int]:
+    """Level-by-level expansion: every frontier node gets branching[l] children."""
+    parents, frontier = [-1], [0]
+    for width in branching:
+        nxt = []
+        for node in frontier:
+            for _ in range(width):
+                parents.append(node)
+                nxt.append(len(parents) - 1)
+        frontier = nxt
+    return parents
+
+
+def random_tree_parents(rng: np.random.Generator, nmin: int = 16, nmax: int = 64,
+                        max_depth: int = 6, max_children: int = 4) -> List[int]:
+    """Dynamic (EAGLE-2-like) draft tree: size ~ U{nmin..nmax}; each new node
+    hangs under a uniformly chosen earlier node that is shallower than
+    max_depth and has fewer than max_children children."""
+    n = int(rng.integers(nmin, nmax + 1))
+    parents, level, nchild = [-1], [0], [0]
+    for _ in range(1, n):
+        open_nodes = [j for j in range(len(parents))
+                      if level[j] < max_depth and nchild[j] < max_children]
+        p = int(open_nodes[int(rng.integers(len(open_nodes)))])
+        parents.append(p)
+        level.append(level[p] + 1)
+        nchild.append(0)
+        nchild[p] += 1
+    return parents
+
+
+def path_to_root(parents: Sequence[int], node: int) -> List[int]:
+    """Nodes from the root down to `node` (inclusive)."""
+    out = []
+    while node != -1:
+        out.append(node)
+        node = parents[node]
+    return out[::-1]
+
+
+def pick_accepted(rng: np.random.Generator, parents: Sequence[int]) -> int:
+    """Uniform leaf, then a uniform accepted prefix length along its path."""
+    n = len(parents)
+    has_child = [False] * n
+    for p in parents[1:]:
+        has_child[p] = True
+    leaves = [i for i in range(n) if not has_child[i]]
+    leaf = leaves[int(rng.integers(len(leaves)))]
+    path = path_to_root(parents, leaf)
+    length = int(rng.integers(1, len(path) + 1))
+    return path[length - 1]
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+CONFIGS = {
+    "c1": dict(desc="tiny: 1 seq, 1 head, dk=dv=32, fp32, tree k=2 d=2 (7 nodes)",
+               B=1, H=1, dk=32, dv=32, io="f32", layers=1, tree="fixed",
+               parents=[-1, 0, 0, 1, 1, 2, 2], accepted="fixed", accepted_node=3, seed=0),
+    "c2": dict(desc="chain gamma=5 (6 nodes incl. root), B=1, 16 heads, 128x128, bf16 io",
+               B=1, H=16, dk=128, dv=128, io="bf16", layers=1, tree="chain", n=6,
+               accepted="leafprefix", seed=1),
+    "c3": dict(desc="tree k=2 d=3 (15 nodes), B=32, 16 heads, 128x128, bf16 io",
+               B=32, H=16, dk=128, dv=128, io="bf16", layers=1, tree="kary", k=2, d=3,
+               accepted="leafprefix", seed=2),
+    "c4": dict(desc="tree k=3 d=3 (40 nodes), 24 GDN layers, B=64, 16 heads, 128x128, bf16 io",
+               B=64, H=16, dk=128, dv=128, io="bf16", layers=24, tree="kary", k=3, d=3,
+               accepted="leafprefix", seed=3),
+    "c5": dict(desc="ragged random trees 16-64 nodes, depth<=6, 1-4 children, B=128, 16 heads, bf16 io",
+               B=128, H=16, dk=128, dv=128, io="bf16", layers=1, tree="random",
+               nmin=16, nmax=64, max_depth=6, max_children=4,
+               accepted="leafprefix", seed=4),
+}
+
+
+@dataclasses.dataclass
+class Workload:
+    """All inputs of one batch. Float tensors hold the exact stored values
+    (bf16-representable when io == 'bf16'); *_bits hold the bf16 bit patterns."""
+    B: int
+    H: int
+    dk: int
+    dv: int
+    io: str
+    layers: int
+    parents_list: List[List[int]]
+    offsets: np.ndarray          # [B+1] int32
+    parents: np.ndarray          # [T] int32, local indices, root -1
+    accepted: np.ndarray         # [B] int32, local index of the last accepted node
+    q: np.ndarray                # [L,T,H,dk] float32
+    k: np.ndarray                # [L,T,H,dk] float32
+    v: np.ndarray                # [L,T,H,dv] float32
+    alpha: np.ndarray            # [L,T,H] float32
+    beta: np.ndarray             # [L,T,H] float32
+    S0: np.ndarray               # [L,B,H,dv,dk] float32, S[r][c] multiplies k[c]
+
+    @property
+    def T(self) -> int:
+        return int(self.offsets[-1])
+
+    @property
+    def max_nodes(self) -> int:
+        return max(len(p) for p in self.parents_list) if self.parents_list else 1
+
+    def max_depth(self) -> int:
+        best = 0
+        for p in self.parents_list:
+            lvl = [0] * len(p)
+            for i in range(1, len(p)):
+                lvl[i] = lvl[p[i]] + 1
+            best = max(best, max(lvl))
+        return best
+
+    def io_bits(self, name: str, layer: int = 0) -> np.ndarray:
+        return bf16_bits(getattr(self, name)[layer])
+
+
+def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / n).astype(np.float32)
+
+
+def make_workload(parents_list: Sequence[Sequence[int]], H: int, dk: int, dv: int,
+                  io: str = "bf16", layers: int = 1, seed: int = 0,
+                  accepted: Optional[Sequence[int]] = None,
+                  rng: Optional[np.random.Generator] = None,
+                  s0_std: float = 0.1) -> Workload:
+    """Draw every per-layer input for the given trees. Draw order per layer:
+    q, k, v, alpha, beta logits, S0; accepted nodes last (unless given)."""
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    parents_list = [list(map(int, p)) for p in parents_list]
+    B = len(parents_list)
+    sizes = [len(p) for p in parents_list]
+    offsets = np.zeros(B + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(sizes)
+    T = int(offsets[-1])
+    parents = np.array([x for p in parents_list for x in p], dtype=np.int32)
+    L = layers
+    q = np.empty((L, T, H, dk), np.float32)
+    k = np.empty((L, T, H, dk), np.float32)
+    v = np.empty((L, T, H, dv), np.float32)
+    alpha = np.empty((L, T, H), np.float32)
+    beta = np.empty((L, T, H), np.float32)
+    S0 = np.empty((L, B, H, dv, dk), np.float32)
+    for layer in range(L):
+        q[layer] = _unit_rows(rng, (T, H, dk))
+        k[layer] = _unit_rows(rng, (T, H, dk))
+        v[layer] = rng.standard_normal((T, H, dv), dtype=np.float32)
+        alpha[layer] = rng.uniform(0.9, 1.0, size=(T, H)).astype(np.float32)
+        logits = rng.standard_normal((T, H)).astype(np.float32)
+        beta[layer] = (1.0 / (1.0 + np.exp(-logits.astype(np.float64)))).astype(np.float32)
+        S0[layer] = rng.standard_normal((B, H, dv, dk), dtype=np.float32) * np.float32(s0_std)
+        if io == "bf16":
+            q[layer] = round_to_bf16(q[layer])
+            k[layer] = round_to_bf16(k[layer])
+            v[layer] = round_to_bf16(v[layer])
+    if accepted is None:
+        acc = np.array([pick_accepted(rng, p) for p in parents_list], dtype=np.int32)
+    else:
+        acc = np.asarray(accepted, dtype=np.int32)
+    return Workload(B=B, H=H, dk=dk, dv=dv, io=io, layers=L, parents_list=parents_list,
+                    offsets=offsets, parents=parents, accepted=acc, q=q, k=k, v=v,
+                    alpha=alpha, beta=beta, S0=S0)
+
+
+def config_trees(name: str, rng: np.random.Generator) -> List[List[int]]:
+    c = CONFIGS[name]
+    if c["tree"] == "fixed":
+        return [list(c["parents"]) for _ in range(c["B"])]
+    if c["tree"] == "chain":
+        return [chain_parents(c["n"]) for _ in range(c["B"])]
+    if c["tree"] == "kary":
+        return [kary_parents(c["k"], c["d"]) for _ in range(c["B"])]
+    if c["tree"] == "random":
+        return [random_tree_parents(rng, c["nmin"], c["nmax"], c["max_depth"], c["max_children"])
+                for _ in range(c["B"])]
+    raise ValueError(c["tree"])
+
+
+def make_config(name: str, layers: Optional[int] = None, batch: Optional[int] = None,
+                seed: Optional[int] = None) -> Workload:
+    """One of the five workload configurations. `layers`/`batch` shrink it
+    (for tests that sample); the draw order is unchanged."""
+    c = CONFIGS[name]
+    rng = np.random.Generator(np.random.PCG64(c["seed"] if seed is None else seed))
+    trees = config_trees(name, rng)
+    if batch is not None:
+        trees = trees[:batch]
+    L = c["layers"] if layers is None else layers
+    # On a chain the only leaf is the last node, so "uniform leaf, then a
+    # uniform prefix length" is a uniform accepted prefix length in [1, n].
+    acc = [c["accepted_node"]] * len(trees) if c["accepted"] == "fixed" else None
+    return make_workload(trees, H=c["H"], dk=c["dk"], dv=c["dv"], io=c["io"],
+                         layers=L, rng=rng, accepted=acc)

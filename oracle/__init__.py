@@ -1,0 +1,153 @@
+"""CPU oracle for tree-verified Gated DeltaNet (fp64, slow, obviously correct).
+
+TEST INFRASTRUCTURE ONLY: tests, the smoke check and the benchmark's CPU
+baseline use it to check and time the GPU library; the library itself never
+imports, links or calls anything here, and this package imports nothing from
+the library.
+
+The arithmetic lives in gdn_oracle.c (plain C, double precision, optional
+OpenMP over (sequence, head)); this module compiles it with gcc and marshals
+numpy arrays. wy.py holds a second, independent formulation (the tree-shaped
+WY form, dense linear algebra in numpy) used to check intermediate results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+STATUS_OK, STATUS_BAD_ROOT, STATUS_BAD_PARENT, STATUS_BAD_SIZE, STATUS_BAD_ACCEPTED = 0, 1, 2, 3, 4
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc -O2 (no fast-math) and OpenMP."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+               "-Wall", "-o", tmp, _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            I = ctypes.c_int
+            lib.oracle_threads.restype = I
+            lib.oracle_set_threads.argtypes = [I]
+            lib.oracle_tree.argtypes = [I, I, I, P, P, P, P, P]
+            lib.oracle_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+            lib.oracle_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+            lib.oracle_fork_replay.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
+            lib.oracle_chain.argtypes = [I, I, I, P, P, P, P, P, P, P, P]
+            _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _i32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    return _load().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def tree(offsets, parents, max_nodes: int = 64):
+    """(depth[T] int32, anc[T] uint64, status[B] int32)."""
+    lib = _load()
+    offsets, parents = _i32(offsets), _i32(parents)
+    B, T = len(offsets) - 1, len(parents)
+    depth = np.full(T, -1, np.int32)
+    anc = np.zeros(T, np.uint64)
+    status = np.zeros(max(B, 1), np.int32)
+    lib.oracle_tree(B, T, max_nodes, _p(offsets), _p(parents), _p(depth), _p(anc), _p(status))
+    return depth, anc, status[:B]
+
+
+def verify(offsets, parents, q, k, v, alpha, beta, S0, max_nodes: int = 64):
+    """Per-node outputs o[T,H,dv] (float64) and per-sequence status[B]."""
+    lib = _load()
+    offsets, parents = _i32(offsets), _i32(parents)
+    q, k, v, alpha, beta, S0 = map(_f64, (q, k, v, alpha, beta, S0))
+    B = len(offsets) - 1
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert S0.shape == (B, H, dv, dk)
+    o = np.zeros((T, H, dv), np.float64)
+    status = np.zeros(max(B, 1), np.int32)
+    lib.oracle_verify(B, H, dk, dv, T, max_nodes, _p(offsets), _p(parents), _p(q), _p(k), _p(v),
+                      _p(alpha), _p(beta), _p(S0), _p(o), _p(status))
+    return o, status[:B]
+
+
+def commit(offsets, parents, accepted, k, v, alpha, beta, S0, S_out=None, max_nodes: int = 64):
+    """Committed states S_out[B,H,dv,dk] (float64) and status[B]. Entries of
+    sequences with a nonzero status keep the values of the S_out passed in
+    (zeros by default)."""
+    lib = _load()
+    offsets, parents, accepted = _i32(offsets), _i32(parents), _i32(accepted)
+    k, v, alpha, beta, S0 = map(_f64, (k, v, alpha, beta, S0))
+    B = len(offsets) - 1
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    out = np.zeros((B, H, dv, dk), np.float64) if S_out is None else _f64(S_out).copy()
+    status = np.zeros(max(B, 1), np.int32)
+    lib.oracle_commit(B, H, dk, dv, T, max_nodes, _p(offsets), _p(parents), _p(accepted), _p(k),
+                      _p(v), _p(alpha), _p(beta), _p(S0), _p(out), _p(status))
+    return out, status[:B]
+
+
+def fork_replay(offsets, parents, q, k, v, alpha, beta, S0, max_nodes: int = 64):
+    """Depth-by-depth fork/checkpoint replay: (o[T,H,dv], ckpt[T,H,dv,dk], status)."""
+    lib = _load()
+    offsets, parents = _i32(offsets), _i32(parents)
+    q, k, v, alpha, beta, S0 = map(_f64, (q, k, v, alpha, beta, S0))
+    B = len(offsets) - 1
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((T, H, dv), np.float64)
+    ck = np.zeros((T, H, dv, dk), np.float64)
+    status = np.zeros(max(B, 1), np.int32)
+    lib.oracle_fork_replay(B, H, dk, dv, T, max_nodes, _p(offsets), _p(parents), _p(q), _p(k),
+                           _p(v), _p(alpha), _p(beta), _p(S0), _p(o), _p(ck), _p(status))
+    return o, ck, status[:B]
+
+
+def chain(q, k, v, alpha, beta, S0):
+    """Plain sequential recurrence of one head over n tokens:
+    q,k [n,dk], v [n,dv], alpha,beta [n], S0 [dv,dk] -> (o [n,dv], S_final)."""
+    lib = _load()
+    q, k, v, alpha, beta, S0 = map(_f64, (q, k, v, alpha, beta, S0))
+    n, dk = q.shape
+    dv = v.shape[1]
+    o = np.zeros((n, dv), np.float64)
+    S = np.zeros((dv, dk), np.float64)
+    lib.oracle_chain(n, dk, dv, _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(S0), _p(o), _p(S))
+    return o, S

@@ -1,0 +1,241 @@
+"""Python binding of libgdntree (MI355X / gfx950): tree verification of Gated
+DeltaNet layers.
+
+The functions here carry the names of the C entry points declared in
+include/gdn_tree.h and only marshal arguments: they check torch tensors
+(device, dtype, shape, contiguity), pass their device pointers and the current
+HIP stream to the library, and raise GdnError for a nonzero gdn_status. Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback. Loading fails loudly when libgdntree.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+__all__ = [
+    "GdnError", "GdnTreeDesc", "load_library", "make_desc", "gdn_tree_workspace_bytes",
+    "gdn_tree_build", "gdn_tree_verify", "gdn_tree_commit", "gdn_tree_status_string",
+    "DTYPE_F32", "DTYPE_BF16", "MODE_WY", "MODE_FORK", "MAX_NODES", "TREE_STATUS",
+    "PreparedCall", "prepare_verify", "prepare_commit",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdntree.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+MODE_WY, MODE_FORK = 0, 1
+MAX_NODES = 64
+TREE_STATUS = {0: "ok", 1: "bad root", 2: "bad parent", 3: "bad size", 4: "bad accepted",
+               5: "too deep"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {gdn_tree_status_string(code)} (gdn_status {code})")
+        self.code = code
+
+
+class GdnTreeDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+        ("total_nodes", ctypes.c_int32), ("max_nodes", ctypes.c_int32),
+        ("max_depth", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libgdntree.so from this package directory (no build, no fallback)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"{LIB_PATH} is missing: build it with `python -m gated_deltanet_tree_02_amd.build` "
+                    "(or __graft_entry__.build()); there is no CPU fallback")
+            lib = ctypes.CDLL(LIB_PATH)
+            P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+            D = ctypes.POINTER(GdnTreeDesc)
+            lib.gdn_tree_workspace_bytes.argtypes = [D]
+            lib.gdn_tree_workspace_bytes.restype = S
+            lib.gdn_tree_build.argtypes = [D, P, P, P, P, P, P]
+            lib.gdn_tree_build.restype = I
+            lib.gdn_tree_verify.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, P, P]
+            lib.gdn_tree_verify.restype = I
+            lib.gdn_tree_commit.argtypes = [D, P, P, P, P, P, P, P, S, P, P]
+            lib.gdn_tree_commit.restype = I
+            lib.gdn_tree_status_string.argtypes = [I]
+            lib.gdn_tree_status_string.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def gdn_tree_status_string(code: int) -> str:
+    return load_library().gdn_tree_status_string(int(code)).decode()
+
+
+def make_desc(num_seqs: int, num_heads: int, dk: int, dv: int, total_nodes: int,
+              max_nodes: int, io_dtype: int = DTYPE_BF16, mode: int = MODE_WY,
+              max_depth: int = 0) -> GdnTreeDesc:
+    return GdnTreeDesc(int(num_seqs), int(num_heads), int(dk), int(dv), int(total_nodes),
+                       int(max_nodes), int(max_depth), int(io_dtype), int(mode))
+
+
+def gdn_tree_workspace_bytes(desc: GdnTreeDesc) -> int:
+    return int(load_library().gdn_tree_workspace_bytes(ctypes.byref(desc)))
+
+
+# ------------------------------------------------------------------ marshalling
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_dtype(desc):
+    torch = _torch()
+    return torch.bfloat16 if desc.io_dtype == DTYPE_BF16 else torch.float32
+
+
+def _ptr(t, name, dtype=None, shape=None, device=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise GdnError(code, where)
+
+
+def gdn_tree_build(desc, offsets, parents, depth, anc_mask, tree_status, stream=None):
+    """Ancestor masks (int64 tensor holding the uint64 bit patterns) and depths."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    args = [
+        _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+        _ptr(parents, "parents", torch.int32, (T,), dev),
+        _ptr(depth, "depth", torch.int32, (T,), dev),
+        _ptr(anc_mask, "anc_mask", torch.int64, (T,), dev),
+        _ptr(tree_status, "tree_status", torch.int32, (B,), dev),
+    ]
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_build(ctypes.byref(desc), *args, _stream(stream, dev)),
+               "gdn_tree_build")
+
+
+def _verify_args(desc, offsets, parents, q, k, v, alpha, beta, S0, o, workspace, tree_status):
+    torch = _torch()
+    B, H, T, dk, dv = desc.num_seqs, desc.num_heads, desc.total_nodes, desc.dk, desc.dv
+    dev = offsets.device
+    io = _io_dtype(desc)
+    return dev, [
+        _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+        _ptr(parents, "parents", torch.int32, (T,), dev),
+        _ptr(q, "q", io, (T, H, dk), dev),
+        _ptr(k, "k", io, (T, H, dk), dev),
+        _ptr(v, "v", io, (T, H, dv), dev),
+        _ptr(alpha, "alpha", torch.float32, (T, H), dev),
+        _ptr(beta, "beta", torch.float32, (T, H), dev),
+        _ptr(S0, "S0", torch.float32, (B, H, dv, dk), dev),
+        _ptr(o, "o", io, (T, H, dv), dev),
+        _ptr(workspace, "workspace", torch.uint8, None, dev),
+        ctypes.c_size_t(workspace.numel()),
+        _ptr(tree_status, "tree_status", torch.int32, (B,), dev),
+    ]
+
+
+def _commit_args(desc, offsets, parents, accepted, k, S0, S_out, workspace, tree_status):
+    torch = _torch()
+    B, H, T, dk, dv = desc.num_seqs, desc.num_heads, desc.total_nodes, desc.dk, desc.dv
+    dev = offsets.device
+    io = _io_dtype(desc)
+    return dev, [
+        _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+        _ptr(parents, "parents", torch.int32, (T,), dev),
+        _ptr(accepted, "accepted", torch.int32, (B,), dev),
+        _ptr(k, "k", io, (T, H, dk), dev, allow_none=desc.mode == MODE_FORK),
+        _ptr(S0, "S0", torch.float32, (B, H, dv, dk), dev),
+        _ptr(S_out, "S_out", torch.float32, (B, H, dv, dk), dev),
+        _ptr(workspace, "workspace", torch.uint8, None, dev),
+        ctypes.c_size_t(workspace.numel()),
+        _ptr(tree_status, "tree_status", torch.int32, (B,), dev),
+    ]
+
+
+def gdn_tree_verify(desc, offsets, parents, q, k, v, alpha, beta, S0, o, workspace,
+                    tree_status, stream=None):
+    torch = _torch()
+    dev, args = _verify_args(desc, offsets, parents, q, k, v, alpha, beta, S0, o, workspace,
+                             tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_verify(ctypes.byref(desc), *args, _stream(stream, dev)),
+               "gdn_tree_verify")
+
+
+def gdn_tree_commit(desc, offsets, parents, accepted, k, S0, S_out, workspace, tree_status,
+                    stream=None):
+    torch = _torch()
+    dev, args = _commit_args(desc, offsets, parents, accepted, k, S0, S_out, workspace,
+                             tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_commit(ctypes.byref(desc), *args, _stream(stream, dev)),
+               "gdn_tree_commit")
+
+
+class PreparedCall:
+    """One entry point with its arguments checked and marshalled once; calling
+    it enqueues the same work again on the stream captured at preparation.
+    The tensors must stay alive and unmoved while the object is used."""
+
+    def __init__(self, name, desc, args, stream, keep):
+        self._fn = getattr(load_library(), name)
+        self._name = name
+        self._desc = GdnTreeDesc.from_buffer_copy(desc)
+        self._args = (ctypes.byref(self._desc),) + tuple(args) + (stream,)
+        self._keep = keep
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code != 0:
+            raise GdnError(code, self._name)
+
+
+def prepare_verify(desc, offsets, parents, q, k, v, alpha, beta, S0, o, workspace, tree_status,
+                   stream=None) -> PreparedCall:
+    tensors = (offsets, parents, q, k, v, alpha, beta, S0, o, workspace, tree_status)
+    dev, args = _verify_args(desc, *tensors)
+    return PreparedCall("gdn_tree_verify", desc, args, _stream(stream, dev), tensors)
+
+
+def prepare_commit(desc, offsets, parents, accepted, k, S0, S_out, workspace, tree_status,
+                   stream=None) -> PreparedCall:
+    tensors = (offsets, parents, accepted, k, S0, S_out, workspace, tree_status)
+    dev, args = _commit_args(desc, *tensors)
+    return PreparedCall("gdn_tree_commit", desc, args, _stream(stream, dev), tensors)

@@ -1,0 +1,146 @@
+// gdn_tree_api.cpp -- the C ABI of libgdntree: host-side checks, workspace
+// sizing and kernel dispatch. Never allocates, never synchronises; every
+// launch goes to the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+
+#include "gdn_tree.h"
+#include "launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+gdn_status check_desc(const gdn_tree_desc* d) {
+  if (d == nullptr) return GDN_ERR_NULL_PTR;
+  if (d->num_seqs < 0 || d->num_heads < 1 || d->total_nodes < 0 || d->max_nodes < 1 ||
+      d->max_nodes > GDN_TREE_MAX_NODES)
+    return GDN_ERR_BAD_SHAPE;
+  if (d->dk != d->dv || (d->dk != 32 && d->dk != 64 && d->dk != 128)) return GDN_ERR_UNSUPPORTED;
+  if (d->io_dtype != GDN_DTYPE_F32 && d->io_dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+  if (d->mode != GDN_MODE_WY && d->mode != GDN_MODE_FORK) return GDN_ERR_UNSUPPORTED;
+  // grids are B*H*(chunks <= 4) workgroups; node indices (T*H) must fit int
+  const long long bh = (long long)d->num_seqs * d->num_heads;
+  if (bh * 4 > INT_MAX || (long long)d->total_nodes * d->num_heads > INT_MAX)
+    return GDN_ERR_BAD_SHAPE;
+  return GDN_OK;
+}
+
+int levels(const gdn_tree_desc* d) {
+  const int md = d->max_depth > 0 ? d->max_depth : d->max_nodes - 1;
+  return (md < d->max_nodes - 1 ? md : d->max_nodes - 1) + 1;
+}
+
+size_t wy_u_bytes(const gdn_tree_desc* d) {
+  return round_up((size_t)d->total_nodes * d->num_heads * d->dv * sizeof(float));
+}
+
+size_t workspace_bytes(const gdn_tree_desc* d) {
+  const size_t th = (size_t)d->total_nodes * d->num_heads;
+  if (d->mode == GDN_MODE_FORK) return round_up(th * d->dv * d->dk * sizeof(float));
+  return wy_u_bytes(d) + round_up(th * sizeof(float));
+}
+
+gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_tree_workspace_bytes(const gdn_tree_desc* desc) {
+  if (check_desc(desc) != GDN_OK) return 0;
+  return workspace_bytes(desc);
+}
+
+gdn_status gdn_tree_build(const gdn_tree_desc* desc, const int32_t* offsets,
+                          const int32_t* parents, int32_t* depth, uint64_t* anc_mask,
+                          int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (desc->num_seqs == 0) return GDN_OK;
+  if (!offsets || !tree_status) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && (!parents || !depth || !anc_mask)) return GDN_ERR_NULL_PTR;
+  gdn::TreeArgs a{desc->num_seqs, desc->total_nodes, desc->max_nodes, offsets, parents,
+                  depth, anc_mask, tree_status};
+  return launched(gdn::launch_tree_build(a, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_tree_verify(const gdn_tree_desc* desc, const int32_t* offsets,
+                           const int32_t* parents, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta,
+                           const float* S0, void* o, void* workspace, size_t ws_bytes,
+                           int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (desc->num_seqs == 0) return GDN_OK;
+  if (!offsets || !tree_status || !S0) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 &&
+      (!parents || !q || !k || !v || !alpha || !beta || !o || !workspace))
+    return GDN_ERR_NULL_PTR;
+  if (ws_bytes < workspace_bytes(desc)) return GDN_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = desc->dk;
+  if (desc->mode == GDN_MODE_WY) {
+    float* U = static_cast<float*>(workspace);
+    float* g2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wy_u_bytes(desc));
+    gdn::VerifyArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                      offsets, parents, q, k, v, alpha, beta, S0, o, U, g2, tree_status};
+    const int mt = (desc->max_nodes + 15) / 16;
+    return launched(gdn::launch_wy_verify(desc->io_dtype, d, mt, a, s));
+  }
+  const int L = levels(desc);
+  for (int level = 0; level < L; ++level) {
+    gdn::ForkArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                    L - 1, level, offsets, parents, q, k, v, alpha, beta, S0, o,
+                    static_cast<float*>(workspace), tree_status};
+    st = launched(gdn::launch_fork_level(desc->io_dtype, d, a, s));
+    if (st != GDN_OK) return st;
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
+                           const int32_t* parents, const int32_t* accepted, const void* k,
+                           const float* S0, float* S_out, const void* workspace,
+                           size_t ws_bytes, int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (desc->num_seqs == 0) return GDN_OK;
+  if (!offsets || !accepted || !S0 || !S_out || !tree_status) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && (!parents || !workspace)) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && desc->mode == GDN_MODE_WY && !k) return GDN_ERR_NULL_PTR;
+  if (ws_bytes < workspace_bytes(desc)) return GDN_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = desc->dk;
+  if (desc->mode == GDN_MODE_WY) {
+    const float* U = static_cast<const float*>(workspace);
+    const float* g2 =
+        reinterpret_cast<const float*>(static_cast<const char*>(workspace) + wy_u_bytes(desc));
+    gdn::CommitArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                      offsets, parents, accepted, k, S0, S_out, U, g2, tree_status};
+    return launched(gdn::launch_wy_commit(desc->io_dtype, d, a, s));
+  }
+  gdn::ForkCommitArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                        levels(desc) - 1, offsets, parents, accepted, S0, S_out,
+                        static_cast<const float*>(workspace), tree_status};
+  return launched(gdn::launch_fork_commit(d, a, s));
+}
+
+const char* gdn_tree_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_PTR: return "a required pointer is NULL";
+    case GDN_ERR_BAD_SHAPE: return "invalid sizes in the descriptor";
+    case GDN_ERR_UNSUPPORTED: return "unsupported dk/dv, io dtype or mode";
+    case GDN_ERR_WORKSPACE: return "workspace smaller than gdn_tree_workspace_bytes()";
+    case GDN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// launch.h -- internal interface between the C ABI host code and the kernel
+// translation units of libgdntree (not installed, not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct TreeArgs {
+  int B, T, max_nodes;
+  const int32_t* offsets;
+  const int32_t* parents;
+  int32_t* depth;
+  uint64_t* anc;
+  int32_t* status;
+};
+
+struct VerifyArgs {
+  int B, H, T, max_nodes;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;
+  void* o;
+  float* U;      // [T,H,dv] pseudo-values
+  float* g2;     // [T,H] base-2 gate prefixes
+  int32_t* status;
+};
+
+struct CommitArgs {
+  int B, H, T, max_nodes;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* accepted;
+  const void* k;
+  const float* S0;
+  float* S_out;
+  const float* U;
+  const float* g2;
+  int32_t* status;
+};
+
+struct ForkArgs {
+  int B, H, T, max_nodes, max_depth, level;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;
+  void* o;
+  float* ckpt;   // [T,H,dv,dk]
+  int32_t* status;
+};
+
+struct ForkCommitArgs {
+  int B, H, T, max_nodes, max_depth;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* accepted;
+  const float* S0;
+  float* S_out;
+  const float* ckpt;
+  int32_t* status;
+};
+
+// io: 0 = fp32, 1 = bf16 (gdn_dtype); d = dk = dv; mt = ceil(max_nodes / 16).
+hipError_t launch_tree_build(const TreeArgs& a, hipStream_t s);
+hipError_t launch_wy_verify(int io, int d, int mt, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s);
+hipError_t launch_fork_level(int io, int d, const ForkArgs& a, hipStream_t s);
+hipError_t launch_fork_commit(int d, const ForkCommitArgs& a, hipStream_t s);
+
+// Kernel launch that reports its own error (no reliance on the sticky
+// last-error state, which other libraries in the process also use).
+template <class Arg>
+inline hipError_t launch_kernel(const void* kernel, unsigned grid, unsigned block, hipStream_t s,
+                                const Arg& arg) {
+  void* args[] = {const_cast<Arg*>(&arg)};
+  return hipLaunchKernel(kernel, dim3(grid), dim3(block), args, 0, s);
+}
+
+}  // namespace gdn

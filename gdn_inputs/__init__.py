@@ -21,7 +21,9 @@ recipe of the five workload configurations this library is measured on.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import List, Optional, Sequence
 
 import numpy as np
@@ -201,15 +203,34 @@ def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
     return (x / n).astype(np.float32)
 
 
+def _draw_layer(seed_seq: np.random.SeedSequence, T: int, B: int, H: int, dk: int, dv: int,
+                io: str, s0_std: float):
+    """One layer's q, k, v, alpha, beta, S0; each tensor from its own child
+    stream, so layers can be drawn in any order or in parallel."""
+    sq, sk, sv, sa, sb, ss = (np.random.Generator(np.random.PCG64(c)) for c in seed_seq.spawn(6))
+    q = _unit_rows(sq, (T, H, dk))
+    k = _unit_rows(sk, (T, H, dk))
+    v = sv.standard_normal((T, H, dv), dtype=np.float32)
+    if io == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    alpha = sa.uniform(0.9, 1.0, size=(T, H)).astype(np.float32)
+    logits = sb.standard_normal((T, H))
+    beta = (1.0 / (1.0 + np.exp(-logits))).astype(np.float32)
+    S0 = ss.standard_normal((B, H, dv, dk), dtype=np.float32)
+    S0 *= np.float32(s0_std)
+    return q, k, v, alpha, beta, S0
+
+
 def make_workload(parents_list: Sequence[Sequence[int]], H: int, dk: int, dv: int,
-                  io: str = "bf16", layers: int = 1, seed: int = 0,
+                  io: str = "bf16", layers: int = 1, seed=0,
                   accepted: Optional[Sequence[int]] = None,
-                  rng: Optional[np.random.Generator] = None,
-                  s0_std: float = 0.1) -> Workload:
-    """Draw every per-layer input for the given trees. Draw order per layer:
-    q, k, v, alpha, beta logits, S0; accepted nodes last (unless given)."""
-    if rng is None:
-        rng = np.random.Generator(np.random.PCG64(seed))
+                  s0_std: float = 0.1, threads: int = 0) -> Workload:
+    """Draw every per-layer input for the given trees.
+
+    Seeding: SeedSequence(seed) (or the SeedSequence passed as seed) spawns a
+    layer parent and an accepted-node child; the layer parent spawns one child
+    per layer, which spawns q, k, v, alpha, beta logits and S0 in that order.
+    Layer i's values therefore do not depend on how many layers are drawn."""
     parents_list = [list(map(int, p)) for p in parents_list]
     B = len(parents_list)
     sizes = [len(p) for p in parents_list]
@@ -218,26 +239,30 @@ def make_workload(parents_list: Sequence[Sequence[int]], H: int, dk: int, dv: in
     T = int(offsets[-1])
     parents = np.array([x for p in parents_list for x in p], dtype=np.int32)
     L = layers
+    root = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    layer_parent, acc_seed = root.spawn(2)
+    children = layer_parent.spawn(L)
     q = np.empty((L, T, H, dk), np.float32)
     k = np.empty((L, T, H, dk), np.float32)
     v = np.empty((L, T, H, dv), np.float32)
     alpha = np.empty((L, T, H), np.float32)
     beta = np.empty((L, T, H), np.float32)
     S0 = np.empty((L, B, H, dv, dk), np.float32)
-    for layer in range(L):
-        q[layer] = _unit_rows(rng, (T, H, dk))
-        k[layer] = _unit_rows(rng, (T, H, dk))
-        v[layer] = rng.standard_normal((T, H, dv), dtype=np.float32)
-        alpha[layer] = rng.uniform(0.9, 1.0, size=(T, H)).astype(np.float32)
-        logits = rng.standard_normal((T, H)).astype(np.float32)
-        beta[layer] = (1.0 / (1.0 + np.exp(-logits.astype(np.float64)))).astype(np.float32)
-        S0[layer] = rng.standard_normal((B, H, dv, dk), dtype=np.float32) * np.float32(s0_std)
-        if io == "bf16":
-            q[layer] = round_to_bf16(q[layer])
-            k[layer] = round_to_bf16(k[layer])
-            v[layer] = round_to_bf16(v[layer])
+
+    def one(layer):
+        q[layer], k[layer], v[layer], alpha[layer], beta[layer], S0[layer] = _draw_layer(
+            children[layer], T, B, H, dk, dv, io, s0_std)
+
+    nthreads = threads or min(L, os.cpu_count() or 1, 16)
+    if nthreads > 1:
+        with concurrent.futures.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(one, range(L)))
+    else:
+        for layer in range(L):
+            one(layer)
     if accepted is None:
-        acc = np.array([pick_accepted(rng, p) for p in parents_list], dtype=np.int32)
+        arng = np.random.Generator(np.random.PCG64(acc_seed))
+        acc = np.array([pick_accepted(arng, p) for p in parents_list], dtype=np.int32)
     else:
         acc = np.asarray(accepted, dtype=np.int32)
     return Workload(B=B, H=H, dk=dk, dv=dv, io=io, layers=L, parents_list=parents_list,
@@ -259,18 +284,13 @@ def config_trees(name: str, rng: np.random.Generator) -> List[List[int]]:
     raise ValueError(c["tree"])
 
 
-def make_config(name: str, layers: Optional[int] = None, batch: Optional[int] = None,
-                seed: Optional[int] = None) -> Workload:
-    """One of the five workload configurations. `layers`/`batch` shrink it
-    (for tests that sample); the draw order is unchanged."""
+def make_config(name: str, layers: Optional[int] = None, seed: Optional[int] = None) -> Workload:
+    """One of the five workload configurations. `layers` keeps only the first
+    layers (the values drawn for them do not change)."""
     c = CONFIGS[name]
-    rng = np.random.Generator(np.random.PCG64(c["seed"] if seed is None else seed))
-    trees = config_trees(name, rng)
-    if batch is not None:
-        trees = trees[:batch]
-    L = c["layers"] if layers is None else layers
-    # On a chain the only leaf is the last node, so "uniform leaf, then a
-    # uniform prefix length" is a uniform accepted prefix length in [1, n].
+    tree_seed, data_seed = np.random.SeedSequence(c["seed"] if seed is None else seed).spawn(2)
+    trees = config_trees(name, np.random.Generator(np.random.PCG64(tree_seed)))
     acc = [c["accepted_node"]] * len(trees) if c["accepted"] == "fixed" else None
     return make_workload(trees, H=c["H"], dk=c["dk"], dv=c["dv"], io=c["io"],
-                         layers=L, rng=rng, accepted=acc)
+                         layers=c["layers"] if layers is None else layers, seed=data_seed,
+                         accepted=acc)

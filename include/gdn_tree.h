@@ -1,0 +1,166 @@
+/*
+ * gdn_tree.h -- C ABI of libgdntree: verification of speculative draft trees
+ * through Gated DeltaNet (GDN) layers on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * A batch holds B independent sequences. Sequence b carries a draft tree of
+ * N_b nodes (1 <= N_b <= 64), flattened into one node order with the root
+ * first and a parent index per node (-1 for the root, otherwise smaller than
+ * the node's own index). The flattening with a parent index per node is the
+ * input the GDN layers receive in the fork page's verify flow
+ * (rainlin-top.pages.dev "Qwen3.5 tree spec", section 7 step 2); the -1 root
+ * convention and the root-first order are the handbook's
+ * (anrans.github.io ai-infra-handbooks "speculative", implementation section).
+ *
+ * Every node t of every head h gets the output the gated delta rule gives
+ * when run from the sequence's initial state S0 along t's own root-to-node
+ * path, and nothing else (siblings never see each other):
+ *     S_t = alpha_t S_parent (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,       S_parent = S0 for the root.
+ * (The state update formula is stripped from the fork page's section 3; this
+ * is the gated delta rule the TreeWY abstract, arxivdaily 2608.20961, builds
+ * on.) Commit then writes the state S_a of the one accepted node a per
+ * sequence (fork page section 5, rollback to the last accepted token).
+ *
+ * Two modes compute the same results:
+ *  - GDN_MODE_WY: tree-structured WY form. One unit-lower-triangular solve per
+ *    (tree, head) yields pseudo-values u_t with
+ *        S_t = G_t S0 + sum_{i in path(t)} (G_t/G_i) u_i k_i^T,
+ *        G_t = product of alpha over path(t);
+ *    verify stores only U and the gate prefixes; commit rebuilds S_a alone
+ *    (TreeWY abstract: single triangular solve, pseudo-value matrix instead
+ *    of per-node states, only the accepted state reconstructed).
+ *  - GDN_MODE_FORK: the fork/checkpoint baseline. Depth-by-depth, every node
+ *    starts from its parent's checkpoint and stores its own full state
+ *    (fork page section 4, depth-by-depth subsection); commit copies the
+ *    accepted node's checkpoint (section 5).
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ *  - Every pointer except `desc` is a DEVICE pointer owned by the caller. The
+ *    library never allocates or frees memory and never synchronises: work is
+ *    enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *    stream) and completes in stream order.
+ *  - Dense row-major layouts, T = total nodes = offsets[B]:
+ *      offsets [B+1] int32   node range of sequence b is [offsets[b], offsets[b+1])
+ *      parents [T]   int32   local parent index within the sequence, root -1
+ *      q, k    [T,H,dk]      io dtype (fp32 or bf16)
+ *      v, o    [T,H,dv]      io dtype
+ *      alpha, beta [T,H]     fp32; alpha in (0,1] (values below 2^-64 act as
+ *                            2^-64), beta in [0,1]
+ *      S0, S_out [B,H,dv,dk] fp32; S[r][c] multiplies k[c]
+ *      tree_status [B] int32 per-sequence result code (GDN_TREE_*)
+ *  - The gdn_status return value reports only host-side checks made before
+ *    anything is enqueued (null pointers, shapes, dtype, workspace size) and
+ *    launch failures. Data-dependent problems are reported per sequence in
+ *    tree_status on the device; such a sequence's output rows are zero and
+ *    its commit writes nothing.
+ *  - Calls are re-entrant; nothing is kept between calls except what the
+ *    caller's workspace holds. q, k, v, alpha, beta need no normalisation by
+ *    the library (the GDN convention of L2-normalised q, k is the caller's).
+ *  - Empty batches (num_seqs == 0) are valid and enqueue nothing.
+ */
+#ifndef GDN_TREE_H
+#define GDN_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_TREE_MAX_NODES 64
+
+/* Host-side result of every entry point. */
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL_PTR = 1,       /* a required pointer is NULL                         */
+  GDN_ERR_BAD_SHAPE = 2,      /* negative/zero sizes, max_nodes outside [1,64], ... */
+  GDN_ERR_UNSUPPORTED = 3,    /* dk/dv/io dtype/mode combination not built          */
+  GDN_ERR_WORKSPACE = 4,      /* workspace smaller than gdn_tree_workspace_bytes()  */
+  GDN_ERR_LAUNCH = 5          /* the HIP runtime refused a launch                   */
+} gdn_status;
+
+/* Element type of q, k, v and o. State, gates and accumulation are fp32. */
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
+
+typedef enum { GDN_MODE_WY = 0, GDN_MODE_FORK = 1 } gdn_mode;
+
+/* Per-sequence codes written to tree_status (checked in this order). */
+enum {
+  GDN_TREE_OK = 0,
+  GDN_TREE_BAD_ROOT = 1,      /* parents[first node] != -1                          */
+  GDN_TREE_BAD_PARENT = 2,    /* a non-root node's parent is < 0 or >= its index    */
+  GDN_TREE_BAD_SIZE = 3,      /* N_b outside [1, max_nodes] or range outside [0,T]  */
+  GDN_TREE_BAD_ACCEPTED = 4,  /* commit: accepted[b] outside [-1, N_b)              */
+  GDN_TREE_TOO_DEEP = 5       /* FORK mode: a node deeper than desc.max_depth       */
+};
+/* Precedence: BAD_SIZE, then BAD_ROOT, then BAD_PARENT, then TOO_DEEP (FORK
+ * verify) or BAD_ACCEPTED (commit). */
+
+typedef struct {
+  int32_t num_seqs;     /* B >= 0                                                   */
+  int32_t num_heads;    /* H >= 1                                                   */
+  int32_t dk, dv;       /* supported: dk == dv in {32, 64, 128}                     */
+  int32_t total_nodes;  /* T = offsets[B] (host copy; sizes outputs and workspace)  */
+  int32_t max_nodes;    /* upper bound on every N_b, in [1, 64]; sizes on-chip tiles */
+  int32_t max_depth;    /* FORK mode: number of levels - 1 to run (root = depth 0);
+                           0 or negative means max_nodes - 1. Ignored in WY mode.    */
+  int32_t io_dtype;     /* gdn_dtype                                                */
+  int32_t mode;         /* gdn_mode                                                 */
+} gdn_tree_desc;
+
+/* Bytes of speculative state a verify call leaves for its commit, i.e. the
+ * workspace size:
+ *   WY:   T*H*(dv + 1)*4 bytes -- pseudo-values U [T,H,dv] fp32, then the
+ *         base-2 gate prefixes g [T,H] fp32 (each part 256-byte aligned);
+ *   FORK: T*H*dv*dk*4 bytes    -- one fp32 checkpoint [T,H,dv,dk] per node-head.
+ * Returns 0 for an invalid descriptor. */
+size_t gdn_tree_workspace_bytes(const gdn_tree_desc* desc);
+
+/* Ancestor masks and depths of every node (handbook implementation section:
+ * tree_mask and depths; fork page section 2 mask table).
+ *   depth    [T] int32  : 0 for the root, parent's depth + 1 otherwise
+ *   anc_mask [T] uint64 : bit j set iff local node j is the node or one of its
+ *                         ancestors (row of the tree attention mask)
+ *   tree_status [B]     : GDN_TREE_OK / BAD_SIZE / BAD_ROOT / BAD_PARENT
+ * Outputs of a sequence with a nonzero status are not written (when its node
+ * range is valid they are set to depth -1 and mask 0). Mode and io dtype are
+ * ignored. */
+gdn_status gdn_tree_build(const gdn_tree_desc* desc, const int32_t* offsets,
+                          const int32_t* parents, int32_t* depth, uint64_t* anc_mask,
+                          int32_t* tree_status, void* stream);
+
+/* Verify: o [T,H,dv] for every node, and the speculative state in `workspace`
+ * (layout per gdn_tree_workspace_bytes) for the matching commit.
+ * `workspace_bytes` is the size of the caller's buffer. o must not alias any
+ * input. tree_status receives the GDN_TREE_* code of every sequence. */
+gdn_status gdn_tree_verify(const gdn_tree_desc* desc, const int32_t* offsets,
+                           const int32_t* parents, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta,
+                           const float* S0, void* o, void* workspace, size_t workspace_bytes,
+                           int32_t* tree_status, void* stream);
+
+/* Commit: for every sequence b, S_out[b] = state of local node accepted[b]
+ * (the last node of the accepted root-to-node path), or S0[b] when
+ * accepted[b] == -1. S_out may equal S0 (in place); partial overlap is not
+ * allowed. `workspace` is the one written by gdn_tree_verify with the same
+ * descriptor, inputs and mode, and must not have been modified since. WY mode
+ * also reads k and the same offsets/parents (k may be NULL in FORK mode);
+ * FORK mode ignores k. tree_status receives the GDN_TREE_* code of every
+ * sequence; sequences with a nonzero code are left unwritten. */
+gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
+                           const int32_t* parents, const int32_t* accepted, const void* k,
+                           const float* S0, float* S_out, const void* workspace,
+                           size_t workspace_bytes, int32_t* tree_status, void* stream);
+
+/* Static text for a gdn_status value. */
+const char* gdn_tree_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_TREE_H */

@@ -1,0 +1,346 @@
+"""GPU parity of libgdntree against the CPU oracle, through the C ABI.
+
+Agreement bar: ancestor masks, depths and status codes bit-exact; node outputs
+and committed states within 1e-4 (fp32 io) or 2e-2 (bf16 io) normwise
+relative error per vector / per (sequence, head) state."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_tree_02_amd as gt
+import gdn_inputs as gi
+import oracle
+from oracle import wy
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # the -m gpu suite only runs on a GPU machine
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_util import (TOL, DeviceLayer, i32, oracle_layer, rel_err_rows,  # noqa: E402
+                      rel_err_states, sub_workload)
+
+
+def _say(*a):
+    print("[gpu-parity]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ tree build
+
+
+def _build_on_gpu(offsets, parents, max_nodes=64):
+    B, T = len(offsets) - 1, len(parents)
+    desc = gt.make_desc(B, 1, 32, 32, T, max_nodes)
+    depth = torch.full((T,), -9, dtype=torch.int32, device="cuda")
+    anc = torch.zeros((T,), dtype=torch.int64, device="cuda")
+    st = torch.full((B,), -9, dtype=torch.int32, device="cuda")
+    gt.gdn_tree_build(desc, i32(offsets), i32(parents), depth, anc, st)
+    return depth.cpu().numpy(), anc.cpu().numpy().view(np.uint64), st.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_tree_build_configs_bit_exact(name):
+    _say("tree_build", name)
+    w = gi.make_config(name, layers=1)
+    d, a, s = _build_on_gpu(w.offsets, w.parents)
+    rd, ra, rs = oracle.tree(w.offsets, w.parents)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(d, rd)
+    np.testing.assert_array_equal(a, ra)
+
+
+def test_tree_build_random_orders_and_errors():
+    rng = np.random.default_rng(30)
+    trees = []
+    for _ in range(40):
+        n = int(rng.integers(1, 65))
+        trees.append([-1] + [int(rng.integers(0, i)) for i in range(1, n)])   # any topological order
+    trees.append(gi.chain_parents(64))
+    trees.append([0, 0, 1])          # bad root
+    trees.append([-1, 1, 0])         # bad parent
+    trees.append([-1, 0, -1])        # second root
+    sizes = [len(t) for t in trees]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    parents = np.concatenate([np.array(t, np.int32) for t in trees])
+    d, a, s = _build_on_gpu(offsets, parents)
+    rd, ra, rs = oracle.tree(offsets, parents)
+    np.testing.assert_array_equal(s, rs)
+    ok = np.repeat(rs == 0, sizes)
+    np.testing.assert_array_equal(d[ok], rd[ok])
+    np.testing.assert_array_equal(a[ok], ra[ok])
+    assert np.all(d[~ok] == -1) and np.all(a[~ok] == 0)
+    # sizes: a tree larger than max_nodes, an empty range, then a valid tree
+    d, a, s = _build_on_gpu(np.array([0, 5, 5, 9], np.int32), np.array([-1, 0, 0, 1, 1, -1, 0, 1, 2], np.int32), 4)
+    assert s.tolist() == [3, 3, 0]
+
+
+# ------------------------------------------------------------ WY verify + commit
+
+
+def _check_layer(w, layer=0, mode=gt.MODE_WY, max_depth=0, check_wy_parts=False):
+    dl = DeviceLayer(w, layer, mode=mode, max_depth=max_depth)
+    dl.verify()
+    dl.commit()
+    torch.cuda.synchronize()
+    o_ref, st_ref, S_ref, stc_ref = oracle_layer(w, layer)
+    st = dl.status.cpu().numpy()
+    np.testing.assert_array_equal(st, stc_ref)
+    e_o = rel_err_rows(dl.o_np(), o_ref)
+    e_s = rel_err_states(dl.S_out.cpu().numpy(), S_ref)
+    _say(f"B={w.B} H={w.H} d={w.dk} io={w.io} T={w.T} mode={mode}: o err {e_o:.3e}, S err {e_s:.3e}")
+    tol = TOL[w.io]
+    assert e_o <= tol and e_s <= tol, (e_o, e_s)
+    if check_wy_parts:
+        U, g2 = dl.wy_parts()
+        Ow, Uw, gw = wy.wy_batch(w.offsets, w.parents, w.q[layer], w.k[layer], w.v[layer],
+                                 w.alpha[layer], w.beta[layer], w.S0[layer])
+        e_u = rel_err_rows(U, Uw)
+        e_g = float(np.max(np.abs(g2 * np.log(2.0) - gw)))
+        _say(f"  U err {e_u:.3e}, gate-prefix abs err {e_g:.3e}")
+        assert e_u <= tol and e_g <= 1e-5
+    return dl
+
+
+def test_c1_tiny_fp32():
+    w = gi.make_config("c1")
+    _check_layer(w, check_wy_parts=True)
+
+
+def test_c2_chain():
+    w = gi.make_config("c2")
+    _check_layer(w, check_wy_parts=True)
+    # chain: every accepted prefix equals the sequential recurrence of its tokens
+    for L in range(1, 7):
+        w.accepted[:] = L - 1
+        _check_layer(w)
+
+
+def test_c3_kary_tree():
+    w = gi.make_config("c3")
+    _check_layer(w, check_wy_parts=True)
+
+
+def test_c4_full_size_sampled():
+    """All 24 layers x 64 sequences on the GPU in the benchmark's launch
+    configuration; the oracle recomputes a sample of (layer, sequence) units."""
+    w = gi.make_config("c4")
+    rng = np.random.default_rng(40)
+    layers = sorted(rng.choice(24, 3, replace=False).tolist())
+    seqs = sorted(rng.choice(64, 6, replace=False).tolist())
+    for layer in layers:
+        dl = DeviceLayer(w, layer)
+        dl.verify()
+        dl.commit()
+        torch.cuda.synchronize()
+        assert np.all(dl.status.cpu().numpy() == 0)
+        sub = sub_workload(w, seqs, layers=[layer])
+        o_ref, _, S_ref, _ = oracle_layer(sub, 0)
+        rows = np.concatenate([np.arange(w.offsets[b], w.offsets[b + 1]) for b in seqs])
+        e_o = rel_err_rows(dl.o_np()[rows], o_ref)
+        e_s = rel_err_states(dl.S_out.cpu().numpy()[seqs], S_ref)
+        _say(f"c4 layer {layer} seqs {seqs}: o err {e_o:.3e}, S err {e_s:.3e}")
+        assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+        assert np.all(np.isfinite(dl.o_np())) and np.all(np.isfinite(dl.S_out.cpu().numpy()))
+
+
+def test_c5_ragged_full_size_sampled():
+    w = gi.make_config("c5")
+    dl = DeviceLayer(w, 0)
+    dl.verify()
+    dl.commit()
+    torch.cuda.synchronize()
+    assert np.all(dl.status.cpu().numpy() == 0)
+    rng = np.random.default_rng(50)
+    # the largest and smallest trees plus a random sample
+    sizes = np.diff(w.offsets)
+    seqs = sorted(set([int(np.argmax(sizes)), int(np.argmin(sizes))] +
+                      rng.choice(w.B, 14, replace=False).tolist()))
+    sub = sub_workload(w, seqs)
+    o_ref, _, S_ref, _ = oracle_layer(sub, 0)
+    rows = np.concatenate([np.arange(w.offsets[b], w.offsets[b + 1]) for b in seqs])
+    e_o = rel_err_rows(dl.o_np()[rows], o_ref)
+    e_s = rel_err_states(dl.S_out.cpu().numpy()[seqs], S_ref)
+    _say(f"c5 seqs {len(seqs)} (sizes {sizes.min()}..{sizes.max()}): o err {e_o:.3e}, S err {e_s:.3e}")
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+    assert np.all(np.isfinite(dl.o_np()))
+
+
+@pytest.mark.parametrize("d,io", [(32, "bf16"), (64, "bf16"), (64, "f32"), (128, "f32")])
+def test_other_shapes_ragged(d, io):
+    rng = np.random.default_rng(60 + d)
+    trees = [gi.random_tree_parents(rng, 1, 64, 8, 3) for _ in range(10)]
+    w = gi.make_workload(trees, H=3, dk=d, dv=d, io=io, seed=61 + d)
+    _check_layer(w, check_wy_parts=True)
+
+
+def test_max_nodes_chain_and_single_nodes():
+    trees = [gi.chain_parents(64), [-1], gi.kary_parents(2, 5)[:63], [-1, 0], gi.chain_parents(17)]
+    w = gi.make_workload(trees, H=2, dk=128, dv=128, io="bf16", seed=70,
+                         accepted=[63, 0, 40, -1, 16])
+    dl = _check_layer(w)
+    # accepted = -1 keeps S0 bit for bit
+    np.testing.assert_array_equal(dl.S_out.cpu().numpy()[3], w.S0[0][3])
+
+
+def test_gate_edge_values():
+    trees = [gi.kary_parents(2, 3), gi.chain_parents(9)]
+    w = gi.make_workload(trees, H=4, dk=128, dv=128, io="bf16", seed=71)
+    w.alpha[0][:, 0] = 1.0          # no decay
+    w.beta[0][:, 1] = 0.0           # no write: pure decay
+    w.beta[0][:, 2] = 1.0           # full overwrite
+    w.alpha[0][:, 3] = 0.05         # strong decay
+    _check_layer(w)
+
+
+# ------------------------------------------------------------------ FORK mode
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_fork_mode(name):
+    w = gi.make_config(name)
+    dl = _check_layer(w, mode=gt.MODE_FORK, max_depth=w.max_depth())
+    if name == "c1":
+        _, ck, _ = oracle.fork_replay(w.offsets, w.parents, w.q[0], w.k[0], w.v[0],
+                                      w.alpha[0], w.beta[0], w.S0[0])
+        got = dl.ws.cpu().numpy()[:ck.size * 4].view(np.float32).reshape(ck.shape)
+        e = rel_err_states(got.reshape(-1, 1, *ck.shape[2:]), ck.reshape(-1, 1, *ck.shape[2:]))
+        _say(f"c1 checkpoints err {e:.3e}")
+        assert e <= TOL["f32"]
+
+
+def test_fork_mode_c4_layer_and_wy_agree():
+    w = gi.make_config("c4", layers=1)
+    dw = DeviceLayer(w, 0, mode=gt.MODE_WY)
+    df = DeviceLayer(w, 0, mode=gt.MODE_FORK, max_depth=3)
+    for dl in (dw, df):
+        dl.verify()
+        dl.commit()
+    torch.cuda.synchronize()
+    e_o = rel_err_rows(df.o_np(), dw.o_np())
+    e_s = rel_err_states(df.S_out.cpu().numpy(), dw.S_out.cpu().numpy())
+    _say(f"c4 WY vs FORK on GPU: o {e_o:.3e}, S {e_s:.3e}")
+    assert e_o <= TOL["bf16"] and e_s <= 1e-4
+    seqs = [0, 17, 63]
+    sub = sub_workload(w, seqs)
+    o_ref, _, S_ref, _ = oracle_layer(sub, 0)
+    rows = np.concatenate([np.arange(w.offsets[b], w.offsets[b + 1]) for b in seqs])
+    assert rel_err_rows(df.o_np()[rows], o_ref) <= TOL["bf16"]
+    assert rel_err_states(df.S_out.cpu().numpy()[seqs], S_ref) <= TOL["bf16"]
+
+
+def test_fork_too_deep_status():
+    w = gi.make_workload([gi.chain_parents(8), gi.kary_parents(2, 2)], H=2, dk=32, dv=32,
+                         io="f32", seed=80)
+    dl = DeviceLayer(w, 0, mode=gt.MODE_FORK, max_depth=3)
+    dl.verify()
+    torch.cuda.synchronize()
+    assert dl.status.cpu().numpy().tolist() == [5, 0]
+    o = dl.o_np()
+    assert np.all(o[:8] == 0)
+
+
+# ------------------------------------------------------------- isolation, aliasing, errors
+
+
+def test_sibling_perturbation_bit_identical_on_gpu():
+    parents = gi.kary_parents(3, 2) + [4, 4, 12]
+    M = wy.ancestor_matrix(parents)
+    base = gi.make_workload([parents] * 2, H=2, dk=128, dv=128, io="bf16", seed=90)
+    d0 = DeviceLayer(base)
+    d0.verify()
+    o0 = d0.o_np()
+    rng = np.random.default_rng(91)
+    for j in (1, 4, 12):
+        w = gi.make_workload([parents] * 2, H=2, dk=128, dv=128, io="bf16", seed=90)
+        for arr in (w.q, w.k, w.v):
+            arr[0][j] = gi.round_to_bf16(arr[0][j] + rng.standard_normal(arr[0][j].shape).astype(np.float32))
+        w.alpha[0][j] *= np.float32(0.5)
+        d1 = DeviceLayer(w)
+        d1.verify()
+        o1 = d1.o_np()
+        sub = M[:, j]
+        n = len(parents)
+        np.testing.assert_array_equal(o1[:n][~sub], o0[:n][~sub])
+        np.testing.assert_array_equal(o1[n:], o0[n:])
+        assert np.all(np.abs(o1[:n][sub] - o0[:n][sub]).max(axis=-1) > 0)
+
+
+def test_inplace_commit_matches_out_of_place():
+    w = gi.make_config("c3")
+    dl = DeviceLayer(w)
+    dl.verify()
+    dl.commit()
+    ref = dl.S_out.clone()
+    inplace = dl.S0.clone()
+    gt.gdn_tree_commit(dl.desc, dl.offsets, dl.parents, dl.accepted, dl.k, inplace, inplace,
+                       dl.ws, dl.status)
+    torch.cuda.synchronize()
+    assert torch.equal(inplace, ref)
+    df = DeviceLayer(w, mode=gt.MODE_FORK, max_depth=3)
+    df.verify()
+    inplace = df.S0.clone()
+    gt.gdn_tree_commit(df.desc, df.offsets, df.parents, df.accepted, None, inplace, inplace,
+                       df.ws, df.status)
+    df.commit()
+    torch.cuda.synchronize()
+    assert torch.equal(inplace, df.S_out)
+
+
+def test_status_codes_and_untouched_outputs():
+    trees = [gi.kary_parents(2, 2), [0, 0, 1], [-1, 0, 2], gi.chain_parents(5), gi.kary_parents(2, 2)]
+    w = gi.make_workload(trees, H=2, dk=64, dv=64, io="bf16", seed=100,
+                         accepted=[2, 1, 1, 9, -2])
+    dl = DeviceLayer(w, max_nodes=7)
+    dl.verify()
+    torch.cuda.synchronize()
+    st_v = dl.status.cpu().numpy()
+    _, st_ref = oracle.verify(w.offsets, w.parents, w.q[0], w.k[0], w.v[0], w.alpha[0],
+                              w.beta[0], w.S0[0], max_nodes=7)
+    np.testing.assert_array_equal(st_v, st_ref)
+    assert st_v.tolist() == [0, 1, 2, 0, 0]
+    o = dl.o_np()
+    assert np.all(o[7:13] == 0)
+    marker = torch.full_like(dl.S0, 3.0)
+    gt.gdn_tree_commit(dl.desc, dl.offsets, dl.parents, dl.accepted, dl.k, dl.S0, marker,
+                       dl.ws, dl.status)
+    torch.cuda.synchronize()
+    st_c = dl.status.cpu().numpy()
+    _, stc_ref = oracle.commit(w.offsets, w.parents, w.accepted, w.k[0], w.v[0], w.alpha[0],
+                               w.beta[0], w.S0[0], max_nodes=7)
+    np.testing.assert_array_equal(st_c, stc_ref)
+    assert st_c.tolist() == [0, 1, 2, 4, 4]
+    m = marker.cpu().numpy()
+    assert np.all(m[1:] == 3.0)
+
+
+def test_bad_offsets_and_oversize():
+    w = gi.make_workload([gi.kary_parents(2, 2), gi.kary_parents(2, 3)], H=1, dk=32, dv=32,
+                         io="f32", seed=110)
+    dl = DeviceLayer(w, max_nodes=8)           # the 15-node tree exceeds max_nodes
+    dl.verify()
+    torch.cuda.synchronize()
+    assert dl.status.cpu().numpy().tolist() == [0, 3]
+    dl.offsets = i32([0, 7, 40])               # range past T
+    dl.verify()
+    torch.cuda.synchronize()
+    assert dl.status.cpu().numpy().tolist() == [0, 3]
+
+
+def test_empty_batch_and_empty_tree():
+    desc = gt.make_desc(0, 16, 128, 128, 0, 8)
+    e = torch.empty(0, device="cuda")
+    gt.gdn_tree_verify(desc, i32([0]), torch.empty(0, dtype=torch.int32, device="cuda"),
+                       e.bfloat16().view(0, 16, 128), e.bfloat16().view(0, 16, 128),
+                       e.bfloat16().view(0, 16, 128), e.view(0, 16), e.view(0, 16),
+                       e.view(0, 16, 128, 128), e.bfloat16().view(0, 16, 128),
+                       torch.empty(0, dtype=torch.uint8, device="cuda"),
+                       torch.empty(0, dtype=torch.int32, device="cuda"))
+    # one sequence with no nodes: status bad size, nothing else touched
+    desc = gt.make_desc(1, 2, 32, 32, 0, 8, gt.DTYPE_F32)
+    S0 = torch.randn(1, 2, 32, 32, device="cuda")
+    st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    gt.gdn_tree_verify(desc, i32([0, 0]), torch.empty(0, dtype=torch.int32, device="cuda"),
+                       e.view(0, 2, 32), e.view(0, 2, 32), e.view(0, 2, 32), e.view(0, 2), e.view(0, 2),
+                       S0, e.view(0, 2, 32), torch.empty(0, dtype=torch.uint8, device="cuda"), st)
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [3]

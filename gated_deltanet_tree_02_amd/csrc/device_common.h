@@ -147,6 +147,28 @@ __device__ __forceinline__ TreeLane load_tree(int b, int T, int max_nodes,
   return tl;
 }
 
+// Pointer jumping over already-loaded parents (lane t holds parent(t), -1 for
+// the root, lanes >= n hold -1): visible set and the sum of x over the path
+// (x = 0 on lanes >= n). Six rounds cover depths below 64.
+__device__ __forceinline__ void path_scan(int par, int lane, int n, float x, uint64_t& anc,
+                                          float& sum) {
+  anc = lane < n ? (1ull << lane) : 0ull;
+  sum = x;
+  int jmp = lane < n ? par : -1;
+#pragma unroll
+  for (int it = 0; it < 6; ++it) {
+    const int src = jmp < 0 ? lane : jmp;
+    const uint64_t a2 = shfl_u64(anc, src);
+    const float s2 = __shfl(sum, src, kWave);
+    const int j2 = __shfl(jmp, src, kWave);
+    if (jmp >= 0) {
+      anc |= a2;
+      sum += s2;
+      jmp = j2;
+    }
+  }
+}
+
 // Sum of x over each lane's path, in increasing node order (root first):
 // every lane reads node j's value by a shuffle and keeps it when j is on its
 // path. n is the (wave-uniform) node count.

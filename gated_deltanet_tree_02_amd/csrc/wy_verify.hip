@@ -13,20 +13,22 @@
 // multiply), so siblings never see each other (fork page, section 2 mask;
 // section 4 isolation of branches).
 //
-// Work split:
-//  * tree prologue: one lane per node, ancestor bitmasks by pointer jumping,
-//    base-2 gate prefixes g2 (G_t = 2^g2_t) summed along each path;
-//  * q and k staged in LDS; A_kk and A_qk as 16x16 tiles of
-//    v_mfma_f32_16x16x32_bf16 over the lower triangle of node tiles;
-//  * the state products X = K S0^T and Y = Q S0^T on MFMA. S0 is fp32 and is
-//    streamed from HBM straight into MFMA operand registers (each wave owns
-//    32 rows of S0), split into bf16 hi + lo parts so that the product keeps
-//    about 16 significant bits of S0 at bf16 MFMA rate (fp32 io also splits
-//    q and k);
-//  * R = diag(beta)(V - diag(G) X) into LDS, then a per-column forward
-//    substitution over the ancestor lists (at most depth(t) terms per row);
-//  * o_t = G_t Y_t + sum_{i in A(t)} A_qk[t,i] u_i, written in io precision;
-//    U and g2 are written to the workspace for the commit kernel.
+// Schedule of one workgroup:
+//  1. issue every global read up front: parents and gates, q and k rows
+//     (16-byte chunks, stored to LDS with an XOR swizzle so that MFMA operand
+//     reads are bank-conflict free), v in the MFMA result layout, and this
+//     wave's 32 rows of S0 straight into MFMA operand registers.
+//  2. wave 0: tree prologue by pointer jumping (ancestor sets, depths, base-2
+//     gate prefixes g2 with G_t = 2^g2_t).
+//  3. A_kk and A_qk as 16x16 tiles of v_mfma_f32_16x16x32_bf16 over the lower
+//     triangle of node tiles, masked and decayed.
+//  4. X = K S0^T and Y = Q S0^T on MFMA: S0 is fp32 and is split into bf16
+//     hi + lo parts (about 16 significant bits) at bf16 MFMA rate; fp32 io
+//     also splits q and k.
+//  5. R = diag(beta)(V - diag(G) X) in registers, then the solve level by
+//     level (all nodes of one depth at once; a node at depth l has exactly l
+//     proper ancestors), each wave on its own dv columns, pseudo-values in LDS.
+//  6. o_t = G_t Y_t + sum_{i in A(t)} A_qk[t,i] u_i; o, U and g2 to memory.
 #include <type_traits>
 
 #include "device_common.h"
@@ -48,49 +50,69 @@ __device__ __forceinline__ void split_hi_lo(const float (&f)[8], bf16x8& hi, bf1
   }
 }
 
-// An MFMA operand fragment of 8 consecutive k-elements of one staged row.
-template <class IO> struct Frag;
+// Staged q/k rows: row-major 16-byte chunks, chunk c of row r stored at
+// position c ^ (r mod chunks-per-row).
+template <int CPR>
+__device__ __forceinline__ int chunk_slot(int row, int c) {
+  return row * CPR + (c ^ (row & (CPR - 1)));
+}
 
-template <> struct Frag<uint16_t> {
+// MFMA operand fragment = 8 consecutive k-elements of one staged row
+// (k-step s, lane group g = lane/16 -> elements 32s + 8g .. +7).
+template <class IO, int CPR> struct Frag;
+
+template <int CPR> struct Frag<uint16_t, CPR> {
   bf16x8 hi;
-  __device__ __forceinline__ void load(const uint16_t* p) {
-    hi = *reinterpret_cast<const bf16x8*>(p);
+  __device__ __forceinline__ void load(const uint4* rows, int row, int s, int g) {
+    hi = __builtin_bit_cast(bf16x8, rows[chunk_slot<CPR>(row, 4 * s + g)]);
   }
 };
 
-template <> struct Frag<float> {
+template <int CPR> struct Frag<float, CPR> {
   bf16x8 hi, lo;
-  __device__ __forceinline__ void load(const float* p) {
-    const float4 x = *reinterpret_cast<const float4*>(p);
-    const float4 y = *reinterpret_cast<const float4*>(p + 4);
+  __device__ __forceinline__ void load(const uint4* rows, int row, int s, int g) {
+    const float4 x = __builtin_bit_cast(float4, rows[chunk_slot<CPR>(row, 8 * s + 2 * g)]);
+    const float4 y = __builtin_bit_cast(float4, rows[chunk_slot<CPR>(row, 8 * s + 2 * g + 1)]);
     const float f[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
     split_hi_lo(f, hi, lo);
   }
 };
 
-// acc += A * B for operands held as fragments (bf16: one product; fp32: the
-// four hi/lo cross products).
-__device__ __forceinline__ f32x4 mma(const Frag<uint16_t>& a, const Frag<uint16_t>& b, f32x4 acc) {
+// acc += A * B (bf16: one product; fp32: the four hi/lo cross products).
+template <int CPR>
+__device__ __forceinline__ f32x4 mma(const Frag<uint16_t, CPR>& a, const Frag<uint16_t, CPR>& b,
+                                     f32x4 acc) {
   return mfma16(a.hi, b.hi, acc);
 }
-__device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 acc) {
+template <int CPR>
+__device__ __forceinline__ f32x4 mma(const Frag<float, CPR>& a, const Frag<float, CPR>& b,
+                                     f32x4 acc) {
   acc = mfma16(a.hi, b.hi, acc);
   acc = mfma16(a.hi, b.lo, acc);
   acc = mfma16(a.lo, b.hi, acc);
   return mfma16(a.lo, b.lo, acc);
 }
 // S0 fragment (hi, lo) times a staged fragment.
+template <int CPR>
 __device__ __forceinline__ f32x4 mma_state(const bf16x8& shi, const bf16x8& slo,
-                                           const Frag<uint16_t>& b, f32x4 acc) {
+                                           const Frag<uint16_t, CPR>& b, f32x4 acc) {
   acc = mfma16(shi, b.hi, acc);
   return mfma16(slo, b.hi, acc);
 }
+template <int CPR>
 __device__ __forceinline__ f32x4 mma_state(const bf16x8& shi, const bf16x8& slo,
-                                           const Frag<float>& b, f32x4 acc) {
+                                           const Frag<float, CPR>& b, f32x4 acc) {
   acc = mfma16(shi, b.hi, acc);
   acc = mfma16(shi, b.lo, acc);
   acc = mfma16(slo, b.hi, acc);
   return mfma16(slo, b.lo, acc);
+}
+
+__device__ __forceinline__ void fma4(float4& acc, float c, const float4& u) {
+  acc.x += c * u.x;
+  acc.y += c * u.y;
+  acc.z += c * u.z;
+  acc.w += c * u.w;
 }
 
 template <class IO, int DK, int DV, int MT>
@@ -100,17 +122,17 @@ __global__ __launch_bounds__(256) void wy_verify_kernel(const VerifyArgs a) {
   constexpr int KS = DK / 32;                 // MFMA k-steps over dk
   constexpr int DVT = DV / 16;                // 16-row tiles of S0 (dv direction)
   constexpr int TPW = (DVT + NW - 1) / NW;    // S0 tiles per wave
-  constexpr int KPAD = 16 / (int)sizeof(IO);  // 16-byte row padding against bank conflicts
-  constexpr int KROW = DK + KPAD;             // staged q/k row, elements
+  constexpr int EPC = 16 / (int)sizeof(IO);   // io elements per 16-byte chunk
+  constexpr int CPR = DK / EPC;               // chunks per staged q/k row
   constexpr int UROW = DV + 4;                // U row, floats
   constexpr int AROW = NP + 1;                // A_kk / A_qk row, floats
-  constexpr int EPC = 16 / (int)sizeof(IO);   // elements per 16-byte chunk
-  constexpr int CPR = DK / EPC;               // chunks per q/k row
   using io = io_traits<IO>;
+  static_assert(NP * CPR % 64 == 0, "q/k staging must be whole 1 KiB transfers");
+  static_assert(DVT % NW == 0 || TPW == 1, "every wave with S0 rows owns whole tiles");
 
   struct KQ {
-    IO k[NP * KROW];
-    IO q[NP * KROW];
+    uint4 k[NP * CPR];
+    uint4 q[NP * CPR];
   };
   union SMem {
     KQ kq;
@@ -126,6 +148,8 @@ __global__ __launch_bounds__(256) void wy_verify_kernel(const VerifyArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  const int g = lane >> 4;      // lane group of an MFMA operand / result
+  const int l16 = lane & 15;
   const int bh = blockIdx.x;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
@@ -135,86 +159,116 @@ __global__ __launch_bounds__(256) void wy_verify_kernel(const VerifyArgs a) {
   const IO* __restrict__ v = static_cast<const IO*>(a.v);
   IO* __restrict__ o = static_cast<IO*>(a.o);
 
-  // ---- 1. Put this wave's share of S0 in flight first: rows 16*jt + (lane%16),
-  // columns 32*s + 8*(lane/16) .. +7 -- exactly the MFMA A-operand fragments.
+  // ---- node range (uniform, scalar loads)
+  const int lo = a.offsets[b];
+  const int hi = a.offsets[b + 1];
+  if (lo < 0 || hi > a.T || hi - lo < 1 || hi - lo > a.max_nodes) {
+    if (h == 0 && tid == 0) a.status[b] = GDN_TREE_BAD_SIZE;
+    return;
+  }
+  const int n = hi - lo;
+  const int mt = (n + 15) >> 4;
+
+  // Every global read of the workgroup is issued here, before any of it is
+  // used (addresses clamped into the sequence, so the issue is unconditional):
+  // one memory round trip for all of q, k, v, the gates and S0.
+
+  // ---- 1a. parents and gates (one lane per node; lanes >= n read node 0)
+  const int nl = lane < n ? lane : 0;
+  const size_t gl = (size_t)(lo + nl) * H + h;
+  const int par_raw = a.parents[lo + nl];
+  const float alpha_l = a.alpha[gl];
+  const float beta_raw = a.beta[gl];
+
+  // ---- 1b. k and q rows into registers, 16-byte chunks (stored to LDS once
+  // the tree prologue is done). Rows past the last node repeat row n-1:
+  // finite values whose products land only in result rows/columns that are
+  // never used.
+  constexpr int NKQ = (2 * NP * CPR + 255) / 256;  // chunks per thread (k and q; a spare
+                                                   // one repeats the last chunk)
+  uint4 kq[NKQ];
+#pragma unroll
+  for (int it = 0; it < NKQ; ++it) {
+    const int idx = min(tid + 256 * it, 2 * NP * CPR - 1);
+    const int which = idx >= NP * CPR;
+    const int slot = idx - which * NP * CPR;
+    const int row = slot / CPR;
+    const int c = slot - row * CPR;
+    const int srow = row < n ? row : n - 1;
+    kq[it] = *reinterpret_cast<const uint4*>((which ? q : k) + ((size_t)(lo + srow) * H + h) * DK +
+                                             c * EPC);
+  }
+
+  // ---- 1c. v in the result layout: node t = 16m + lane%16, dv r = 16jt + 4g + 0..3
+  const int jt0 = min(wave * TPW, DVT - TPW);      // waves without a tile of their own repeat one
+  float4 vreg[TPW][MT];
+#pragma unroll
+  for (int jj = 0; jj < TPW; ++jj)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int t = min(16 * m + l16, n - 1);
+      vreg[jj][m] = io::load4(v + ((size_t)(lo + t) * H + h) * DV + 16 * (jt0 + jj) + 4 * g);
+    }
+
+  // ---- 1d. this wave's S0 rows 16jt + lane%16, columns 32s + 8g .. +7
   const float* __restrict__ S0bh = a.S0 + (size_t)bh * DV * DK;
   float4 sraw[TPW][KS][2];
 #pragma unroll
   for (int jj = 0; jj < TPW; ++jj) {
-    const int jt = wave * TPW + jj;
-    if (jt < DVT) {
-      const float* rowp = S0bh + (size_t)(16 * jt + (lane & 15)) * DK + 8 * (lane >> 4);
+    const float* rowp = S0bh + (size_t)(16 * (jt0 + jj) + l16) * DK + 8 * g;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        sraw[jj][s][0] = *reinterpret_cast<const float4*>(rowp + 32 * s);
-        sraw[jj][s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
-      }
+    for (int s = 0; s < KS; ++s) {
+      sraw[jj][s][0] = *reinterpret_cast<const float4*>(rowp + 32 * s);
+      sraw[jj][s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
     }
   }
 
-  // ---- 2. Tree of sequence b (every wave holds it; wave 0 publishes it).
-  const TreeLane tl = load_tree(b, a.T, a.max_nodes, a.offsets, a.parents, lane);
-  if (tl.status != GDN_TREE_OK) {
-    if (tl.status != GDN_TREE_BAD_SIZE) {
-      const int n = tl.n, lo = tl.lo;
-      for (int idx = tid; idx < n * (DV / 4); idx += 256) {
-        const int t = idx / (DV / 4);
-        const int r = 4 * (idx - t * (DV / 4));
-        const size_t row = ((size_t)(lo + t) * H + h) * DV + r;
-        io::store4(o + row, make_float4(0.f, 0.f, 0.f, 0.f));
-        *reinterpret_cast<float4*>(a.U + row) = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      for (int t = tid; t < n; t += 256) a.g2[(size_t)(lo + t) * H + h] = 0.f;
-    }
-    if (h == 0 && tid == 0) a.status[b] = tl.status;
-    return;
+  // ---- 2. q/k chunks to LDS (waits for them only), then the tree prologue,
+  // computed by every wave so that no branch separates the loads from their
+  // first use.
+#pragma unroll
+  for (int it = 0; it < NKQ; ++it) {
+    const int idx = min(tid + 256 * it, 2 * NP * CPR - 1);
+    const int which = idx >= NP * CPR;
+    const int slot = idx - which * NP * CPR;
+    const int row = slot / CPR;
+    (which ? sm.kq.q : sm.kq.k)[chunk_slot<CPR>(row, slot - row * CPR)] = kq[it];
   }
-  const int n = tl.n;
-  const int lo = tl.lo;
-  const int mt = (n + 15) >> 4;
-
-  float beta_l = 0.f, l2a = 0.f;
-  if (lane < n) {
-    const size_t gi = (size_t)(lo + lane) * H + h;
-    l2a = gate_log2(a.alpha[gi]);
-    beta_l = a.beta[gi];
-  }
-  const float g2_l = path_sum(tl.anc, l2a, n);
+  const int par = lane < n ? par_raw : -1;
+  const float beta_l = lane < n ? beta_raw : 0.f;
+  int st = GDN_TREE_OK;
+  if (__shfl(par, 0, kWave) != -1)
+    st = GDN_TREE_BAD_ROOT;
+  else if (__ballot(lane >= 1 && lane < n && (par < 0 || par >= lane)) != 0ull)
+    st = GDN_TREE_BAD_PARENT;
+  uint64_t anc;
+  float g2;
+  // (on a bad tree the scan still terminates; its results are not used)
+  path_scan(par, lane, n, lane < n ? gate_log2(alpha_l) : 0.f, anc, g2);
+  int maxd = lane < n ? __popcll(anc) - 1 : 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) maxd = max(maxd, __shfl_xor(maxd, off, kWave));
   if (wave == 0) {
-    sAnc[lane] = tl.anc;
-    sG2[lane] = g2_l;
+    sAnc[lane] = anc;
+    sG2[lane] = g2;
     sBeta[lane] = beta_l;
   }
-
-  // ---- 3. Stage k and q rows (zero rows up to the tile edge).
-  for (int idx = tid; idx < 2 * 16 * mt * CPR; idx += 256) {
-    const int which = idx >= 16 * mt * CPR;
-    const int rem = idx - which * 16 * mt * CPR;
-    const int row = rem / CPR;
-    const int ch = rem - row * CPR;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (row < n)
-      val = *reinterpret_cast<const uint4*>((which ? q : k) + ((size_t)(lo + row) * H + h) * DK +
-                                            ch * EPC);
-    *reinterpret_cast<uint4*>((which ? sm.kq.q : sm.kq.k) + row * KROW + ch * EPC) = val;
-  }
-
-  // ---- 4. v in the output layout: node t = 16m + lane%16, dv r = 16jt + 4*(lane/16) + 0..3.
-  float4 vreg[TPW][MT];
-#pragma unroll
-  for (int jj = 0; jj < TPW; ++jj) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      vreg[jj][m] = make_float4(0.f, 0.f, 0.f, 0.f);
-      const int jt = wave * TPW + jj;
-      const int t = 16 * m + (lane & 15);
-      if (jt < DVT && m < mt && t < n)
-        vreg[jj][m] = io::load4(v + ((size_t)(lo + t) * H + h) * DV + 16 * jt + 4 * (lane >> 4));
-    }
-  }
   __syncthreads();
+  const int status = st;
+  if (status != GDN_TREE_OK) {
+    for (int idx = tid; idx < n * (DV / 4); idx += 256) {
+      const int t = idx / (DV / 4);
+      const int r = 4 * (idx - t * (DV / 4));
+      const size_t row = ((size_t)(lo + t) * H + h) * DV + r;
+      io::store4(o + row, make_float4(0.f, 0.f, 0.f, 0.f));
+      *reinterpret_cast<float4*>(a.U + row) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int t = tid; t < n; t += 256) a.g2[(size_t)(lo + t) * H + h] = 0.f;
+    if (h == 0 && tid == 0) a.status[b] = status;
+    return;
+  }
 
-  // ---- 5. Masked, decayed K K^T and Q K^T on MFMA (lower triangle of node tiles).
+  // ---- 3. masked, decayed K K^T and Q K^T (lower triangle of node tiles)
   {
     const int ntile = mt * (mt + 1) / 2;
     for (int ti = wave; ti < 2 * ntile; ti += NW) {
@@ -223,23 +277,21 @@ __global__ __launch_bounds__(256) void wy_verify_kernel(const VerifyArgs a) {
       int mi = 0;
       while ((mi + 1) * (mi + 2) / 2 <= tt) ++mi;
       const int mj = tt - mi * (mi + 1) / 2;
-      const IO* arow = (is_qk ? sm.kq.q : sm.kq.k) + (16 * mi + (lane & 15)) * KROW + 8 * (lane >> 4);
-      const IO* brow = sm.kq.k + (16 * mj + (lane & 15)) * KROW + 8 * (lane >> 4);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        Frag<IO> fa, fb;
-        fa.load(arow + 32 * s);
-        fb.load(brow + 32 * s);
+        Frag<IO, CPR> fa, fb;
+        fa.load(is_qk ? sm.kq.q : sm.kq.k, 16 * mi + l16, s, g);
+        fb.load(sm.kq.k, 16 * mj + l16, s, g);
         acc = mma(fa, fb, acc);
       }
-      // D layout: column i = 16*mj + lane%16, rows t = 16*mi + 4*(lane/16) + e.
-      const int i = 16 * mj + (lane & 15);
+      // result: column i = 16mj + lane%16, rows t = 16mi + 4g + e
+      const int i = 16 * mj + l16;
       const float g2i = sG2[i];
       float* dstA = is_qk ? sAqk : sAkk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * mi + 4 * (lane >> 4) + e;
+        const int t = 16 * mi + 4 * g + e;
         const bool vis = t < n && i < n && ((sAnc[t] >> i) & 1ull) && (is_qk || i != t);
         float val = 0.f;
         if (vis) val = exp2f(sG2[t] - g2i) * acc[e] * (is_qk ? 1.f : sBeta[t]);
@@ -248,7 +300,7 @@ __global__ __launch_bounds__(256) void wy_verify_kernel(const VerifyArgs a) {
     }
   }
 
-  // ---- 6. X = K S0^T, Y = Q S0^T: A operand = S0 fragment (hi, lo), B = staged k / q.
+  // ---- 4. X = K S0^T, Y = Q S0^T (A operand = S0 hi/lo, B = staged k / q)
   f32x4 accX[TPW][MT], accY[TPW][MT];
 #pragma unroll
   for (int jj = 0; jj < TPW; ++jj)
@@ -270,94 +322,123 @@ __global__ __launch_bounds__(256) void wy_verify_kernel(const VerifyArgs a) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < mt) {
-          Frag<IO> fk, fq;
-          fk.load(sm.kq.k + (16 * m + (lane & 15)) * KROW + 32 * s + 8 * (lane >> 4));
-          fq.load(sm.kq.q + (16 * m + (lane & 15)) * KROW + 32 * s + 8 * (lane >> 4));
+          Frag<IO, CPR> fk, fq;
+          fk.load(sm.kq.k, 16 * m + l16, s, g);
+          fq.load(sm.kq.q, 16 * m + l16, s, g);
           accX[jj][m] = mma_state(shi, slo, fk, accX[jj][m]);
           accY[jj][m] = mma_state(shi, slo, fq, accY[jj][m]);
         }
       }
     }
   }
-  __syncthreads();  // every read of staged k/q is done: U may now reuse that LDS
+  __syncthreads();  // all reads of staged k/q are done: U reuses that LDS
+  if (wave * TPW >= DVT) return;  // (dv = 32) waves without S0 rows of their own
 
-  // ---- 7. R = diag(beta)(V - diag(G) X) -> LDS; keep G*Y for the output.
+  // ---- 5. per item (node t = 16m + lane%16, columns r..r+3): R into accX,
+  // G*Y into accY; then the level-by-level solve of (I + A_kk) U = R.
   float* __restrict__ sU = sm.u;
+  int tdep[MT];
+  uint64_t tanc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = 16 * m + l16;
+    const bool live = m < mt && t < n;
+    tanc[m] = live ? sAnc[t] : 0ull;
+    tdep[m] = live ? __popcll(tanc[m]) - 1 : -1;
+    const float G = live ? exp2f(sG2[t]) : 0.f;
+    const float bt = live ? sBeta[t] : 0.f;
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+      const f32x4 x = accX[jj][m];
+      const float4 vv = vreg[jj][m];
+      accX[jj][m] = f32x4{bt * (vv.x - G * x[0]), bt * (vv.y - G * x[1]), bt * (vv.z - G * x[2]),
+                          bt * (vv.w - G * x[3])};
+      accY[jj][m] = accY[jj][m] * G;
+    }
+  }
+  for (int lvl = 0; lvl <= maxd; ++lvl) {
+    float4 un[TPW][MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int t = 16 * m + l16;
+      uint64_t msk = tanc[m] & ~(1ull << (t & 63));
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) {
+        const f32x4 rr = accX[jj][m];
+        un[jj][m] = make_float4(rr[0], rr[1], rr[2], rr[3]);
+      }
+      if (tdep[m] == lvl) {
+        // the lvl proper ancestors of t, root first
+        for (int d = 0; d < lvl; ++d) {
+          const int i = __builtin_ctzll(msk);
+          msk &= msk - 1;
+          const float c = -sAkk[t * AROW + i];
+#pragma unroll
+          for (int jj = 0; jj < TPW; ++jj) {
+            const int r = 16 * (wave * TPW + jj) + 4 * g;
+            fma4(un[jj][m], c, *reinterpret_cast<const float4*>(sU + i * UROW + r));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int t = 16 * m + l16;
+      if (tdep[m] == lvl) {
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) {
+          const int jt = wave * TPW + jj;
+          if (jt < DVT) *reinterpret_cast<float4*>(sU + t * UROW + 16 * jt + 4 * g) = un[jj][m];
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // ---- 6. o_t = G_t Y_t + sum_{i in A(t)} A_qk[t,i] u_i, one ancestor depth at a time
+  float4 out[TPW][MT];
+  uint64_t rem[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    rem[m] = tanc[m];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+      const f32x4 y = accY[jj][m];
+      out[jj][m] = make_float4(y[0], y[1], y[2], y[3]);
+    }
+  }
+  for (int d = 0; d <= maxd; ++d) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (rem[m]) {
+        const int t = 16 * m + l16;
+        const int i = __builtin_ctzll(rem[m]);
+        rem[m] &= rem[m] - 1;
+        const float c = sAqk[t * AROW + i];
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) {
+          const int r = 16 * (wave * TPW + jj) + 4 * g;
+          fma4(out[jj][m], c, *reinterpret_cast<const float4*>(sU + i * UROW + r));
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int jj = 0; jj < TPW; ++jj) {
     const int jt = wave * TPW + jj;
     if (jt >= DVT) continue;
-    const int r = 16 * jt + 4 * (lane >> 4);
+    const int r = 16 * jt + 4 * g;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int t = 16 * m + (lane & 15);
-      if (m < mt && t < n) {
-        const float G = exp2f(sG2[t]);
-        const float bt = sBeta[t];
-        const f32x4 x = accX[jj][m];
-        const float4 vv = vreg[jj][m];
-        float4 R;
-        R.x = bt * (vv.x - G * x[0]);
-        R.y = bt * (vv.y - G * x[1]);
-        R.z = bt * (vv.z - G * x[2]);
-        R.w = bt * (vv.w - G * x[3]);
-        *reinterpret_cast<float4*>(sU + t * UROW + r) = R;
-        accY[jj][m] = accY[jj][m] * G;
-      }
-    }
-  }
-  wave_lds_sync();
-
-  // ---- 8. Forward substitution on this wave's columns: u_t = r_t - sum A_kk[t,i] u_i
-  // over the proper ancestors i of t, nodes in index (= topological) order.
-  {
-    const int col0 = 16 * wave * TPW;
-    const int col = col0 + lane;
-    if (col0 < DV && lane < 16 * TPW && col < DV) {
-      for (int t = 1; t < n; ++t) {
-        float acc = sU[t * UROW + col];
-        uint64_t msk = sAnc[t] & ~(1ull << t);
-        while (msk) {
-          const int i = __builtin_ctzll(msk);
-          msk &= msk - 1;
-          acc -= sAkk[t * AROW + i] * sU[i * UROW + col];
-        }
-        sU[t * UROW + col] = acc;
-      }
-    }
-  }
-  wave_lds_sync();
-
-  // ---- 9. o_t = G_t Y_t + sum_{i in A(t)} A_qk[t,i] u_i; store o, U and g2.
-#pragma unroll
-  for (int jj = 0; jj < TPW; ++jj) {
-    const int jt = wave * TPW + jj;
-    if (jt >= DVT) continue;
-    const int r = 16 * jt + 4 * (lane >> 4);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int t = 16 * m + (lane & 15);
-      if (m < mt && t < n) {
-        const f32x4 y = accY[jj][m];
-        float4 acc = make_float4(y[0], y[1], y[2], y[3]);
-        uint64_t msk = sAnc[t];
-        while (msk) {
-          const int i = __builtin_ctzll(msk);
-          msk &= msk - 1;
-          const float c = sAqk[t * AROW + i];
-          const float4 u = *reinterpret_cast<const float4*>(sU + i * UROW + r);
-          acc.x += c * u.x;
-          acc.y += c * u.y;
-          acc.z += c * u.z;
-          acc.w += c * u.w;
-        }
+      const int t = 16 * m + l16;
+      if (tdep[m] >= 0) {
         const size_t row = ((size_t)(lo + t) * H + h) * DV + r;
-        io::store4(o + row, acc);
+        io::store4(o + row, out[jj][m]);
         *reinterpret_cast<float4*>(a.U + row) = *reinterpret_cast<const float4*>(sU + t * UROW + r);
       }
     }
   }
-  if (wave == 0 && lane < n) a.g2[(size_t)(lo + lane) * H + h] = g2_l;
+  if (wave == 0 && lane < n) a.g2[(size_t)(lo + lane) * H + h] = sG2[lane];
   if (h == 0 && tid == 0) a.status[b] = GDN_TREE_OK;
 }
 

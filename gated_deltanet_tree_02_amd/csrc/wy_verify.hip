@@ -53,12 +53,12 @@ __device__ __forceinline__ void split_hi_lo(const float (&f)[8], bf16x8& hi, bf1
   }
 }
 
-// Staged rows: row-major 16-byte chunks, chunk c of row r stored at position
-// c ^ (r mod chunks-per-row), so that 16 lanes on 16 consecutive rows at one
-// chunk index hit 16 different bank groups.
+// Staged rows: row-major 16-byte chunks with one spare chunk per row, so that
+// 16 lanes on 16 consecutive rows at one chunk index hit disjoint banks and
+// every operand address is a per-lane base plus a compile-time offset.
 template <int CPR>
 __device__ __forceinline__ int chunk_slot(int row, int c) {
-  return row * CPR + (c ^ (row & (CPR - 1)));
+  return row * (CPR + 1) + c;
 }
 
 // MFMA operand fragment = 8 consecutive k-elements of one staged row
@@ -96,57 +96,103 @@ __device__ __forceinline__ f32x4 mma(const Frag<float, CPR>& a, const Frag<float
   acc = mfma16(a.lo, b.hi, acc);
   return mfma16(a.lo, b.lo, acc);
 }
-// S0 fragment (hi, lo) times a staged fragment.
+// Staged fragment times S0 fragment (hi, lo): result rows = nodes, columns = dv.
 template <int CPR>
-__device__ __forceinline__ f32x4 mma_state(const bf16x8& shi, const bf16x8& slo,
-                                           const Frag<uint16_t, CPR>& b, f32x4 acc) {
-  acc = mfma16(shi, b.hi, acc);
-  return mfma16(slo, b.hi, acc);
+__device__ __forceinline__ f32x4 mma_state_t(const Frag<uint16_t, CPR>& a, const bf16x8& shi,
+                                             const bf16x8& slo, f32x4 acc) {
+  acc = mfma16(a.hi, shi, acc);
+  return mfma16(a.hi, slo, acc);
 }
 template <int CPR>
-__device__ __forceinline__ f32x4 mma_state(const bf16x8& shi, const bf16x8& slo,
-                                           const Frag<float, CPR>& b, f32x4 acc) {
-  acc = mfma16(shi, b.hi, acc);
-  acc = mfma16(shi, b.lo, acc);
-  acc = mfma16(slo, b.hi, acc);
-  return mfma16(slo, b.lo, acc);
+__device__ __forceinline__ f32x4 mma_state_t(const Frag<float, CPR>& a, const bf16x8& shi,
+                                             const bf16x8& slo, f32x4 acc) {
+  acc = mfma16(a.hi, shi, acc);
+  acc = mfma16(a.lo, shi, acc);
+  acc = mfma16(a.hi, slo, acc);
+  return mfma16(a.lo, slo, acc);
 }
 
-__device__ __forceinline__ void fma4(float4& acc, float c, const float4& u) {
-  acc.x += c * u.x;
-  acc.y += c * u.y;
-  acc.z += c * u.z;
-  acc.w += c * u.w;
+// 2^x with the hardware transcendental (about 1 ulp; results below the
+// smallest normal flush to 0, far below fp32 resolution of any sum here).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 hi | lo packed in one 32-bit word (hi in the low half)
+__device__ __forceinline__ uint32_t pack_hi_lo(float x) {
+  const __bf16 h = (__bf16)x;
+  const __bf16 l = (__bf16)(x - (float)h);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+}
+// four packed words -> bf16x4 hi and bf16x4 lo
+__device__ __forceinline__ void unpack_hi_lo(const uint4& w, bf16x4& hi, bf16x4& lo) {
+  const uint32_t h01 = __builtin_amdgcn_perm(w.y, w.x, 0x05040100u);
+  const uint32_t h23 = __builtin_amdgcn_perm(w.w, w.z, 0x05040100u);
+  const uint32_t l01 = __builtin_amdgcn_perm(w.y, w.x, 0x07060302u);
+  const uint32_t l23 = __builtin_amdgcn_perm(w.w, w.z, 0x07060302u);
+  hi = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
+  lo = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
+}
+
+// 16x16x16 bf16 MFMA: A lane l holds A[l%16][4(l/16)..+3], B lane l holds
+// B[4(l/16)..+3][l%16]; the result lane l holds D[4(l/16)..+3][l%16], so a
+// result tile is directly the B operand of the next product.
+__device__ __forceinline__ f32x4 mfma16k(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split4(const f32x4& x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    hi[e] = h;
+    lo[e] = (__bf16)(x[e] - (float)h);
+  }
+}
+
+// acc += A * B with both operands carried as bf16 hi + lo (the lo*lo term is
+// below fp32 resolution of the sum and is dropped).
+__device__ __forceinline__ f32x4 mma3(const bf16x4& ah, const bf16x4& al, const bf16x4& bh,
+                                      const bf16x4& bl, f32x4 acc) {
+  acc = mfma16k(ah, bh, acc);
+  acc = mfma16k(ah, bl, acc);
+  return mfma16k(al, bh, acc);
 }
 
 constexpr int kVerifyWaves = 8;
+constexpr int kTPath = 8;     // paths of up to 8 nodes (depth <= 7) solve T rows in registers
 
 template <class IO, int DK, int DV, int MT>
 __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const VerifyArgs a) {
   constexpr int NW = kVerifyWaves;
   constexpr int NT = 64 * NW;                 // threads
   constexpr int NP = MT * 16;                 // padded node rows
-  constexpr int KS = DK / 32;                 // MFMA k-steps over dk
-  constexpr int DVT = DV / 16;                // 16-row tiles of S0 (dv direction)
-  constexpr int TPW = (DVT + NW - 1) / NW;    // S0 tiles per wave
+  constexpr int KS = DK / 32;                 // 16x16x32 k-steps over dk
+  constexpr int DVT = DV / 16;                // 16-column tiles of dv; wave w owns tile w
   constexpr int EPC = 16 / (int)sizeof(IO);   // io elements per 16-byte chunk
   constexpr int CPR = DK / EPC;               // chunks per q/k row
   constexpr int CPV = DV / EPC;               // chunks per v/o row
-  constexpr int UROW = DV + 4;                // U row, floats
+  // U / o staging rows are unpadded; column r of node row t is stored at
+  // r ^ (16 * ((t >> 2) & 3)) (when dv >= 64), so that the four row groups of
+  // an MFMA result tile write disjoint banks while every 16-byte chunk of a
+  // row stays contiguous for the row-wise global stores.
+  constexpr int SWZ = DV >= 64 ? 1 : 0;
+  constexpr int TTW = 16;                     // row of a stored 16x16 tile
+  constexpr int TTS = 16 * TTW;               // stored tile size
   constexpr int NTRI = NP * (NP + 1) / 2;     // packed lower triangle
+  constexpr int NQT = MT * (MT + 1) / 2;      // lower-triangular 16x16 node tiles
   constexpr int NSTAGE = NP * (2 * CPR + CPV);  // staged q, k, v chunks
   constexpr int NLD = (NSTAGE + NT - 1) / NT;   // per thread (a spare one repeats the last)
+  constexpr bool kF32 = std::is_same<IO, float>::value;
   using io = io_traits<IO>;
-  static_assert(DVT % NW == 0 || TPW == 1, "every wave with S0 rows owns whole tiles");
+  static_assert(DVT <= NW, "one 16-column dv tile per wave");
 
   struct Stage1 {             // until the state products are done
-    uint4 k[NP * CPR];
-    uint4 q[NP * CPR];
-    uint4 v[NP * CPV];
+    uint4 k[NP * (CPR + 1)];
+    uint4 q[NP * (CPR + 1)];
+    uint4 v[NP * (CPV + 1)];
   };
-  struct Stage2 {             // solve and output
-    float u[NP * UROW];
-    uint4 o[NP * CPV];
+  struct Stage2 {             // products with T and A_qk, output staging
+    float u[NP * DV];
+    IO o[NP * DV];
   };
   union SMem {
     Stage1 s1;
@@ -154,7 +200,16 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
   };
   __shared__ SMem sm;
   __shared__ float sAkk[NTRI];
-  __shared__ float sAqk[NTRI];
+  // T (fp32 while it is computed, then packed bf16 hi|lo words) and A_qk as
+  // their lower-triangular 16x16 node tiles (mi, ki), ki <= mi,
+  // tile qt = mi(mi+1)/2 + ki, unpadded 16x16 (the few operand reads take a
+  // 4-way bank conflict; the bytes saved keep three 48-node workgroups per
+  // CU within the LDS). A_qk is kept in io
+  // precision for bf16 io (its product with U is rounded to bf16 anyway) and
+  // as fp32 for fp32 io.
+  using AqT = typename std::conditional<std::is_same<IO, float>::value, float, __bf16>::type;
+  __shared__ __align__(16) float sT[NQT * TTS];
+  __shared__ __align__(16) AqT sAqk[NQT * TTS];
   __shared__ uint64_t sAnc[64];
   __shared__ float sG2[64];
   __shared__ float sBeta[64];
@@ -208,17 +263,17 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
     const int dd = mat == 2 ? DV : DK;
     stg[it] = *reinterpret_cast<const uint4*>(base + ((size_t)(lo + srow) * H + h) * dd + c * EPC);
   }
-  // 1c. this wave's S0 rows 16jt + lane%16, columns 32s + 8g .. +7
-  const int jt0 = min(wave * TPW, DVT - TPW);   // waves without a tile of their own repeat one
+  // 1c. this wave's S0 rows 16w + lane%16, columns 32s + 8g .. +7
+  const bool owns = wave < DVT;                 // dv < 128: the last waves own no columns
+  const int jt = owns ? wave : DVT - 1;
   const float* __restrict__ S0bh = a.S0 + (size_t)bh * DV * DK;
-  float4 sraw[TPW][KS][2];
-#pragma unroll
-  for (int jj = 0; jj < TPW; ++jj) {
-    const float* rowp = S0bh + (size_t)(16 * (jt0 + jj) + l16) * DK + 8 * g;
+  float4 sraw[KS][2];
+  {
+    const float* rowp = S0bh + (size_t)(16 * jt + l16) * DK + 8 * g;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      sraw[jj][s][0] = *reinterpret_cast<const float4*>(rowp + 32 * s);
-      sraw[jj][s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
+      sraw[s][0] = *reinterpret_cast<const float4*>(rowp + 32 * s);
+      sraw[s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
     }
   }
 
@@ -248,9 +303,6 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
   float g2;
   // (on a bad tree the scan still terminates; its results are not used)
   path_scan(par, lane, n, lane < n ? gate_log2(alpha_l) : 0.f, anc, g2);
-  int maxd = lane < n ? __popcll(anc) - 1 : 0;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) maxd = max(maxd, __shfl_xor(maxd, off, kWave));
   if (wave == 0) {
     sAnc[lane] = anc;
     sG2[lane] = g2;
@@ -270,13 +322,19 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
     return;
   }
 
-  // ---- 3. masked, decayed K K^T and Q K^T (lower triangle of node tiles),
-  // stored packed: entry (t, i), i <= t, at t(t+1)/2 + i
+  // ---- 3. The masked, decayed products over the lower-triangular node tiles,
+  // spread over the waves:
+  //   A_kk[t,i] = beta_t 2^(g2_t - g2_i) k_t.k_i  (i a proper ancestor of t),
+  //     as K K^T: result column i = 16mj + lane%16, rows t = 16mi + 4g + e,
+  //     stored packed, entry (t, i) at t(t+1)/2 + i;
+  //   A_qk[t,i] = 2^(g2_t - g2_i) q_t.k_i  (i in A(t)),
+  //     as K Q^T: lane holds t = 16mi + lane%16, i = 16mj + 4g + e, i.e. the
+  //     A-operand layout of the product A_qk U, stored as tile (mi, mj).
   {
     const int ntile = mt * (mt + 1) / 2;
-    for (int ti = wave; ti < 2 * ntile; ti += NW) {
-      const bool is_qk = ti >= ntile;
-      const int tt = is_qk ? ti - ntile : ti;
+    for (int tt2 = wave; tt2 < 2 * ntile; tt2 += NW) {
+      const bool is_qk = tt2 >= ntile;
+      const int tt = is_qk ? tt2 - ntile : tt2;
       int mi = 0;
       while ((mi + 1) * (mi + 2) / 2 <= tt) ++mi;
       const int mj = tt - mi * (mi + 1) / 2;
@@ -284,166 +342,227 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         Frag<IO, CPR> fa, fb;
-        fa.load(is_qk ? sm.s1.q : sm.s1.k, 16 * mi + l16, s, g);
-        fb.load(sm.s1.k, 16 * mj + l16, s, g);
+        fa.load(sm.s1.k, 16 * (is_qk ? mj : mi) + l16, s, g);
+        fb.load(is_qk ? sm.s1.q : sm.s1.k, 16 * (is_qk ? mi : mj) + l16, s, g);
         acc = mma(fa, fb, acc);
       }
-      // result: column i = 16mj + lane%16, rows t = 16mi + 4g + e
-      const int i = 16 * mj + l16;
-      const float g2i = sG2[i];
-      float* dstA = is_qk ? sAqk : sAkk;
+      if (!is_qk) {
+        const int i = 16 * mj + l16;
+        const float g2i = sG2[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * mi + 4 * g + e;
-        if (i <= t) {
-          const bool vis = t < n && ((sAnc[t] >> i) & 1ull) && (is_qk || i != t);
-          float val = 0.f;
-          if (vis) val = exp2f(sG2[t] - g2i) * acc[e] * (is_qk ? 1.f : sBeta[t]);
-          dstA[t * (t + 1) / 2 + i] = val;
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * mi + 4 * g + e;
+          const bool vis = ((sAnc[t] >> i) & 1ull) && i != t;
+          const float val = vis ? sBeta[t] * fast_exp2(sG2[t] - g2i) * acc[e] : 0.f;
+          if (i <= t) sAkk[t * (t + 1) / 2 + i] = val;
         }
-      }
-    }
-  }
-
-  // ---- 4. X = K S0^T, Y = Q S0^T (A operand = S0 hi/lo, B = staged k / q)
-  const bool owns = wave * TPW < DVT;           // (dv = 32) waves 2, 3 own no S0 rows
-  f32x4 accX[TPW][MT], accY[TPW][MT];
+      } else {
+        const int t = 16 * mi + l16;
+        const uint64_t at = sAnc[t];
+        const float g2t = sG2[t];
+        AqT* dst = sAqk + tt * TTS + l16 * TTW + 4 * g;
 #pragma unroll
-  for (int jj = 0; jj < TPW; ++jj)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      accX[jj][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accY[jj][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  if (owns) {
-#pragma unroll
-    for (int jj = 0; jj < TPW; ++jj) {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const float4 x0 = sraw[jj][s][0], x1 = sraw[jj][s][1];
-        const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        bf16x8 shi, slo;
-        split_hi_lo(f, shi, slo);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m < mt) {
-            Frag<IO, CPR> fk, fq;
-            fk.load(sm.s1.k, 16 * m + l16, s, g);
-            fq.load(sm.s1.q, 16 * m + l16, s, g);
-            accX[jj][m] = mma_state(shi, slo, fk, accX[jj][m]);
-            accY[jj][m] = mma_state(shi, slo, fq, accY[jj][m]);
-          }
-        }
-      }
-    }
-  }
-
-  // ---- 5. per item (node t = 16m + lane%16, columns r..r+3): R into accX,
-  // G*Y into accY
-  int tdep[MT];
-  uint64_t tanc[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int t = 16 * m + l16;
-    const bool live = owns && m < mt && t < n;
-    tanc[m] = live ? sAnc[t] : 0ull;
-    tdep[m] = live ? __popcll(tanc[m]) - 1 : -1;
-    const float G = live ? exp2f(sG2[t]) : 0.f;
-    const float bt = live ? sBeta[t] : 0.f;
-#pragma unroll
-    for (int jj = 0; jj < TPW; ++jj) {
-      const int r = 16 * (jt0 + jj) + 4 * g;
-      const float4 vv = io::load4(reinterpret_cast<const IO*>(sm.s1.v) +
-                                  chunk_slot<CPV>(t, r / EPC) * EPC + r % EPC);
-      const f32x4 x = accX[jj][m];
-      accX[jj][m] = f32x4{bt * (vv.x - G * x[0]), bt * (vv.y - G * x[1]), bt * (vv.z - G * x[2]),
-                          bt * (vv.w - G * x[3])};
-      accY[jj][m] = accY[jj][m] * G;
-    }
-  }
-  __syncthreads();  // staged q, k, v are dead: U and the o staging reuse that LDS
-
-  // ---- 6. level-by-level solve of (I + A_kk) U = R on this wave's columns,
-  // fused with the output: all nodes of one depth at once (a node at depth l
-  // has exactly l proper ancestors, visited root first); each ancestor's
-  // pseudo-value is read once and serves both
-  //     u_t = r_t - sum_{i in A(t), i != t} A_kk[t,i] u_i
-  //     o_t = G_t y_t + sum_{i in A(t), i != t} A_qk[t,i] u_i + A_qk[t,t] u_t
-  float* __restrict__ sU = sm.s2.u;
-  if (owns) {
-    float4 out[TPW][MT];
-    for (int lvl = 0; lvl <= maxd; ++lvl) {
-      float4 un[TPW][MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int t = 16 * m + l16;
-        if (tdep[m] == lvl) {
-          uint64_t msk = tanc[m] & ~(1ull << (t & 63));
-#pragma unroll
-          for (int jj = 0; jj < TPW; ++jj) {
-            const f32x4 rr = accX[jj][m];
-            const f32x4 yy = accY[jj][m];
-            un[jj][m] = make_float4(rr[0], rr[1], rr[2], rr[3]);
-            out[jj][m] = make_float4(yy[0], yy[1], yy[2], yy[3]);
-          }
-          const int trow = t * (t + 1) / 2;
-          for (int d = 0; d < lvl; ++d) {
-            const int i = __builtin_ctzll(msk);
-            msk &= msk - 1;
-            const float ckk = -sAkk[trow + i];
-            const float cqk = sAqk[trow + i];
-#pragma unroll
-            for (int jj = 0; jj < TPW; ++jj) {
-              const int r = 16 * (wave * TPW + jj) + 4 * g;
-              const float4 ui = *reinterpret_cast<const float4*>(sU + i * UROW + r);
-              fma4(un[jj][m], ckk, ui);
-              fma4(out[jj][m], cqk, ui);
-            }
-          }
-          const float cself = sAqk[trow + t];
-#pragma unroll
-          for (int jj = 0; jj < TPW; ++jj) fma4(out[jj][m], cself, un[jj][m]);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int t = 16 * m + l16;
-        if (tdep[m] == lvl) {
-#pragma unroll
-          for (int jj = 0; jj < TPW; ++jj)
-            *reinterpret_cast<float4*>(sU + t * UROW + 16 * (wave * TPW + jj) + 4 * g) = un[jj][m];
-        }
-      }
-      wave_lds_sync();
-    }
-    // o in io precision into the LDS staging rows
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int t = 16 * m + l16;
-      if (tdep[m] >= 0) {
-#pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) {
-          const int r = 16 * (wave * TPW + jj) + 4 * g;
-          io::store4(reinterpret_cast<IO*>(sm.s2.o) + chunk_slot<CPV>(t, r / EPC) * EPC + r % EPC,
-                     out[jj][m]);
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * mj + 4 * g + e;
+          const bool vis = (at >> i) & 1ull;
+          dst[e] = (AqT)(vis ? fast_exp2(g2t - sG2[i]) * acc[e] : 0.f);
         }
       }
     }
   }
   __syncthreads();
 
-  // ---- 8. o, U and g2 to memory, consecutive lanes on consecutive chunks of a row
+  // ---- 4. wave 0: T = (I + A_kk)^-1, one lane per row. Row t is nonzero only
+  // on t's path p_0 (root) .. p_d = t, where it is the last row of the inverse
+  // of the path's own unit-lower block: y_t = 1 and, from the deepest proper
+  // ancestor up to the root, y_j = -sum_{i on the path below j} y_i A_kk[i,j].
+  // Rows of padding nodes are zero.
+  if (wave == 0 && lane < NP) {
+    // row t lives in tiles (t/16, ki), ki <= t/16, at row t%16
+    const int t = lane;
+    const int mrow = t >> 4;
+    float* Tbase = sT + (mrow * (mrow + 1) / 2) * TTS + (t & 15) * TTW;   // tile (mrow, 0)
+#pragma unroll
+    for (int ki = 0; ki < MT; ++ki)
+      if (ki <= mrow)
+#pragma unroll
+        for (int c = 0; c < 16; c += 4)
+          *reinterpret_cast<float4*>(Tbase + ki * TTS + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < n) {
+      const int d = __popcll(anc) - 1;
+      if (d < kTPath) {
+        // path p_0 = root .. p_d = t in registers; every A_kk entry the
+        // back-substitution needs is loaded up front, then only FMAs
+        int p[kTPath];
+        uint64_t m = anc;
+#pragma unroll
+        for (int s2 = 0; s2 < kTPath; ++s2) {
+          p[s2] = m ? __builtin_ctzll(m) : 0;
+          m &= m - 1;
+        }
+        float akk[kTPath][kTPath];
+#pragma unroll
+        for (int s2 = 1; s2 < kTPath; ++s2)
+#pragma unroll
+          for (int r2 = 0; r2 < s2; ++r2)
+            akk[s2][r2] = s2 <= d ? sAkk[p[s2] * (p[s2] + 1) / 2 + p[r2]] : 0.f;
+        float y[kTPath];
+#pragma unroll
+        for (int s2 = 0; s2 < kTPath; ++s2) y[s2] = s2 == d ? 1.f : 0.f;
+#pragma unroll
+        for (int r2 = kTPath - 2; r2 >= 0; --r2) {
+          if (r2 < d) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s2 = r2 + 1; s2 < kTPath; ++s2) acc += y[s2] * akk[s2][r2];
+            y[r2] = -acc;
+          }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < kTPath; ++s2)
+          if (s2 <= d)
+            *reinterpret_cast<uint32_t*>(Tbase + (p[s2] >> 4) * TTS + (p[s2] & 15)) = pack_hi_lo(y[s2]);
+      } else {
+        // deep paths: the same substitution with the row kept in LDS
+        Tbase[(t >> 4) * TTS + (t & 15)] = 1.f;
+        uint64_t rest = anc & ~(1ull << t);
+        while (rest) {
+          const int j = 63 - __builtin_clzll(rest);
+          rest &= ~(1ull << j);
+          uint64_t below = anc & ~((2ull << j) - 1ull);
+          float acc = 0.f;
+          while (below) {
+            const int i = __builtin_ctzll(below);
+            below &= below - 1;
+            acc += Tbase[(i >> 4) * TTS + (i & 15)] * sAkk[i * (i + 1) / 2 + j];
+          }
+          Tbase[(j >> 4) * TTS + (j & 15)] = -acc;
+        }
+        // the row's nonzero entries (t's path) become packed bf16 hi|lo words,
+        // the form the product U = T R consumes
+        uint64_t path = anc;
+        while (path) {
+          const int i = __builtin_ctzll(path);
+          path &= path - 1;
+          float* e = Tbase + (i >> 4) * TTS + (i & 15);
+          *reinterpret_cast<uint32_t*>(e) = pack_hi_lo(*e);
+        }
+      }
+    }
+  }
+
+  // ---- 5. per wave: X = K S0^T and Y = Q S0^T for node tiles m, with the
+  // wave's 16 dv columns (A = staged k / q rows, B = S0 hi/lo); result lane
+  // holds column r = 16w + lane%16 of nodes t = 16m + 4g + e. Then
+  // R = diag(beta)(V - diag(G) X) and G*Y.
+  f32x4 rX[MT], rY[MT];
+  if (owns) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      rX[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      rY[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float4 x0 = sraw[s][0], x1 = sraw[s][1];
+      const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      bf16x8 shi, slo;
+      split_hi_lo(f, shi, slo);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < mt) {
+          Frag<IO, CPR> fk, fq;
+          fk.load(sm.s1.k, 16 * m + l16, s, g);
+          fq.load(sm.s1.q, 16 * m + l16, s, g);
+          rX[m] = mma_state_t(fk, shi, slo, rX[m]);
+          rY[m] = mma_state_t(fq, shi, slo, rY[m]);
+        }
+      }
+    }
+    const int r = 16 * jt + l16;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * m + 4 * g + e;
+        const float G = fast_exp2(sG2[t]);
+        const float vv = io::load1(reinterpret_cast<const IO*>(sm.s1.v) +
+                                   chunk_slot<CPV>(t, r / EPC) * EPC + r % EPC);
+        rX[m][e] = sBeta[t] * (vv - G * rX[m][e]);
+        rY[m][e] = G * rY[m][e];
+      }
+    }
+  }
+  __syncthreads();  // T is complete; staged q, k, v are dead (stage 2 reuses the LDS)
+
+  // ---- 6. U = T R and O = G*Y + A_qk U on MFMA (16x16x16, node tiles as the
+  // k dimension); U and O leave through LDS staging rows.
+  if (owns) {
+    bf16x4 rh[MT], rl[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) split4(rX[m], rh[m], rl[m]);
+    f32x4 uu[MT];
+    bf16x4 uh[MT], ul[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      uu[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (m < mt) {
+#pragma unroll
+        for (int ki = 0; ki <= m; ++ki) {
+          const uint4 tw = *reinterpret_cast<const uint4*>(
+              sT + (m * (m + 1) / 2 + ki) * TTS + l16 * TTW + 4 * g);
+          bf16x4 th, tl;
+          unpack_hi_lo(tw, th, tl);
+          uu[m] = mma3(th, tl, rh[ki], rl[ki], uu[m]);
+        }
+      }
+      split4(uu[m], uh[m], ul[m]);
+    }
+    const int r = 16 * jt + l16;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      f32x4 oo = rY[m];
+      if (m < mt) {
+#pragma unroll
+        for (int ki = 0; ki <= m; ++ki) {
+          const AqT* src = sAqk + (m * (m + 1) / 2 + ki) * TTS + l16 * TTW + 4 * g;
+          if constexpr (kF32) {
+            const float4 av = *reinterpret_cast<const float4*>(src);
+            bf16x4 ah, al;
+            split4(f32x4{av.x, av.y, av.z, av.w}, ah, al);
+            oo = mma3(ah, al, uh[ki], ul[ki], oo);
+          } else {
+            const bf16x4 ah = *reinterpret_cast<const bf16x4*>(src);
+            oo = mfma16k(ah, uh[ki], oo);
+            oo = mfma16k(ah, ul[ki], oo);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * m + 4 * g + e;
+        const int rs = r ^ (SWZ * 16 * ((t >> 2) & 3));
+        sm.s2.u[t * DV + rs] = uu[m][e];
+        io::store1(sm.s2.o + t * DV + rs, oo[e]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 7. o, U and g2 to memory, consecutive lanes on consecutive chunks of a row
   for (int idx = tid; idx < n * CPV; idx += NT) {
     const int t = idx / CPV;
     const int c = idx - t * CPV;
+    const int cs = (c * EPC) ^ (SWZ * 16 * ((t >> 2) & 3));
     *reinterpret_cast<uint4*>(o + ((size_t)(lo + t) * H + h) * DV + c * EPC) =
-        sm.s2.o[chunk_slot<CPV>(t, c)];
+        *reinterpret_cast<const uint4*>(sm.s2.o + t * DV + cs);
   }
   for (int idx = tid; idx < n * (DV / 4); idx += NT) {
     const int t = idx / (DV / 4);
     const int c = idx - t * (DV / 4);
+    const int cs = (4 * c) ^ (SWZ * 16 * ((t >> 2) & 3));
     *reinterpret_cast<float4*>(a.U + ((size_t)(lo + t) * H + h) * DV + 4 * c) =
-        *reinterpret_cast<const float4*>(sU + t * UROW + 4 * c);
+        *reinterpret_cast<const float4*>(sm.s2.u + t * DV + cs);
   }
   if (wave == 0 && lane < n) a.g2[(size_t)(lo + lane) * H + h] = g2;
   if (h == 0 && tid == 0) a.status[b] = GDN_TREE_OK;

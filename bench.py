@@ -17,8 +17,10 @@ memory, and the CPU oracle timed on a bounded sample as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +29,35 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tree-GDN verified draft nodes/s per layer (1 GPU) + % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "gated_deltanet_tree_02_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wy_verify_commit_c4_hbm_traffic.md")
+# sources whose hash ties a recorded counter measurement to the kernels it measured
+KERNEL_SOURCES = {"verify": ["wy_verify.hip", "device_common.h", "launch.h"],
+                  "commit": ["wy_commit.hip", "device_common.h", "launch.h"]}
+
+
+def kernel_source_hash(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kind, config):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on this config with the current kernel sources;
+    else None. The summary holds lines
+      traffic <kind> <config> <source-hash> <bytes>"""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    pat = re.compile(rf"^traffic\s+{kind}\s+{config}\s+(\w+)\s+(\d+)\s*$")
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            m = pat.match(line.strip().strip("`"))
+            if m and m.group(1) == kernel_source_hash(kind):
+                return int(m.group(2))
+    return None
 
 
 def log(*a):
@@ -42,6 +73,10 @@ def parse():
     p.add_argument("--mode", default="wy", choices=["wy", "fork"])
     p.add_argument("--fork-steps", type=int, default=3, help="timed steps of the fork baseline (0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0 = skip)")
+    p.add_argument("--pmc-calibration", action="store_true",
+                   help="after the timed legs, run a plain 256 MiB device copy three times "
+                        "(reads and writes 256 MiB each): the known-size kernel that scales "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return p.parse_args()
 
 
@@ -160,9 +195,14 @@ def main():
                    "frac_hbm": round(cb / c_us / 1e3 / HBM_PEAK_GBS, 4)},
     }
     dom = "verify" if v_us >= c_us else "commit"
+    traffic = recorded_traffic(dom, args.config) if args.mode == "wy" else None
+    for kind in ("verify", "commit"):
+        t = recorded_traffic(kind, args.config) if args.mode == "wy" else None
+        kern[kind]["traffic_bytes"] = t
+        kern[kind]["traffic_over_alg"] = round(t / kern[kind]["alg_bytes"], 3) if t else None
     roof = {"kernel": f"{'wy' if args.mode == 'wy' else 'fork'}_{dom}", "bound": "hbm",
             "achieved": kern[dom]["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": kern[dom]["frac_hbm"], "traffic": None}
+            "frac": kern[dom]["frac_hbm"], "traffic": traffic}
     log(f"{args.mode}: {ms_step:.3f} ms/step, verify {v_us:.2f} us, commit {c_us:.2f} us per layer")
 
     # ------------------------------------------------------------- fork baseline
@@ -184,6 +224,15 @@ def main():
             ly.pop("o_fork"), ly.pop("ws_fork")
         fver = fcom = None
         torch.cuda.empty_cache()
+
+    if args.pmc_calibration:
+        x = torch.ones(64 << 20, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        del x, y
+        log("pmc calibration: 3 x copy of 256 MiB done")
 
     # speculative state per request (one sequence), summed over the layers
     n_req = w.T / w.B

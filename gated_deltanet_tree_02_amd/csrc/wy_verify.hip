@@ -158,7 +158,47 @@ __device__ __forceinline__ f32x4 mma3(const bf16x4& ah, const bf16x4& al, const 
 }
 
 constexpr int kVerifyWaves = 8;
-constexpr int kTPath = 8;     // paths of up to 8 nodes (depth <= 7) solve T rows in registers
+
+// Row t of T = (I + A_kk)^-1 for a node whose path p_0 (root) .. p_d = t has
+// at most P nodes. Row t is nonzero only on that path, where it is the last
+// row of the inverse of the path's own unit-lower block: y_t = 1 and, from the
+// deepest proper ancestor up to the root, y_j = -sum_{i on the path below j}
+// y_i A_kk[i,j]. Every A_kk entry of the path is loaded at once, then the
+// substitution runs in registers; the path entries are written into the
+// (zeroed) row as packed bf16 hi|lo words, the form U = T R consumes.
+template <int P, int TTS>
+__device__ __forceinline__ void t_row_in_registers(uint64_t anc, int d, const float* sAkk,
+                                                   float* Tbase) {
+  int p[P];
+  uint64_t m = anc;
+#pragma unroll
+  for (int s2 = 0; s2 < P; ++s2) {
+    p[s2] = m ? __builtin_ctzll(m) : 0;
+    m &= m - 1;
+  }
+  float akk[P][P];
+#pragma unroll
+  for (int s2 = 1; s2 < P; ++s2)
+#pragma unroll
+    for (int r2 = 0; r2 < s2; ++r2)
+      akk[s2][r2] = s2 <= d ? sAkk[p[s2] * (p[s2] + 1) / 2 + p[r2]] : 0.f;
+  float y[P];
+#pragma unroll
+  for (int s2 = 0; s2 < P; ++s2) y[s2] = s2 == d ? 1.f : 0.f;
+#pragma unroll
+  for (int r2 = P - 2; r2 >= 0; --r2) {
+    if (r2 < d) {
+      float acc = 0.f;
+#pragma unroll
+      for (int s2 = r2 + 1; s2 < P; ++s2) acc += y[s2] * akk[s2][r2];
+      y[r2] = -acc;
+    }
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < P; ++s2)
+    if (s2 <= d)
+      *reinterpret_cast<uint32_t*>(Tbase + (p[s2] >> 4) * TTS + (p[s2] & 15)) = pack_hi_lo(y[s2]);
+}
 
 template <class IO, int DK, int DV, int MT>
 __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const VerifyArgs a) {
@@ -215,7 +255,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
   __shared__ float sBeta[64];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;      // lane group of an MFMA operand / result
   const int l16 = lane & 15;
@@ -263,19 +303,8 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
     const int dd = mat == 2 ? DV : DK;
     stg[it] = *reinterpret_cast<const uint4*>(base + ((size_t)(lo + srow) * H + h) * dd + c * EPC);
   }
-  // 1c. this wave's S0 rows 16w + lane%16, columns 32s + 8g .. +7
   const bool owns = wave < DVT;                 // dv < 128: the last waves own no columns
   const int jt = owns ? wave : DVT - 1;
-  const float* __restrict__ S0bh = a.S0 + (size_t)bh * DV * DK;
-  float4 sraw[KS][2];
-  {
-    const float* rowp = S0bh + (size_t)(16 * jt + l16) * DK + 8 * g;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sraw[s][0] = *reinterpret_cast<const float4*>(rowp + 32 * s);
-      sraw[s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
-    }
-  }
 
   // ---- 2. staged chunks to LDS (swizzled), then the tree prologue, computed
   // by every wave so that no branch separates the loads from their first use.
@@ -292,13 +321,15 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
       (mat == 0 ? sm.s1.k : sm.s1.q)[chunk_slot<CPR>(row, rel - row * CPR)] = stg[it];
     }
   }
+  // (every wave runs it: a branch around it would let the compiler sink the
+  // parent and gate loads into the branch, behind the staged-row waits)
   const int par = lane < n ? par_raw : -1;
-  const float beta_l = lane < n ? beta_raw : 0.f;
   int st = GDN_TREE_OK;
   if (__shfl(par, 0, kWave) != -1)
     st = GDN_TREE_BAD_ROOT;
   else if (__ballot(lane >= 1 && lane < n && (par < 0 || par >= lane)) != 0ull)
     st = GDN_TREE_BAD_PARENT;
+  st = __builtin_amdgcn_readfirstlane(st);
   uint64_t anc;
   float g2;
   // (on a bad tree the scan still terminates; its results are not used)
@@ -306,9 +337,22 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
   if (wave == 0) {
     sAnc[lane] = anc;
     sG2[lane] = g2;
-    sBeta[lane] = beta_l;
+    sBeta[lane] = lane < n ? beta_raw : 0.f;
   }
   __syncthreads();
+  // 1c. this wave's S0 rows 16w + lane%16, columns 32s + 8g .. +7. Issued only
+  // now, once the q, k, v rows have arrived: when every resident workgroup
+  // loads at once, the rows that the first phases need are not queued behind
+  // the state, which then streams in while the node products are computed.
+  float4 sraw[KS][2];
+  {
+    const float* rowp = a.S0 + (size_t)bh * DV * DK + (size_t)(16 * jt + l16) * DK + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sraw[s][0] = *reinterpret_cast<const float4*>(rowp + 32 * s);
+      sraw[s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
+    }
+  }
   if (st != GDN_TREE_OK) {
     for (int idx = tid; idx < n * (DV / 4); idx += NT) {
       const int t = idx / (DV / 4);
@@ -388,40 +432,14 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
 #pragma unroll
         for (int c = 0; c < 16; c += 4)
           *reinterpret_cast<float4*>(Tbase + ki * TTS + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    // every path of at most 4 nodes (a wave-uniform test): the short solve
+    const int d = __popcll(anc) - 1;
+    const bool shallow4 = __ballot(t < n && d >= 4) == 0ull;
     if (t < n) {
-      const int d = __popcll(anc) - 1;
-      if (d < kTPath) {
-        // path p_0 = root .. p_d = t in registers; every A_kk entry the
-        // back-substitution needs is loaded up front, then only FMAs
-        int p[kTPath];
-        uint64_t m = anc;
-#pragma unroll
-        for (int s2 = 0; s2 < kTPath; ++s2) {
-          p[s2] = m ? __builtin_ctzll(m) : 0;
-          m &= m - 1;
-        }
-        float akk[kTPath][kTPath];
-#pragma unroll
-        for (int s2 = 1; s2 < kTPath; ++s2)
-#pragma unroll
-          for (int r2 = 0; r2 < s2; ++r2)
-            akk[s2][r2] = s2 <= d ? sAkk[p[s2] * (p[s2] + 1) / 2 + p[r2]] : 0.f;
-        float y[kTPath];
-#pragma unroll
-        for (int s2 = 0; s2 < kTPath; ++s2) y[s2] = s2 == d ? 1.f : 0.f;
-#pragma unroll
-        for (int r2 = kTPath - 2; r2 >= 0; --r2) {
-          if (r2 < d) {
-            float acc = 0.f;
-#pragma unroll
-            for (int s2 = r2 + 1; s2 < kTPath; ++s2) acc += y[s2] * akk[s2][r2];
-            y[r2] = -acc;
-          }
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < kTPath; ++s2)
-          if (s2 <= d)
-            *reinterpret_cast<uint32_t*>(Tbase + (p[s2] >> 4) * TTS + (p[s2] & 15)) = pack_hi_lo(y[s2]);
+      if (shallow4) {
+        t_row_in_registers<4, TTS>(anc, d, sAkk, Tbase);
+      } else if (d < 8) {
+        t_row_in_registers<8, TTS>(anc, d, sAkk, Tbase);
       } else {
         // deep paths: the same substitution with the row kept in LDS
         Tbase[(t >> 4) * TTS + (t & 15)] = 1.f;

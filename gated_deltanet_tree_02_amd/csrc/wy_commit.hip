@@ -6,29 +6,37 @@
 //     S_out = G_a S0 + sum_{i in A(a)} (G_a / G_i) u_i k_i^T
 // with G = 2^g2 from the verify workspace. accepted = -1 keeps S0.
 //
-// A streaming kernel: each workgroup owns a 16 KiB slab of one (b, h) state
-// (CR rows x dk), puts all of it in flight at once with 16-byte loads, then
-// applies the rank-|path| update from path data staged in LDS and writes the
-// slab back with 16-byte stores. In-place (S_out == S0) is safe: every
-// element is read and written by the same thread.
+// A streaming kernel with one workgroup (256 threads) per (b, h): every
+// thread puts its 16-byte pieces of the state in flight first (each load
+// instruction of the workgroup covers one contiguous stretch of rows), while
+// wave 0 reads the sequence's parents, all of its nodes' gate prefixes and the
+// accepted node in one round and forms the path coefficients without a
+// further load; the path's k rows and pseudo-values follow in one more round.
+// The rank-|path| update runs in registers and the state goes back with
+// 16-byte stores. In-place (S_out == S0) is safe: every element is read and
+// written by the same thread.
 #include "device_common.h"
 #include "launch.h"
 
 namespace gdn {
 namespace {
 
+constexpr int kCommitThreads = 256;
+
 template <class IO, int DK, int DV>
-__global__ __launch_bounds__(256) void wy_commit_kernel(const CommitArgs a) {
-  constexpr int CR0 = 4096 / DK;
-  constexpr int CR = CR0 < DV ? CR0 : DV;   // state rows per workgroup
-  constexpr int NCH = DV / CR;              // workgroups per (b, h)
-  constexpr int F4 = CR * DK / 4;           // float4 per workgroup
-  constexpr int NF = (F4 + 255) / 256;      // float4 per thread
+__global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const CommitArgs a) {
+  constexpr int NT = kCommitThreads;
+  constexpr int CPROW = DK / 4;             // float4 per state row
+  constexpr int F4 = DV * DK / 4;           // float4 per (b, h) state
+  constexpr int NF = F4 / NT;               // float4 per thread
+  constexpr int RSTEP = NT / CPROW;         // rows between a thread's pieces
   constexpr int PCH = 16;                   // path nodes staged per round
+  constexpr int EPC = 16 / (int)sizeof(IO); // io elements per 16-byte chunk
+  static_assert(F4 % NT == 0 && NT % CPROW == 0, "state tiles the workgroup");
   using io = io_traits<IO>;
 
-  __shared__ float sK[PCH * DK];
-  __shared__ float sW[PCH * CR];
+  __shared__ __align__(16) float sK[PCH * DK];
+  __shared__ __align__(16) float sW[PCH * DV];
   __shared__ int sPath[64];
   __shared__ float sCoef[64];
   __shared__ int sInfo[4];
@@ -36,45 +44,62 @@ __global__ __launch_bounds__(256) void wy_commit_kernel(const CommitArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int bh = blockIdx.x / NCH;
-  const int ch = blockIdx.x - bh * NCH;
+  const int bh = blockIdx.x;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int H = a.H;
-  const size_t sbase = (size_t)bh * DV * DK + (size_t)ch * CR * DK;
+  const size_t sbase = (size_t)bh * DV * DK;
+  const int c4 = tid % CPROW;               // this thread's float4 column
+  const int row0 = tid / CPROW;             // its rows: row0 + RSTEP * i
 
   float4 s[NF];
+  const float* __restrict__ src0 = a.S0 + sbase;
 #pragma unroll
-  for (int it = 0; it < NF; ++it) {
-    const int f = tid + 256 * it;
-    if (f < F4) s[it] = *reinterpret_cast<const float4*>(a.S0 + sbase + 4 * (size_t)f);
-  }
+  for (int i = 0; i < NF; ++i) s[i] = *reinterpret_cast<const float4*>(src0 + 4 * (tid + NT * i));
 
   if (tid < 64) {
-    const TreeLane tl = load_tree(b, a.T, a.max_nodes, a.offsets, a.parents, lane);
-    int st = tl.status;
-    const int acc = a.accepted[b];
-    if (st == GDN_TREE_OK && (acc < -1 || acc >= tl.n)) st = GDN_TREE_BAD_ACCEPTED;
-    int P = 0;
+    // node range, then parents, gate prefixes and the accepted node together
+    const int lo = a.offsets[b];
+    const int hi = a.offsets[b + 1];
+    const int n = hi - lo;
+    int st = GDN_TREE_OK;
+    int acc = -1, P = 0;
     float gA = 0.f;
-    if (st == GDN_TREE_OK && acc >= 0) {
-      const uint64_t path = shfl_u64(tl.anc, acc);
-      gA = a.g2[(size_t)(tl.lo + acc) * H + h];
-      if ((path >> lane) & 1ull) {
-        const int rank = __popcll(path & ((1ull << lane) - 1ull));
-        const float gi = a.g2[(size_t)(tl.lo + lane) * H + h];
-        sPath[rank] = lane;
-        sCoef[rank] = exp2f(gA - gi);
+    if (lo < 0 || hi > a.T || n < 1 || n > a.max_nodes) {
+      st = GDN_TREE_BAD_SIZE;
+    } else {
+      const int nl = lane < n ? lane : 0;
+      const int par_raw = a.parents[lo + nl];
+      const float g2_raw = a.g2[(size_t)(lo + nl) * H + h];
+      acc = a.accepted[b];
+      const int par = lane < n ? par_raw : -1;
+      if (__shfl(par, 0, kWave) != -1)
+        st = GDN_TREE_BAD_ROOT;
+      else if (__ballot(lane >= 1 && lane < n && (par < 0 || par >= lane)) != 0ull)
+        st = GDN_TREE_BAD_PARENT;
+      else if (acc < -1 || acc >= n)
+        st = GDN_TREE_BAD_ACCEPTED;
+      if (st == GDN_TREE_OK && acc >= 0) {
+        uint64_t anc;
+        float unused;
+        path_scan(par, lane, n, 0.f, anc, unused);
+        const uint64_t path = shfl_u64(anc, acc);
+        gA = __shfl(g2_raw, acc, kWave);
+        if ((path >> lane) & 1ull) {
+          const int rank = __popcll(path & ((1ull << lane) - 1ull));
+          sPath[rank] = lane;
+          sCoef[rank] = exp2f(gA - g2_raw);
+        }
+        P = __popcll(path);
       }
-      P = __popcll(path);
     }
     if (lane == 0) {
       sInfo[0] = st;
       sInfo[1] = acc;
       sInfo[2] = P;
-      sInfo[3] = tl.lo;
+      sInfo[3] = lo;
       sGA = exp2f(gA);
-      if (h == 0 && ch == 0) a.status[b] = st;
+      if (h == 0) a.status[b] = st;
     }
   }
   __syncthreads();
@@ -83,72 +108,70 @@ __global__ __launch_bounds__(256) void wy_commit_kernel(const CommitArgs a) {
   const int P = sInfo[2];
   const int lo = sInfo[3];
   if (st != GDN_TREE_OK) return;
+  if (acc < 0 && a.S_out == a.S0) return;   // keep S0, in place: nothing to write
   float* __restrict__ dst = a.S_out + sbase;
-  if (acc < 0) {
-    if (a.S_out != a.S0) {
+  // accepted = -1 copies S0: factor 1 (exact) and an empty path (P = 0), so
+  // both cases share one register set
+  const float GA = acc < 0 ? 1.f : sGA;
 #pragma unroll
-      for (int it = 0; it < NF; ++it) {
-        const int f = tid + 256 * it;
-        if (f < F4) *reinterpret_cast<float4*>(dst + 4 * (size_t)f) = s[it];
-      }
-    }
-    return;
-  }
-
-  const float GA = sGA;
-#pragma unroll
-  for (int it = 0; it < NF; ++it) {
-    s[it].x *= GA;
-    s[it].y *= GA;
-    s[it].z *= GA;
-    s[it].w *= GA;
+  for (int i = 0; i < NF; ++i) {
+    s[i].x *= GA;
+    s[i].y *= GA;
+    s[i].z *= GA;
+    s[i].w *= GA;
   }
   const IO* __restrict__ k = static_cast<const IO*>(a.k);
   for (int p0 = 0; p0 < P; p0 += PCH) {
     const int pc = P - p0 < PCH ? P - p0 : PCH;
-    for (int idx = tid; idx < pc * DK; idx += 256) {
-      const int p = idx / DK;
-      const int c = idx - p * DK;
-      sK[idx] = io::load1(k + ((size_t)(lo + sPath[p0 + p]) * H + h) * DK + c);
+    // k rows of the chunk's path nodes, 16-byte pieces, widened to fp32
+    for (int idx = tid; idx < pc * (DK / EPC); idx += NT) {
+      const int p = idx / (DK / EPC);
+      const int c = idx - p * (DK / EPC);
+      const IO* src = k + ((size_t)(lo + sPath[p0 + p]) * H + h) * DK + c * EPC;
+      float* d = sK + p * DK + c * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) *reinterpret_cast<float4*>(d + e) = io::load4(src + e);
     }
-    for (int idx = tid; idx < pc * CR; idx += 256) {
-      const int p = idx / CR;
-      const int r = idx - p * CR;
-      sW[idx] = sCoef[p0 + p] *
-                a.U[((size_t)(lo + sPath[p0 + p]) * H + h) * DV + (size_t)ch * CR + r];
+    // coefficient-scaled pseudo-values of the chunk, 16-byte pieces
+    for (int idx = tid; idx < pc * (DV / 4); idx += NT) {
+      const int p = idx / (DV / 4);
+      const int r = 4 * (idx - p * (DV / 4));
+      const float cf = sCoef[p0 + p];
+      float4 u = *reinterpret_cast<const float4*>(
+          a.U + ((size_t)(lo + sPath[p0 + p]) * H + h) * DV + r);
+      u.x *= cf;
+      u.y *= cf;
+      u.z *= cf;
+      u.w *= cf;
+      *reinterpret_cast<float4*>(sW + p * DV + r) = u;
     }
     __syncthreads();
+    for (int p = 0; p < pc; ++p) {
+      const float4 kk = *reinterpret_cast<const float4*>(sK + p * DK + 4 * c4);
 #pragma unroll
-    for (int it = 0; it < NF; ++it) {
-      const int f = tid + 256 * it;
-      if (f < F4) {
-        const int row = f / (DK / 4);
-        const int c = 4 * (f - row * (DK / 4));
-        for (int p = 0; p < pc; ++p) {
-          const float w = sW[p * CR + row];
-          const float4 kk = *reinterpret_cast<const float4*>(sK + p * DK + c);
-          s[it].x += w * kk.x;
-          s[it].y += w * kk.y;
-          s[it].z += w * kk.z;
-          s[it].w += w * kk.w;
-        }
+      for (int i = 0; i < NF; ++i) {
+        const float w = sW[p * DV + row0 + RSTEP * i];
+        s[i].x += w * kk.x;
+        s[i].y += w * kk.y;
+        s[i].z += w * kk.z;
+        s[i].w += w * kk.w;
       }
     }
     __syncthreads();
   }
+  // (the store addresses are recomputed from an opaque copy of the thread
+  // index instead of being held in registers since the loads)
+  int t2 = tid;
+  asm volatile("" : "+v"(t2));
 #pragma unroll
-  for (int it = 0; it < NF; ++it) {
-    const int f = tid + 256 * it;
-    if (f < F4) *reinterpret_cast<float4*>(dst + 4 * (size_t)f) = s[it];
-  }
+  for (int i = 0; i < NF; ++i)
+    *reinterpret_cast<float4*>(dst + 4 * (t2 + NT * i)) = s[i];
 }
 
 template <class IO, int D>
 hipError_t launch_t(const CommitArgs& a, hipStream_t s) {
-  constexpr int CR0 = 4096 / D;
-  constexpr int CR = CR0 < D ? CR0 : D;
   return launch_kernel(reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D>),
-                       (unsigned)(a.B * a.H * (D / CR)), 256u, s, a);
+                       (unsigned)(a.B * a.H), (unsigned)kCommitThreads, s, a);
 }
 
 template <class IO>

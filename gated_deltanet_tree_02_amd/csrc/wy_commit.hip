@@ -6,15 +6,28 @@
 //     S_out = G_a S0 + sum_{i in A(a)} (G_a / G_i) u_i k_i^T
 // with G = 2^g2 from the verify workspace. accepted = -1 keeps S0.
 //
-// A streaming kernel with one workgroup (256 threads) per (b, h): every
-// thread puts its 16-byte pieces of the state in flight first (each load
-// instruction of the workgroup covers one contiguous stretch of rows), while
-// wave 0 reads the sequence's parents, all of its nodes' gate prefixes and the
-// accepted node in one round and forms the path coefficients without a
-// further load; the path's k rows and pseudo-values follow in one more round.
-// The rank-|path| update runs in registers and the state goes back with
-// 16-byte stores. In-place (S_out == S0) is safe: every element is read and
-// written by the same thread.
+// A streaming kernel with one workgroup (four waves) per (b, h). Each thread
+// holds 16 float4 of the 64 KiB state, rows interleaved so that each load
+// instruction of the workgroup covers one contiguous stretch of rows. Waves
+// 1-3 put their state in flight at once. Wave 0 first reads the sequence's
+// parents, all of its nodes' gate prefixes and the accepted node in one round,
+// forms the path coefficients and stages the path's k rows and scaled
+// pseudo-values in LDS. With kPathFirst it issues its own state loads only
+// after that, so that no wave's wait for path data also waits for state:
+// because loads complete in order per wave, every wave then takes its state
+// in four pieces as they land, applying the rank-|path| update to each and
+// storing it while the later pieces are still in flight, and the writes
+// overlap the reads. That pays when every workgroup of the launch is resident
+// at once; when workgroups run in several generations, wave 0 loads its state
+// first and each workgroup takes its whole state as one piece
+// (kPathFirst = false), which keeps workgroups short and their reads and
+// writes in long runs. In-place
+// (S_out == S0) is safe: every element is read and written by the same thread.
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -23,16 +36,20 @@ namespace {
 
 constexpr int kCommitThreads = 256;
 
-template <class IO, int DK, int DV>
+template <class IO, int DK, int DV, bool kPathFirst>
 __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const CommitArgs a) {
   constexpr int NT = kCommitThreads;
   constexpr int CPROW = DK / 4;             // float4 per state row
   constexpr int F4 = DV * DK / 4;           // float4 per (b, h) state
-  constexpr int NF = F4 / NT;               // float4 per thread
-  constexpr int RSTEP = NT / CPROW;         // rows between a thread's pieces
+  constexpr int NF = F4 / NT;               // float4 per state thread
+  // pieces the state is taken in: four when the launch is resident at once,
+  // else one (all reads, then all writes, per workgroup)
+  constexpr int NPC = kPathFirst ? (NF >= 4 ? 4 : NF) : 1;
+  constexpr int FPC = NF / NPC;             // float4 per piece
+  constexpr int RSTEP = NT / CPROW;         // rows between a thread's float4s
   constexpr int PCH = 16;                   // path nodes staged per round
   constexpr int EPC = 16 / (int)sizeof(IO); // io elements per 16-byte chunk
-  static_assert(F4 % NT == 0 && NT % CPROW == 0, "state tiles the workgroup");
+  static_assert(F4 % NT == 0 && NT % CPROW == 0 && NF % NPC == 0, "state tiles the waves");
   using io = io_traits<IO>;
 
   __shared__ __align__(16) float sK[PCH * DK];
@@ -44,20 +61,48 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const CommitA
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const bool path_wave = tid < kWave;       // wave 0 (wave-uniform)
   const int bh = blockIdx.x;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int H = a.H;
   const size_t sbase = (size_t)bh * DV * DK;
-  const int c4 = tid % CPROW;               // this thread's float4 column
-  const int row0 = tid / CPROW;             // its rows: row0 + RSTEP * i
+  const IO* __restrict__ k = static_cast<const IO*>(a.k);
+
+  // threads [0, nthr) stage path rows [p0, p0 + pc) of the path in sK / sW
+  auto stage_path_rows = [&](int lo, int p0, int pc, int t, int nthr) {
+    for (int idx = t; idx < pc * (DK / EPC); idx += nthr) {
+      const int p = idx / (DK / EPC);
+      const int c = idx - p * (DK / EPC);
+      const IO* src = k + ((size_t)(lo + sPath[p0 + p]) * H + h) * DK + c * EPC;
+      float* d = sK + p * DK + c * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) *reinterpret_cast<float4*>(d + e) = io::load4(src + e);
+    }
+    for (int idx = t; idx < pc * (DV / 4); idx += nthr) {
+      const int p = idx / (DV / 4);
+      const int r = 4 * (idx - p * (DV / 4));
+      const float cf = sCoef[p0 + p];
+      float4 u = *reinterpret_cast<const float4*>(
+          a.U + ((size_t)(lo + sPath[p0 + p]) * H + h) * DV + r);
+      u.x *= cf;
+      u.y *= cf;
+      u.z *= cf;
+      u.w *= cf;
+      *reinterpret_cast<float4*>(sW + p * DV + r) = u;
+    }
+  };
 
   float4 s[NF];
-  const float* __restrict__ src0 = a.S0 + sbase;
+  auto load_state = [&]() {
+    const float* __restrict__ src0 = a.S0 + sbase;
 #pragma unroll
-  for (int i = 0; i < NF; ++i) s[i] = *reinterpret_cast<const float4*>(src0 + 4 * (tid + NT * i));
-
-  if (tid < 64) {
+    for (int i = 0; i < NF; ++i) s[i] = *reinterpret_cast<const float4*>(src0 + 4 * (tid + NT * i));
+  };
+  if (!path_wave || !kPathFirst) {
+    load_state();
+  }
+  if (path_wave) {
     // node range, then parents, gate prefixes and the accepted node together
     const int lo = a.offsets[b];
     const int hi = a.offsets[b + 1];
@@ -101,6 +146,11 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const CommitA
       sGA = exp2f(gA);
       if (h == 0) a.status[b] = st;
     }
+    wave_lds_sync();   // sPath / sCoef written by other lanes of this wave
+    if (kPathFirst && st == GDN_TREE_OK && P > 0) stage_path_rows(lo, 0, P < PCH ? P : PCH, lane, kWave);
+    // the staged rows are complete (their loads were waited for) before this
+    // wave's state loads go out
+    if constexpr (kPathFirst) load_state();
   }
   __syncthreads();
   const int st = sInfo[0];
@@ -110,68 +160,96 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const CommitA
   if (st != GDN_TREE_OK) return;
   if (acc < 0 && a.S_out == a.S0) return;   // keep S0, in place: nothing to write
   float* __restrict__ dst = a.S_out + sbase;
-  // accepted = -1 copies S0: factor 1 (exact) and an empty path (P = 0), so
-  // both cases share one register set
+  // accepted = -1 copies S0: factor 1 (exact) and an empty path (P = 0)
   const float GA = acc < 0 ? 1.f : sGA;
-#pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    s[i].x *= GA;
-    s[i].y *= GA;
-    s[i].z *= GA;
-    s[i].w *= GA;
-  }
-  const IO* __restrict__ k = static_cast<const IO*>(a.k);
-  for (int p0 = 0; p0 < P; p0 += PCH) {
-    const int pc = P - p0 < PCH ? P - p0 : PCH;
-    // k rows of the chunk's path nodes, 16-byte pieces, widened to fp32
-    for (int idx = tid; idx < pc * (DK / EPC); idx += NT) {
-      const int p = idx / (DK / EPC);
-      const int c = idx - p * (DK / EPC);
-      const IO* src = k + ((size_t)(lo + sPath[p0 + p]) * H + h) * DK + c * EPC;
-      float* d = sK + p * DK + c * EPC;
-#pragma unroll
-      for (int e = 0; e < EPC; e += 4) *reinterpret_cast<float4*>(d + e) = io::load4(src + e);
-    }
-    // coefficient-scaled pseudo-values of the chunk, 16-byte pieces
-    for (int idx = tid; idx < pc * (DV / 4); idx += NT) {
-      const int p = idx / (DV / 4);
-      const int r = 4 * (idx - p * (DV / 4));
-      const float cf = sCoef[p0 + p];
-      float4 u = *reinterpret_cast<const float4*>(
-          a.U + ((size_t)(lo + sPath[p0 + p]) * H + h) * DV + r);
-      u.x *= cf;
-      u.y *= cf;
-      u.z *= cf;
-      u.w *= cf;
-      *reinterpret_cast<float4*>(sW + p * DV + r) = u;
-    }
-    __syncthreads();
-    for (int p = 0; p < pc; ++p) {
-      const float4 kk = *reinterpret_cast<const float4*>(sK + p * DK + 4 * c4);
-#pragma unroll
-      for (int i = 0; i < NF; ++i) {
-        const float w = sW[p * DV + row0 + RSTEP * i];
-        s[i].x += w * kk.x;
-        s[i].y += w * kk.y;
-        s[i].z += w * kk.z;
-        s[i].w += w * kk.w;
-      }
-    }
+  if constexpr (!kPathFirst) {
+    // the whole workgroup stages the first round of path rows
+    if (P > 0) stage_path_rows(lo, 0, P < PCH ? P : PCH, tid, NT);
     __syncthreads();
   }
-  // (the store addresses are recomputed from an opaque copy of the thread
-  // index instead of being held in registers since the loads)
+  // per-lane offsets are taken from an opaque copy of the thread index, so
+  // that they are recomputed here rather than held since the loads
   int t2 = tid;
   asm volatile("" : "+v"(t2));
+  const int c4 = t2 % CPROW;                // this thread's float4 column
+  const int row0 = t2 / CPROW;              // its rows: row0 + RSTEP * i
+
+  // Each piece of the state is scaled, updated with every path row and stored
+  // as soon as it has landed. Paths longer than PCH nodes (rare: deep chains)
+  // walk the path in rounds per piece, the path wave re-staging each round.
 #pragma unroll
-  for (int i = 0; i < NF; ++i)
-    *reinterpret_cast<float4*>(dst + 4 * (t2 + NT * i)) = s[i];
+  for (int pcx = 0; pcx < NPC; ++pcx) {
+#pragma unroll
+    for (int j = 0; j < FPC; ++j) {
+      const int i = pcx * FPC + j;
+      s[i].x *= GA;
+      s[i].y *= GA;
+      s[i].z *= GA;
+      s[i].w *= GA;
+    }
+    for (int p0 = 0; p0 < P; p0 += PCH) {
+      const int pc = P - p0 < PCH ? P - p0 : PCH;
+      if (P > PCH) {
+        __syncthreads();   // the rows of the previous round are consumed
+        if (path_wave) stage_path_rows(lo, p0, pc, lane, kWave);
+        __syncthreads();
+      }
+      {
+        for (int p = 0; p < pc; ++p) {
+          const float4 kk = *reinterpret_cast<const float4*>(sK + p * DK + 4 * c4);
+#pragma unroll
+          for (int j = 0; j < FPC; ++j) {
+            const int i = pcx * FPC + j;
+            const float w = sW[p * DV + row0 + RSTEP * i];
+            s[i].x += w * kk.x;
+            s[i].y += w * kk.y;
+            s[i].z += w * kk.z;
+            s[i].w += w * kk.w;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FPC; ++j) {
+      const int i = pcx * FPC + j;
+      *reinterpret_cast<float4*>(dst + 4 * (t2 + NT * i)) = s[i];
+    }
+  }
+}
+
+// Workgroups of `kernel` the current device holds at once (occupancy per CU
+// times the CU count), cached per kernel and device.
+hipError_t resident_workgroups(const void* kernel, int block, int* out) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kernel, dev);
+  auto f = cache.find(key);
+  if (f == cache.end()) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0);
+    if (e != hipSuccess) return e;
+    f = cache.emplace(key, std::max(1, per_cu) * std::max(1, cus)).first;
+  }
+  *out = f->second;
+  return hipSuccess;
 }
 
 template <class IO, int D>
 hipError_t launch_t(const CommitArgs& a, hipStream_t s) {
-  return launch_kernel(reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D>),
-                       (unsigned)(a.B * a.H), (unsigned)kCommitThreads, s, a);
+  const void* first = reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, true>);
+  const void* state_first = reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, false>);
+  int slots = 0;
+  const hipError_t e = resident_workgroups(first, kCommitThreads, &slots);
+  if (e != hipSuccess) return e;
+  const int grid = a.B * a.H;
+  return launch_kernel(grid <= slots ? first : state_first, (unsigned)grid,
+                       (unsigned)kCommitThreads, s, a);
 }
 
 template <class IO>

@@ -200,8 +200,32 @@ __device__ __forceinline__ void t_row_in_registers(uint64_t anc, int d, const fl
       *reinterpret_cast<uint32_t*>(Tbase + (p[s2] >> 4) * TTS + (p[s2] & 15)) = pack_hi_lo(y[s2]);
 }
 
+// LDS bytes of one workgroup with the v staging rows unpadded (the layout
+// declared in the kernel below).
 template <class IO, int DK, int DV, int MT>
-__global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const VerifyArgs a) {
+constexpr int verify_lds_bytes() {
+  constexpr int NP = MT * 16, EPC = 16 / (int)sizeof(IO), CPR = DK / EPC, CPV = DV / EPC;
+  constexpr int st1 = 16 * (2 * NP * (CPR + 1) + NP * CPV);
+  constexpr int st2 = NP * DV * (4 + (int)sizeof(IO));
+  constexpr int nqt = MT * (MT + 1) / 2;
+  return (st1 > st2 ? st1 : st2) + 4 * (NP * (NP + 1) / 2) + 4 * 256 * nqt +
+         (int)sizeof(IO) * 256 * nqt + 16 * NP;
+}
+// Three workgroups per CU (6 waves per SIMD, at most 80 VGPRs, the v rows
+// staged unpadded) where the LDS allows three; else the default register
+// budget and padded v rows, which read faster at the same occupancy.
+template <class IO, int DK, int DV, int MT>
+constexpr bool verify_three_per_cu() {
+  return verify_lds_bytes<IO, DK, DV, MT>() <= 52 * 1024;
+}
+template <class IO, int DK, int DV, int MT>
+constexpr int verify_waves_per_simd() {
+  return verify_three_per_cu<IO, DK, DV, MT>() ? 6 : 1;
+}
+
+template <class IO, int DK, int DV, int MT>
+__global__ __launch_bounds__(64 * kVerifyWaves, (verify_waves_per_simd<IO, DK, DV, MT>()))
+void wy_verify_kernel(const VerifyArgs a) {
   constexpr int NW = kVerifyWaves;
   constexpr int NT = 64 * NW;                 // threads
   constexpr int NP = MT * 16;                 // padded node rows
@@ -210,11 +234,15 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
   constexpr int EPC = 16 / (int)sizeof(IO);   // io elements per 16-byte chunk
   constexpr int CPR = DK / EPC;               // chunks per q/k row
   constexpr int CPV = DV / EPC;               // chunks per v/o row
-  // U / o staging rows are unpadded; column r of node row t is stored at
+  // U and o staging rows are unpadded; column r of node row t is stored at
   // r ^ (16 * ((t >> 2) & 3)) (when dv >= 64), so that the four row groups of
-  // an MFMA result tile write disjoint banks while every 16-byte chunk of a
-  // row stays contiguous for the row-wise global stores.
+  // an MFMA result tile touch disjoint banks while every 16-byte chunk of a
+  // row stays contiguous for the row-wise global loads and stores.
   constexpr int SWZ = DV >= 64 ? 1 : 0;
+  // v rows: unpadded with the swizzle above when that buys the third
+  // workgroup per CU, else one spare chunk per row (like the k / q rows)
+  constexpr bool kVSwz = verify_three_per_cu<IO, DK, DV, MT>();
+  constexpr int kVPad = kVSwz ? 0 : 1;
   constexpr int TTW = 16;                     // row of a stored 16x16 tile
   constexpr int TTS = 16 * TTW;               // stored tile size
   constexpr int NTRI = NP * (NP + 1) / 2;     // packed lower triangle
@@ -228,7 +256,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
   struct Stage1 {             // until the state products are done
     uint4 k[NP * (CPR + 1)];
     uint4 q[NP * (CPR + 1)];
-    uint4 v[NP * (CPV + 1)];
+    uint4 v[NP * (CPV + kVPad)];
   };
   struct Stage2 {             // products with T and A_qk, output staging
     float u[NP * DV];
@@ -250,9 +278,9 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
   using AqT = typename std::conditional<std::is_same<IO, float>::value, float, __bf16>::type;
   __shared__ __align__(16) float sT[NQT * TTS];
   __shared__ __align__(16) AqT sAqk[NQT * TTS];
-  __shared__ uint64_t sAnc[64];
-  __shared__ float sG2[64];
-  __shared__ float sBeta[64];
+  __shared__ uint64_t sAnc[NP];
+  __shared__ float sG2[NP];
+  __shared__ float sBeta[NP];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -315,7 +343,12 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
     const int rel = idx - mat * NP * CPR;
     if (mat == 2) {
       const int row = rel / CPV;
-      sm.s1.v[chunk_slot<CPV>(row, rel - row * CPV)] = stg[it];
+      if constexpr (kVSwz) {
+        const int cs = ((rel - row * CPV) * EPC) ^ (SWZ * 16 * ((row >> 2) & 3));
+        *reinterpret_cast<uint4*>(reinterpret_cast<IO*>(sm.s1.v) + row * DV + cs) = stg[it];
+      } else {
+        sm.s1.v[chunk_slot<CPV>(row, rel - row * CPV)] = stg[it];
+      }
     } else {
       const int row = rel / CPR;
       (mat == 0 ? sm.s1.k : sm.s1.q)[chunk_slot<CPR>(row, rel - row * CPR)] = stg[it];
@@ -334,7 +367,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
   float g2;
   // (on a bad tree the scan still terminates; its results are not used)
   path_scan(par, lane, n, lane < n ? gate_log2(alpha_l) : 0.f, anc, g2);
-  if (wave == 0) {
+  if (wave == 0 && lane < NP) {
     sAnc[lane] = anc;
     sG2[lane] = g2;
     sBeta[lane] = lane < n ? beta_raw : 0.f;
@@ -504,8 +537,11 @@ __global__ __launch_bounds__(64 * kVerifyWaves) void wy_verify_kernel(const Veri
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * m + 4 * g + e;
         const float G = fast_exp2(sG2[t]);
-        const float vv = io::load1(reinterpret_cast<const IO*>(sm.s1.v) +
-                                   chunk_slot<CPV>(t, r / EPC) * EPC + r % EPC);
+        const float vv =
+            kVSwz ? io::load1(reinterpret_cast<const IO*>(sm.s1.v) + t * DV +
+                              (r ^ (SWZ * 16 * ((t >> 2) & 3))))
+                  : io::load1(reinterpret_cast<const IO*>(sm.s1.v) +
+                              chunk_slot<CPV>(t, r / EPC) * EPC + r % EPC);
         rX[m][e] = sBeta[t] * (vv - G * rX[m][e]);
         rY[m][e] = G * rY[m][e];
       }

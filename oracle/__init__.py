@@ -6,9 +6,11 @@ imports, links or calls anything here, and this package imports nothing from
 the library.
 
 The arithmetic lives in gdn_oracle.c (plain C, double precision, optional
-OpenMP over (sequence, head)); this module compiles it with gcc and marshals
-numpy arrays. wy.py holds a second, independent formulation (the tree-shaped
-WY form, dense linear algebra in numpy) used to check intermediate results.
+OpenMP over (sequence, head)) and, for the full-attention layers of a hybrid
+model (tree-masked attention and the accepted-path KV commit), in
+attn_oracle.c; this module compiles both with gcc and marshals numpy arrays.
+wy.py holds a second, independent formulation (the tree-shaped WY form, dense
+linear algebra in numpy) used to check intermediate results.
 """
 from __future__ import annotations
 
@@ -20,12 +22,13 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_SRCS = [os.path.join(_HERE, "gdn_oracle.c"), os.path.join(_HERE, "attn_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
 STATUS_OK, STATUS_BAD_ROOT, STATUS_BAD_PARENT, STATUS_BAD_SIZE, STATUS_BAD_ACCEPTED = 0, 1, 2, 3, 4
+STATUS_CACHE_FULL = 6
 
 
 def build(force: bool = True) -> str:
@@ -33,7 +36,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC", "-std=c11",
-               "-Wall", "-o", tmp, _SRC]
+               "-Wall", "-o", tmp] + _SRCS + ["-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -43,7 +46,8 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+                    os.path.getmtime(f) for f in _SRCS):
                 build(force=True)
             lib = ctypes.CDLL(_LIB_PATH)
             P = ctypes.c_void_p
@@ -55,6 +59,9 @@ def _load():
             lib.oracle_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
             lib.oracle_fork_replay.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
             lib.oracle_chain.argtypes = [I, I, I, P, P, P, P, P, P, P, P]
+            lib.oracle_tree_attn.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
+                                             ctypes.c_double, P, P]
+            lib.oracle_tree_attn_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
             _lib = lib
     return _lib
 
@@ -151,3 +158,43 @@ def chain(q, k, v, alpha, beta, S0):
     S = np.zeros((dv, dk), np.float64)
     lib.oracle_chain(n, dk, dv, _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(S0), _p(o), _p(S))
     return o, S
+
+
+# --------------------------------------------------------------- attention
+
+
+def tree_attn(offsets, parents, q, k, v, k_cache, v_cache, cache_len, scale=None,
+              max_nodes: int = 64):
+    """Tree-masked attention o[T,Hq,d] (float64) and status[B].
+
+    q [T,Hq,d]; k, v [T,Hkv,d]; k_cache, v_cache [B,Hkv,cap,d]; cache_len [B].
+    scale defaults to 1/sqrt(d)."""
+    lib = _load()
+    offsets, parents, cache_len = _i32(offsets), _i32(parents), _i32(cache_len)
+    q, k, v, kc, vc = (_f64(x) for x in (q, k, v, k_cache, v_cache))
+    B, T = len(offsets) - 1, len(parents)
+    Hq, d = q.shape[1], q.shape[2]
+    Hkv, cap = k.shape[1], kc.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros((T, Hq, d), np.float64)
+    status = np.zeros(max(B, 1), np.int32)
+    lib.oracle_tree_attn(B, Hq, Hkv, d, T, max_nodes, cap, _p(offsets), _p(parents), _p(q), _p(k),
+                         _p(v), _p(kc), _p(vc), _p(cache_len), float(scale), _p(o), _p(status))
+    return o, status[:B]
+
+
+def tree_attn_commit(offsets, parents, accepted, k, v, k_cache, v_cache, cache_len,
+                     max_nodes: int = 64):
+    """Caches after appending each accepted path: (k_cache, v_cache, cache_len, status)."""
+    lib = _load()
+    offsets, parents, accepted = _i32(offsets), _i32(parents), _i32(accepted)
+    k, v = _f64(k), _f64(v)
+    kc, vc = np.array(k_cache, np.float64), np.array(v_cache, np.float64)
+    lens = np.array(cache_len, np.int32)
+    B, T = len(offsets) - 1, len(parents)
+    Hkv, cap, d = kc.shape[1], kc.shape[2], kc.shape[3]
+    status = np.zeros(max(B, 1), np.int32)
+    lib.oracle_tree_attn_commit(B, Hkv, d, T, max_nodes, cap, _p(offsets), _p(parents),
+                                _p(accepted), _p(k), _p(v), _p(kc), _p(vc), _p(lens), _p(status))
+    return kc, vc, lens, status[:B]

@@ -13,6 +13,11 @@ Prints ONE JSON line. The metric is verified draft nodes per second per GDN
 layer (nodes of all trees, root included, times layers, per second), with the
 dominant kernel's roofline fraction, the fork/checkpoint baseline's time and
 memory, and the CPU oracle timed on a bounded sample as a reported baseline.
+
+A second leg ("fa_layers") times the 8 full-attention layers of the same
+32-layer hybrid stack on the same trees: tree-masked attention verify over a
+4096-row committed prefix (16 query heads sharing 4 K/V heads of 128, bf16)
+and the accepted-path KV commit, each layer with its own inputs and cache.
 """
 from __future__ import annotations
 
@@ -29,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tree-GDN verified draft nodes/s per layer (1 GPU) + % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "gated_deltanet_tree_02_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wy_verify_commit_c4_hbm_traffic.md")
 # sources whose hash ties a recorded counter measurement to the kernels it measured
@@ -73,6 +79,10 @@ def parse():
     p.add_argument("--mode", default="wy", choices=["wy", "fork"])
     p.add_argument("--fork-steps", type=int, default=3, help="timed steps of the fork baseline (0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0 = skip)")
+    p.add_argument("--attn-steps", type=int, default=10,
+                   help="timed steps of the full-attention leg (0 = skip)")
+    p.add_argument("--attn-only", action="store_true",
+                   help="run only the full-attention leg (profiling)")
     p.add_argument("--pmc-calibration", action="store_true",
                    help="after the timed legs, run a plain 256 MiB device copy three times "
                         "(reads and writes 256 MiB each): the known-size kernel that scales "
@@ -94,6 +104,123 @@ def algorithmic_bytes(w, io_bytes, gi):
     return verify, commit, fork_verify, fork_commit
 
 
+def attn_algorithmic_bytes(offsets, Hq, Hkv, d, cache_len, path_nodes):
+    """Bytes one full-attention layer must move: every node's query and
+    output, the tree's own K/V rows and each sequence's committed K/V rows
+    read once (verify); the accepted rows read and written once (commit)."""
+    B = len(offsets) - 1
+    T = int(offsets[-1])
+    meta = (B + 1) * 4 + T * 4 + B * 4 + B * 4
+    verify = (T * Hq * d * 2 * 2 + T * Hkv * d * 2 * 2
+              + int(sum(int(x) for x in cache_len)) * Hkv * d * 2 * 2 + meta)
+    commit = path_nodes * Hkv * d * 2 * 2 * 2 + meta + B * 4
+    return verify, commit
+
+
+def attention_leg(args, gt, gi, w_trees, dev):
+    """The full-attention layers of the hybrid stack on the GDN workload's
+    trees: per step every layer verified, then every layer committed; the
+    committed lengths are reset after each step (outside the kernel timings)."""
+    import numpy as np
+    import torch
+    c = gi.ATTN_CONFIGS["fa_c4"]
+    n_layers = 8
+    Hq, Hkv, d, cap, L0 = c["Hq"], c["Hkv"], c["d"], c["cap"], c["lens"][1]
+    B, T = w_trees.B, w_trees.T
+    t0 = time.time()
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    wl = gi.make_attn_workload(w_trees.parents_list, Hq, Hkv, d, 0, [L0] * B, seed=4321,
+                               accepted=w_trees.accepted)
+    offsets = torch.from_numpy(wl.offsets).to(dev)
+    parents = torch.from_numpy(wl.parents).to(dev)
+    accepted = torch.from_numpy(wl.accepted).to(dev)
+    lens0 = torch.full((n_layers, B), L0, dtype=torch.int32, device=dev)
+    lens = lens0.clone()
+    status = torch.zeros(B, dtype=torch.int32, device=dev)
+    desc = gt.make_attn_desc(B, Hq, Hkv, d, T, wl.max_nodes, cap, cap)
+    nbytes = gt.gdn_tree_attn_workspace_bytes(desc)
+    ver, com, keep = [], [], []
+    for layer in range(n_layers):
+        randn = lambda *shape: torch.randn(*shape, generator=g, device=dev).to(torch.bfloat16)
+        q, k, v = randn(T, Hq, d), randn(T, Hkv, d), randn(T, Hkv, d)
+        kc, vc = randn(B, Hkv, cap, d), randn(B, Hkv, cap, d)
+        o = torch.empty_like(q)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        cl = lens[layer]
+        ver.append(gt.prepare_attn_verify(desc, offsets, parents, q, k, v, kc, vc, cl, o, ws,
+                                          status))
+        com.append(gt.prepare_attn_commit(desc, offsets, parents, accepted, k, v, kc, vc, cl,
+                                          status))
+        keep.append((q, k, v, kc, vc, o, ws))
+    torch.cuda.synchronize()
+    log(f"attention leg: {n_layers} layers, cap {cap}, prefix {L0}, split workspace "
+        f"{nbytes / 2**20:.1f} MiB, gen {time.time() - t0:.1f}s")
+
+    def one_step():
+        for f in ver:
+            f()
+        for f in com:
+            f()
+        lens.copy_(lens0)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    steps = args.attn_steps
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for f in ver:
+            f()
+        ev[s][1].record(stream)
+        for f in com:
+            f()
+        ev[s][2].record(stream)
+        lens.copy_(lens0)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    st = status.cpu().numpy()
+    if np.any(st != 0):
+        raise RuntimeError(f"nonzero attention tree status {np.unique(st)}")
+    v_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in ev) / steps / n_layers
+    c_us = 1e3 * sum(e[1].elapsed_time(e[2]) for e in ev) / steps / n_layers
+    path = sum(len(gi.path_to_root(p, int(a))) if a >= 0 else 0
+               for p, a in zip(wl.parents_list, wl.accepted))
+    vb, cb = attn_algorithmic_bytes(wl.offsets, Hq, Hkv, d, [L0] * B, path)
+    flops = 0
+    for b in range(B):
+        n = int(wl.offsets[b + 1] - wl.offsets[b])
+        depth_sum = sum(len(gi.path_to_root(wl.parents_list[b], t)) for t in range(n))
+        flops += 4 * d * Hq * (n * L0 + depth_sum)          # QK^T and PV over the visible keys
+    kern = {
+        "verify": {"avg_us": round(v_us, 3), "alg_bytes": int(vb),
+                   "achieved_GBs": round(vb / v_us / 1e3, 1),
+                   "frac_hbm": round(vb / v_us / 1e3 / HBM_PEAK_GBS, 4),
+                   "flops": int(flops), "achieved_TFLOPs": round(flops / v_us / 1e6, 1),
+                   "frac_mfma_bf16": round(flops / v_us / 1e6 / MFMA_BF16_TFLOPS, 4)},
+        "commit": {"avg_us": round(c_us, 3), "alg_bytes": int(cb),
+                   "achieved_GBs": round(cb / c_us / 1e3, 1),
+                   "frac_hbm": round(cb / c_us / 1e3 / HBM_PEAK_GBS, 4)},
+    }
+    out = {
+        "workload": c["desc"].replace("64 seqs, tree k=3 d=3 (40 nodes)",
+                                      f"{B} seqs, the GDN workload's trees ({T} nodes)"),
+        "layers": n_layers, "steps": steps,
+        "ms_per_step": round(1e3 * elapsed / steps, 4),
+        "nodes_per_s_per_layer": round(T * n_layers * steps / elapsed, 1),
+        "roofline": {"kernel": "tree_attn_verify", "bound": "hbm", "achieved": kern["verify"]["achieved_GBs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern["verify"]["frac_hbm"],
+                     "traffic": None},
+        "kernels": kern, "split_workspace_bytes": int(nbytes),
+    }
+    log(f"attention: {out['ms_per_step']} ms/step, verify {v_us:.2f} us, commit {c_us:.2f} us per layer")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -113,6 +240,9 @@ def main():
     w = gi.make_config(args.config)
     log(f"workload {args.config}: B={w.B} T={w.T} layers={w.layers} gen {time.time() - t0:.1f}s")
     L = w.layers
+    if args.attn_only:
+        print(json.dumps({"fa_layers": attention_leg(args, gt, gi, w, dev)}), flush=True)
+        return
     io_t = torch.bfloat16 if w.io == "bf16" else torch.float32
     io_bytes = 2 if w.io == "bf16" else 4
     max_depth = w.max_depth()
@@ -264,6 +394,15 @@ def main():
                          f"fp64 per-path replay, {spent:.1f} s"}
         log(f"cpu oracle: {cpu}")
 
+    fa = None
+    if args.attn_steps > 0:
+        for ly in layers:
+            for key in [k for k in ly if k.startswith("o_") or k.startswith("ws_")]:
+                ly.pop(key)
+        ver = com = None
+        torch.cuda.empty_cache()
+        fa = attention_leg(args, gt, gi, w, dev)
+
     out = {
         "metric": METRIC, "value": round(nodes_per_s, 1), "unit": "nodes/s/layer", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -274,7 +413,7 @@ def main():
                    "dv": w.dv, "io": w.io, "state": "fp32", "mode": args.mode,
                    "parallelism": "single-gpu"},
         "roofline": roof, "kernels": kern, "cpu_baseline": cpu, "fork_baseline": fork,
-        "spec_state_per_request": spec,
+        "spec_state_per_request": spec, "fa_layers": fa,
     }
     print(json.dumps(out), flush=True)
 

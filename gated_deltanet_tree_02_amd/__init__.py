@@ -1,10 +1,10 @@
 """Python binding of libgdntree (MI355X / gfx950): tree verification of Gated
-DeltaNet layers.
+DeltaNet layers and of the full-attention layers beside them.
 
 The functions here carry the names of the C entry points declared in
-include/gdn_tree.h and only marshal arguments: they check torch tensors
-(device, dtype, shape, contiguity), pass their device pointers and the current
-HIP stream to the library, and raise GdnError for a nonzero gdn_status. Every
+include/gdn_tree.h and include/gdn_tree_attn.h and only marshal arguments:
+they check torch tensors (device, dtype, shape, contiguity), pass their device
+pointers and the current HIP stream to the library, and raise GdnError for a nonzero gdn_status. Every
 step of the computation runs in the library's HIP kernels; there is no
 fallback. Loading fails loudly when libgdntree.so has not been built.
 """
@@ -20,6 +20,8 @@ __all__ = [
     "gdn_tree_build", "gdn_tree_verify", "gdn_tree_commit", "gdn_tree_status_string",
     "DTYPE_F32", "DTYPE_BF16", "MODE_WY", "MODE_FORK", "MAX_NODES", "TREE_STATUS",
     "PreparedCall", "prepare_verify", "prepare_commit",
+    "GdnAttnDesc", "make_attn_desc", "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
+    "gdn_tree_attn_commit", "prepare_attn_verify", "prepare_attn_commit",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdntree.so")
@@ -28,7 +30,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE_WY, MODE_FORK = 0, 1
 MAX_NODES = 64
 TREE_STATUS = {0: "ok", 1: "bad root", 2: "bad parent", 3: "bad size", 4: "bad accepted",
-               5: "too deep"}
+               5: "too deep", 6: "cache full"}
 
 
 class GdnError(RuntimeError):
@@ -43,6 +45,15 @@ class GdnTreeDesc(ctypes.Structure):
         ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
         ("total_nodes", ctypes.c_int32), ("max_nodes", ctypes.c_int32),
         ("max_depth", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
+    ]
+
+
+class GdnAttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("total_nodes", ctypes.c_int32), ("max_nodes", ctypes.c_int32),
+        ("cache_capacity", ctypes.c_int32), ("max_cache_len", ctypes.c_int32),
     ]
 
 
@@ -70,6 +81,14 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_verify.restype = I
             lib.gdn_tree_commit.argtypes = [D, P, P, P, P, P, P, P, S, P, P]
             lib.gdn_tree_commit.restype = I
+            A = ctypes.POINTER(GdnAttnDesc)
+            lib.gdn_tree_attn_workspace_bytes.argtypes = [A]
+            lib.gdn_tree_attn_workspace_bytes.restype = S
+            lib.gdn_tree_attn_verify.argtypes = [A, P, P, P, P, P, P, P, P, ctypes.c_float, P, P,
+                                                 S, P, P]
+            lib.gdn_tree_attn_verify.restype = I
+            lib.gdn_tree_attn_commit.argtypes = [A, P, P, P, P, P, P, P, P, P, P]
+            lib.gdn_tree_attn_commit.restype = I
             lib.gdn_tree_status_string.argtypes = [I]
             lib.gdn_tree_status_string.restype = ctypes.c_char_p
             _lib = lib
@@ -89,6 +108,18 @@ def make_desc(num_seqs: int, num_heads: int, dk: int, dv: int, total_nodes: int,
 
 def gdn_tree_workspace_bytes(desc: GdnTreeDesc) -> int:
     return int(load_library().gdn_tree_workspace_bytes(ctypes.byref(desc)))
+
+
+def make_attn_desc(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   total_nodes: int, max_nodes: int, cache_capacity: int,
+                   max_cache_len: Optional[int] = None) -> GdnAttnDesc:
+    mcl = cache_capacity if max_cache_len is None else max_cache_len
+    return GdnAttnDesc(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                       int(total_nodes), int(max_nodes), int(cache_capacity), int(mcl))
+
+
+def gdn_tree_attn_workspace_bytes(desc: GdnAttnDesc) -> int:
+    return int(load_library().gdn_tree_attn_workspace_bytes(ctypes.byref(desc)))
 
 
 # ------------------------------------------------------------------ marshalling
@@ -217,7 +248,7 @@ class PreparedCall:
     def __init__(self, name, desc, args, stream, keep):
         self._fn = getattr(load_library(), name)
         self._name = name
-        self._desc = GdnTreeDesc.from_buffer_copy(desc)
+        self._desc = type(desc).from_buffer_copy(desc)
         self._args = (ctypes.byref(self._desc),) + tuple(args) + (stream,)
         self._keep = keep
 
@@ -239,3 +270,94 @@ def prepare_commit(desc, offsets, parents, accepted, k, S0, S_out, workspace, tr
     tensors = (offsets, parents, accepted, k, S0, S_out, workspace, tree_status)
     dev, args = _commit_args(desc, *tensors)
     return PreparedCall("gdn_tree_commit", desc, args, _stream(stream, dev), tensors)
+
+
+# ------------------------------------------------------------------ attention layers
+
+
+def _attn_verify_args(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len, scale, o,
+                      workspace, tree_status):
+    torch = _torch()
+    B, Hq, Hkv, T, d = (desc.num_seqs, desc.num_q_heads, desc.num_kv_heads, desc.total_nodes,
+                        desc.head_dim)
+    cap = desc.cache_capacity
+    dev = offsets.device
+    bf = torch.bfloat16
+    if scale is None:
+        scale = d ** -0.5
+    ws = None if workspace is None else _ptr(workspace, "workspace", torch.uint8, None, dev)
+    return dev, [
+        _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+        _ptr(parents, "parents", torch.int32, (T,), dev),
+        _ptr(q, "q", bf, (T, Hq, d), dev),
+        _ptr(k, "k", bf, (T, Hkv, d), dev),
+        _ptr(v, "v", bf, (T, Hkv, d), dev),
+        _ptr(k_cache, "k_cache", bf, (B, Hkv, cap, d), dev),
+        _ptr(v_cache, "v_cache", bf, (B, Hkv, cap, d), dev),
+        _ptr(cache_len, "cache_len", torch.int32, (B,), dev),
+        ctypes.c_float(float(scale)),
+        _ptr(o, "o", bf, (T, Hq, d), dev),
+        ws,
+        ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+        _ptr(tree_status, "tree_status", torch.int32, (B,), dev),
+    ]
+
+
+def _attn_commit_args(desc, offsets, parents, accepted, k, v, k_cache, v_cache, cache_len,
+                      tree_status):
+    torch = _torch()
+    B, Hkv, T, d = desc.num_seqs, desc.num_kv_heads, desc.total_nodes, desc.head_dim
+    cap = desc.cache_capacity
+    dev = offsets.device
+    bf = torch.bfloat16
+    return dev, [
+        _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+        _ptr(parents, "parents", torch.int32, (T,), dev),
+        _ptr(accepted, "accepted", torch.int32, (B,), dev),
+        _ptr(k, "k", bf, (T, Hkv, d), dev),
+        _ptr(v, "v", bf, (T, Hkv, d), dev),
+        _ptr(k_cache, "k_cache", bf, (B, Hkv, cap, d), dev),
+        _ptr(v_cache, "v_cache", bf, (B, Hkv, cap, d), dev),
+        _ptr(cache_len, "cache_len", torch.int32, (B,), dev),
+        _ptr(tree_status, "tree_status", torch.int32, (B,), dev),
+    ]
+
+
+def gdn_tree_attn_verify(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len, o,
+                         workspace, tree_status, scale=None, stream=None):
+    """Tree-masked attention of every node over its cached prefix and its root
+    path (bf16 tensors; scale defaults to 1/sqrt(head_dim))."""
+    torch = _torch()
+    dev, args = _attn_verify_args(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len,
+                                  scale, o, workspace, tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_attn_verify(ctypes.byref(desc), *args,
+                                                   _stream(stream, dev)),
+               "gdn_tree_attn_verify")
+
+
+def gdn_tree_attn_commit(desc, offsets, parents, accepted, k, v, k_cache, v_cache, cache_len,
+                         tree_status, stream=None):
+    """Append the accepted path's K/V rows to the caches and advance cache_len."""
+    torch = _torch()
+    dev, args = _attn_commit_args(desc, offsets, parents, accepted, k, v, k_cache, v_cache,
+                                  cache_len, tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_attn_commit(ctypes.byref(desc), *args,
+                                                   _stream(stream, dev)),
+               "gdn_tree_attn_commit")
+
+
+def prepare_attn_verify(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len, o,
+                        workspace, tree_status, scale=None, stream=None) -> PreparedCall:
+    tensors = (offsets, parents, q, k, v, k_cache, v_cache, cache_len, o, workspace, tree_status)
+    dev, args = _attn_verify_args(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len,
+                                  scale, o, workspace, tree_status)
+    return PreparedCall("gdn_tree_attn_verify", desc, args, _stream(stream, dev), tensors)
+
+
+def prepare_attn_commit(desc, offsets, parents, accepted, k, v, k_cache, v_cache, cache_len,
+                        tree_status, stream=None) -> PreparedCall:
+    tensors = (offsets, parents, accepted, k, v, k_cache, v_cache, cache_len, tree_status)
+    dev, args = _attn_commit_args(desc, *tensors)
+    return PreparedCall("gdn_tree_attn_commit", desc, args, _stream(stream, dev), tensors)

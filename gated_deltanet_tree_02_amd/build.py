@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "gdntree")
 LIB = os.path.join(PKG, "libgdntree.so")
 
-SOURCES = ["gdn_tree_api.cpp", "tree_build.hip", "wy_verify.hip", "wy_commit.hip", "fork.hip"]
+SOURCES = ["gdn_tree_api.cpp", "tree_build.hip", "wy_verify.hip", "wy_commit.hip", "fork.hip",
+           "tree_attn_api.cpp", "tree_attn.hip"]
 ARCH = "gfx950"
 
 
@@ -67,7 +68,8 @@ def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, "gdn_tree.h")]
+    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [
+        os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
     return any(os.path.getmtime(p) > t for p in deps)
 
 

@@ -136,8 +136,8 @@ const char* gdn_tree_status_string(int status) {
     case GDN_OK: return "ok";
     case GDN_ERR_NULL_PTR: return "a required pointer is NULL";
     case GDN_ERR_BAD_SHAPE: return "invalid sizes in the descriptor";
-    case GDN_ERR_UNSUPPORTED: return "unsupported dk/dv, io dtype or mode";
-    case GDN_ERR_WORKSPACE: return "workspace smaller than gdn_tree_workspace_bytes()";
+    case GDN_ERR_UNSUPPORTED: return "unsupported head size, io dtype, mode or head grouping";
+    case GDN_ERR_WORKSPACE: return "workspace smaller than the entry point's workspace_bytes()";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
   }
   return "unknown status";

@@ -73,7 +73,42 @@ struct ForkCommitArgs {
 
 // io: 0 = fp32, 1 = bf16 (gdn_dtype); d = dk = dv; mt = ceil(max_nodes / 16).
 hipError_t launch_tree_build(const TreeArgs& a, hipStream_t s);
+// tree-masked attention (bf16 io)
+struct AttnArgs {
+  int B, Hq, Hkv, T, max_nodes, cap, max_len;
+  int NS;            // splits of the cache per (sequence, K/V head)
+  int CL;            // cache rows per split (a multiple of 64)
+  float scale_log2;  // scale * log2(e)
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* cache_len;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  uint16_t* o;
+  float* part_o;     // [T, Hq, NS, d] (NS > 1)
+  float* part_ml;    // [T, Hq, NS, 2] (NS > 1)
+  int32_t* status;
+};
+
+struct AttnCommitArgs {
+  int B, Hkv, T, max_nodes, cap;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* accepted;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* kc;
+  uint16_t* vc;
+  int32_t* cache_len;
+  int32_t* status;
+};
+
 hipError_t launch_wy_verify(int io, int d, int mt, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_tree_attn(int d, const AttnArgs& a, hipStream_t s);
+hipError_t launch_tree_attn_commit(int d, const AttnCommitArgs& a, hipStream_t s);
 hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s);
 hipError_t launch_fork_level(int io, int d, const ForkArgs& a, hipStream_t s);
 hipError_t launch_fork_commit(int d, const ForkCommitArgs& a, hipStream_t s);

@@ -18,6 +18,13 @@ Workload shapes follow the pages:
 Value distributions (q,k ~ N(0,1) then L2-normalised, v ~ N(0,1),
 alpha ~ U(0.9,1), beta = sigmoid(N(0,1)), S0 ~ N(0, 0.1^2)) are the synthetic
 recipe of the five workload configurations this library is measured on.
+
+The full-attention layers of the same hybrid stack (rainlin-top "Qwen3.5 tree
+spec", section 3: one attention layer after every three GDN layers) get their
+own workloads (ATTN_CONFIGS): q, k, v and the committed K/V cache ~ N(0,1)
+per element, bf16, so scaled scores are O(1) as after the per-head norms of
+the handbook's reference model; cache rows past a sequence's committed length
+hold values too, which verification must never read into a result.
 """
 from __future__ import annotations
 
@@ -32,6 +39,7 @@ __all__ = [
     "CONFIGS", "Workload", "kary_parents", "chain_parents", "branching_parents",
     "random_tree_parents", "make_workload", "make_config", "round_to_bf16",
     "bf16_bits", "bf16_bits_to_f32", "path_to_root", "pick_accepted",
+    "ATTN_CONFIGS", "AttnWorkload", "make_attn_workload", "make_attn_config",
 ]
 
 # ---------------------------------------------------------------------------
@@ -294,3 +302,118 @@ def make_config(name: str, layers: Optional[int] = None, seed: Optional[int] = N
     return make_workload(trees, H=c["H"], dk=c["dk"], dv=c["dv"], io=c["io"],
                          layers=c["layers"] if layers is None else layers, seed=data_seed,
                          accepted=acc)
+
+
+# ---------------------------------------------------------------------------
+# Full-attention layer workloads (tree-masked attention verify and the KV
+# commit). The pages give no attention head shape; these use 16 query heads
+# sharing 4 K/V heads of size 128 beside the 16-head GDN layers.
+# ---------------------------------------------------------------------------
+
+ATTN_CONFIGS = {
+    "fa_small": dict(desc="8 seqs, tree k=2 d=3 (15 nodes), Hq=16, Hkv=4, d=128, "
+                          "ragged cached prefixes 0..600 (cap 640)",
+                     B=8, Hq=16, Hkv=4, d=128, tree="kary", k=2, depth=3, cap=640,
+                     lens=("uniform", 0, 600), seed=11),
+    "fa_c4": dict(desc="64 seqs, tree k=3 d=3 (40 nodes), Hq=16, Hkv=4, d=128, "
+                       "cached prefix 4096 per sequence (cap 4160)",
+                  B=64, Hq=16, Hkv=4, d=128, tree="kary", k=3, depth=3, cap=4160,
+                  lens=("fixed", 4096), seed=12),
+}
+
+
+@dataclasses.dataclass
+class AttnWorkload:
+    """Inputs of one full-attention layer under a draft tree. q, k, v hold the
+    exact stored values (bf16-representable fp32); the caches are kept as bf16
+    bit patterns [B, Hkv, cap, d] (cache_values widens one sequence)."""
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    cap: int
+    parents_list: List[List[int]]
+    offsets: np.ndarray          # [B+1] int32
+    parents: np.ndarray          # [T] int32
+    accepted: np.ndarray         # [B] int32
+    cache_len: np.ndarray        # [B] int32
+    q: np.ndarray                # [T, Hq, d] float32
+    k: np.ndarray                # [T, Hkv, d] float32
+    v: np.ndarray                # [T, Hkv, d] float32
+    kc_bits: np.ndarray          # [B, Hkv, cap, d] uint16
+    vc_bits: np.ndarray          # [B, Hkv, cap, d] uint16
+
+    @property
+    def T(self) -> int:
+        return int(self.offsets[-1])
+
+    @property
+    def max_nodes(self) -> int:
+        return max(len(p) for p in self.parents_list) if self.parents_list else 1
+
+    def cache_values(self, seqs=None):
+        """(k_cache, v_cache) as float32 for the listed sequences (all by default)."""
+        idx = slice(None) if seqs is None else np.asarray(list(seqs))
+        return bf16_bits_to_f32(self.kc_bits[idx]), bf16_bits_to_f32(self.vc_bits[idx])
+
+
+def make_attn_workload(parents_list: Sequence[Sequence[int]], Hq: int, Hkv: int, d: int,
+                       cap: int, cache_len: Sequence[int], seed=0,
+                       accepted: Optional[Sequence[int]] = None,
+                       threads: int = 0) -> AttnWorkload:
+    """Draw q, k, v and both caches for the given trees and committed lengths.
+
+    Seeding: SeedSequence(seed) spawns (q, k, v, accepted, caches); the cache
+    child spawns one child per sequence, which draws that sequence's K then V
+    cache rows, so a sequence's cache does not depend on the batch size."""
+    parents_list = [list(map(int, p)) for p in parents_list]
+    B = len(parents_list)
+    offsets = np.zeros(B + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum([len(p) for p in parents_list])
+    T = int(offsets[-1])
+    parents = np.array([x for p in parents_list for x in p], dtype=np.int32)
+    root = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    sq, sk, sv, sa, sc = root.spawn(5)
+    draw = lambda ss, shape: round_to_bf16(
+        np.random.Generator(np.random.PCG64(ss)).standard_normal(shape, dtype=np.float32))
+    q = draw(sq, (T, Hq, d))
+    k = draw(sk, (T, Hkv, d))
+    v = draw(sv, (T, Hkv, d))
+    kc = np.empty((B, Hkv, cap, d), np.uint16)
+    vc = np.empty((B, Hkv, cap, d), np.uint16)
+    children = sc.spawn(B)
+
+    def one(b):
+        g = np.random.Generator(np.random.PCG64(children[b]))
+        kc[b] = bf16_bits(g.standard_normal((Hkv, cap, d), dtype=np.float32))
+        vc[b] = bf16_bits(g.standard_normal((Hkv, cap, d), dtype=np.float32))
+
+    nthreads = threads or min(B, os.cpu_count() or 1, 16)
+    if nthreads > 1:
+        with concurrent.futures.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(one, range(B)))
+    else:
+        for b in range(B):
+            one(b)
+    if accepted is None:
+        arng = np.random.Generator(np.random.PCG64(sa))
+        acc = np.array([pick_accepted(arng, p) for p in parents_list], dtype=np.int32)
+    else:
+        acc = np.asarray(accepted, dtype=np.int32)
+    return AttnWorkload(B=B, Hq=Hq, Hkv=Hkv, d=d, cap=cap, parents_list=parents_list,
+                        offsets=offsets, parents=parents, accepted=acc,
+                        cache_len=np.asarray(cache_len, np.int32), q=q, k=k, v=v,
+                        kc_bits=kc, vc_bits=vc)
+
+
+def make_attn_config(name: str, seed: Optional[int] = None) -> AttnWorkload:
+    c = ATTN_CONFIGS[name]
+    tree_seed, data_seed = np.random.SeedSequence(c["seed"] if seed is None else seed).spawn(2)
+    rng = np.random.Generator(np.random.PCG64(tree_seed))
+    trees = [kary_parents(c["k"], c["depth"]) for _ in range(c["B"])]
+    kind = c["lens"][0]
+    if kind == "fixed":
+        lens = [c["lens"][1]] * c["B"]
+    else:
+        lens = rng.integers(c["lens"][1], c["lens"][2] + 1, size=c["B"]).tolist()
+    return make_attn_workload(trees, c["Hq"], c["Hkv"], c["d"], c["cap"], lens, seed=data_seed)

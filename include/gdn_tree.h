@@ -95,7 +95,8 @@ enum {
   GDN_TREE_BAD_PARENT = 2,    /* a non-root node's parent is < 0 or >= its index    */
   GDN_TREE_BAD_SIZE = 3,      /* N_b outside [1, max_nodes] or range outside [0,T]  */
   GDN_TREE_BAD_ACCEPTED = 4,  /* commit: accepted[b] outside [-1, N_b)              */
-  GDN_TREE_TOO_DEEP = 5       /* FORK mode: a node deeper than desc.max_depth       */
+  GDN_TREE_TOO_DEEP = 5,      /* FORK mode: a node deeper than desc.max_depth       */
+  GDN_TREE_CACHE_FULL = 6     /* attention commit: the path would overflow the cache */
 };
 /* Precedence: BAD_SIZE, then BAD_ROOT, then BAD_PARENT, then TOO_DEEP (FORK
  * verify) or BAD_ACCEPTED (commit). */

@@ -136,3 +136,81 @@ def sub_workload(w: gi.Workload, seqs, layers=None, heads=None) -> gi.Workload:
         v=w.v[L, rows][:, :, heads].copy(), alpha=w.alpha[L, rows][:, :, heads].copy(),
         beta=w.beta[L, rows][:, :, heads].copy(),
         S0=w.S0[L, np.array(seqs)][:, :, heads].copy())
+
+
+# ------------------------------------------------------------------ attention layers
+
+
+def bits_to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev()).view(torch.bfloat16)
+
+
+def dev_to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DeviceAttn:
+    """One attention layer's inputs on the GPU, outputs and workspace."""
+
+    def __init__(self, w: gi.AttnWorkload, max_nodes: int | None = None,
+                 max_cache_len: int | None = None):
+        self.w = w
+        lens = w.cache_len
+        mcl = max_cache_len if max_cache_len is not None else (
+            int(min(max(lens.max(initial=0), 0), w.cap)))
+        self.desc = gt.make_attn_desc(w.B, w.Hq, w.Hkv, w.d, w.T,
+                                      max_nodes if max_nodes is not None else min(64, w.max_nodes),
+                                      w.cap, mcl)
+        self.offsets = i32(w.offsets)
+        self.parents = i32(w.parents)
+        self.accepted = i32(w.accepted)
+        self.cache_len = i32(w.cache_len)
+        self.q = to_dev_io(w.q, "bf16")
+        self.k = to_dev_io(w.k, "bf16")
+        self.v = to_dev_io(w.v, "bf16")
+        self.kc = bits_to_dev(w.kc_bits)
+        self.vc = bits_to_dev(w.vc_bits)
+        self.o = torch.full_like(self.q, float("nan"))
+        nbytes = gt.gdn_tree_attn_workspace_bytes(self.desc)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev()) if nbytes else None
+        self.status = torch.full((w.B,), -7, dtype=torch.int32, device=dev())
+
+    def verify(self, scale=None):
+        gt.gdn_tree_attn_verify(self.desc, self.offsets, self.parents, self.q, self.k, self.v,
+                                self.kc, self.vc, self.cache_len, self.o, self.ws, self.status,
+                                scale=scale)
+
+    def commit(self):
+        gt.gdn_tree_attn_commit(self.desc, self.offsets, self.parents, self.accepted, self.k,
+                                self.v, self.kc, self.vc, self.cache_len, self.status)
+
+    def o_np(self):
+        return from_dev_io(self.o).astype(np.float64)
+
+
+def attn_sub(w: gi.AttnWorkload, seqs) -> gi.AttnWorkload:
+    """The listed sequences of an attention workload, renumbered."""
+    seqs = list(seqs)
+    rows = np.concatenate([np.arange(w.offsets[b], w.offsets[b + 1]) for b in seqs])
+    sizes = [int(w.offsets[b + 1] - w.offsets[b]) for b in seqs]
+    offsets = np.zeros(len(seqs) + 1, np.int32)
+    offsets[1:] = np.cumsum(sizes)
+    idx = np.array(seqs)
+    return gi.AttnWorkload(
+        B=len(seqs), Hq=w.Hq, Hkv=w.Hkv, d=w.d, cap=w.cap,
+        parents_list=[w.parents_list[b] for b in seqs], offsets=offsets,
+        parents=w.parents[rows].copy(), accepted=w.accepted[idx].copy(),
+        cache_len=w.cache_len[idx].copy(), q=w.q[rows].copy(), k=w.k[rows].copy(),
+        v=w.v[rows].copy(), kc_bits=w.kc_bits[idx].copy(), vc_bits=w.vc_bits[idx].copy())
+
+
+def oracle_attn(w: gi.AttnWorkload, max_nodes: int = 64, scale=None):
+    kc, vc = w.cache_values()
+    return oracle.tree_attn(w.offsets, w.parents, w.q, w.k, w.v, kc, vc, w.cache_len,
+                            scale=scale, max_nodes=max_nodes)
+
+
+def oracle_attn_commit(w: gi.AttnWorkload, max_nodes: int = 64):
+    kc, vc = w.cache_values()
+    return oracle.tree_attn_commit(w.offsets, w.parents, w.accepted, w.k, w.v, kc, vc,
+                                   w.cache_len, max_nodes=max_nodes)

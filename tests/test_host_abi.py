@@ -11,19 +11,25 @@ import gated_deltanet_tree_02_amd as gt
 from conftest import ROOT, read_golden
 
 HEADER = os.path.join(ROOT, "include", "gdn_tree.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_tree_\w+)\s*\(", text)))
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
+            names.update(re.findall(r"\b(gdn_tree_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     lib = gt.load_library()
     names = _declared_functions()
     assert names == sorted(["gdn_tree_workspace_bytes", "gdn_tree_build", "gdn_tree_verify",
-                            "gdn_tree_commit", "gdn_tree_status_string"])
+                            "gdn_tree_commit", "gdn_tree_status_string",
+                            "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
+                            "gdn_tree_attn_commit"])
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -109,3 +115,73 @@ def test_status_strings():
     for code in range(6):
         assert gt.gdn_tree_status_string(code)
     assert gt.gdn_tree_status_string(99) == "unknown status"
+
+
+# ------------------------------------------------------------------ attention layers
+
+ATTN_HEADER = os.path.join(ROOT, "include", "gdn_tree_attn.h")
+
+
+def test_attn_desc_layout_matches_header():
+    text = open(ATTN_HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} gdn_attn_desc;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(\w+)\s*[,;]", body)
+    assert fields == [f for f, _ in gt.GdnAttnDesc._fields_]
+    assert ctypes.sizeof(gt.GdnAttnDesc) == 4 * len(fields)
+
+
+def _split_bytes(T, Hq, d, ns):
+    rows = T * Hq * ns
+    return -(-rows * d * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+
+
+@pytest.mark.parametrize("B,Hkv,mcl,ns", [
+    (64, 4, 4096, 2),      # 256 (sequence, K/V head) pairs: two splits of 2048 rows
+    (64, 4, 0, 1),         # no cached prefix: one workgroup per pair
+    (1, 1, 4096, 64),      # one pair: 64 splits of one key block each
+    (1, 1, 100, 2),        # as many splits as key blocks
+    (512, 4, 8192, 1),     # enough pairs already
+    (3, 2, 1000, 16),      # 6 pairs want 86 splits; 16 blocks allow 16
+])
+def test_attn_workspace_follows_the_cache_split(B, Hkv, mcl, ns):
+    T, Hq, d = 10 * B, 4 * Hkv, 128
+    desc = gt.make_attn_desc(B, Hq, Hkv, d, T, 10, max(mcl, 1), mcl)
+    expect = 0 if ns == 1 else _split_bytes(T, Hq, d, ns)
+    assert gt.gdn_tree_attn_workspace_bytes(desc) == expect
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_seqs", -1, 2), ("num_q_heads", 0, 2), ("num_kv_heads", 0, 2), ("num_kv_heads", 3, 2),
+    ("head_dim", 96, 3), ("head_dim", 256, 3), ("total_nodes", -1, 2), ("max_nodes", 0, 2),
+    ("max_nodes", 65, 2), ("max_nodes", 40, 3),           # 8 query heads per K/V head x 40 > 256
+    ("cache_capacity", -1, 2), ("max_cache_len", 33, 2), ("max_cache_len", -1, 2),
+])
+def test_attn_bad_descriptors_rejected_before_launch(field, value, code):
+    lib = gt.load_library()
+    d = gt.make_attn_desc(2, 16, 2, 128, 10, 8, 32, 32)
+    setattr(d, field, value)
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: the check fails first
+    r = lib.gdn_tree_attn_verify(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
+                                 ctypes.c_float(0.1), fake, fake, 1 << 30, fake, None)
+    assert r == code
+    r = lib.gdn_tree_attn_commit(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
+                                 fake, None)
+    assert r == code
+    assert gt.gdn_tree_attn_workspace_bytes(d) == 0
+
+
+def test_attn_null_pointers_and_small_workspace():
+    lib = gt.load_library()
+    d = gt.make_attn_desc(1, 4, 1, 128, 10, 10, 4096, 4096)      # splits: workspace needed
+    need = gt.gdn_tree_attn_workspace_bytes(d)
+    assert need > 0
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake] * 8 + [ctypes.c_float(0.1), fake, fake, need - 1, fake, None]
+    assert lib.gdn_tree_attn_verify(ctypes.byref(d), *args) == 4
+    args = [fake] * 8 + [ctypes.c_float(0.1), fake, None, need, fake, None]
+    assert lib.gdn_tree_attn_verify(ctypes.byref(d), *args) == 1
+    args = [None] + [fake] * 7 + [ctypes.c_float(0.1), fake, fake, need, fake, None]
+    assert lib.gdn_tree_attn_verify(ctypes.byref(d), *args) == 1
+    assert lib.gdn_tree_attn_commit(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake,
+                                    fake, fake, None) == 1

@@ -39,30 +39,230 @@
 namespace gdn {
 namespace {
 
-constexpr int kAttnThreads = 1024;   // 16 waves, one 16-row query tile each
-constexpr int KB = 64;               // keys per staged block
-constexpr int PF = 2;                // key blocks in flight in registers
-constexpr float kMasked = -1.0e30f;  // score of an invisible key (base-2 domain)
+constexpr int KB = 64;                           // keys per staged block
+constexpr int kStages = 4;                       // key blocks resident in LDS (three in flight)
+constexpr float kMasked = -1.0e30f;              // score of an invisible key
+constexpr float kSlack = 8.f;                    // see attend_block
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (s_waitcnt with the export and LDS counters left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D>
-__global__ __launch_bounds__(kAttnThreads) void tree_attn_kernel(const AttnArgs a) {
-  constexpr int KSD = D / 32;                 // 16x16x32 steps over d
-  constexpr int DT = D / 16;                  // 16-row tiles of O^T (over d)
-  constexpr int KP = D + 8;                   // staged K row, 16 spare bytes (bank spread)
-  constexpr int VP = KB + 8;                  // staged V^T row (keys), 16 spare bytes
-  constexpr int CPB = KB * D / 8;             // 16-byte chunks of K (and of V) per block
-  constexpr int CPT = 2 * CPB / kAttnThreads; // chunks per thread per block
-  static_assert(2 * CPB % kAttnThreads == 0, "every thread stages whole chunks");
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
+// the wave's 64 lanes fill 1 KiB of LDS at lds_base + 16 * lane, lane l
+// reading its own address. Issued as inline assembly so that the compiler
+// does not wait for every such load before each LDS read; the kernel waits
+// for them itself (vmcnt, then a barrier). M0 holds the LDS base for the
+// instruction and is restored afterwards.
+__device__ __forceinline__ void load_lds_16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(src)
+      : "memory");
+}
 
-  __shared__ __align__(16) uint16_t sK[KB * KP];
-  __shared__ __align__(16) uint16_t sVt[D * VP];
+// Transposing LDS read (gfx950): in each group of 16 lanes, lane i receives
+// element i % 4 of the 8 bytes read by lanes 4e + i / 4, e = 0..3. With lane
+// j of the group reading row R0 + j / 4, columns C0 + 4 (j % 4) .. +3 of a
+// row-major bf16 matrix, lane i therefore holds column C0 + i of rows
+// R0 .. R0 + 3: a column of four consecutive rows, the MFMA operand layout.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const lds_char* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// LDS layout of a staged block: 64 key rows of D bf16, row-major, the 16-byte
+// chunk c of row r stored at chunk position c ^ f(r). The LDS serves 256
+// bytes (64 banks) per cycle; f is chosen so that the 16 rows of a K
+// fragment read (same logical chunk) fill 16 different 16-byte bank groups,
+// and so that the 8 rows of a half transposing read (two chunks each) fill
+// them as well: for 256-byte rows f is a bijection on r mod 16 with f / 2 a
+// bijection on r mod 8; for 128-byte rows (two per bank window) the same
+// holds per row parity.
+template <int D>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+
+// Online-softmax state and output accumulator of one 16-row query tile.
+template <int D>
+struct Tile {
+  bf16x8 qf[D / 32];     // B operand of S^T = K Q^T: column = query row, k = d 32s + 8g .. +7,
+                         // holding q * scale * log2(e)
+  f32x4 o[D / 16];       // O^T rows d = 16 dt + 4g + e, column = query row
+  float m, l;            // row reference (base-2 units) and this lane's part of the sum
+  uint64_t anc;          // ancestor bits of the lane's node
+};
+
+// Lane byte offsets of the MFMA operand reads inside a staged block. A row
+// starts at a multiple of 2D bytes and the permuted chunk index occupies the
+// address bits just below, so a chunk permutation is an XOR on the address:
+// K fragment (kt, s) at (k ^ 64 s) + 32 D kt, V^T fragment (mg, dt, half) at
+// (v ^ 32 dt) + 64 D mg + 32 D half.
+struct LaneOffsets {
+  int k, v;
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets lane_offsets(int g, int l16) {
+  constexpr int RB = 2 * D;
+  LaneOffsets o;
+  // K fragment: rows 16 kt + l16, logical chunk 4s + g
+  o.k = l16 * RB | ((swz_key<D>(l16) ^ g) << 4);
+  // V^T fragment: transposing reads of rows 32 mg + 4g + i (+16), i = l16 / 4,
+  // columns 16 dt + 4 (l16 % 4) .. +3: logical chunk 2 dt + h, h = (l16 % 4) / 2,
+  // byte 8 (l16 % 2) of it
+  const int row = 4 * g + (l16 >> 2);
+  const int h = (l16 & 3) >> 1;
+  o.v = row * RB | ((swz_key<D>(row) ^ h) << 4) | ((l16 & 1) << 3);
+  return o;
+}
+
+// Scores, online softmax and output update of one staged key block (K at
+// sK, V right after it) for the wave's first NT query tiles; each K and V
+// fragment read from LDS serves all of them. The query fragments hold
+// q * scale * log2(e), so a score is already in base-2 units; the MFMA starts
+// from -m, the lane's reference, and returns x - m directly.
+//
+// FULL: every key of the block is visible; otherwise bit 16 kt + e of vm[u]
+// says whether key 16 kt + 4g + e is visible to the lane's row of tile u (the
+// row's ancestor bits shifted by 4g for the tree block, a prefix of keys for
+// the last cache block), and invisible keys get x - m = -1e30, weight 0.
+//
+// first (the split's first block): the reference is set to the row maximum.
+// Later blocks raise it only when some lane of the wave sees x - m > kSlack,
+// so the O^T rescale is rare and every weight stays below 2^kSlack; the
+// final o = O^T / l does not depend on the reference.
+template <int D, int NT, bool FULL, int TPW>
+__device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char* sK,
+                                             const LaneOffsets& lo, const uint64_t (&vm)[TPW],
+                                             bool first) {
+  constexpr int KSD = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int RB = 2 * D;
+  const lds_char* sV = sK + KB * RB;
+
+  // the block in two halves of 32 keys (key group mg = key tiles 2mg, 2mg+1)
+#pragma unroll
+  for (int mg = 0; mg < 2; ++mg) {
+    // S^T tiles: lane holds its row of tile u and keys 16 kt + 4g + e, as x - m
+    f32x4 acc[NT][2];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const float c0 = (first && mg == 0) ? 0.f : -tl[u].m;
+      acc[u][0] = f32x4{c0, c0, c0, c0};
+      acc[u][1] = acc[u][0];
+    }
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      bf16x8 ka[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        ka[h] = *(const lds_bf16x8*)(sK + (lo.k ^ (64 * s)) + 16 * RB * (2 * mg + h));
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) acc[u][h] = mfma_k32(ka[h], tl[u].qf[s], acc[u][h]);
+    }
+
+    bf16x8 pk[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      Tile<D>& T = tl[u];
+      if (!FULL) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (((vm[u] >> (32 * mg + 16 * h + e)) & 1ull) == 0) acc[u][h][e] = kMasked;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(acc[u][0][0], acc[u][0][1]), fmaxf(acc[u][0][2], acc[u][0][3])),
+                       fmaxf(fmaxf(acc[u][1][0], acc[u][1][1]), fmaxf(acc[u][1][2], acc[u][1][3])));
+      const bool set = first && mg == 0;
+      if (set || __ballot(mx > kSlack) != 0ull) {    // wave-uniform
+        // raise each row's reference to its maximum (the four lanes of a
+        // row, g = 0..3, hold its keys between them)
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float delta = set ? mx : fmaxf(mx, 0.f);
+        T.m = set ? mx : T.m + delta;
+        acc[u][0] -= delta;
+        acc[u][1] -= delta;
+        if (!set) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          T.l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) T.o[dt] *= alpha;
+        }
+      }
+      // P^T as the B operand of 16x16x32 over the 32 keys: k slot 8g + i
+      // holds key 32 mg + 4g + i (i < 4) or 32 mg + 16 + 4g + i - 4
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(acc[u][h][e]);
+          T.l += p;
+          pk[u][4 * h + e] = (__bf16)p;
+        }
+      }
+    }
+    // O^T += V^T P^T: A = V^T rows d = 16 dt + l16 over the same key slots,
+    // read column-wise from the row-major V block; each V fragment serves
+    // every tile of the wave
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const lds_char* p1 = sV + (lo.v ^ (32 * dt)) + 32 * RB * mg;
+      const bf16x4 v1 = lds_read_tr16(p1);
+      const bf16x4 v2 = lds_read_tr16(p1 + 16 * RB);
+      const bf16x8 va = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) tl[u].o[dt] = mfma_k32(va, pk[u], tl[u].o[dt]);
+    }
+  }
+}
+
+// W waves, wave w owning query tiles w, w + W, ... (TPW of them at most):
+// W * TPW * 16 >= the rows of a (sequence, K/V head).
+template <int N>
+__device__ __forceinline__ void wait_blocks_ahead(int ahead) {
+  if (ahead >= 2) wait_vmem<2 * N>();
+  else if (ahead == 1) wait_vmem<N>();
+  else wait_vmem<0>();
+}
+
+template <int D, int W, int TPW>
+__global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int KSD = D / 32;                 // 16x16x32 steps over d (scores)
+  constexpr int DT = D / 16;                  // 16-row tiles of O^T (over d)
+  constexpr int MAT = KB * 2 * D;             // bytes of one staged matrix (K or V)
+  constexpr int STAGE = 2 * MAT;              // K block then V block
+  constexpr int NU = STAGE / 1024;            // 1 KiB wave loads per block
+  constexpr int LMAX = (NU + W - 1) / W;      // loads per thread per block: LMAX or LMAX - 1
+  static_assert(MAT % 1024 == 0, "a wave's 1 KiB load falls in one matrix");
+
+  __shared__ __align__(16) char smem[kStages * STAGE];
   __shared__ uint64_t sAnc[64];
   __shared__ int sStatus;
 
@@ -106,31 +306,64 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_kernel(const AttnArgs 
   const int st = __builtin_amdgcn_readfirstlane(sStatus);
   if (split == 0 && kvh == 0 && tid == 0) a.status[b] = st;
 
-  // ---- this lane's query row: the transposed score / output column
+  // ---- query rows: wave w owns tiles w, w + waves, ... (rows 16 tile + l16
+  // of the G * n rows of the K/V head, query-head-major, node inner)
   const int R = range_ok ? G * n : 0;
-  const int r = 16 * wave + l16;
-  const bool rv = r < R;
-  const int hg = rv ? r / n : 0;
-  const int t = rv ? r - hg * n : 0;
-  const int h = kvh * G + hg;
-  const size_t orow = ((size_t)(lo + t) * a.Hq + h);   // row of o / the partials
+  const int ntiles = (R + 15) >> 4;
+  const int nt = ntiles > wave ? (ntiles - wave + W - 1) / W : 0;   // wave-uniform
+  size_t orow[TPW];
+  bool rv[TPW];
+  Tile<D> tl[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int r = 16 * (wave + W * u) + l16;
+    rv[u] = r < R;
+    const int hg = rv[u] ? r / n : 0;
+    const int t = rv[u] ? r - hg * n : 0;
+    orow[u] = (size_t)(lo + t) * a.Hq + kvh * G + hg;
+    tl[u].anc = sAnc[t];
+    tl[u].m = 0.f;
+    tl[u].l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) tl[u].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (st != GDN_TREE_OK) {
     // rows of a rejected sequence (with a valid node range) are zero
-    if (rv) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (!rv[u]) continue;
       if (NS == 1) {
         for (int c = 4 * g; c < D; c += 16)
-          *reinterpret_cast<uint2*>(a.o + orow * D + c) = make_uint2(0u, 0u);
+          *reinterpret_cast<uint2*>(a.o + orow[u] * D + c) = make_uint2(0u, 0u);
       } else {
         for (int c = 4 * g; c < D; c += 16)
-          *reinterpret_cast<float4*>(a.part_o + (orow * NS + split) * D + c) =
+          *reinterpret_cast<float4*>(a.part_o + (orow[u] * NS + split) * D + c) =
               make_float4(0.f, 0.f, 0.f, 0.f);
-        if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (orow * NS + split) * 2) =
+        if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (orow[u] * NS + split) * 2) =
             make_float2(kMasked, 0.f);
       }
     }
     return;
   }
+
+  // query fragments, scaled to base-2 score units and rounded to bf16,
+  // waited for before the key blocks are issued (the block waits below count
+  // only the block loads)
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const uint16_t* qrow = a.q + orow[u] * D;
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      const uint4 v = rv[u] ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
+                            : make_uint4(0u, 0u, 0u, 0u);
+      const bf16x8 x = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tl[u].qf[s][e] = (__bf16)((float)x[e] * a.scale_log2);
+    }
+  }
+  wait_vmem<0>();
+  const LaneOffsets lofs = lane_offsets<D>(g, l16);
 
   // ---- key range of this split: cache rows [c0, c1), then the tree slots
   // (last split only)
@@ -138,208 +371,140 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_kernel(const AttnArgs 
   const int c1 = min(c0 + a.CL, L);
   const int ncb = (c1 - c0 + KB - 1) / KB;
   const int nblk = ncb + (split == NS - 1 ? 1 : 0);
-
   const size_t kvbase = ((size_t)b * a.Hkv + kvh) * a.cap;   // cache row 0 of (b, kvh)
-  // The chunks this thread stages per block: chunk id = tid + 1024 i; ids
-  // below CPB are K chunks, the rest V chunks; within a matrix, consecutive
-  // ids walk the 64 keys first, so a wave stages one 16-byte column of 64 rows.
-  // Keys that are masked (past the split's cache rows, or unused tree slots)
-  // read a valid row instead: finite values whose weight is exactly zero.
-  auto issue_block = [&](int j, u32x4 (&reg)[CPT]) {
+  const uint32_t smem_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char*)smem);
+
+  // Loads of block j into stage s. Wave w issues the 1 KiB units
+  // w, w + W, ... of the stage; in unit u lane l fills LDS slot q = 64 u + l
+  // (16 bytes; consecutive per wave, as the instruction requires): slots
+  // below 64 * CPR are K, the rest V; slot q holds row q / CPR, stored chunk
+  // q % CPR, i.e. logical chunk (q % CPR) ^ f(row). Keys past the split's
+  // cache rows, and unused tree slots, read a valid row instead: finite
+  // values that the mask gives zero weight.
+  const int nload = (NU - wave + W - 1) / W;  // this wave's loads per block (wave-uniform)
+  auto issue_block = [&](int j, int s) {
     const bool tree = j >= ncb;
     const int p0 = c0 + j * KB;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int id = tid + kAttnThreads * i;
-      const int mat = id >= CPB ? 1 : 0;
-      const int rem = id - mat * CPB;
-      const int kk = rem % KB;
-      const int c = rem / KB;
-      const uint16_t* base;
+    for (int i = 0; i < LMAX; ++i) {
+      if (i == LMAX - 1 && i >= nload) break;
+      const int wbase = 64 * (wave + W * i);  // wave-uniform
+      const int mat = wbase >= KB * CPR ? 1 : 0;
+      const int rem = wbase + lane - mat * KB * CPR;
+      const int row = rem / CPR;
+      const int chunk = (rem % CPR) ^ swz_key<D>(row);
+      const uint16_t* src;
       if (!tree) {
-        const int p = min(p0 + kk, c1 - 1);
-        base = (mat ? a.vc : a.kc) + (kvbase + p) * D;
+        const int p = min(p0 + row, c1 - 1);
+        src = (mat ? a.vc : a.kc) + kvbase * D + (p * D + 8 * chunk);
       } else {
-        const int node = kk < n ? kk : 0;
-        base = (mat ? a.v : a.k) + ((size_t)(lo + node) * a.Hkv + kvh) * D;
+        const int node = row < n ? row : 0;
+        src = (mat ? a.v : a.k) + ((size_t)(lo + node) * a.Hkv + kvh) * D + 8 * chunk;
       }
-      reg[i] = *reinterpret_cast<const u32x4*>(base + 8 * c);
-    }
-  };
-  auto stage_block = [&](const u32x4 (&reg)[CPT]) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int id = tid + kAttnThreads * i;
-      const int mat = id >= CPB ? 1 : 0;
-      const int rem = id - mat * CPB;
-      const int kk = rem % KB;
-      const int c = rem / KB;
-      if (mat == 0) {
-        *reinterpret_cast<u32x4*>(sK + kk * KP + 8 * c) = reg[i];
-      } else {
-        const uint32_t w[4] = {reg[i][0], reg[i][1], reg[i][2], reg[i][3]};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sVt[(8 * c + 2 * e) * VP + kk] = (uint16_t)(w[e] & 0xffffu);
-          sVt[(8 * c + 2 * e + 1) * VP + kk] = (uint16_t)(w[e] >> 16);
-        }
-      }
+      load_lds_16(src, __builtin_amdgcn_readfirstlane(smem_base + s * STAGE + 16 * wbase));
     }
   };
 
-  // query fragments: B operand of S^T = K Q^T (lane: column = query row,
-  // k = d 32s + 8g .. +7); issued before the key blocks
-  bf16x8 qf[KSD];
-  {
-    const uint16_t* qrow = a.q + orow * D;
 #pragma unroll
-    for (int s = 0; s < KSD; ++s) {
-      const uint4 u = rv ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
-                         : make_uint4(0u, 0u, 0u, 0u);
-      qf[s] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-  // two blocks in flight: ring0 holds even blocks, ring1 odd ones; a block
-  // past the last is re-issued as the last (never computed), so every step
-  // issues the same loads and the waits for in-flight blocks stay exact
-  u32x4 ring0[CPT], ring1[CPT];
-  if (nblk > 0) {
-    issue_block(0, ring0);
-    issue_block(min(1, nblk - 1), ring1);
-  }
-  const uint64_t anc_t = sAnc[t];
-  const bool active = 16 * wave < R;          // wave-uniform: the tile holds query rows
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < nblk) issue_block(j, j);
 
-  float m = kMasked;                          // running max (base-2 domain)
-  float lsum = 0.f;                           // this lane's part of the running sum
-  f32x4 oacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < nblk; ++j) {
+    // block j's loads are this thread's oldest outstanding ones
+    const int ahead = min(kStages - 2, nblk - 1 - j);
+    static_assert(kStages - 2 <= 2, "wait_blocks_ahead covers two blocks ahead");
+    if (nload == LMAX) wait_blocks_ahead<LMAX>(ahead);
+    else wait_blocks_ahead<(LMAX > 1 ? LMAX - 1 : 1)>(ahead);
+    __syncthreads();                          // every thread's part landed; stage j-1 is free
+    if (j + kStages - 1 < nblk) issue_block(j + kStages - 1, (j + kStages - 1) % kStages);
+    if (nt == 0) continue;
 
-  auto step = [&](int j, u32x4 (&reg)[CPT]) {
-    __syncthreads();                          // the previous block is consumed
-    stage_block(reg);
-    issue_block(min(j + PF, nblk - 1), reg);
-    __syncthreads();
-    if (!active || j >= nblk) return;
+    const lds_char* sK = (const lds_char*)smem + (j % kStages) * STAGE;
     const bool tree = j >= ncb;
-    const int p0 = c0 + j * KB;
-    // S^T tiles: lane holds query row l16 and keys 16 kt + 4g + e
-    float x[4][4];
-    float mb = kMasked;
+    const int lim = tree ? KB : c1 - (c0 + j * KB);   // cache keys below lim are visible
+    const bool first = j == 0;
+    if (!tree && lim >= KB) {
+      const uint64_t vm[TPW] = {};
+      if (TPW > 1 && nt > 1) attend_block<D, TPW, true, TPW>(tl, sK, lofs, vm, first);
+      else attend_block<D, 1, true, TPW>(tl, sK, lofs, vm, first);
+    } else {
+      const int lm = lim - 4 * g;             // lane keys 16 kt + e below lm are visible
+      uint64_t vm[TPW];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KSD; ++s) {
-        const bf16x8 ka = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(sK + (16 * kt + l16) * KP + 32 * s + 8 * g));
-        acc = mfma_k32(ka, qf[s], acc);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = 16 * kt + 4 * g + e;
-        const bool vis = rv && (tree ? ((anc_t >> kk) & 1ull) != 0 : p0 + kk < c1);
-        x[kt][e] = vis ? acc[e] * a.scale_log2 : kMasked;
-        mb = fmaxf(mb, x[kt][e]);
-      }
+      for (int u = 0; u < TPW; ++u)
+        vm[u] = tree ? tl[u].anc >> (4 * g)
+                     : (lm >= 64 ? ~0ull : lm <= 0 ? 0ull : (1ull << lm) - 1ull);
+      if (TPW > 1 && nt > 1) attend_block<D, TPW, false, TPW>(tl, sK, lofs, vm, first);
+      else attend_block<D, 1, false, TPW>(tl, sK, lofs, vm, first);
     }
-    mb = fmaxf(mb, __shfl_xor(mb, 16, kWave));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
-    const float m_new = fmaxf(m, mb);
-    const float alpha = exp2f(m - m_new);
-    m = m_new;
-    lsum *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      oacc[dt][0] *= alpha;
-      oacc[dt][1] *= alpha;
-      oacc[dt][2] *= alpha;
-      oacc[dt][3] *= alpha;
-    }
-    bf16x4 pk[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = x[kt][e] > 0.5f * kMasked ? exp2f(x[kt][e] - m_new) : 0.f;
-        lsum += p;
-        pk[kt][e] = (__bf16)p;
-      }
-    }
-    // O^T += V^T P^T: A = V^T rows 16 dt + l16, keys 16 kt + 4g .. +3
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x4 va = __builtin_bit_cast(
-            bf16x4, *reinterpret_cast<const uint2*>(sVt + (16 * dt + l16) * VP + 16 * kt + 4 * g));
-        oacc[dt] = mfma_k16(va, pk[kt], oacc[dt]);
-      }
-    }
-  };
-  for (int j = 0; j < nblk; j += 2) {
-    step(j, ring0);
-    step(j + 1, ring1);
   }
 
-  // ---- results: lane (g, l16) holds O^T rows d = 16 dt + 4g + e of query row r
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
-  if (!rv) return;
-  if (NS == 1) {
-    const float inv = 1.f / lsum;
+  // ---- results: lane (g, l16) holds O^T rows d = 16 dt + 4g + e of its row
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t w0 = (uint32_t)float_to_bf16_bits(oacc[dt][0] * inv) |
-                          ((uint32_t)float_to_bf16_bits(oacc[dt][1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)float_to_bf16_bits(oacc[dt][2] * inv) |
-                          ((uint32_t)float_to_bf16_bits(oacc[dt][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(a.o + orow * D + 16 * dt + 4 * g) = make_uint2(w0, w1);
+  for (int u = 0; u < TPW; ++u) {
+    Tile<D>& T = tl[u];
+    float lsum = T.l;
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+    if (!rv[u]) continue;
+    if (NS == 1) {
+      const float inv = 1.f / lsum;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t w0 = (uint32_t)float_to_bf16_bits(T.o[dt][0] * inv) |
+                            ((uint32_t)float_to_bf16_bits(T.o[dt][1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)float_to_bf16_bits(T.o[dt][2] * inv) |
+                            ((uint32_t)float_to_bf16_bits(T.o[dt][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(a.o + orow[u] * D + 16 * dt + 4 * g) = make_uint2(w0, w1);
+      }
+    } else {
+      float* po = a.part_o + (orow[u] * NS + split) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
+            make_float4(T.o[dt][0], T.o[dt][1], T.o[dt][2], T.o[dt][3]);
+      if (g == 0)
+        *reinterpret_cast<float2*>(a.part_ml + (orow[u] * NS + split) * 2) =
+            make_float2(T.m, lsum);
     }
-  } else {
-    float* po = a.part_o + (orow * NS + split) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
-          make_float4(oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
-    if (g == 0)
-      *reinterpret_cast<float2*>(a.part_ml + (orow * NS + split) * 2) = make_float2(m, lsum);
   }
 }
 
 // o[row] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the splits
-// (zero when no split saw a key: the rows of a rejected sequence). One
-// workgroup per sequence (rows of an invalid node range are left alone), one
-// wave per output row, 64 lanes over d.
+// (zero when no split saw a key: the rows of a rejected sequence). One wave
+// per output row, 64 lanes over d; workgroup (b, c) takes 4 of sequence b's
+// rows (node-major, query heads inner); rows of an invalid node range are
+// left alone.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine_kernel(const AttnArgs a) {
-  const int b = blockIdx.x;
+  const int chunks = (a.max_nodes * a.Hq + 3) / 4;
+  const int b = blockIdx.x / chunks;
   const int lo = a.offsets[b];
   const int hi = a.offsets[b + 1];
   if (lo < 0 || hi > a.T || hi - lo < 1 || hi - lo > a.max_nodes) return;
+  const int row = lo * a.Hq + 4 * (blockIdx.x - b * chunks) + (threadIdx.x >> 6);
+  if (row >= hi * a.Hq) return;
   const int lane = threadIdx.x & 63;
   const int NS = a.NS;
-  for (int row = lo * a.Hq + (threadIdx.x >> 6); row < hi * a.Hq; row += 4) {
-    const float* ml = a.part_ml + (size_t)row * NS * 2;
-    float M = kMasked;
-    for (int s = 0; s < NS; ++s) M = fmaxf(M, ml[2 * s]);
-    float den = 0.f;
-    float acc[D / 64];
+  const float* ml = a.part_ml + (size_t)row * NS * 2;
+  float M = kMasked;
+  for (int s = 0; s < NS; ++s) M = fmaxf(M, ml[2 * s]);
+  float den = 0.f;
+  float acc[D / 64];
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) acc[c] = 0.f;
-    for (int s = 0; s < NS; ++s) {
-      const float w = ml[2 * s + 1] > 0.f ? exp2f(ml[2 * s] - M) : 0.f;
-      den += w * ml[2 * s + 1];
-      const float* po = a.part_o + ((size_t)row * NS + s) * D;
+  for (int c = 0; c < D / 64; ++c) acc[c] = 0.f;
+  for (int s = 0; s < NS; ++s) {
+    const float w = ml[2 * s + 1] > 0.f ? exp2f(ml[2 * s] - M) : 0.f;
+    den += w * ml[2 * s + 1];
+    const float* po = a.part_o + ((size_t)row * NS + s) * D;
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) acc[c] += w * po[lane + 64 * c];
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 64; ++c)
-      a.o[(size_t)row * D + lane + 64 * c] = float_to_bf16_bits(acc[c] * inv);
+    for (int c = 0; c < D / 64; ++c) acc[c] += w * po[lane + 64 * c];
   }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c)
+    a.o[(size_t)row * D + lane + 64 * c] = float_to_bf16_bits(acc[c] * inv);
 }
 
 // One workgroup per sequence: validate, find the accepted path, append its
@@ -412,14 +577,20 @@ __global__ __launch_bounds__(256) void tree_attn_commit_kernel(const AttnCommitA
   if (tid == 0) a.cache_len[b] = L + P;
 }
 
+// Workgroup shape from the most query rows a (sequence, K/V head) can have:
+// up to 192 rows, one 16-row tile per wave on 12 waves (three per SIMD);
+// beyond, two tiles per wave on 8 waves.
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.B * a.Hkv * a.NS);
-  hipError_t e = launch_kernel(reinterpret_cast<const void*>(&tree_attn_kernel<D>), grid,
-                               (unsigned)kAttnThreads, s, a);
+  const int rows = (a.Hq / a.Hkv) * a.max_nodes;
+  hipError_t e = rows <= 192
+      ? launch_kernel(reinterpret_cast<const void*>(&tree_attn_kernel<D, 12, 1>), grid, 768u, s, a)
+      : launch_kernel(reinterpret_cast<const void*>(&tree_attn_kernel<D, 8, 2>), grid, 512u, s, a);
   if (e != hipSuccess || a.NS == 1) return e;
+  const unsigned chunks = (unsigned)((a.max_nodes * a.Hq + 3) / 4);
   return launch_kernel(reinterpret_cast<const void*>(&tree_attn_combine_kernel<D>),
-                       (unsigned)a.B, 256u, s, a);
+                       (unsigned)a.B * chunks, 256u, s, a);
 }
 
 }  // namespace

@@ -16,7 +16,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kKeyBlock = 64;          // keys per staged block in the verify kernel
 constexpr int kMaxQueryRows = 256;     // query rows per (sequence, KV head) workgroup
-constexpr long long kTargetGroups = 512;  // workgroups that keep every CU busy (two rounds)
+constexpr long long kTargetGroups = 256;  // one verify workgroup per CU (a CU holds one)
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

@@ -37,9 +37,14 @@ def _flags():
     ]
 
 
+# per-source extra flags: the attention kernels take only finite inputs and
+# compare scores with fmaxf, which then needs no NaN canonicalisation
+EXTRA_FLAGS = {"tree_attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

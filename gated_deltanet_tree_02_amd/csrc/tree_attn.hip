@@ -62,20 +62,22 @@ __device__ __forceinline__ void wait_vmem() {
 
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
 // the wave's 64 lanes fill 1 KiB of LDS at lds_base + 16 * lane, lane l
-// reading its own address. Issued as inline assembly so that the compiler
+// reading base + offset_l. Issued as inline assembly so that the compiler
 // does not wait for every such load before each LDS read; the kernel waits
 // for them itself (vmcnt, then a barrier). M0 holds the LDS base for the
 // instruction and is restored afterwards.
-__device__ __forceinline__ void load_lds_16(const void* src, uint32_t lds_base) {
+// The address is a wave-uniform base plus the lane's 32-bit byte offset.
+__device__ __forceinline__ void load_lds_16(const void* base, uint32_t offset,
+                                            uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_base), "v"(src)
+      : "s"(lds_base), "v"(offset), "s"(base)
       : "memory");
 }
 
@@ -110,7 +112,8 @@ struct Tile {
   bf16x8 qf[D / 32];     // B operand of S^T = K Q^T: column = query row, k = d 32s + 8g .. +7,
                          // holding q * scale * log2(e)
   f32x4 o[D / 16];       // O^T rows d = 16 dt + 4g + e, column = query row
-  float m, l;            // row reference (base-2 units) and this lane's part of the sum
+  f32x4 l;               // row sums of P^T as an MFMA result: element 0 of the g = 0 lanes
+  float m;               // row reference (base-2 units)
   uint64_t anc;          // ancestor bits of the lane's node
 };
 
@@ -156,7 +159,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int g, int l16) {
 template <int D, int NT, bool FULL, int TPW>
 __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char* sK,
                                              const LaneOffsets& lo, const uint64_t (&vm)[TPW],
-                                             bool first) {
+                                             bool first, const bf16x8& ones) {
   constexpr int KSD = D / 32;
   constexpr int DT = D / 16;
   constexpr int RB = 2 * D;
@@ -210,7 +213,7 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
         acc[u][1] -= delta;
         if (!set) {
           const float alpha = __builtin_amdgcn_exp2f(-delta);
-          T.l *= alpha;
+          T.l[0] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) T.o[dt] *= alpha;
         }
@@ -218,14 +221,12 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
       // P^T as the B operand of 16x16x32 over the 32 keys: k slot 8g + i
       // holds key 32 mg + 4g + i (i < 4) or 32 mg + 16 + 4g + i - 4
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(acc[u][h][e]);
-          T.l += p;
-          pk[u][4 * h + e] = (__bf16)p;
-        }
-      }
+        for (int e = 0; e < 4; ++e) pk[u][4 * h + e] = (__bf16)__builtin_amdgcn_exp2f(acc[u][h][e]);
+      // row sums of the same bf16 weights the output uses: a ones row
+      // (row 0 of the A operand) against P^T
+      T.l = mfma_k32(ones, pk[u], T.l);
     }
     // O^T += V^T P^T: A = V^T rows d = 16 dt + l16 over the same key slots,
     // read column-wise from the row-major V block; each V fragment serves
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
     orow[u] = (size_t)(lo + t) * a.Hq + kvh * G + hg;
     tl[u].anc = sAnc[t];
     tl[u].m = 0.f;
-    tl[u].l = 0.f;
+    tl[u].l = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) tl[u].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -364,6 +365,8 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
   }
   wait_vmem<0>();
   const LaneOffsets lofs = lane_offsets<D>(g, l16);
+  const __bf16 one = l16 == 0 ? (__bf16)1.f : (__bf16)0.f;
+  const bf16x8 ones = {one, one, one, one, one, one, one, one};
 
   // ---- key range of this split: cache rows [c0, c1), then the tree slots
   // (last split only)
@@ -383,26 +386,43 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
   // cache rows, and unused tree slots, read a valid row instead: finite
   // values that the mask gives zero weight.
   const int nload = (NU - wave + W - 1) / W;  // this wave's loads per block (wave-uniform)
+  // lane byte offset of load i inside a full cache block (row r at r * 2D)
+  uint32_t loff[LMAX];
+#pragma unroll
+  for (int i = 0; i < LMAX; ++i) {
+    const int rem = (64 * (wave + W * i) + lane) % (KB * CPR);
+    const int row = rem / CPR;
+    loff[i] = (uint32_t)(row * D + 8 * ((rem % CPR) ^ swz_key<D>(row))) * 2u;
+  }
+  const uint16_t* kc_seq = a.kc + kvbase * D;      // cache row 0 of (b, kvh)
+  const uint16_t* vc_seq = a.vc + kvbase * D;
+  const size_t tree0 = ((size_t)lo * a.Hkv + kvh) * D;   // tree node 0 of (b, kvh)
   auto issue_block = [&](int j, int s) {
     const bool tree = j >= ncb;
     const int p0 = c0 + j * KB;
+    const bool partial = !tree && p0 + KB > c1;   // wave-uniform
 #pragma unroll
     for (int i = 0; i < LMAX; ++i) {
       if (i == LMAX - 1 && i >= nload) break;
       const int wbase = 64 * (wave + W * i);  // wave-uniform
       const int mat = wbase >= KB * CPR ? 1 : 0;
-      const int rem = wbase + lane - mat * KB * CPR;
-      const int row = rem / CPR;
-      const int chunk = (rem % CPR) ^ swz_key<D>(row);
-      const uint16_t* src;
-      if (!tree) {
-        const int p = min(p0 + row, c1 - 1);
-        src = (mat ? a.vc : a.kc) + kvbase * D + (p * D + 8 * chunk);
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(smem_base + s * STAGE + 16 * wbase);
+      if (!tree && !partial) {
+        load_lds_16((mat ? vc_seq : kc_seq) + (size_t)p0 * D, loff[i], lds);
       } else {
-        const int node = row < n ? row : 0;
-        src = (mat ? a.v : a.k) + ((size_t)(lo + node) * a.Hkv + kvh) * D + 8 * chunk;
+        const int rem = wbase + lane - mat * KB * CPR;
+        const int row = rem / CPR;
+        const int chunk = (rem % CPR) ^ swz_key<D>(row);
+        if (!tree) {
+          const int p = min(row, c1 - 1 - p0);
+          load_lds_16((mat ? vc_seq : kc_seq) + (size_t)p0 * D,
+                      (uint32_t)(p * D + 8 * chunk) * 2u, lds);
+        } else {
+          const int node = row < n ? row : 0;
+          load_lds_16((mat ? a.v : a.k) + tree0,
+                      (uint32_t)(node * a.Hkv * D + 8 * chunk) * 2u, lds);
+        }
       }
-      load_lds_16(src, __builtin_amdgcn_readfirstlane(smem_base + s * STAGE + 16 * wbase));
     }
   };
 
@@ -426,8 +446,8 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
     const bool first = j == 0;
     if (!tree && lim >= KB) {
       const uint64_t vm[TPW] = {};
-      if (TPW > 1 && nt > 1) attend_block<D, TPW, true, TPW>(tl, sK, lofs, vm, first);
-      else attend_block<D, 1, true, TPW>(tl, sK, lofs, vm, first);
+      if (TPW > 1 && nt > 1) attend_block<D, TPW, true, TPW>(tl, sK, lofs, vm, first, ones);
+      else attend_block<D, 1, true, TPW>(tl, sK, lofs, vm, first, ones);
     } else {
       const int lm = lim - 4 * g;             // lane keys 16 kt + e below lm are visible
       uint64_t vm[TPW];
@@ -435,8 +455,8 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
       for (int u = 0; u < TPW; ++u)
         vm[u] = tree ? tl[u].anc >> (4 * g)
                      : (lm >= 64 ? ~0ull : lm <= 0 ? 0ull : (1ull << lm) - 1ull);
-      if (TPW > 1 && nt > 1) attend_block<D, TPW, false, TPW>(tl, sK, lofs, vm, first);
-      else attend_block<D, 1, false, TPW>(tl, sK, lofs, vm, first);
+      if (TPW > 1 && nt > 1) attend_block<D, TPW, false, TPW>(tl, sK, lofs, vm, first, ones);
+      else attend_block<D, 1, false, TPW>(tl, sK, lofs, vm, first, ones);
     }
   }
 
@@ -444,9 +464,7 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     Tile<D>& T = tl[u];
-    float lsum = T.l;
-    lsum += __shfl_xor(lsum, 16, kWave);
-    lsum += __shfl_xor(lsum, 32, kWave);
+    const float lsum = __shfl(T.l[0], l16, kWave);   // from lane (g = 0, l16)
     if (!rv[u]) continue;
     if (NS == 1) {
       const float inv = 1.f / lsum;

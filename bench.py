@@ -36,10 +36,13 @@ METRIC = "tree-GDN verified draft nodes/s per layer (1 GPU) + % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "gated_deltanet_tree_02_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wy_verify_commit_c4_hbm_traffic.md")
+TRAFFIC_FILES = [os.path.join(ROOT, "profiles", "wy_verify_commit_c4_hbm_traffic.md"),
+                 os.path.join(ROOT, "profiles", "tree_attn_fa_c4_hbm_traffic.md")]
 # sources whose hash ties a recorded counter measurement to the kernels it measured
 KERNEL_SOURCES = {"verify": ["wy_verify.hip", "device_common.h", "launch.h"],
-                  "commit": ["wy_commit.hip", "device_common.h", "launch.h"]}
+                  "commit": ["wy_commit.hip", "device_common.h", "launch.h"],
+                  "attn_verify": ["tree_attn.hip", "device_common.h", "launch.h",
+                                  "tree_attn_api.cpp"]}
 
 
 def kernel_source_hash(kind):
@@ -55,14 +58,15 @@ def recorded_traffic(kind, config):
     summary, if it was taken on this config with the current kernel sources;
     else None. The summary holds lines
       traffic <kind> <config> <source-hash> <bytes>"""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
     pat = re.compile(rf"^traffic\s+{kind}\s+{config}\s+(\w+)\s+(\d+)\s*$")
-    with open(TRAFFIC_FILE) as fh:
-        for line in fh:
-            m = pat.match(line.strip().strip("`"))
-            if m and m.group(1) == kernel_source_hash(kind):
-                return int(m.group(2))
+    for path in TRAFFIC_FILES:
+        if not os.path.exists(path):
+            continue
+        with open(path) as fh:
+            for line in fh:
+                m = pat.match(line.strip().strip("`"))
+                if m and m.group(1) == kernel_source_hash(kind):
+                    return int(m.group(2))
     return None
 
 
@@ -102,6 +106,19 @@ def algorithmic_bytes(w, io_bytes, gi):
     fork_verify = T * H * (8 * dv * dk + io_bytes * (2 * dk + dv) + 8 + io_bytes * dv) + tree
     fork_commit = B * H * 8 * dv * dk + tree + B * 4
     return verify, commit, fork_verify, fork_commit
+
+
+def pmc_calibration(dev):
+    """A plain copy of known size for scaling FETCH_SIZE / WRITE_SIZE counters:
+    torch.mul over 256 MiB of fp32, three times (reads and writes 256 MiB)."""
+    import torch
+    x = torch.ones(64 << 20, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    log("pmc calibration: 3 x copy of 256 MiB done")
 
 
 def attn_algorithmic_bytes(offsets, Hq, Hkv, d, cache_len, path_nodes):
@@ -214,7 +231,7 @@ def attention_leg(args, gt, gi, w_trees, dev):
         "nodes_per_s_per_layer": round(T * n_layers * steps / elapsed, 1),
         "roofline": {"kernel": "tree_attn_verify", "bound": "hbm", "achieved": kern["verify"]["achieved_GBs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern["verify"]["frac_hbm"],
-                     "traffic": None},
+                     "traffic": recorded_traffic("attn_verify", "fa_c4")},
         "kernels": kern, "split_workspace_bytes": int(nbytes),
     }
     log(f"attention: {out['ms_per_step']} ms/step, verify {v_us:.2f} us, commit {c_us:.2f} us per layer")
@@ -241,7 +258,10 @@ def main():
     log(f"workload {args.config}: B={w.B} T={w.T} layers={w.layers} gen {time.time() - t0:.1f}s")
     L = w.layers
     if args.attn_only:
-        print(json.dumps({"fa_layers": attention_leg(args, gt, gi, w, dev)}), flush=True)
+        fa = attention_leg(args, gt, gi, w, dev)
+        if args.pmc_calibration:
+            pmc_calibration(dev)
+        print(json.dumps({"fa_layers": fa}), flush=True)
         return
     io_t = torch.bfloat16 if w.io == "bf16" else torch.float32
     io_bytes = 2 if w.io == "bf16" else 4
@@ -356,13 +376,7 @@ def main():
         torch.cuda.empty_cache()
 
     if args.pmc_calibration:
-        x = torch.ones(64 << 20, device=dev)
-        y = torch.empty_like(x)
-        for _ in range(3):
-            torch.mul(x, 1.0, out=y)
-        torch.cuda.synchronize()
-        del x, y
-        log("pmc calibration: 3 x copy of 256 MiB done")
+        pmc_calibration(dev)
 
     # speculative state per request (one sequence), summed over the layers
     n_req = w.T / w.B

@@ -176,6 +176,7 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
       acc[u][0] = f32x4{c0, c0, c0, c0};
       acc[u][1] = acc[u][0];
     }
+    __builtin_amdgcn_s_setprio(1);            // MFMA phases first
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
       bf16x8 ka[2];
@@ -188,6 +189,7 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
         for (int u = 0; u < NT; ++u) acc[u][h] = mfma_k32(ka[h], tl[u].qf[s], acc[u][h]);
     }
 
+    __builtin_amdgcn_s_setprio(0);
     bf16x8 pk[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
@@ -231,6 +233,7 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
     // O^T += V^T P^T: A = V^T rows d = 16 dt + l16 over the same key slots,
     // read column-wise from the row-major V block; each V fragment serves
     // every tile of the wave
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const lds_char* p1 = sV + (lo.v ^ (32 * dt)) + 32 * RB * mg;
@@ -240,6 +243,7 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
 #pragma unroll
       for (int u = 0; u < NT; ++u) tl[u].o[dt] = mfma_k32(va, pk[u], tl[u].o[dt]);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
@@ -247,7 +251,8 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
 // W * TPW * 16 >= the rows of a (sequence, K/V head).
 template <int N>
 __device__ __forceinline__ void wait_blocks_ahead(int ahead) {
-  if (ahead >= 2) wait_vmem<2 * N>();
+  if (ahead >= 3) wait_vmem<3 * N>();
+  else if (ahead == 2) wait_vmem<2 * N>();
   else if (ahead == 1) wait_vmem<N>();
   else wait_vmem<0>();
 }
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
   for (int j = 0; j < nblk; ++j) {
     // block j's loads are this thread's oldest outstanding ones
     const int ahead = min(kStages - 2, nblk - 1 - j);
-    static_assert(kStages - 2 <= 2, "wait_blocks_ahead covers two blocks ahead");
+    static_assert(kStages - 2 <= 3, "wait_blocks_ahead covers three blocks ahead");
     if (nload == LMAX) wait_blocks_ahead<LMAX>(ahead);
     else wait_blocks_ahead<(LMAX > 1 ? LMAX - 1 : 1)>(ahead);
     __syncthreads();                          // every thread's part landed; stage j-1 is free

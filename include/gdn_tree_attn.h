@@ -23,8 +23,9 @@
  * Conventions follow gdn_tree.h: device pointers owned by the caller, no
  * allocation or synchronisation, work enqueued on `stream`, host-side checks
  * reported by the gdn_status return value, data-dependent problems per
- * sequence in tree_status (GDN_TREE_* codes; a rejected sequence's output
- * rows are zero and its commit writes nothing). All tensors are dense and
+ * sequence in tree_status (GDN_TREE_* codes; a rejected sequence whose
+ * node range is well formed gets zero output rows, rows of a malformed node
+ * range are not written, and a rejected commit writes nothing). All tensors are dense and
  * row-major; q, k, v, the caches and o are bf16 (as raw 16-bit patterns);
  * arithmetic is fp32.
  *   offsets      [B+1] int32       node range of sequence b: [offsets[b], offsets[b+1])

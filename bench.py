@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Tree-GDN verify + commit throughput on one MI355X.
 
-One step = every GDN layer of the workload verified (gdn_tree_verify) and
-then committed in place (gdn_tree_commit): the whole hot path over one batch.
+One step = every GDN layer of the workload verified and then committed in
+place: the whole hot path over one batch. By default the layers go out as one
+launch per kernel (gdn_tree_verify_layers, gdn_tree_commit_layers);
+`--launch per-layer` issues gdn_tree_verify / gdn_tree_commit per layer.
 Default workload: k=3 d=3 draft trees (40 nodes incl. root), 24 GDN layers
 with independent inputs and states, batch 64, 16 heads, 128x128 fp32 state,
 bf16 q/k/v (Qwen3.5-9B GDN shape). Inputs are seeded synthetic data resident
@@ -83,6 +85,9 @@ def parse():
     p.add_argument("--mode", default="wy", choices=["wy", "fork"])
     p.add_argument("--fork-steps", type=int, default=3, help="timed steps of the fork baseline (0 = skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0 = skip)")
+    p.add_argument("--launch", default="layers", choices=["layers", "per-layer"],
+                   help="WY leg: every layer in one launch per kernel (gdn_tree_*_layers) or one "
+                        "launch per layer")
     p.add_argument("--attn-steps", type=int, default=10,
                    help="timed steps of the full-attention leg (0 = skip)")
     p.add_argument("--attn-only", action="store_true",
@@ -281,7 +286,7 @@ def main():
                            alpha=put(w.alpha[layer]), beta=put(w.beta[layer]), S=put(w.S0[layer])))
     torch.cuda.synchronize()
 
-    def make_calls(mode):
+    def make_calls(mode, batched=False):
         desc = gt.make_desc(w.B, w.H, w.dk, w.dv, w.T, w.max_nodes,
                             gt.DTYPE_BF16 if w.io == "bf16" else gt.DTYPE_F32,
                             gt.MODE_WY if mode == "wy" else gt.MODE_FORK, max_depth)
@@ -295,6 +300,14 @@ def main():
                                          ly["ws_" + mode], status))
             com.append(gt.prepare_commit(desc, offsets, parents, accepted, ly["k"], ly["S"], ly["S"],
                                          ly["ws_" + mode], status))
+        if batched:
+            # one launch per kernel for all layers (commit in place: S_out = S0)
+            ios = [gt.make_layer_io(desc, q=ly["q"], k=ly["k"], v=ly["v"], alpha=ly["alpha"],
+                                    beta=ly["beta"], S0=ly["S"], o=ly["o_" + mode], S_out=ly["S"],
+                                    workspace=ly["ws_" + mode]) for ly in layers]
+            ver = [gt.prepare_verify_layers(desc, offsets, parents, ios, nbytes, status, keep=layers)]
+            com = [gt.prepare_commit_layers(desc, offsets, parents, accepted, ios, nbytes, status,
+                                            keep=layers)]
         return desc, nbytes, ver, com
 
     def run(ver, com, steps, warmup):
@@ -323,8 +336,10 @@ def main():
         return elapsed, v_ms, c_ms
 
     # ------------------------------------------------------------------ main leg
-    desc, nbytes, ver, com = make_calls(args.mode)
-    log(f"mode {args.mode}: workspace {nbytes / 2**20:.1f} MiB per layer")
+    batched = args.mode == "wy" and args.launch == "layers"
+    desc, nbytes, ver, com = make_calls(args.mode, batched)
+    log(f"mode {args.mode}: workspace {nbytes / 2**20:.1f} MiB per layer, "
+        f"{'all layers per launch' if batched else 'one launch per layer'}")
     elapsed, v_ms, c_ms = run(ver, com, args.steps, args.warmup)
     st = status.cpu().numpy()
     if np.any(st != 0):
@@ -334,7 +349,10 @@ def main():
     vb, cb, fvb, fcb = algorithmic_bytes(w, io_bytes, gi)
     if args.mode == "fork":
         vb, cb = fvb, fcb
-    v_us = 1e3 * v_ms / L      # average launch duration (events around back-to-back launches)
+    # per-layer figures (events around the step's launches / layers); with
+    # batched launches one launch carries all L layers
+    lpl = L if batched else 1
+    v_us = 1e3 * v_ms / L
     c_us = 1e3 * c_ms / L
     kern = {
         "verify": {"avg_us": round(v_us, 3), "alg_bytes": int(vb),
@@ -344,15 +362,20 @@ def main():
                    "achieved_GBs": round(cb / c_us / 1e3, 1),
                    "frac_hbm": round(cb / c_us / 1e3 / HBM_PEAK_GBS, 4)},
     }
-    dom = "verify" if v_us >= c_us else "commit"
-    traffic = recorded_traffic(dom, args.config) if args.mode == "wy" else None
     for kind in ("verify", "commit"):
-        t = recorded_traffic(kind, args.config) if args.mode == "wy" else None
-        kern[kind]["traffic_bytes"] = t
-        kern[kind]["traffic_over_alg"] = round(t / kern[kind]["alg_bytes"], 3) if t else None
+        t = recorded_traffic(kind, args.config) if args.mode == "wy" else None   # per layer
+        k = kern[kind]
+        k["layers_per_launch"] = lpl
+        k["launch_us"] = round(k["avg_us"] * lpl, 3)
+        k["alg_bytes_per_launch"] = k["alg_bytes"] * lpl
+        k["traffic_bytes"] = t
+        k["traffic_over_alg"] = round(t / k["alg_bytes"], 3) if t else None
+    dom = "verify" if v_us >= c_us else "commit"
     roof = {"kernel": f"{'wy' if args.mode == 'wy' else 'fork'}_{dom}", "bound": "hbm",
             "achieved": kern[dom]["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": kern[dom]["frac_hbm"], "traffic": traffic}
+            "frac": kern[dom]["frac_hbm"],
+            "traffic": kern[dom]["traffic_bytes"] * lpl if kern[dom]["traffic_bytes"] else None,
+            "layers_per_launch": lpl}
     log(f"{args.mode}: {ms_step:.3f} ms/step, verify {v_us:.2f} us, commit {c_us:.2f} us per layer")
 
     # ------------------------------------------------------------- fork baseline
@@ -425,6 +448,7 @@ def main():
         "config": {"workload": gi.CONFIGS[args.config]["desc"], "config_id": args.config,
                    "layers": L, "batch": w.B, "total_nodes": w.T, "heads": w.H, "dk": w.dk,
                    "dv": w.dv, "io": w.io, "state": "fp32", "mode": args.mode,
+                   "launch": "all layers per launch" if batched else "one launch per layer",
                    "parallelism": "single-gpu"},
         "roofline": roof, "kernels": kern, "cpu_baseline": cpu, "fork_baseline": fork,
         "spec_state_per_request": spec, "fa_layers": fa,

@@ -22,6 +22,8 @@ __all__ = [
     "PreparedCall", "prepare_verify", "prepare_commit",
     "GdnAttnDesc", "make_attn_desc", "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
     "gdn_tree_attn_commit", "prepare_attn_verify", "prepare_attn_commit",
+    "GdnLayerIO", "make_layer_io", "gdn_tree_verify_layers", "gdn_tree_commit_layers",
+    "prepare_verify_layers", "prepare_commit_layers",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdntree.so")
@@ -57,6 +59,11 @@ class GdnAttnDesc(ctypes.Structure):
     ]
 
 
+class GdnLayerIO(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("q", "k", "v", "alpha", "beta", "S0", "o", "S_out", "workspace")]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -89,6 +96,11 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_attn_verify.restype = I
             lib.gdn_tree_attn_commit.argtypes = [A, P, P, P, P, P, P, P, P, P, P]
             lib.gdn_tree_attn_commit.restype = I
+            LY = ctypes.POINTER(GdnLayerIO)
+            lib.gdn_tree_verify_layers.argtypes = [D, ctypes.c_int32, P, P, LY, S, P, P]
+            lib.gdn_tree_verify_layers.restype = I
+            lib.gdn_tree_commit_layers.argtypes = [D, ctypes.c_int32, P, P, P, LY, S, P, P]
+            lib.gdn_tree_commit_layers.restype = I
             lib.gdn_tree_status_string.argtypes = [I]
             lib.gdn_tree_status_string.restype = ctypes.c_char_p
             _lib = lib
@@ -361,3 +373,92 @@ def prepare_attn_commit(desc, offsets, parents, accepted, k, v, k_cache, v_cache
     tensors = (offsets, parents, accepted, k, v, k_cache, v_cache, cache_len, tree_status)
     dev, args = _attn_commit_args(desc, *tensors)
     return PreparedCall("gdn_tree_attn_commit", desc, args, _stream(stream, dev), tensors)
+
+
+# ------------------------------------------------------------------ layer-batched calls
+
+
+def make_layer_io(desc, q=None, k=None, v=None, alpha=None, beta=None, S0=None, o=None,
+                  S_out=None, workspace=None) -> GdnLayerIO:
+    """One layer's buffers for the layer-batched calls (shapes checked against
+    the descriptor; a field a call does not use may be None)."""
+    torch = _torch()
+    B, H, T, dk, dv = desc.num_seqs, desc.num_heads, desc.total_nodes, desc.dk, desc.dv
+    io = _io_dtype(desc)
+    f = lambda t, name, dt, shape: _ptr(t, name, dt, shape, allow_none=True)
+    return GdnLayerIO(
+        f(q, "q", io, (T, H, dk)), f(k, "k", io, (T, H, dk)), f(v, "v", io, (T, H, dv)),
+        f(alpha, "alpha", torch.float32, (T, H)), f(beta, "beta", torch.float32, (T, H)),
+        f(S0, "S0", torch.float32, (B, H, dv, dk)), f(o, "o", io, (T, H, dv)),
+        f(S_out, "S_out", torch.float32, (B, H, dv, dk)),
+        f(workspace, "workspace", torch.uint8, None))
+
+
+def _layers_array(layers):
+    arr = (GdnLayerIO * max(1, len(layers)))()
+    for i, ly in enumerate(layers):
+        arr[i] = ly
+    return arr
+
+
+def gdn_tree_verify_layers(desc, offsets, parents, layers, workspace_bytes, tree_status,
+                           stream=None):
+    """Verify every layer in `layers` (GdnLayerIO list) on the shared tree."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    arr = _layers_array(layers)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_verify_layers(
+            ctypes.byref(desc), len(layers), _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+            _ptr(parents, "parents", torch.int32, (T,), dev), arr, ctypes.c_size_t(workspace_bytes),
+            _ptr(tree_status, "tree_status", torch.int32, (B,), dev), _stream(stream, dev)),
+            "gdn_tree_verify_layers")
+
+
+def gdn_tree_commit_layers(desc, offsets, parents, accepted, layers, workspace_bytes,
+                           tree_status, stream=None):
+    """Commit every layer in `layers` (GdnLayerIO list) on the shared tree."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    arr = _layers_array(layers)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_commit_layers(
+            ctypes.byref(desc), len(layers), _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+            _ptr(parents, "parents", torch.int32, (T,), dev),
+            _ptr(accepted, "accepted", torch.int32, (B,), dev), arr,
+            ctypes.c_size_t(workspace_bytes),
+            _ptr(tree_status, "tree_status", torch.int32, (B,), dev), _stream(stream, dev)),
+            "gdn_tree_commit_layers")
+
+
+def prepare_verify_layers(desc, offsets, parents, layers, workspace_bytes, tree_status,
+                          keep=(), stream=None) -> PreparedCall:
+    """Marshalled gdn_tree_verify_layers; `keep` holds the tensors behind `layers`."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    arr = _layers_array(layers)
+    args = [ctypes.c_int32(len(layers)), _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+            _ptr(parents, "parents", torch.int32, (T,), dev), arr,
+            ctypes.c_size_t(workspace_bytes),
+            _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
+    return PreparedCall("gdn_tree_verify_layers", desc, args, _stream(stream, dev),
+                        (offsets, parents, tree_status, arr, tuple(keep)))
+
+
+def prepare_commit_layers(desc, offsets, parents, accepted, layers, workspace_bytes, tree_status,
+                          keep=(), stream=None) -> PreparedCall:
+    """Marshalled gdn_tree_commit_layers; `keep` holds the tensors behind `layers`."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    arr = _layers_array(layers)
+    args = [ctypes.c_int32(len(layers)), _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+            _ptr(parents, "parents", torch.int32, (T,), dev),
+            _ptr(accepted, "accepted", torch.int32, (B,), dev), arr,
+            ctypes.c_size_t(workspace_bytes),
+            _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
+    return PreparedCall("gdn_tree_commit_layers", desc, args, _stream(stream, dev),
+                        (offsets, parents, accepted, tree_status, arr, tuple(keep)))

@@ -3,6 +3,7 @@
 // launch goes to the caller's stream.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstddef>
 #include <cstdint>
@@ -129,6 +130,102 @@ gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
                         levels(desc) - 1, offsets, parents, accepted, S0, S_out,
                         static_cast<const float*>(workspace), tree_status};
   return launched(gdn::launch_fork_commit(d, a, s));
+}
+
+gdn_status gdn_tree_verify_layers(const gdn_tree_desc* desc, int32_t n_layers,
+                                  const int32_t* offsets, const int32_t* parents,
+                                  const gdn_layer_io* layers, size_t ws_bytes,
+                                  int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (n_layers <= 0 || desc->num_seqs == 0) return GDN_OK;
+  if (!layers) return GDN_ERR_NULL_PTR;
+  if (desc->mode != GDN_MODE_WY) {
+    for (int l = 0; l < n_layers; ++l) {
+      const gdn_layer_io& y = layers[l];
+      st = gdn_tree_verify(desc, offsets, parents, y.q, y.k, y.v, y.alpha, y.beta, y.S0, y.o,
+                           y.workspace, ws_bytes, tree_status, stream);
+      if (st != GDN_OK) return st;
+    }
+    return GDN_OK;
+  }
+  if (!offsets || !tree_status) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && !parents) return GDN_ERR_NULL_PTR;
+  for (int l = 0; l < n_layers; ++l) {
+    const gdn_layer_io& y = layers[l];
+    if (!y.S0) return GDN_ERR_NULL_PTR;
+    if (desc->total_nodes > 0 && (!y.q || !y.k || !y.v || !y.alpha || !y.beta || !y.o ||
+                                  !y.workspace))
+      return GDN_ERR_NULL_PTR;
+  }
+  if (ws_bytes < workspace_bytes(desc)) return GDN_ERR_WORKSPACE;
+  if ((long long)desc->num_seqs * desc->num_heads * gdn::kMaxLayersPerLaunch > INT_MAX)
+    return GDN_ERR_BAD_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int mt = (desc->max_nodes + 15) / 16;
+  gdn::VerifyLayersArgs a{};
+  a.base = gdn::VerifyArgs{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                           offsets, parents, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, nullptr, nullptr, tree_status};
+  for (int l0 = 0; l0 < n_layers; l0 += gdn::kMaxLayersPerLaunch) {
+    a.layers = std::min(n_layers - l0, gdn::kMaxLayersPerLaunch);
+    for (int i = 0; i < a.layers; ++i) {
+      const gdn_layer_io& y = layers[l0 + i];
+      float* U = static_cast<float*>(y.workspace);
+      float* g2 = reinterpret_cast<float*>(static_cast<char*>(y.workspace) + wy_u_bytes(desc));
+      a.L[i] = gdn::VerifyLayer{y.q, y.k, y.v, y.alpha, y.beta, y.S0, y.o, U, g2};
+    }
+    st = launched(gdn::launch_wy_verify_layers(desc->io_dtype, desc->dk, mt, a, s));
+    if (st != GDN_OK) return st;
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
+                                  const int32_t* offsets, const int32_t* parents,
+                                  const int32_t* accepted, const gdn_layer_io* layers,
+                                  size_t ws_bytes, int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (n_layers <= 0 || desc->num_seqs == 0) return GDN_OK;
+  if (!layers) return GDN_ERR_NULL_PTR;
+  if (desc->mode != GDN_MODE_WY) {
+    for (int l = 0; l < n_layers; ++l) {
+      const gdn_layer_io& y = layers[l];
+      st = gdn_tree_commit(desc, offsets, parents, accepted, y.k, y.S0, y.S_out, y.workspace,
+                           ws_bytes, tree_status, stream);
+      if (st != GDN_OK) return st;
+    }
+    return GDN_OK;
+  }
+  if (!offsets || !accepted || !tree_status) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && !parents) return GDN_ERR_NULL_PTR;
+  for (int l = 0; l < n_layers; ++l) {
+    const gdn_layer_io& y = layers[l];
+    if (!y.S0 || !y.S_out) return GDN_ERR_NULL_PTR;
+    if (desc->total_nodes > 0 && (!y.workspace || !y.k)) return GDN_ERR_NULL_PTR;
+  }
+  if (ws_bytes < workspace_bytes(desc)) return GDN_ERR_WORKSPACE;
+  if ((long long)desc->num_seqs * desc->num_heads * gdn::kMaxLayersPerLaunch > INT_MAX)
+    return GDN_ERR_BAD_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  gdn::CommitLayersArgs a{};
+  a.base = gdn::CommitArgs{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                           offsets, parents, accepted, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, tree_status};
+  for (int l0 = 0; l0 < n_layers; l0 += gdn::kMaxLayersPerLaunch) {
+    a.layers = std::min(n_layers - l0, gdn::kMaxLayersPerLaunch);
+    for (int i = 0; i < a.layers; ++i) {
+      const gdn_layer_io& y = layers[l0 + i];
+      const float* U = static_cast<const float*>(y.workspace);
+      const float* g2 = reinterpret_cast<const float*>(static_cast<const char*>(y.workspace) +
+                                                       wy_u_bytes(desc));
+      a.L[i] = gdn::CommitLayer{y.k, y.S0, y.S_out, U, g2};
+    }
+    st = launched(gdn::launch_wy_commit_layers(desc->io_dtype, desc->dk, a, s));
+    if (st != GDN_OK) return st;
+  }
+  return GDN_OK;
 }
 
 const char* gdn_tree_status_string(int status) {

@@ -106,10 +106,81 @@ struct AttnCommitArgs {
   int32_t* status;
 };
 
+// Layer-batched verify / commit: one launch covers several layers that share
+// the tree (offsets, parents, accepted, status); workgroup i works on layer
+// i / (B * H) with that layer's pointers.
+constexpr int kMaxLayersPerLaunch = 32;
+
+struct VerifyLayer {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;
+  void* o;
+  float* U;
+  float* g2;
+};
+
+struct VerifyLayersArgs {
+  VerifyArgs base;   // sizes and the shared tree; its per-layer pointers are unused
+  int layers;
+  VerifyLayer L[kMaxLayersPerLaunch];
+};
+
+struct CommitLayer {
+  const void* k;
+  const float* S0;
+  float* S_out;
+  const float* U;
+  const float* g2;
+};
+
+struct CommitLayersArgs {
+  CommitArgs base;
+  int layers;
+  CommitLayer L[kMaxLayersPerLaunch];
+};
+
+__device__ __forceinline__ VerifyArgs layer_args(const VerifyArgs& a, int) { return a; }
+__device__ __forceinline__ VerifyArgs layer_args(const VerifyLayersArgs& la, int layer) {
+  VerifyArgs a = la.base;
+  const VerifyLayer& l = la.L[layer];
+  a.q = l.q;
+  a.k = l.k;
+  a.v = l.v;
+  a.alpha = l.alpha;
+  a.beta = l.beta;
+  a.S0 = l.S0;
+  a.o = l.o;
+  a.U = l.U;
+  a.g2 = l.g2;
+  return a;
+}
+__device__ __forceinline__ CommitArgs layer_args(const CommitArgs& a, int) { return a; }
+__device__ __forceinline__ CommitArgs layer_args(const CommitLayersArgs& la, int layer) {
+  CommitArgs a = la.base;
+  const CommitLayer& l = la.L[layer];
+  a.k = l.k;
+  a.S0 = l.S0;
+  a.S_out = l.S_out;
+  a.U = l.U;
+  a.g2 = l.g2;
+  return a;
+}
+__device__ __forceinline__ const VerifyArgs& base_args(const VerifyArgs& a) { return a; }
+__device__ __forceinline__ const VerifyArgs& base_args(const VerifyLayersArgs& a) { return a.base; }
+__device__ __forceinline__ const CommitArgs& base_args(const CommitArgs& a) { return a; }
+__device__ __forceinline__ const CommitArgs& base_args(const CommitLayersArgs& a) { return a.base; }
+
 hipError_t launch_wy_verify(int io, int d, int mt, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_wy_verify_layers(int io, int d, int mt, const VerifyLayersArgs& a,
+                                   hipStream_t s);
 hipError_t launch_tree_attn(int d, const AttnArgs& a, hipStream_t s);
 hipError_t launch_tree_attn_commit(int d, const AttnCommitArgs& a, hipStream_t s);
 hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s);
+hipError_t launch_wy_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s);
 hipError_t launch_fork_level(int io, int d, const ForkArgs& a, hipStream_t s);
 hipError_t launch_fork_commit(int d, const ForkCommitArgs& a, hipStream_t s);
 

@@ -36,8 +36,10 @@ namespace {
 
 constexpr int kCommitThreads = 256;
 
-template <class IO, int DK, int DV, bool kPathFirst>
-__global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const CommitArgs a) {
+// Args: CommitArgs (one layer) or CommitLayersArgs (workgroup i takes layer
+// i / (B * H) of a layer-batched launch).
+template <class IO, int DK, int DV, bool kPathFirst, class Args>
+__global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args args) {
   constexpr int NT = kCommitThreads;
   constexpr int CPROW = DK / 4;             // float4 per state row
   constexpr int F4 = DV * DK / 4;           // float4 per (b, h) state
@@ -62,7 +64,10 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const CommitA
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const bool path_wave = tid < kWave;       // wave 0 (wave-uniform)
-  const int bh = blockIdx.x;
+  const int nbh = base_args(args).B * base_args(args).H;
+  const int layer = blockIdx.x / nbh;
+  const CommitArgs a = layer_args(args, layer);
+  const int bh = blockIdx.x - layer * nbh;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int H = a.H;
@@ -240,20 +245,24 @@ hipError_t resident_workgroups(const void* kernel, int block, int* out) {
   return hipSuccess;
 }
 
-template <class IO, int D>
-hipError_t launch_t(const CommitArgs& a, hipStream_t s) {
-  const void* first = reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, true>);
-  const void* state_first = reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, false>);
+inline int grid_of(const CommitArgs& a) { return a.B * a.H; }
+inline int grid_of(const CommitLayersArgs& a) { return a.base.B * a.base.H * a.layers; }
+
+template <class IO, int D, class Args>
+hipError_t launch_t(const Args& a, hipStream_t s) {
+  const void* first = reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, true, Args>);
+  const void* state_first =
+      reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, false, Args>);
   int slots = 0;
   const hipError_t e = resident_workgroups(first, kCommitThreads, &slots);
   if (e != hipSuccess) return e;
-  const int grid = a.B * a.H;
+  const int grid = grid_of(a);
   return launch_kernel(grid <= slots ? first : state_first, (unsigned)grid,
                        (unsigned)kCommitThreads, s, a);
 }
 
-template <class IO>
-hipError_t launch_d(int d, const CommitArgs& a, hipStream_t s) {
+template <class IO, class Args>
+hipError_t launch_d(int d, const Args& a, hipStream_t s) {
   switch (d) {
     case 32: return launch_t<IO, 32>(a, s);
     case 64: return launch_t<IO, 64>(a, s);
@@ -265,6 +274,10 @@ hipError_t launch_d(int d, const CommitArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s) {
+  return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, a, s) : launch_d<float>(d, a, s);
+}
+
+hipError_t launch_wy_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s) {
   return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, a, s) : launch_d<float>(d, a, s);
 }
 

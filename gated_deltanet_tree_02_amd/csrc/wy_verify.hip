@@ -223,9 +223,11 @@ constexpr int verify_waves_per_simd() {
   return verify_three_per_cu<IO, DK, DV, MT>() ? 6 : 1;
 }
 
-template <class IO, int DK, int DV, int MT>
+// Args: VerifyArgs (one layer) or VerifyLayersArgs (workgroup i takes layer
+// i / (B * H) of a layer-batched launch).
+template <class IO, int DK, int DV, int MT, class Args>
 __global__ __launch_bounds__(64 * kVerifyWaves, (verify_waves_per_simd<IO, DK, DV, MT>()))
-void wy_verify_kernel(const VerifyArgs a) {
+void wy_verify_kernel(const Args args) {
   constexpr int NW = kVerifyWaves;
   constexpr int NT = 64 * NW;                 // threads
   constexpr int NP = MT * 16;                 // padded node rows
@@ -287,7 +289,10 @@ void wy_verify_kernel(const VerifyArgs a) {
   const int lane = tid & 63;
   const int g = lane >> 4;      // lane group of an MFMA operand / result
   const int l16 = lane & 15;
-  const int bh = blockIdx.x;
+  const int nbh = base_args(args).B * base_args(args).H;
+  const int layer = blockIdx.x / nbh;
+  const VerifyArgs a = layer_args(args, layer);
+  const int bh = blockIdx.x - layer * nbh;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int H = a.H;
@@ -622,14 +627,19 @@ void wy_verify_kernel(const VerifyArgs a) {
   if (h == 0 && tid == 0) a.status[b] = GDN_TREE_OK;
 }
 
-template <class IO, int D, int MT>
-hipError_t launch_t(const VerifyArgs& a, hipStream_t s) {
-  return launch_kernel(reinterpret_cast<const void*>(&wy_verify_kernel<IO, D, D, MT>),
-                       (unsigned)(a.B * a.H), 64u * kVerifyWaves, s, a);
+inline unsigned grid_of(const VerifyArgs& a) { return (unsigned)(a.B * a.H); }
+inline unsigned grid_of(const VerifyLayersArgs& a) {
+  return (unsigned)(a.base.B * a.base.H * a.layers);
 }
 
-template <class IO, int D>
-hipError_t launch_mt(int mt, const VerifyArgs& a, hipStream_t s) {
+template <class IO, int D, int MT, class Args>
+hipError_t launch_t(const Args& a, hipStream_t s) {
+  return launch_kernel(reinterpret_cast<const void*>(&wy_verify_kernel<IO, D, D, MT, Args>),
+                       grid_of(a), 64u * kVerifyWaves, s, a);
+}
+
+template <class IO, int D, class Args>
+hipError_t launch_mt(int mt, const Args& a, hipStream_t s) {
   switch (mt) {
     case 1: return launch_t<IO, D, 1>(a, s);
     case 2: return launch_t<IO, D, 2>(a, s);
@@ -639,8 +649,8 @@ hipError_t launch_mt(int mt, const VerifyArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <class IO>
-hipError_t launch_d(int d, int mt, const VerifyArgs& a, hipStream_t s) {
+template <class IO, class Args>
+hipError_t launch_d(int d, int mt, const Args& a, hipStream_t s) {
   switch (d) {
     case 32: return launch_mt<IO, 32>(mt, a, s);
     case 64: return launch_mt<IO, 64>(mt, a, s);
@@ -652,6 +662,11 @@ hipError_t launch_d(int d, int mt, const VerifyArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_wy_verify(int io, int d, int mt, const VerifyArgs& a, hipStream_t s) {
+  return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, mt, a, s) : launch_d<float>(d, mt, a, s);
+}
+
+hipError_t launch_wy_verify_layers(int io, int d, int mt, const VerifyLayersArgs& a,
+                                   hipStream_t s) {
   return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, mt, a, s) : launch_d<float>(d, mt, a, s);
 }
 

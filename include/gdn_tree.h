@@ -157,6 +157,40 @@ gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
                            const float* S0, float* S_out, const void* workspace,
                            size_t workspace_bytes, int32_t* tree_status, void* stream);
 
+/* One layer's buffers for the layer-batched calls below: the per-layer
+ * arguments of gdn_tree_verify / gdn_tree_commit (device pointers, same
+ * layouts). Verify reads q, k, v, alpha, beta, S0 and writes o and workspace;
+ * commit reads k, S0 and workspace and writes S_out (fields a call does not
+ * use are ignored). */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;
+  void* o;
+  float* S_out;
+  void* workspace;
+} gdn_layer_io;
+
+/* Layer-batched verify and commit: the same work as n_layers calls of
+ * gdn_tree_verify / gdn_tree_commit on layers that share one draft tree
+ * (offsets, parents, accepted, tree_status), issued as a few launches instead
+ * of one per layer (the round runs every GDN layer of the model on the same
+ * tree: fork page section 7, steps 2 and 4). `layers` is a HOST array of
+ * n_layers entries; every layer's workspace holds workspace_bytes bytes.
+ * Results are identical to the per-layer calls. FORK mode runs the per-layer
+ * calls. n_layers <= 0 is a no-op. */
+gdn_status gdn_tree_verify_layers(const gdn_tree_desc* desc, int32_t n_layers,
+                                  const int32_t* offsets, const int32_t* parents,
+                                  const gdn_layer_io* layers, size_t workspace_bytes,
+                                  int32_t* tree_status, void* stream);
+gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
+                                  const int32_t* offsets, const int32_t* parents,
+                                  const int32_t* accepted, const gdn_layer_io* layers,
+                                  size_t workspace_bytes, int32_t* tree_status, void* stream);
+
 /* Static text for a gdn_status value. */
 const char* gdn_tree_status_string(int status);
 

@@ -29,7 +29,8 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["gdn_tree_workspace_bytes", "gdn_tree_build", "gdn_tree_verify",
                             "gdn_tree_commit", "gdn_tree_status_string",
                             "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
-                            "gdn_tree_attn_commit"])
+                            "gdn_tree_attn_commit", "gdn_tree_verify_layers",
+                            "gdn_tree_commit_layers"])
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -185,3 +186,38 @@ def test_attn_null_pointers_and_small_workspace():
     assert lib.gdn_tree_attn_verify(ctypes.byref(d), *args) == 1
     assert lib.gdn_tree_attn_commit(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake,
                                     fake, fake, None) == 1
+
+
+# ------------------------------------------------------------------ layer-batched calls
+
+
+def test_layer_io_layout_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{([^{}]*)\} gdn_layer_io;", text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(\w+)\s*;", body)
+    assert fields == [f for f, _ in gt.GdnLayerIO._fields_]
+    assert ctypes.sizeof(gt.GdnLayerIO) == 8 * len(fields)
+
+
+def test_layers_calls_check_before_launch():
+    lib = gt.load_library()
+    d = gt.make_desc(2, 16, 128, 128, 10, 8)
+    fake = ctypes.c_void_p(0x1000)
+    need = gt.gdn_tree_workspace_bytes(d)
+    ly = (gt.GdnLayerIO * 2)(*[gt.GdnLayerIO(*([0x1000] * 9)) for _ in range(2)])
+    # no layers: nothing to do; a NULL table with layers: error
+    assert lib.gdn_tree_verify_layers(ctypes.byref(d), 0, fake, fake, None, need, fake, None) == 0
+    assert lib.gdn_tree_verify_layers(ctypes.byref(d), 2, fake, fake, None, need, fake, None) == 1
+    assert lib.gdn_tree_commit_layers(ctypes.byref(d), 2, fake, fake, fake, None, need, fake,
+                                      None) == 1
+    # a small workspace, a NULL field, a bad descriptor
+    assert lib.gdn_tree_verify_layers(ctypes.byref(d), 2, fake, fake, ly, need - 1, fake,
+                                      None) == 4
+    ly[1].o = None
+    assert lib.gdn_tree_verify_layers(ctypes.byref(d), 2, fake, fake, ly, need, fake, None) == 1
+    ly[1].S_out = None
+    assert lib.gdn_tree_commit_layers(ctypes.byref(d), 2, fake, fake, fake, ly, need, fake,
+                                      None) == 1
+    d.dk = 96
+    assert lib.gdn_tree_verify_layers(ctypes.byref(d), 2, fake, fake, ly, need, fake, None) == 3

@@ -8,20 +8,20 @@
 // tokens, query heads share K/V heads in groups):
 //     o[t,h] = softmax_x(scale <q[t,h], key_x>) . value_x .
 //
-// Verify kernel. One workgroup (16 waves) per (sequence, K/V head, split of
-// the cache). The G * N_b query rows that share the K/V head (<= 256) are
-// 16-row tiles, one per wave. Keys stream through LDS in blocks of 64: the
-// cache rows of the split, then (in the last split) the 64 tree slots, masked
-// per query row by the node's ancestor bits. Per block a wave computes the
-// transposed scores S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = staged K
-// rows, B = the wave's query rows held in registers), so that a lane owns one
-// query row: the online softmax (running max and sum, base-2 exponentials)
-// needs only two cross-lane shuffles, and the probabilities come out in the
-// B-operand layout of v_mfma_f32_16x16x16_bf16, which accumulates
-// O^T += V^T P^T with V staged transposed. Two blocks of K/V are in flight in
-// registers while one is computed. A split's unnormalised output, running max
-// and sum go to the workspace when the cache is split over several
-// workgroups, and a combine kernel merges them.
+// Verify kernels. One workgroup per (sequence, K/V head, split of the cache).
+// The G * N_b query rows that share the K/V head (<= 256) are split into
+// tiles, one per wave (16-row tiles on 12 waves up to 192 rows, 32-row tiles
+// on 8 waves beyond). Keys stream through a 4-stage LDS ring in blocks of 64,
+// loaded straight from HBM into LDS: the cache rows of the split, then (in the
+// last split) the 64 tree slots, masked per query row by the node's ancestor
+// bits. Per block a wave computes the transposed scores S^T = K Q^T on MFMA
+// (A = staged K rows, B = the wave's query rows held in registers), so that a
+// lane owns one query row: the online softmax needs at most two cross-lane
+// shuffles, and the weights come out in the B-operand layout of the same MFMA,
+// which accumulates O^T += V^T P^T with V read column-wise from LDS by the
+// transposing read. A split's unnormalised output, reference and sum go to the
+// workspace when the cache is split over several workgroups, and a combine
+// kernel merges them.
 //
 // Commit kernel. One workgroup per sequence copies the K/V rows of the
 // accepted path, root first, behind the sequence's committed rows and
@@ -142,40 +142,38 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int g, int l16) {
 }
 
 // Scores, online softmax and output update of one staged key block (K at
-// sK, V right after it) for the wave's first NT query tiles; each K and V
-// fragment read from LDS serves all of them. The query fragments hold
-// q * scale * log2(e), so a score is already in base-2 units; the MFMA starts
-// from -m, the lane's reference, and returns x - m directly.
+// sK, V right after it) for the wave's 16-row query tile. The query fragments
+// hold q * scale * log2(e), so a score is already in base-2 units; the MFMA
+// starts from -m, the lane's reference, and returns x - m directly.
 //
-// FULL: every key of the block is visible; otherwise bit 16 kt + e of vm[u]
-// says whether key 16 kt + 4g + e is visible to the lane's row of tile u (the
-// row's ancestor bits shifted by 4g for the tree block, a prefix of keys for
-// the last cache block), and invisible keys get x - m = -1e30, weight 0.
+// FULL: every key of the block is visible; otherwise bit 16 kt + e of vm says
+// whether key 16 kt + 4g + e is visible to the lane's row (the row's ancestor
+// bits shifted by 4g for the tree block, a prefix of keys for the last cache
+// block), and invisible keys get x - m = -1e30, weight 0.
 //
-// first (the split's first block): the reference is set to the row maximum.
-// Later blocks raise it only when some lane of the wave sees x - m > kSlack,
-// so the O^T rescale is rare and every weight stays below 2^kSlack; the
-// final o = O^T / l does not depend on the reference.
-template <int D, int NT, bool FULL, int TPW>
-__device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char* sK,
-                                             const LaneOffsets& lo, const uint64_t (&vm)[TPW],
-                                             bool first, const bf16x8& ones) {
+// A row takes its maximum as its reference at its first visible key; later
+// halves raise it only when some lane of the wave sees x - m > kSlack, so the
+// O^T rescale is rare and every weight stays below 2^kSlack; the final
+// o = O^T / l does not depend on the reference.
+template <int D, bool FULL, int HALF>
+__device__ __forceinline__ void attend_block(Tile<D>& T, const lds_char* sK,
+                                             const LaneOffsets& lo, uint64_t vm,
+                                             const bf16x8& ones) {
   constexpr int KSD = D / 32;
   constexpr int DT = D / 16;
   constexpr int RB = 2 * D;
   const lds_char* sV = sK + KB * RB;
 
-  // the block in two halves of 32 keys (key group mg = key tiles 2mg, 2mg+1)
+  // the block in two halves of 32 keys (key group mg = key tiles 2mg, 2mg+1);
+  // HALF >= 0: this wave takes only that half (another wave takes the other)
 #pragma unroll
-  for (int mg = 0; mg < 2; ++mg) {
-    // S^T tiles: lane holds its row of tile u and keys 16 kt + 4g + e, as x - m
-    f32x4 acc[NT][2];
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      const float c0 = (first && mg == 0) ? 0.f : -tl[u].m;
-      acc[u][0] = f32x4{c0, c0, c0, c0};
-      acc[u][1] = acc[u][0];
-    }
+  for (int mg = (HALF == 1 ? 1 : 0); mg < (HALF == 0 ? 1 : 2); ++mg) {
+    // S^T tiles: lane holds query row l16 and keys 16 kt + 4g + e, as x - m
+    // (as x while the row has no reference yet)
+    const float c0 = T.m > 0.5f * kMasked ? -T.m : 0.f;
+    f32x4 acc[2];
+    acc[0] = f32x4{c0, c0, c0, c0};
+    acc[1] = acc[0];
     __builtin_amdgcn_s_setprio(1);            // MFMA phases first
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
@@ -184,55 +182,45 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
       for (int h = 0; h < 2; ++h)
         ka[h] = *(const lds_bf16x8*)(sK + (lo.k ^ (64 * s)) + 16 * RB * (2 * mg + h));
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < NT; ++u) acc[u][h] = mfma_k32(ka[h], tl[u].qf[s], acc[u][h]);
+      for (int h = 0; h < 2; ++h) acc[h] = mfma_k32(ka[h], T.qf[s], acc[h]);
     }
-
     __builtin_amdgcn_s_setprio(0);
-    bf16x8 pk[NT];
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      Tile<D>& T = tl[u];
-      if (!FULL) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (((vm[u] >> (32 * mg + 16 * h + e)) & 1ull) == 0) acc[u][h][e] = kMasked;
-      }
-      float mx = fmaxf(fmaxf(fmaxf(acc[u][0][0], acc[u][0][1]), fmaxf(acc[u][0][2], acc[u][0][3])),
-                       fmaxf(fmaxf(acc[u][1][0], acc[u][1][1]), fmaxf(acc[u][1][2], acc[u][1][3])));
-      const bool set = first && mg == 0;
-      if (set || __ballot(mx > kSlack) != 0ull) {    // wave-uniform
-        // raise each row's reference to its maximum (the four lanes of a
-        // row, g = 0..3, hold its keys between them)
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float delta = set ? mx : fmaxf(mx, 0.f);
-        T.m = set ? mx : T.m + delta;
-        acc[u][0] -= delta;
-        acc[u][1] -= delta;
-        if (!set) {
-          const float alpha = __builtin_amdgcn_exp2f(-delta);
-          T.l[0] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) T.o[dt] *= alpha;
-        }
-      }
-      // P^T as the B operand of 16x16x32 over the 32 keys: k slot 8g + i
-      // holds key 32 mg + 4g + i (i < 4) or 32 mg + 16 + 4g + i - 4
+    if (!FULL) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pk[u][4 * h + e] = (__bf16)__builtin_amdgcn_exp2f(acc[u][h][e]);
-      // row sums of the same bf16 weights the output uses: a ones row
-      // (row 0 of the A operand) against P^T
-      T.l = mfma_k32(ones, pk[u], T.l);
+        for (int e = 0; e < 4; ++e)
+          if (((vm >> (32 * mg + 16 * h + e)) & 1ull) == 0) acc[h][e] = kMasked;
     }
+    float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
+                     fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
+    const bool has = T.m > 0.5f * kMasked;
+    if (__ballot(has ? mx > kSlack : mx > 0.5f * kMasked) != 0ull) {   // wave-uniform
+      // the four lanes of a row, g = 0..3, hold its keys between them
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const bool seen = mx > 0.5f * kMasked;
+      const float delta = has ? fmaxf(mx, 0.f) : (seen ? mx : 0.f);
+      T.m = has ? T.m + delta : (seen ? mx : T.m);
+      acc[0] -= delta;
+      acc[1] -= delta;
+      const float alpha = has ? __builtin_amdgcn_exp2f(-delta) : 1.f;
+      T.l[0] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) T.o[dt] *= alpha;
+    }
+    // P^T as the B operand of 16x16x32 over the 32 keys: k slot 8g + i holds
+    // key 32 mg + 4g + i (i < 4) or 32 mg + 16 + 4g + i - 4
+    bf16x8 pk;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[4 * h + e] = (__bf16)__builtin_amdgcn_exp2f(acc[h][e]);
+    // row sums of the same bf16 weights the output uses: a ones row (row 0
+    // of the A operand) against P^T
+    T.l = mfma_k32(ones, pk, T.l);
     // O^T += V^T P^T: A = V^T rows d = 16 dt + l16 over the same key slots,
-    // read column-wise from the row-major V block; each V fragment serves
-    // every tile of the wave
+    // read column-wise from the row-major V block
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -240,15 +228,12 @@ __device__ __forceinline__ void attend_block(Tile<D> (&tl)[TPW], const lds_char*
       const bf16x4 v1 = lds_read_tr16(p1);
       const bf16x4 v2 = lds_read_tr16(p1 + 16 * RB);
       const bf16x8 va = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int u = 0; u < NT; ++u) tl[u].o[dt] = mfma_k32(va, pk[u], tl[u].o[dt]);
+      T.o[dt] = mfma_k32(va, pk, T.o[dt]);
     }
     __builtin_amdgcn_s_setprio(0);
   }
 }
 
-// W waves, wave w owning query tiles w, w + W, ... (TPW of them at most):
-// W * TPW * 16 >= the rows of a (sequence, K/V head).
 template <int N>
 __device__ __forceinline__ void wait_blocks_ahead(int ahead) {
   if (ahead >= 3) wait_vmem<3 * N>();
@@ -257,7 +242,9 @@ __device__ __forceinline__ void wait_blocks_ahead(int ahead) {
   else wait_vmem<0>();
 }
 
-template <int D, int W, int TPW>
+// W waves of one 16-row query tile each (W * 16 >= the rows of a (sequence,
+// K/V head)); see the tile assignment below.
+template <int D, int W>
 __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int KSD = D / 32;                 // 16x16x32 steps over d (scores)
@@ -316,37 +303,42 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
   // of the G * n rows of the K/V head, query-head-major, node inner)
   const int R = range_ok ? G * n : 0;
   const int ntiles = (R + 15) >> 4;
-  const int nt = ntiles > wave ? (ntiles - wave + W - 1) / W : 0;   // wave-uniform
-  size_t orow[TPW];
-  bool rv[TPW];
-  Tile<D> tl[TPW];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int r = 16 * (wave + W * u) + l16;
-    rv[u] = r < R;
-    const int hg = rv[u] ? r / n : 0;
-    const int t = rv[u] ? r - hg * n : 0;
-    orow[u] = (size_t)(lo + t) * a.Hq + kvh * G + hg;
-    tl[u].anc = sAnc[t];
-    tl[u].m = 0.f;
-    tl[u].l = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) tl[u].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Tiles [0, nfull) get a wave each, and each of the last nsplit tiles gets
+  // two waves, one per 32-key half of every block (merged at the end), so that
+  // the four SIMDs carry equal work when the tiles do not divide evenly
+  // (10 tiles on 12 waves: 2.5 tiles per SIMD).
+  const int nsplit = max(0, min(ntiles, W - ntiles));   // workgroup-uniform
+  const int nfull = ntiles - nsplit;
+  int tile = wave, half = -1;                 // wave-uniform role
+  if (wave >= nfull) {
+    const int q2 = wave - nfull;
+    tile = q2 < 2 * nsplit ? nfull + (q2 >> 1) : ntiles;   // ntiles: idle
+    half = q2 & 1;
   }
+  const bool active = tile < ntiles;          // wave-uniform
+  const int r = 16 * tile + l16;
+  const bool rv = r < R;
+  const int hg = rv ? r / n : 0;
+  const int t = rv ? r - hg * n : 0;
+  const size_t orow = (size_t)(lo + t) * a.Hq + kvh * G + hg;   // row of o / the partials
+  Tile<D> T;
+  T.anc = sAnc[t];
+  T.m = kMasked;                              // no reference yet
+  T.l = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) T.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (st != GDN_TREE_OK) {
     // rows of a rejected sequence (with a valid node range) are zero
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      if (!rv[u]) continue;
+    if (rv && half <= 0) {
       if (NS == 1) {
         for (int c = 4 * g; c < D; c += 16)
-          *reinterpret_cast<uint2*>(a.o + orow[u] * D + c) = make_uint2(0u, 0u);
+          *reinterpret_cast<uint2*>(a.o + orow * D + c) = make_uint2(0u, 0u);
       } else {
         for (int c = 4 * g; c < D; c += 16)
-          *reinterpret_cast<float4*>(a.part_o + (orow[u] * NS + split) * D + c) =
+          *reinterpret_cast<float4*>(a.part_o + (orow * NS + split) * D + c) =
               make_float4(0.f, 0.f, 0.f, 0.f);
-        if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (orow[u] * NS + split) * 2) =
+        if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (orow * NS + split) * 2) =
             make_float2(kMasked, 0.f);
       }
     }
@@ -356,16 +348,15 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
   // query fragments, scaled to base-2 score units and rounded to bf16,
   // waited for before the key blocks are issued (the block waits below count
   // only the block loads)
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const uint16_t* qrow = a.q + orow[u] * D;
+  {
+    const uint16_t* qrow = a.q + orow * D;
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
-      const uint4 v = rv[u] ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
-                            : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v = rv ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
+                         : make_uint4(0u, 0u, 0u, 0u);
       const bf16x8 x = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tl[u].qf[s][e] = (__bf16)((float)x[e] * a.scale_log2);
+      for (int e = 0; e < 8; ++e) T.qf[s][e] = (__bf16)((float)x[e] * a.scale_log2);
     }
   }
   wait_vmem<0>();
@@ -443,54 +434,413 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
     else wait_blocks_ahead<(LMAX > 1 ? LMAX - 1 : 1)>(ahead);
     __syncthreads();                          // every thread's part landed; stage j-1 is free
     if (j + kStages - 1 < nblk) issue_block(j + kStages - 1, (j + kStages - 1) % kStages);
-    if (nt == 0) continue;
+    if (!active) continue;
 
     const lds_char* sK = (const lds_char*)smem + (j % kStages) * STAGE;
     const bool tree = j >= ncb;
     const int lim = tree ? KB : c1 - (c0 + j * KB);   // cache keys below lim are visible
-    const bool first = j == 0;
     if (!tree && lim >= KB) {
-      const uint64_t vm[TPW] = {};
-      if (TPW > 1 && nt > 1) attend_block<D, TPW, true, TPW>(tl, sK, lofs, vm, first, ones);
-      else attend_block<D, 1, true, TPW>(tl, sK, lofs, vm, first, ones);
+      if (half < 0) attend_block<D, true, -1>(T, sK, lofs, 0ull, ones);
+      else if (half == 0) attend_block<D, true, 0>(T, sK, lofs, 0ull, ones);
+      else attend_block<D, true, 1>(T, sK, lofs, 0ull, ones);
     } else {
       const int lm = lim - 4 * g;             // lane keys 16 kt + e below lm are visible
-      uint64_t vm[TPW];
-#pragma unroll
-      for (int u = 0; u < TPW; ++u)
-        vm[u] = tree ? tl[u].anc >> (4 * g)
-                     : (lm >= 64 ? ~0ull : lm <= 0 ? 0ull : (1ull << lm) - 1ull);
-      if (TPW > 1 && nt > 1) attend_block<D, TPW, false, TPW>(tl, sK, lofs, vm, first, ones);
-      else attend_block<D, 1, false, TPW>(tl, sK, lofs, vm, first, ones);
+      const uint64_t vm = tree ? T.anc >> (4 * g)
+                               : (lm >= 64 ? ~0ull : lm <= 0 ? 0ull : (1ull << lm) - 1ull);
+      if (half < 0) attend_block<D, false, -1>(T, sK, lofs, vm, ones);
+      else if (half == 0) attend_block<D, false, 0>(T, sK, lofs, vm, ones);
+      else attend_block<D, false, 1>(T, sK, lofs, vm, ones);
     }
   }
 
-  // ---- results: lane (g, l16) holds O^T rows d = 16 dt + 4g + e of its row
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    Tile<D>& T = tl[u];
-    const float lsum = __shfl(T.l[0], l16, kWave);   // from lane (g = 0, l16)
-    if (!rv[u]) continue;
-    if (NS == 1) {
-      const float inv = 1.f / lsum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint32_t w0 = (uint32_t)float_to_bf16_bits(T.o[dt][0] * inv) |
-                            ((uint32_t)float_to_bf16_bits(T.o[dt][1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)float_to_bf16_bits(T.o[dt][2] * inv) |
-                            ((uint32_t)float_to_bf16_bits(T.o[dt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(a.o + orow[u] * D + 16 * dt + 4 * g) = make_uint2(w0, w1);
-      }
-    } else {
-      float* po = a.part_o + (orow[u] * NS + split) * D;
+  // ---- split tiles: the half-1 wave hands its (m, l, O^T) to the half-0
+  // wave through LDS (the stages are free once every wave passed the loop)
+  if (nsplit > 0) {
+    constexpr int SLOT = 64 * (DT * 4 + 8);   // floats per split tile: O^T, l, m
+    __syncthreads();
+    float* xs = reinterpret_cast<float*>(smem) + (tile - nfull) * SLOT;
+    if (active && half == 1) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
-            make_float4(T.o[dt][0], T.o[dt][1], T.o[dt][2], T.o[dt][3]);
-      if (g == 0)
-        *reinterpret_cast<float2*>(a.part_ml + (orow[u] * NS + split) * 2) =
-            make_float2(T.m, lsum);
+        *reinterpret_cast<f32x4*>(xs + (dt * 64 + lane) * 4) = T.o[dt];
+      *reinterpret_cast<f32x4*>(xs + (DT * 64 + lane) * 4) = T.l;
+      xs[DT * 256 + 256 + lane] = T.m;
     }
+    __syncthreads();
+    if (active && half == 0) {
+      const float m1 = xs[DT * 256 + 256 + lane];
+      const float M = fmaxf(T.m, m1);
+      const float a0 = T.m > 0.5f * kMasked ? __builtin_amdgcn_exp2f(T.m - M) : 0.f;
+      const float a1 = m1 > 0.5f * kMasked ? __builtin_amdgcn_exp2f(m1 - M) : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        T.o[dt] = T.o[dt] * a0 + *reinterpret_cast<const f32x4*>(xs + (dt * 64 + lane) * 4) * a1;
+      T.l = T.l * a0 + *reinterpret_cast<const f32x4*>(xs + (DT * 64 + lane) * 4) * a1;
+      T.m = M;
+    }
+  }
+
+  // ---- results: lane (g, l16) holds O^T rows d = 16 dt + 4g + e of row r
+  const float lsum = __shfl(T.l[0], l16, kWave);   // from lane (g = 0, l16)
+  if (!rv || half == 1) return;
+  if (NS == 1) {
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t w0 = (uint32_t)float_to_bf16_bits(T.o[dt][0] * inv) |
+                          ((uint32_t)float_to_bf16_bits(T.o[dt][1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)float_to_bf16_bits(T.o[dt][2] * inv) |
+                          ((uint32_t)float_to_bf16_bits(T.o[dt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(a.o + orow * D + 16 * dt + 4 * g) = make_uint2(w0, w1);
+    }
+  } else {
+    float* po = a.part_o + (orow * NS + split) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
+          make_float4(T.o[dt][0], T.o[dt][1], T.o[dt][2], T.o[dt][3]);
+    if (g == 0)
+      *reinterpret_cast<float2*>(a.part_ml + (orow * NS + split) * 2) = make_float2(T.m, lsum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 32-row query tiles on v_mfma_f32_32x32x16_bf16. A K or V fragment read from
+// LDS then serves 32 query rows instead of 16, halving the LDS reads per row.
+// Layouts (A: lane = row l % 32, k = 8 (l / 32) .. +7; B: lane = column
+// l % 32, the same k; D: lane = column l % 32, rows 8 (i / 4) + 4 (l / 32) +
+// i % 4 for result element i = 0..15).
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Chunk permutation of the 32-row kernels' staged blocks: chunk c of row r at
+// c ^ f(r). A K fragment read touches rows 0..15 (16 lanes per LDS cycle) at
+// one logical chunk, so f is a bijection on r mod 16 (256-byte rows) or on
+// r / 2 mod 8 per row parity (128-byte rows, two per 256-byte bank window);
+// a transposing V read touches rows 0..3 at four consecutive chunks, so the
+// bits of f above the lowest two differ between those rows.
+template <int D>
+__device__ __forceinline__ int swz32_key(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+template <int D>
+struct Tile32 {
+  bf16x8 qf[D / 16];     // B operand of S^T = K Q^T: column = query row l % 32,
+                         // k = d 16s + 8 (l / 32) .. +7, holding q * scale * log2(e)
+  f32x16 o[D / 32];      // O^T rows d = 32 dt + 8 (i / 4) + 4 (l / 32) + i % 4
+  float l;               // this lane's part of the row sum
+  float m;               // row reference (base-2 units); kMasked: none yet
+  uint64_t anc;          // ancestor bits of the lane's node
+};
+
+// K fragment (key tile mg, step s) at (k ^ 32 s) + 32 RB mg; V^T fragment
+// (key group mg, 16-key step ms, d tile dt) at (v1 ^ 64 dt) + (32 mg + 16 ms) RB
+// and (v2 ^ 64 dt) + the same, RB = 2D bytes per row.
+struct LaneOffsets32 {
+  int k, v1, v2;
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets32 lane_offsets32(int lane) {
+  constexpr int RB = 2 * D;
+  LaneOffsets32 o;
+  const int r32 = lane & 31, hh = lane >> 5;
+  o.k = r32 * RB | ((swz32_key<D>(r32) ^ hh) << 4);      // logical chunk 2s + hh
+  // transposing reads: 16-lane group (dsub, hh) = ((lane >> 4) & 1, lane >> 5);
+  // lane j of the group reads row 4 hh + j / 4 (+8 for the second read),
+  // columns 32 dt + 16 dsub + 4 (j % 4) .. +3: logical chunk 4 dt + c',
+  // c' = 2 dsub + (j % 4) / 2, byte 8 (j % 2) of it
+  const int j = lane & 15;
+  const int c = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+  const int r1 = 4 * hh + (j >> 2), r2 = r1 + 8;
+  o.v1 = r1 * RB | ((c ^ swz32_key<D>(r1)) << 4) | ((j & 1) << 3);
+  o.v2 = r2 * RB | ((c ^ swz32_key<D>(r2)) << 4) | ((j & 1) << 3);
+  return o;
+}
+
+// One 64-key block for a wave's 32-row tile. FULL and vm as in attend_block,
+// with bit 32 mg + 8 q + r of vm for the lane's key 32 mg + 8 q + 4 (l / 32) + r
+// (vm = the row's ancestor bits shifted by 4 (l / 32), or a prefix).
+template <int D, bool FULL>
+__device__ __forceinline__ void attend_block32(Tile32<D>& T, const lds_char* sK,
+                                               const LaneOffsets32& lo, uint64_t vm) {
+  constexpr int KS = D / 16;                  // 32x32x16 steps over d (scores)
+  constexpr int DT = D / 32;                  // 32-row tiles of O^T
+  constexpr int RB = 2 * D;
+  const lds_char* sV = sK + KB * RB;
+#pragma unroll
+  for (int mg = 0; mg < 2; ++mg) {
+    const float c0 = T.m > 0.5f * kMasked ? -T.m : 0.f;
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = c0;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 ka = *(const lds_bf16x8*)(sK + (lo.k ^ (32 * s)) + 32 * RB * mg);
+      acc = mfma32(ka, T.qf[s], acc);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (!FULL) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (((vm >> (32 * mg + 8 * (i >> 2) + (i & 3))) & 1ull) == 0) acc[i] = kMasked;
+    }
+    float mx = acc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
+    const bool has = T.m > 0.5f * kMasked;
+    if (__ballot(has ? mx > kSlack : mx > 0.5f * kMasked) != 0ull) {   // wave-uniform
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));   // lanes l, l ^ 32 hold the same row
+      const bool seen = mx > 0.5f * kMasked;
+      const float delta = has ? fmaxf(mx, 0.f) : (seen ? mx : 0.f);
+      T.m = has ? T.m + delta : (seen ? mx : T.m);
+      acc -= delta;
+      const float alpha = has ? __builtin_amdgcn_exp2f(-delta) : 1.f;
+      T.l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) T.o[dt] *= alpha;
+    }
+    // P^T as the B operand of 32x32x16 over 16-key steps: step ms holds the
+    // results 8 ms .. 8 ms + 7 (keys 16 ms + 4 (l / 32) + 0..3, then + 8)
+    bf16x8 pk[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(acc[i]);
+      T.l += p;
+      pk[i >> 3][i & 7] = (__bf16)p;
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int rows = (32 * mg + 16 * ms) * RB;
+        const bf16x4 v1 = lds_read_tr16(sV + (lo.v1 ^ (64 * dt)) + rows);
+        const bf16x4 v2 = lds_read_tr16(sV + (lo.v2 ^ (64 * dt)) + rows);
+        const bf16x8 va = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+        T.o[dt] = mfma32(va, pk[ms], T.o[dt]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+}
+
+// W waves, the 32-row tile t on wave t (W * 32 >= the rows of a (sequence,
+// K/V head)); the rest as in tree_attn_kernel.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void tree_attn32_kernel(const AttnArgs a) {
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int MAT = KB * 2 * D;             // bytes of one staged matrix (K or V)
+  constexpr int STAGE = 2 * MAT;              // K block then V block
+  constexpr int NU = STAGE / 1024;            // 1 KiB wave loads per block
+  constexpr int LMAX = (NU + W - 1) / W;      // loads per thread per block: LMAX or LMAX - 1
+  static_assert(MAT % 1024 == 0, "a wave's 1 KiB load falls in one matrix");
+
+  __shared__ __align__(16) char smem[kStages * STAGE];
+  __shared__ uint64_t sAnc[64];
+  __shared__ int sStatus;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int r32 = lane & 31;
+  const int NS = a.NS;
+  const int split = blockIdx.x % NS;
+  const int bkv = blockIdx.x / NS;
+  const int b = bkv / a.Hkv;
+  const int kvh = bkv - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+
+  // ---- sequence checks and ancestor masks (wave 0)
+  const int lo = a.offsets[b];
+  const int hi = a.offsets[b + 1];
+  const int n = hi - lo;
+  const int L = a.cache_len[b];
+  const bool range_ok = lo >= 0 && hi <= a.T && n >= 1 && n <= a.max_nodes;
+  if (wave == 0) {
+    int st = GDN_TREE_OK;
+    uint64_t anc = 0;
+    if (!range_ok || L < 0 || L > a.max_len) {
+      st = GDN_TREE_BAD_SIZE;
+    } else {
+      const int par_raw = a.parents[lo + (lane < n ? lane : 0)];
+      const int par = lane < n ? par_raw : -1;
+      if (__shfl(par, 0, kWave) != -1)
+        st = GDN_TREE_BAD_ROOT;
+      else if (__ballot(lane >= 1 && lane < n && (par < 0 || par >= lane)) != 0ull)
+        st = GDN_TREE_BAD_PARENT;
+      float unused;
+      path_scan(par, lane, n, 0.f, anc, unused);
+    }
+    sAnc[lane] = anc;
+    if (lane == 0) sStatus = st;
+  }
+  __syncthreads();
+  const int st = __builtin_amdgcn_readfirstlane(sStatus);
+  if (split == 0 && kvh == 0 && tid == 0) a.status[b] = st;
+
+  // ---- this wave's tile: rows 32 wave + l % 32 of the G * n rows of the
+  // K/V head (query-head-major, node inner)
+  const int R = range_ok ? G * n : 0;
+  const bool active = 32 * wave < R;          // wave-uniform
+  const int r = 32 * wave + r32;
+  const bool rv = r < R;
+  const int hg = rv ? r / n : 0;
+  const int t = rv ? r - hg * n : 0;
+  const size_t orow = (size_t)(lo + t) * a.Hq + kvh * G + hg;
+
+  if (st != GDN_TREE_OK) {
+    // rows of a rejected sequence (with a valid node range) are zero
+    if (rv) {
+      if (NS == 1) {
+        for (int c = 4 * hh; c < D; c += 8)
+          *reinterpret_cast<uint2*>(a.o + orow * D + c) = make_uint2(0u, 0u);
+      } else {
+        for (int c = 4 * hh; c < D; c += 8)
+          *reinterpret_cast<float4*>(a.part_o + (orow * NS + split) * D + c) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+        if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + (orow * NS + split) * 2) =
+            make_float2(kMasked, 0.f);
+      }
+    }
+    return;
+  }
+
+  Tile32<D> T;
+  T.anc = sAnc[t];
+  T.m = kMasked;
+  T.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) T.o[dt][i] = 0.f;
+  {
+    // query fragments, scaled to base-2 score units and rounded to bf16,
+    // waited for before the key blocks are issued
+    const uint16_t* qrow = a.q + orow * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 v = rv ? *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hh)
+                         : make_uint4(0u, 0u, 0u, 0u);
+      const bf16x8 x = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) T.qf[s][e] = (__bf16)((float)x[e] * a.scale_log2);
+    }
+  }
+  wait_vmem<0>();
+  const LaneOffsets32 lofs = lane_offsets32<D>(lane);
+
+  // ---- key range of this split: cache rows [c0, c1), then the tree slots
+  const int c0 = min(split * a.CL, L);
+  const int c1 = min(c0 + a.CL, L);
+  const int ncb = (c1 - c0 + KB - 1) / KB;
+  const int nblk = ncb + (split == NS - 1 ? 1 : 0);
+  const size_t kvbase = ((size_t)b * a.Hkv + kvh) * a.cap;
+  const uint32_t smem_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char*)smem);
+
+  // Block loads, as in tree_attn_kernel (slot q of a stage holds row q / CPR,
+  // stored chunk q % CPR, i.e. logical chunk (q % CPR) ^ f(row)).
+  const int nload = (NU - wave + W - 1) / W;
+  uint32_t loff[LMAX];
+#pragma unroll
+  for (int i = 0; i < LMAX; ++i) {
+    const int rem = (64 * (wave + W * i) + lane) % (KB * CPR);
+    const int row = rem / CPR;
+    loff[i] = (uint32_t)(row * D + 8 * ((rem % CPR) ^ swz32_key<D>(row))) * 2u;
+  }
+  const uint16_t* kc_seq = a.kc + kvbase * D;
+  const uint16_t* vc_seq = a.vc + kvbase * D;
+  const size_t tree0 = ((size_t)lo * a.Hkv + kvh) * D;
+  auto issue_block = [&](int j, int s) {
+    const bool tree = j >= ncb;
+    const int p0 = c0 + j * KB;
+    const bool partial = !tree && p0 + KB > c1;
+#pragma unroll
+    for (int i = 0; i < LMAX; ++i) {
+      if (i == LMAX - 1 && i >= nload) break;
+      const int wbase = 64 * (wave + W * i);
+      const int mat = wbase >= KB * CPR ? 1 : 0;
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(smem_base + s * STAGE + 16 * wbase);
+      if (!tree && !partial) {
+        load_lds_16((mat ? vc_seq : kc_seq) + (size_t)p0 * D, loff[i], lds);
+      } else {
+        const int rem = wbase + lane - mat * KB * CPR;
+        const int row = rem / CPR;
+        const int chunk = (rem % CPR) ^ swz32_key<D>(row);
+        if (!tree) {
+          const int p = min(row, c1 - 1 - p0);
+          load_lds_16((mat ? vc_seq : kc_seq) + (size_t)p0 * D,
+                      (uint32_t)(p * D + 8 * chunk) * 2u, lds);
+        } else {
+          const int node = row < n ? row : 0;
+          load_lds_16((mat ? a.v : a.k) + tree0,
+                      (uint32_t)(node * a.Hkv * D + 8 * chunk) * 2u, lds);
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < nblk) issue_block(j, j);
+
+  for (int j = 0; j < nblk; ++j) {
+    const int ahead = min(kStages - 2, nblk - 1 - j);
+    if (nload == LMAX) wait_blocks_ahead<LMAX>(ahead);
+    else wait_blocks_ahead<(LMAX > 1 ? LMAX - 1 : 1)>(ahead);
+    __syncthreads();
+    if (j + kStages - 1 < nblk) issue_block(j + kStages - 1, (j + kStages - 1) % kStages);
+    if (!active) continue;
+
+    const lds_char* sK = (const lds_char*)smem + (j % kStages) * STAGE;
+    const bool tree = j >= ncb;
+    const int lim = tree ? KB : c1 - (c0 + j * KB);
+    if (!tree && lim >= KB) {
+      attend_block32<D, true>(T, sK, lofs, 0ull);
+    } else {
+      const int lm = lim - 4 * hh;            // lane keys 8 q + r below lm are visible
+      const uint64_t vm = tree ? T.anc >> (4 * hh)
+                               : (lm >= 64 ? ~0ull : lm <= 0 ? 0ull : (1ull << lm) - 1ull);
+      attend_block32<D, false>(T, sK, lofs, vm);
+    }
+  }
+
+  // ---- results: lane (hh, r32) holds O^T rows d = 32 dt + 8 q + 4 hh + 0..3
+  const float lsum = T.l + __shfl_xor(T.l, 32, kWave);
+  if (!rv) return;
+  if (NS == 1) {
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w0 = (uint32_t)float_to_bf16_bits(T.o[dt][4 * q] * inv) |
+                            ((uint32_t)float_to_bf16_bits(T.o[dt][4 * q + 1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)float_to_bf16_bits(T.o[dt][4 * q + 2] * inv) |
+                            ((uint32_t)float_to_bf16_bits(T.o[dt][4 * q + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(a.o + orow * D + 32 * dt + 8 * q + 4 * hh) = make_uint2(w0, w1);
+      }
+  } else {
+    float* po = a.part_o + (orow * NS + split) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * q + 4 * hh) =
+            make_float4(T.o[dt][4 * q], T.o[dt][4 * q + 1], T.o[dt][4 * q + 2], T.o[dt][4 * q + 3]);
+    if (hh == 0)
+      *reinterpret_cast<float2*>(a.part_ml + (orow * NS + split) * 2) = make_float2(T.m, lsum);
   }
 }
 
@@ -600,16 +950,17 @@ __global__ __launch_bounds__(256) void tree_attn_commit_kernel(const AttnCommitA
   if (tid == 0) a.cache_len[b] = L + P;
 }
 
-// Workgroup shape from the most query rows a (sequence, K/V head) can have:
-// up to 192 rows, one 16-row tile per wave on 12 waves (three per SIMD);
-// beyond, two tiles per wave on 8 waves.
+// Kernel from the most query rows a (sequence, K/V head) can have: up to 192
+// rows, 16-row tiles on 12 waves (three per SIMD); beyond, 32-row tiles on 8
+// waves (measured faster there: each LDS fragment serves twice the rows, and
+// 8 tiles of 32 spread evenly over the SIMDs).
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.B * a.Hkv * a.NS);
   const int rows = (a.Hq / a.Hkv) * a.max_nodes;
   hipError_t e = rows <= 192
-      ? launch_kernel(reinterpret_cast<const void*>(&tree_attn_kernel<D, 12, 1>), grid, 768u, s, a)
-      : launch_kernel(reinterpret_cast<const void*>(&tree_attn_kernel<D, 8, 2>), grid, 512u, s, a);
+      ? launch_kernel(reinterpret_cast<const void*>(&tree_attn_kernel<D, 12>), grid, 768u, s, a)
+      : launch_kernel(reinterpret_cast<const void*>(&tree_attn32_kernel<D, 8>), grid, 512u, s, a);
   if (e != hipSuccess || a.NS == 1) return e;
   const unsigned chunks = (unsigned)((a.max_nodes * a.Hq + 3) / 4);
   return launch_kernel(reinterpret_cast<const void*>(&tree_attn_combine_kernel<D>),

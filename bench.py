@@ -88,6 +88,11 @@ def parse():
     p.add_argument("--launch", default="layers", choices=["layers", "per-layer"],
                    help="WY leg: every layer in one launch per kernel (gdn_tree_*_layers) or one "
                         "launch per layer")
+    p.add_argument("--per-layer-steps", type=int, default=5,
+                   help="after a layer-batched WY leg, timed steps with one launch per layer "
+                        "(0 = skip)")
+    p.add_argument("--round-steps", type=int, default=10,
+                   help="timed rounds of the hybrid stack as one captured graph (0 = skip)")
     p.add_argument("--attn-steps", type=int, default=10,
                    help="timed steps of the full-attention leg (0 = skip)")
     p.add_argument("--attn-only", action="store_true",
@@ -210,6 +215,32 @@ def attention_leg(args, gt, gi, w_trees, dev):
         raise RuntimeError(f"nonzero attention tree status {np.unique(st)}")
     v_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in ev) / steps / n_layers
     c_us = 1e3 * sum(e[1].elapsed_time(e[2]) for e in ev) / steps / n_layers
+    # the KV append of all layers as one launch (one committed length shared
+    # by the layers, as in a model); not in --attn-only runs, which profile
+    # the per-layer kernels
+    # (several launches back to back between the events, each appending after
+    # the previous one, so the GPU does not wait for the host; the cache has
+    # room for reps appends of the longest path)
+    cb_us = None
+    if not args.attn_only:
+        ios = [gt.make_attn_layer_io(desc, k=x[1], v=x[2], k_cache=x[3], v_cache=x[4]) for x in keep]
+        shared = lens0[0].clone()
+        batched = gt.prepare_attn_commit_layers(desc, offsets, parents, accepted, ios, shared, status,
+                                                keep=keep)
+        longest = max(len(gi.path_to_root(p, int(a))) for p, a in
+                      zip(wl.parents_list, wl.accepted) if a >= 0)
+        reps = max(1, min(8, (cap - L0) // longest))
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for s in range(steps):
+            evb[s][0].record(stream)
+            for _ in range(reps):
+                batched()
+            evb[s][1].record(stream)
+            shared.copy_(lens0[0])
+        torch.cuda.synchronize()
+        if np.any(status.cpu().numpy() != 0):
+            raise RuntimeError("nonzero status in the layer-batched KV append")
+        cb_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in evb) / steps / reps
     path = sum(len(gi.path_to_root(p, int(a))) if a >= 0 else 0
                for p, a in zip(wl.parents_list, wl.accepted))
     vb, cb = attn_algorithmic_bytes(wl.offsets, Hq, Hkv, d, [L0] * B, path)
@@ -226,7 +257,8 @@ def attention_leg(args, gt, gi, w_trees, dev):
                    "frac_mfma_bf16": round(flops / v_us / 1e6 / MFMA_BF16_TFLOPS, 4)},
         "commit": {"avg_us": round(c_us, 3), "alg_bytes": int(cb),
                    "achieved_GBs": round(cb / c_us / 1e3, 1),
-                   "frac_hbm": round(cb / c_us / 1e3 / HBM_PEAK_GBS, 4)},
+                   "frac_hbm": round(cb / c_us / 1e3 / HBM_PEAK_GBS, 4),
+                   "all_layers_one_launch_us": round(cb_us, 3) if cb_us else None},
     }
     out = {
         "workload": c["desc"].replace("64 seqs, tree k=3 d=3 (40 nodes)",
@@ -240,6 +272,174 @@ def attention_leg(args, gt, gi, w_trees, dev):
         "kernels": kern, "split_workspace_bytes": int(nbytes),
     }
     log(f"attention: {out['ms_per_step']} ms/step, verify {v_us:.2f} us, commit {c_us:.2f} us per layer")
+    return out
+
+
+def fork_delta_leg(args, gt, gi, w, layers, offsets, parents, accepted, status, max_depth, run,
+                   dev):
+    """The fork baseline with delta-compressed checkpoints (GDN_MODE_FORK_DELTA):
+    verify depth by depth, one layer at a time, keeping per node only the
+    rank-one delta (the WY pseudo-value) and the gate; commit of all layers
+    in one launch from the deltas. The layers' verify-time states share one
+    region of a round arena (gdn_round_plan)."""
+    import torch
+    L = len(layers)
+    desc = gt.make_desc(w.B, w.H, w.dk, w.dv, w.T, w.max_nodes, gt.DTYPE_BF16,
+                        gt.MODE_FORK_DELTA, max_depth)
+    plan = gt.gdn_round_plan(gt.make_round_desc(desc, L))
+    arena = torch.empty(plan.total_bytes, dtype=torch.uint8, device=dev)
+    ws = [arena[l * plan.gdn_ws_stride:l * plan.gdn_ws_stride + plan.gdn_ws_bytes]
+          for l in range(L)]
+    outs = [torch.empty_like(ly["v"]) for ly in layers]
+    ver = [gt.prepare_verify(desc, offsets, parents, ly["q"], ly["k"], ly["v"], ly["alpha"],
+                             ly["beta"], ly["S"], o, wl, status)
+           for ly, o, wl in zip(layers, outs, ws)]
+    ios = [gt.make_layer_io(desc, k=ly["k"], S0=ly["S"], S_out=ly["S"], workspace=wl)
+           for ly, wl in zip(layers, ws)]
+    com = [gt.prepare_commit_layers(desc, offsets, parents, accepted, ios, plan.gdn_ws_bytes,
+                                    status, keep=(layers, arena))]
+    el, v_ms, c_ms = run(ver, com, args.fork_steps, 1)
+    import numpy as np
+    if np.any(status.cpu().numpy() != 0):
+        raise RuntimeError("nonzero status in the delta-fork leg")
+    internal = sum(len(set(p[1:])) for p in w.parents_list)      # nodes with children
+    out = {"ms_per_step": round(1e3 * el / args.fork_steps, 3),
+           "nodes_per_s_per_layer": round(w.T * L * args.fork_steps / el, 1),
+           "verify_us_per_layer": round(1e3 * v_ms / L, 2),
+           "commit_us_per_layer": round(1e3 * c_ms / L, 2),
+           "kept_bytes_per_layer": int(plan.gdn_ws_stride),
+           "verify_state_bytes_shared": int(plan.gdn_ws_bytes - plan.gdn_ws_stride),
+           "states_written_per_layer_bytes": int(internal * w.H * w.dv * w.dk * 4),
+           "arena_bytes": int(plan.total_bytes), "steps": args.fork_steps}
+    log(f"fork with delta checkpoints: {out}")
+    del arena, ws, outs, ver, com
+    torch.cuda.empty_cache()
+    return out
+
+
+def round_leg(args, gt, gi, w, layers, offsets, parents, dev):
+    """One whole speculative round of the 32-layer hybrid stack, in model
+    order (three GDN layers, then one full-attention layer, eight times):
+    every layer's verify, greedy acceptance from draft and target tokens
+    (drawn so that the workload's accepted paths are the ones accepted),
+    the commit of all GDN layers and the KV append of all attention layers.
+    Timed as one captured HIP graph per round (gdn_round_capture) and as the
+    same calls issued one by one from Python."""
+    import numpy as np
+    import torch
+    c = gi.ATTN_CONFIGS["fa_c4"]
+    n_attn = 8
+    n_gdn = len(layers)
+    Hq, Hkv, d, cap, L0 = c["Hq"], c["Hkv"], c["d"], c["cap"], c["lens"][1]
+    B, T = w.B, w.T
+    kinds = ([0, 0, 0, 1] * n_attn)[:n_gdn + n_attn] if n_gdn == 3 * n_attn else \
+        [0] * n_gdn + [1] * n_attn
+    gdesc = gt.make_desc(B, w.H, w.dk, w.dv, T, w.max_nodes, gt.DTYPE_BF16, gt.MODE_WY)
+    adesc = gt.make_attn_desc(B, Hq, Hkv, d, T, w.max_nodes, cap, cap)
+    rdesc = gt.make_round_desc(gdesc, n_gdn, adesc, n_attn)
+    layout = gt.gdn_round_plan(rdesc)
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    randn = lambda *shape: torch.randn(*shape, generator=g, device=dev).to(torch.bfloat16)
+    attn = []
+    for _ in range(n_attn):
+        attn.append(dict(q=randn(T, Hq, d), k=randn(T, Hkv, d), v=randn(T, Hkv, d),
+                         kc=randn(B, Hkv, cap, d), vc=randn(B, Hkv, cap, d),
+                         o=torch.empty(T, Hq, d, dtype=torch.bfloat16, device=dev)))
+    outs = [torch.empty_like(ly["v"]) for ly in layers]
+    rng = np.random.default_rng(7)
+    d_np, t_np = gi.draft_target_tokens(rng, w.parents_list, w.accepted)
+    draft = torch.from_numpy(d_np).to(dev)
+    target = torch.from_numpy(t_np).to(dev)
+    lens0 = torch.full((B,), L0, dtype=torch.int32, device=dev)
+    cache_len = lens0.clone()
+    acc, alen, nxt, status = (torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(4))
+    arena = torch.empty(max(1, layout.total_bytes), dtype=torch.uint8, device=dev)
+    gdn_io = [gt.make_layer_io(gdesc, q=ly["q"], k=ly["k"], v=ly["v"], alpha=ly["alpha"],
+                               beta=ly["beta"], S0=ly["S"], o=o, S_out=ly["S"])
+              for ly, o in zip(layers, outs)]
+    attn_io = [gt.make_attn_layer_io(adesc, q=a["q"], k=a["k"], v=a["v"], k_cache=a["kc"],
+                                     v_cache=a["vc"], o=a["o"]) for a in attn]
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    graph = gt.RoundGraph(rdesc, offsets, parents, gdn_io, attn_io, arena, draft, target, acc,
+                          alen, nxt, status, cache_len=cache_len, layer_kinds=kinds,
+                          stream=stream, keep=(layers, attn, outs))
+    # the same round as individual calls (per-layer workspaces carved from the arena)
+    ws = lambda l: arena[l * layout.gdn_ws_stride:l * layout.gdn_ws_stride + layout.gdn_ws_bytes]
+    calls, gi_, ai_ = [], 0, 0
+    for kind in kinds:
+        if kind == 0:
+            ly = layers[gi_]
+            calls.append(gt.prepare_verify(gdesc, offsets, parents, ly["q"], ly["k"], ly["v"],
+                                           ly["alpha"], ly["beta"], ly["S"], outs[gi_], ws(gi_),
+                                           status, stream=stream))
+            gi_ += 1
+        else:
+            a = attn[ai_]
+            calls.append(gt.prepare_attn_verify(adesc, offsets, parents, a["q"], a["k"], a["v"],
+                                                a["kc"], a["vc"], cache_len, a["o"], None, status,
+                                                stream=stream))
+            ai_ += 1
+    e_gdn = [gt.make_layer_io(gdesc, k=ly["k"], S0=ly["S"], S_out=ly["S"], workspace=ws(l))
+             for l, ly in enumerate(layers)]
+
+    def eager():
+        for f in calls:
+            f()
+        gt.gdn_tree_accept_greedy(gdesc, offsets, parents, draft, target, acc, alen, nxt, status,
+                                  stream=stream)
+        gt.gdn_tree_commit_layers(gdesc, offsets, parents, acc, e_gdn, layout.gdn_ws_bytes,
+                                  status, stream=stream)
+        gt.gdn_tree_attn_commit_layers(adesc, offsets, parents, acc, attn_io, cache_len, status,
+                                       stream=stream)
+
+    def timed(fn, steps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            ev[s][0].record(stream)
+            fn()
+            ev[s][1].record(stream)
+            with torch.cuda.stream(stream):
+                cache_len.copy_(lens0)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if np.any(status.cpu().numpy() != 0):
+            raise RuntimeError(f"nonzero status in the round: {np.unique(status.cpu().numpy())}")
+        times = sorted(e[0].elapsed_time(e[1]) for e in ev)
+        return wall / steps * 1e3, times[len(times) // 2], times
+
+    launch = lambda: graph.launch(stream)
+    for _ in range(2):
+        launch()
+        eager()
+        with torch.cuda.stream(stream):
+            cache_len.copy_(lens0)
+    steps = args.round_steps
+    g_wall, g_med, g_times = timed(launch, steps)
+    e_wall, e_med, _ = timed(eager, steps)
+    expect = np.array([len(gi.path_to_root(p, int(a))) for p, a in
+                       zip(w.parents_list, w.accepted)], np.int32)
+    got_len = alen.cpu().numpy()
+    if not np.array_equal(got_len, expect):
+        raise RuntimeError("round acceptance differs from the drawn accepted paths")
+    graph.close()
+    out = {
+        "layers": {"gdn": n_gdn, "attention": n_attn,
+                   "order": "3 GDN, 1 attention, x8" if kinds[:4] == [0, 0, 0, 1] else "GDN, attention"},
+        "steps": steps, "graph_ms_per_round_median": round(g_med, 4),
+        "graph_ms_per_round_p10_p90": [round(g_times[steps // 10], 4),
+                                       round(g_times[(9 * steps) // 10], 4)],
+        "eager_ms_per_round_median": round(e_med, 4),
+        "graph_wall_ms_per_round": round(g_wall, 4), "eager_wall_ms_per_round": round(e_wall, 4),
+        "kernel_launches_per_round": n_gdn + n_attn + 3,
+        "nodes_per_s_all_layers": round(T / (g_med * 1e-3), 1),
+        "mean_accept_len": round(float(got_len.mean()), 3),
+        "arena_bytes": int(layout.total_bytes),
+    }
+    log(f"round: {out}")
     return out
 
 
@@ -378,11 +578,37 @@ def main():
             "layers_per_launch": lpl}
     log(f"{args.mode}: {ms_step:.3f} ms/step, verify {v_us:.2f} us, commit {c_us:.2f} us per layer")
 
+    # ------------------------------------------ one launch per layer (secondary)
+    # In a model forward layer l+1's q, k, v come from layer l's output, so
+    # verify goes out one layer at a time; the commits of all layers follow
+    # acceptance and batch freely. Both schedules are reported.
+    per_layer = None
+    if batched and args.per_layer_steps > 0:
+        for ly in layers:
+            ly.pop("o_wy"), ly.pop("ws_wy")
+        ver = com = None
+        _, _, pver, pcom = make_calls("wy", False)
+        p_el, p_v, p_c = run(pver, pcom, args.per_layer_steps, 2)
+        pv_us, pc_us = 1e3 * p_v / L, 1e3 * p_c / L
+        per_layer = {
+            "verify_us_per_layer": round(pv_us, 3), "commit_us_per_layer": round(pc_us, 3),
+            "verify_frac_hbm": round(vb / pv_us / 1e3 / HBM_PEAK_GBS, 4),
+            "commit_frac_hbm": round(cb / pc_us / 1e3 / HBM_PEAK_GBS, 4),
+            "nodes_per_s_per_layer": round(w.T * L * args.per_layer_steps / p_el, 1),
+            # verify per layer (as a forward issues it), commit of all layers batched
+            "model_order_nodes_per_s_per_layer": round(w.T / ((pv_us + c_us) * 1e-6), 1),
+            "steps": args.per_layer_steps}
+        log(f"one launch per layer: {per_layer}")
+        for ly in layers:
+            ly.pop("o_wy"), ly.pop("ws_wy")
+        pver = pcom = None
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------- fork baseline
     fork = None
     if args.mode == "wy" and args.fork_steps > 0:
         for ly in layers:
-            ly.pop("o_wy"), ly.pop("ws_wy")
+            ly.pop("o_wy", None), ly.pop("ws_wy", None)
         ver = com = None
         torch.cuda.empty_cache()
         fdesc, fbytes, fver, fcom = make_calls("fork")
@@ -397,6 +623,8 @@ def main():
             ly.pop("o_fork"), ly.pop("ws_fork")
         fver = fcom = None
         torch.cuda.empty_cache()
+        fork["delta_checkpoints"] = fork_delta_leg(args, gt, gi, w, layers, offsets, parents,
+                                                   accepted, status, max_depth, run, dev)
 
     if args.pmc_calibration:
         pmc_calibration(dev)
@@ -432,13 +660,17 @@ def main():
         log(f"cpu oracle: {cpu}")
 
     fa = None
+    for ly in layers:
+        for key in [k for k in ly if k.startswith("o_") or k.startswith("ws_")]:
+            ly.pop(key)
+    ver = com = None
+    torch.cuda.empty_cache()
     if args.attn_steps > 0:
-        for ly in layers:
-            for key in [k for k in ly if k.startswith("o_") or k.startswith("ws_")]:
-                ly.pop(key)
-        ver = com = None
-        torch.cuda.empty_cache()
         fa = attention_leg(args, gt, gi, w, dev)
+        torch.cuda.empty_cache()
+    rnd = None
+    if args.round_steps > 0 and args.mode == "wy" and w.io == "bf16":
+        rnd = round_leg(args, gt, gi, w, layers, offsets, parents, dev)
 
     out = {
         "metric": METRIC, "value": round(nodes_per_s, 1), "unit": "nodes/s/layer", "n_gpus": 1,
@@ -451,7 +683,8 @@ def main():
                    "launch": "all layers per launch" if batched else "one launch per layer",
                    "parallelism": "single-gpu"},
         "roofline": roof, "kernels": kern, "cpu_baseline": cpu, "fork_baseline": fork,
-        "spec_state_per_request": spec, "fa_layers": fa,
+        "per_layer_launches": per_layer, "spec_state_per_request": spec, "fa_layers": fa,
+        "round": rnd,
     }
     print(json.dumps(out), flush=True)
 

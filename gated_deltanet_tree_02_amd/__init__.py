@@ -2,7 +2,8 @@
 DeltaNet layers and of the full-attention layers beside them.
 
 The functions here carry the names of the C entry points declared in
-include/gdn_tree.h and include/gdn_tree_attn.h and only marshal arguments:
+include/gdn_tree.h, include/gdn_tree_attn.h and include/gdn_round.h and only
+marshal arguments:
 they check torch tensors (device, dtype, shape, contiguity), pass their device
 pointers and the current HIP stream to the library, and raise GdnError for a nonzero gdn_status. Every
 step of the computation runs in the library's HIP kernels; there is no
@@ -18,18 +19,23 @@ from typing import Optional
 __all__ = [
     "GdnError", "GdnTreeDesc", "load_library", "make_desc", "gdn_tree_workspace_bytes",
     "gdn_tree_build", "gdn_tree_verify", "gdn_tree_commit", "gdn_tree_status_string",
-    "DTYPE_F32", "DTYPE_BF16", "MODE_WY", "MODE_FORK", "MAX_NODES", "TREE_STATUS",
+    "DTYPE_F32", "DTYPE_BF16", "MODE_WY", "MODE_FORK", "MODE_FORK_DELTA", "MAX_NODES",
+    "TREE_STATUS",
     "PreparedCall", "prepare_verify", "prepare_commit",
     "GdnAttnDesc", "make_attn_desc", "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
     "gdn_tree_attn_commit", "prepare_attn_verify", "prepare_attn_commit",
     "GdnLayerIO", "make_layer_io", "gdn_tree_verify_layers", "gdn_tree_commit_layers",
     "prepare_verify_layers", "prepare_commit_layers",
+    "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
+    "prepare_attn_commit_layers",
+    "gdn_tree_accept_greedy", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
+    "gdn_round_plan", "gdn_round_tree_for_budget", "RoundGraph",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdntree.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
-MODE_WY, MODE_FORK = 0, 1
+MODE_WY, MODE_FORK, MODE_FORK_DELTA = 0, 1, 2
 MAX_NODES = 64
 TREE_STATUS = {0: "ok", 1: "bad root", 2: "bad parent", 3: "bad size", 4: "bad accepted",
                5: "too deep", 6: "cache full"}
@@ -62,6 +68,33 @@ class GdnAttnDesc(ctypes.Structure):
 class GdnLayerIO(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("q", "k", "v", "alpha", "beta", "S0", "o", "S_out", "workspace")]
+
+
+class GdnAttnLayerIO(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in ("q", "k", "v", "k_cache", "v_cache", "o")]
+
+
+class GdnRoundDesc(ctypes.Structure):
+    _fields_ = [("gdn", GdnTreeDesc), ("n_gdn_layers", ctypes.c_int32),
+                ("attn", GdnAttnDesc), ("n_attn_layers", ctypes.c_int32)]
+
+
+class GdnRoundLayout(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_size_t) for name in
+                ("total_bytes", "gdn_ws_bytes", "gdn_ws_stride", "attn_ws_bytes",
+                 "attn_ws_offset", "attn_ws_stride")]
+
+
+class GdnRoundIO(ctypes.Structure):
+    _fields_ = [
+        ("offsets", ctypes.c_void_p), ("parents", ctypes.c_void_p),
+        ("gdn_layers", ctypes.POINTER(GdnLayerIO)), ("attn_layers", ctypes.POINTER(GdnAttnLayerIO)),
+        ("layer_kinds", ctypes.POINTER(ctypes.c_int32)), ("cache_len", ctypes.c_void_p),
+        ("attn_scale", ctypes.c_float), ("arena", ctypes.c_void_p), ("arena_bytes", ctypes.c_size_t),
+        ("draft_tokens", ctypes.c_void_p), ("target_tokens", ctypes.c_void_p),
+        ("accepted", ctypes.c_void_p), ("accept_len", ctypes.c_void_p),
+        ("next_token", ctypes.c_void_p), ("tree_status", ctypes.c_void_p),
+    ]
 
 
 _lock = threading.Lock()
@@ -101,6 +134,25 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_verify_layers.restype = I
             lib.gdn_tree_commit_layers.argtypes = [D, ctypes.c_int32, P, P, P, LY, S, P, P]
             lib.gdn_tree_commit_layers.restype = I
+            AL = ctypes.POINTER(GdnAttnLayerIO)
+            lib.gdn_tree_attn_commit_layers.argtypes = [A, ctypes.c_int32, P, P, P, AL, P, P, P]
+            lib.gdn_tree_attn_commit_layers.restype = I
+            lib.gdn_tree_accept_greedy.argtypes = [D, P, P, P, P, P, P, P, P, P]
+            lib.gdn_tree_accept_greedy.restype = I
+            R = ctypes.POINTER(GdnRoundDesc)
+            lib.gdn_round_plan.argtypes = [R, ctypes.POINTER(GdnRoundLayout)]
+            lib.gdn_round_plan.restype = I
+            i32p = ctypes.POINTER(ctypes.c_int32)
+            lib.gdn_round_tree_for_budget.argtypes = [R, S, ctypes.c_int32, i32p, i32p, i32p,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn_round_tree_for_budget.restype = I
+            lib.gdn_round_capture.argtypes = [R, ctypes.POINTER(GdnRoundIO), P,
+                                              ctypes.POINTER(ctypes.c_void_p)]
+            lib.gdn_round_capture.restype = I
+            lib.gdn_round_launch.argtypes = [P, P]
+            lib.gdn_round_launch.restype = I
+            lib.gdn_round_destroy.argtypes = [P]
+            lib.gdn_round_destroy.restype = None
             lib.gdn_tree_status_string.argtypes = [I]
             lib.gdn_tree_status_string.restype = ctypes.c_char_p
             _lib = lib
@@ -462,3 +514,180 @@ def prepare_commit_layers(desc, offsets, parents, accepted, layers, workspace_by
             _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
     return PreparedCall("gdn_tree_commit_layers", desc, args, _stream(stream, dev),
                         (offsets, parents, accepted, tree_status, arr, tuple(keep)))
+
+
+# ------------------------------------------------------------------ attention layers, batched
+
+
+def make_attn_layer_io(desc, q=None, k=None, v=None, k_cache=None, v_cache=None,
+                       o=None) -> GdnAttnLayerIO:
+    """One attention layer's buffers for gdn_tree_attn_commit_layers and a
+    captured round (shapes checked against the descriptor)."""
+    torch = _torch()
+    B, Hq, Hkv, T, d = (desc.num_seqs, desc.num_q_heads, desc.num_kv_heads, desc.total_nodes,
+                        desc.head_dim)
+    cap = desc.cache_capacity
+    bf = torch.bfloat16
+    f = lambda t, name, shape: _ptr(t, name, bf, shape, allow_none=True)
+    return GdnAttnLayerIO(f(q, "q", (T, Hq, d)), f(k, "k", (T, Hkv, d)), f(v, "v", (T, Hkv, d)),
+                          f(k_cache, "k_cache", (B, Hkv, cap, d)),
+                          f(v_cache, "v_cache", (B, Hkv, cap, d)), f(o, "o", (T, Hq, d)))
+
+
+def _attn_layers_array(layers):
+    arr = (GdnAttnLayerIO * max(1, len(layers)))()
+    for i, ly in enumerate(layers):
+        arr[i] = ly
+    return arr
+
+
+def gdn_tree_attn_commit_layers(desc, offsets, parents, accepted, layers, cache_len, tree_status,
+                                stream=None):
+    """Append the accepted path's K/V rows to every layer's caches (layers:
+    GdnAttnLayerIO list sharing cache_len), then advance cache_len once."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    arr = _attn_layers_array(layers)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_attn_commit_layers(
+            ctypes.byref(desc), len(layers), _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+            _ptr(parents, "parents", torch.int32, (T,), dev),
+            _ptr(accepted, "accepted", torch.int32, (B,), dev), arr,
+            _ptr(cache_len, "cache_len", torch.int32, (B,), dev),
+            _ptr(tree_status, "tree_status", torch.int32, (B,), dev), _stream(stream, dev)),
+            "gdn_tree_attn_commit_layers")
+
+
+def prepare_attn_commit_layers(desc, offsets, parents, accepted, layers, cache_len, tree_status,
+                               keep=(), stream=None) -> PreparedCall:
+    """Marshalled gdn_tree_attn_commit_layers; `keep` holds the tensors behind `layers`."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    arr = _attn_layers_array(layers)
+    args = [ctypes.c_int32(len(layers)), _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+            _ptr(parents, "parents", torch.int32, (T,), dev),
+            _ptr(accepted, "accepted", torch.int32, (B,), dev), arr,
+            _ptr(cache_len, "cache_len", torch.int32, (B,), dev),
+            _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
+    return PreparedCall("gdn_tree_attn_commit_layers", desc, args, _stream(stream, dev),
+                        (offsets, parents, accepted, cache_len, tree_status, arr, tuple(keep)))
+
+
+# ------------------------------------------------------------------ acceptance and rounds
+
+
+def gdn_tree_accept_greedy(desc, offsets, parents, draft_tokens, target_tokens, accepted,
+                           accept_len, next_token, tree_status, stream=None):
+    """Greedy acceptance of every tree: accepted node, path length and the
+    target's next token per sequence (int32 tensors)."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    i32 = torch.int32
+    args = [_ptr(offsets, "offsets", i32, (B + 1,), dev), _ptr(parents, "parents", i32, (T,), dev),
+            _ptr(draft_tokens, "draft_tokens", i32, (T,), dev),
+            _ptr(target_tokens, "target_tokens", i32, (T,), dev),
+            _ptr(accepted, "accepted", i32, (B,), dev), _ptr(accept_len, "accept_len", i32, (B,), dev),
+            _ptr(next_token, "next_token", i32, (B,), dev),
+            _ptr(tree_status, "tree_status", i32, (B,), dev)]
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_accept_greedy(ctypes.byref(desc), *args,
+                                                     _stream(stream, dev)),
+               "gdn_tree_accept_greedy")
+
+
+def make_round_desc(gdn_desc=None, n_gdn_layers=0, attn_desc=None, n_attn_layers=0) -> GdnRoundDesc:
+    return GdnRoundDesc(gdn_desc if gdn_desc is not None else GdnTreeDesc(), int(n_gdn_layers),
+                        attn_desc if attn_desc is not None else GdnAttnDesc(), int(n_attn_layers))
+
+
+def gdn_round_plan(rdesc) -> GdnRoundLayout:
+    out = GdnRoundLayout()
+    _check(load_library().gdn_round_plan(ctypes.byref(rdesc), ctypes.byref(out)), "gdn_round_plan")
+    return out
+
+
+def gdn_round_tree_for_budget(rdesc, budget_bytes: int, max_depth: int):
+    """(branching, depth, nodes, state_bytes) of the largest complete tree
+    whose speculative state fits the budget."""
+    k, d, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    nb = ctypes.c_size_t()
+    _check(load_library().gdn_round_tree_for_budget(
+        ctypes.byref(rdesc), ctypes.c_size_t(int(budget_bytes)), int(max_depth), ctypes.byref(k),
+        ctypes.byref(d), ctypes.byref(n), ctypes.byref(nb)), "gdn_round_tree_for_budget")
+    return k.value, d.value, n.value, nb.value
+
+
+class RoundGraph:
+    """One speculative round (every layer's verify in model order, greedy
+    acceptance, every layer's commit) recorded once with gdn_round_capture on
+    `stream` (a torch.cuda.Stream, not the null stream) and replayed with
+    launch(). Tensors are checked here and kept alive by the object; the graph
+    reads their contents at each launch."""
+
+    def __init__(self, rdesc, offsets, parents, gdn_layers, attn_layers, arena, draft_tokens,
+                 target_tokens, accepted, accept_len, next_token, tree_status, cache_len=None,
+                 layer_kinds=None, attn_scale=None, stream=None, keep=()):
+        torch = _torch()
+        g, a = rdesc.gdn, rdesc.attn
+        B = g.num_seqs if rdesc.n_gdn_layers > 0 else a.num_seqs
+        T = g.total_nodes if rdesc.n_gdn_layers > 0 else a.total_nodes
+        if len(gdn_layers) != rdesc.n_gdn_layers or len(attn_layers) != rdesc.n_attn_layers:
+            raise ValueError("layer lists do not match the round descriptor")
+        dev = offsets.device
+        i32 = torch.int32
+        self._rdesc = GdnRoundDesc.from_buffer_copy(rdesc)
+        self._gdn = _layers_array(gdn_layers)
+        self._attn = _attn_layers_array(attn_layers)
+        kinds = None
+        if layer_kinds is not None:
+            kinds = (ctypes.c_int32 * max(1, len(layer_kinds)))(*[int(x) for x in layer_kinds])
+        self._kinds = kinds
+        scale = (a.head_dim ** -0.5 if a.head_dim > 0 else 1.0) if attn_scale is None else attn_scale
+        io = GdnRoundIO()
+        io.offsets = _ptr(offsets, "offsets", i32, (B + 1,), dev)
+        io.parents = _ptr(parents, "parents", i32, (T,), dev)
+        io.gdn_layers = ctypes.cast(self._gdn, ctypes.POINTER(GdnLayerIO))
+        io.attn_layers = ctypes.cast(self._attn, ctypes.POINTER(GdnAttnLayerIO))
+        io.layer_kinds = ctypes.cast(kinds, ctypes.POINTER(ctypes.c_int32)) if kinds else None
+        io.cache_len = _ptr(cache_len, "cache_len", i32, (B,), dev, allow_none=True)
+        io.attn_scale = float(scale)
+        io.arena = _ptr(arena, "arena", torch.uint8, None, dev, allow_none=True)
+        io.arena_bytes = 0 if arena is None else arena.numel()
+        io.draft_tokens = _ptr(draft_tokens, "draft_tokens", i32, (T,), dev)
+        io.target_tokens = _ptr(target_tokens, "target_tokens", i32, (T,), dev)
+        io.accepted = _ptr(accepted, "accepted", i32, (B,), dev)
+        io.accept_len = _ptr(accept_len, "accept_len", i32, (B,), dev)
+        io.next_token = _ptr(next_token, "next_token", i32, (B,), dev)
+        io.tree_status = _ptr(tree_status, "tree_status", i32, (B,), dev)
+        self._io = io
+        self._keep = (offsets, parents, arena, draft_tokens, target_tokens, accepted, accept_len,
+                      next_token, tree_status, cache_len, tuple(keep))
+        self._lib = load_library()
+        self._handle = ctypes.c_void_p()
+        s = torch.cuda.current_stream(dev) if stream is None else stream
+        with torch.cuda.device(dev):
+            _check(self._lib.gdn_round_capture(ctypes.byref(self._rdesc), ctypes.byref(io),
+                                               ctypes.c_void_p(s.cuda_stream),
+                                               ctypes.byref(self._handle)),
+                   "gdn_round_capture")
+        self._dev = dev
+
+    def launch(self, stream=None):
+        if not self._handle:
+            raise RuntimeError("round graph already destroyed")
+        _check(self._lib.gdn_round_launch(self._handle, _stream(stream, self._dev)),
+               "gdn_round_launch")
+
+    def close(self):
+        if self._handle:
+            self._lib.gdn_round_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build", "gdntree")
 LIB = os.path.join(PKG, "libgdntree.so")
 
 SOURCES = ["gdn_tree_api.cpp", "tree_build.hip", "wy_verify.hip", "wy_commit.hip", "fork.hip",
-           "tree_attn_api.cpp", "tree_attn.hip"]
+           "tree_attn_api.cpp", "tree_attn.hip", "accept.hip", "round_api.cpp"]
 ARCH = "gfx950"
 
 

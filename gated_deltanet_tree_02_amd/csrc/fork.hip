@@ -9,6 +9,15 @@
 // and stores C_t as the node's checkpoint. Rows of the state evolve
 // independently under the gated delta rule, so splitting rows across
 // workgroups is exact. Commit copies the accepted node's checkpoint.
+//
+// With delta-compressed checkpoints (DELTA; fork page, section 8, checkpoint
+// compression: keep only what a child adds to its parent's state), the kept
+// part of node t is what C_t adds to alpha_t C_p: the rank-one term
+// u_t k_t^T, u_t = beta_t (v_t - alpha_t w), and the gate. Verify stores u_t
+// and the base-2 gate prefix g2_t in the WY workspace layout, and a node's full
+// state only while its children still need it (nodes without children are
+// never written); commit rebuilds the accepted state from S0 and the deltas
+// of its path, which is the WY commit.
 #include "device_common.h"
 #include "launch.h"
 
@@ -23,7 +32,7 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-template <class IO, int DK, int DV>
+template <class IO, int DK, int DV, bool DELTA>
 __global__ __launch_bounds__(256) void fork_level_kernel(const ForkArgs a) {
   constexpr int TPR = DK / 4;        // threads per state row (one float4 each)
   constexpr int RPP = 256 / TPR;     // rows per pass
@@ -35,6 +44,8 @@ __global__ __launch_bounds__(256) void fork_level_kernel(const ForkArgs a) {
   __shared__ int sPar[64];
   __shared__ int sInfo[3];
   __shared__ uint64_t sLevel;
+  __shared__ uint64_t sHasChild;   // DELTA: nodes whose state a child reads
+  __shared__ float sG2[64];        // DELTA: base-2 gate prefixes
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -55,6 +66,22 @@ __global__ __launch_bounds__(256) void fork_level_kernel(const ForkArgs a) {
     }
     const uint64_t lvl = __ballot(st == GDN_TREE_OK && lane < tl.n && tl.depth == a.level);
     sPar[lane] = tl.parent;
+    if constexpr (DELTA) {
+      // gate prefix along the path (the same pointer-jumping sum the WY
+      // verify uses, so both write identical g2), and which nodes have children
+      const int n0 = st == GDN_TREE_BAD_SIZE ? 0 : tl.n;
+      const float x = lane < n0 ? gate_log2(a.alpha[(size_t)(tl.lo + lane) * a.H + h]) : 0.f;
+      uint64_t anc;
+      float g2;
+      path_scan(lane < n0 ? tl.parent : -1, lane, n0, x, anc, g2);
+      sG2[lane] = g2;
+      uint64_t kids = 0ull;
+      for (int j = 1; j < n0; ++j) {
+        const int pj = __shfl(tl.parent, j, kWave);
+        if (pj >= 0 && pj < 64) kids |= 1ull << pj;
+      }
+      if (lane == 0) sHasChild = kids;
+    }
     if (lane == 0) {
       sInfo[0] = st;
       sInfo[1] = tl.lo;
@@ -75,8 +102,15 @@ __global__ __launch_bounds__(256) void fork_level_kernel(const ForkArgs a) {
     if (st != GDN_TREE_BAD_SIZE && a.level == 0 && c == 0) {
       for (int t = 0; t < n; ++t)
 #pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps)
-          io::store1(o + ((size_t)(lo + t) * H + h) * DV + ch * CR + ps * RPP + rin, 0.f);
+        for (int ps = 0; ps < NPASS; ++ps) {
+          const size_t r = ((size_t)(lo + t) * H + h) * DV + ch * CR + ps * RPP + rin;
+          io::store1(o + r, 0.f);
+          if constexpr (DELTA) a.U[r] = 0.f;
+        }
+      if constexpr (DELTA) {
+        if (ch == 0 && rin == 0)
+          for (int t = 0; t < n; ++t) a.g2[(size_t)(lo + t) * H + h] = 0.f;
+      }
     }
     return;
   }
@@ -93,6 +127,11 @@ __global__ __launch_bounds__(256) void fork_level_kernel(const ForkArgs a) {
     const float* __restrict__ src =
         p < 0 ? a.S0 + (size_t)bh * DV * DK : a.ckpt + ((size_t)(lo + p) * H + h) * DV * DK;
     float* __restrict__ dst = a.ckpt + gt * DV * DK;
+    // DELTA: a leaf's state is never read again and is not stored
+    const bool keep = !DELTA || ((sHasChild >> t) & 1ull);
+    if constexpr (DELTA) {
+      if (ch == 0 && tid == 0) a.g2[gt] = sG2[t];
+    }
     float4 C[NPASS];
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
@@ -113,9 +152,12 @@ __global__ __launch_bounds__(256) void fork_level_kernel(const ForkArgs a) {
       Ct.y = al * C[ps].y + coef * kk.y;
       Ct.z = al * C[ps].z + coef * kk.z;
       Ct.w = al * C[ps].w + coef * kk.w;
-      *reinterpret_cast<float4*>(dst + (size_t)row * DK + c) = Ct;
+      if (keep) *reinterpret_cast<float4*>(dst + (size_t)row * DK + c) = Ct;
       const float ov = row_sum<TPR>(Ct.x * qq.x + Ct.y * qq.y + Ct.z * qq.z + Ct.w * qq.w);
       if (c == 0) io::store1(o + gt * DV + row, ov);
+      if constexpr (DELTA) {
+        if (c == 0) a.U[gt * DV + row] = coef;
+      }
     }
   }
 }
@@ -176,8 +218,9 @@ __global__ __launch_bounds__(256) void fork_commit_kernel(const ForkCommitArgs a
 
 template <class IO, int D>
 hipError_t launch_level(const ForkArgs& a, hipStream_t s) {
-  return launch_kernel(reinterpret_cast<const void*>(&fork_level_kernel<IO, D, D>),
-                       (unsigned)(a.B * a.H * (D / 32)), 256u, s, a);
+  const void* kern = a.U ? reinterpret_cast<const void*>(&fork_level_kernel<IO, D, D, true>)
+                         : reinterpret_cast<const void*>(&fork_level_kernel<IO, D, D, false>);
+  return launch_kernel(kern, (unsigned)(a.B * a.H * (D / 32)), 256u, s, a);
 }
 
 template <class IO>

@@ -9,7 +9,28 @@
 #include <cstdint>
 
 #include "gdn_tree.h"
+#include "api_internal.h"
 #include "launch.h"
+
+namespace gdn {
+
+gdn_status check_tree_desc(const gdn_tree_desc* d) {
+  if (d == nullptr) return GDN_ERR_NULL_PTR;
+  if (d->num_seqs < 0 || d->num_heads < 1 || d->total_nodes < 0 || d->max_nodes < 1 ||
+      d->max_nodes > GDN_TREE_MAX_NODES)
+    return GDN_ERR_BAD_SHAPE;
+  if (d->dk != d->dv || (d->dk != 32 && d->dk != 64 && d->dk != 128)) return GDN_ERR_UNSUPPORTED;
+  if (d->io_dtype != GDN_DTYPE_F32 && d->io_dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+  if (d->mode != GDN_MODE_WY && d->mode != GDN_MODE_FORK && d->mode != GDN_MODE_FORK_DELTA)
+    return GDN_ERR_UNSUPPORTED;
+  // grids are B*H*(chunks <= 4) workgroups; node indices (T*H) must fit int
+  const long long bh = (long long)d->num_seqs * d->num_heads;
+  if (bh * 4 > INT_MAX || (long long)d->total_nodes * d->num_heads > INT_MAX)
+    return GDN_ERR_BAD_SHAPE;
+  return GDN_OK;
+}
+
+}  // namespace gdn
 
 namespace {
 
@@ -17,20 +38,7 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-gdn_status check_desc(const gdn_tree_desc* d) {
-  if (d == nullptr) return GDN_ERR_NULL_PTR;
-  if (d->num_seqs < 0 || d->num_heads < 1 || d->total_nodes < 0 || d->max_nodes < 1 ||
-      d->max_nodes > GDN_TREE_MAX_NODES)
-    return GDN_ERR_BAD_SHAPE;
-  if (d->dk != d->dv || (d->dk != 32 && d->dk != 64 && d->dk != 128)) return GDN_ERR_UNSUPPORTED;
-  if (d->io_dtype != GDN_DTYPE_F32 && d->io_dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
-  if (d->mode != GDN_MODE_WY && d->mode != GDN_MODE_FORK) return GDN_ERR_UNSUPPORTED;
-  // grids are B*H*(chunks <= 4) workgroups; node indices (T*H) must fit int
-  const long long bh = (long long)d->num_seqs * d->num_heads;
-  if (bh * 4 > INT_MAX || (long long)d->total_nodes * d->num_heads > INT_MAX)
-    return GDN_ERR_BAD_SHAPE;
-  return GDN_OK;
-}
+gdn_status check_desc(const gdn_tree_desc* d) { return gdn::check_tree_desc(d); }
 
 int levels(const gdn_tree_desc* d) {
   const int md = d->max_depth > 0 ? d->max_depth : d->max_nodes - 1;
@@ -41,13 +49,29 @@ size_t wy_u_bytes(const gdn_tree_desc* d) {
   return round_up((size_t)d->total_nodes * d->num_heads * d->dv * sizeof(float));
 }
 
-size_t workspace_bytes(const gdn_tree_desc* d) {
+// U and g2: the part of the workspace that commit reads (WY and FORK_DELTA)
+size_t wy_bytes(const gdn_tree_desc* d) {
   const size_t th = (size_t)d->total_nodes * d->num_heads;
-  if (d->mode == GDN_MODE_FORK) return round_up(th * d->dv * d->dk * sizeof(float));
   return wy_u_bytes(d) + round_up(th * sizeof(float));
 }
 
+size_t state_bytes(const gdn_tree_desc* d) {
+  return round_up((size_t)d->total_nodes * d->num_heads * d->dv * d->dk * sizeof(float));
+}
+
+size_t workspace_bytes(const gdn_tree_desc* d) {
+  if (d->mode == GDN_MODE_FORK) return state_bytes(d);
+  if (d->mode == GDN_MODE_FORK_DELTA) return wy_bytes(d) + state_bytes(d);
+  return wy_bytes(d);
+}
+
 gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+// FORK_DELTA verify runs a fixed number of levels; its commit rejects deeper
+// trees as FORK's does. WY has no depth limit.
+int commit_depth_limit(const gdn_tree_desc* d) {
+  return d->mode == GDN_MODE_FORK_DELTA ? levels(d) - 1 : -1;
+}
 
 }  // namespace
 
@@ -95,10 +119,15 @@ gdn_status gdn_tree_verify(const gdn_tree_desc* desc, const int32_t* offsets,
     return launched(gdn::launch_wy_verify(desc->io_dtype, d, mt, a, s));
   }
   const int L = levels(desc);
+  const bool delta = desc->mode == GDN_MODE_FORK_DELTA;
+  char* ws = static_cast<char*>(workspace);
+  float* ckpt = reinterpret_cast<float*>(delta ? ws + wy_bytes(desc) : ws);
+  float* U = delta ? reinterpret_cast<float*>(ws) : nullptr;
+  float* g2 = delta ? reinterpret_cast<float*>(ws + wy_u_bytes(desc)) : nullptr;
   for (int level = 0; level < L; ++level) {
     gdn::ForkArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
                     L - 1, level, offsets, parents, q, k, v, alpha, beta, S0, o,
-                    static_cast<float*>(workspace), tree_status};
+                    ckpt, tree_status, U, g2};
     st = launched(gdn::launch_fork_level(desc->io_dtype, d, a, s));
     if (st != GDN_OK) return st;
   }
@@ -114,16 +143,18 @@ gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
   if (desc->num_seqs == 0) return GDN_OK;
   if (!offsets || !accepted || !S0 || !S_out || !tree_status) return GDN_ERR_NULL_PTR;
   if (desc->total_nodes > 0 && (!parents || !workspace)) return GDN_ERR_NULL_PTR;
-  if (desc->total_nodes > 0 && desc->mode == GDN_MODE_WY && !k) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && desc->mode != GDN_MODE_FORK && !k) return GDN_ERR_NULL_PTR;
   if (ws_bytes < workspace_bytes(desc)) return GDN_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int d = desc->dk;
-  if (desc->mode == GDN_MODE_WY) {
+  if (desc->mode != GDN_MODE_FORK) {
+    // WY, and FORK_DELTA, whose deltas are the same pseudo-values
     const float* U = static_cast<const float*>(workspace);
     const float* g2 =
         reinterpret_cast<const float*>(static_cast<const char*>(workspace) + wy_u_bytes(desc));
     gdn::CommitArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
-                      offsets, parents, accepted, k, S0, S_out, U, g2, tree_status};
+                      offsets, parents, accepted, k, S0, S_out, U, g2, tree_status,
+                      commit_depth_limit(desc)};
     return launched(gdn::launch_wy_commit(desc->io_dtype, d, a, s));
   }
   gdn::ForkCommitArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
@@ -189,7 +220,7 @@ gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
   if (st != GDN_OK) return st;
   if (n_layers <= 0 || desc->num_seqs == 0) return GDN_OK;
   if (!layers) return GDN_ERR_NULL_PTR;
-  if (desc->mode != GDN_MODE_WY) {
+  if (desc->mode == GDN_MODE_FORK) {
     for (int l = 0; l < n_layers; ++l) {
       const gdn_layer_io& y = layers[l];
       st = gdn_tree_commit(desc, offsets, parents, accepted, y.k, y.S0, y.S_out, y.workspace,
@@ -212,7 +243,7 @@ gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
   gdn::CommitLayersArgs a{};
   a.base = gdn::CommitArgs{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
                            offsets, parents, accepted, nullptr, nullptr, nullptr, nullptr,
-                           nullptr, tree_status};
+                           nullptr, tree_status, commit_depth_limit(desc)};
   for (int l0 = 0; l0 < n_layers; l0 += gdn::kMaxLayersPerLaunch) {
     a.layers = std::min(n_layers - l0, gdn::kMaxLayersPerLaunch);
     for (int i = 0; i < a.layers; ++i) {
@@ -236,6 +267,7 @@ const char* gdn_tree_status_string(int status) {
     case GDN_ERR_UNSUPPORTED: return "unsupported head size, io dtype, mode or head grouping";
     case GDN_ERR_WORKSPACE: return "workspace smaller than the entry point's workspace_bytes()";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
+    case GDN_ERR_GRAPH: return "graph capture, instantiation or launch failed";
   }
   return "unknown status";
 }

@@ -43,6 +43,7 @@ struct CommitArgs {
   const float* U;
   const float* g2;
   int32_t* status;
+  int max_depth;   // >= 0: a tree deeper than this is rejected (FORK_DELTA); -1: no limit
 };
 
 struct ForkArgs {
@@ -58,6 +59,8 @@ struct ForkArgs {
   void* o;
   float* ckpt;   // [T,H,dv,dk]
   int32_t* status;
+  float* U;      // FORK_DELTA: [T,H,dv] the per-node deltas, else null
+  float* g2;     // FORK_DELTA: [T,H] base-2 gate prefixes, else null
 };
 
 struct ForkCommitArgs {
@@ -93,23 +96,45 @@ struct AttnArgs {
   int32_t* status;
 };
 
-struct AttnCommitArgs {
-  int B, Hkv, T, max_nodes, cap;
-  const int32_t* offsets;
-  const int32_t* parents;
-  const int32_t* accepted;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* kc;
-  uint16_t* vc;
-  int32_t* cache_len;
-  int32_t* status;
-};
-
 // Layer-batched verify / commit: one launch covers several layers that share
 // the tree (offsets, parents, accepted, status); workgroup i works on layer
 // i / (B * H) with that layer's pointers.
 constexpr int kMaxLayersPerLaunch = 32;
+
+// Accepted-path KV append for `layers` attention layers that share the tree
+// and the committed length: every layer's rows go to rows cache_len[b] ..,
+// and cache_len advances (once) only when `advance` is set.
+struct AttnCommitLayer {
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* kc;
+  uint16_t* vc;
+};
+
+struct AttnCommitArgs {
+  int B, Hkv, T, max_nodes, cap;
+  int layers;
+  int advance;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* accepted;
+  int32_t* cache_len;
+  int32_t* status;
+  AttnCommitLayer L[kMaxLayersPerLaunch];
+};
+
+// Greedy acceptance of the verified trees.
+struct AcceptArgs {
+  int B, T, max_nodes;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* draft;
+  const int32_t* target;
+  int32_t* accepted;
+  int32_t* accept_len;
+  int32_t* next_token;
+  int32_t* status;
+};
 
 struct VerifyLayer {
   const void* q;
@@ -183,6 +208,7 @@ hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s);
 hipError_t launch_wy_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s);
 hipError_t launch_fork_level(int io, int d, const ForkArgs& a, hipStream_t s);
 hipError_t launch_fork_commit(int d, const ForkCommitArgs& a, hipStream_t s);
+hipError_t launch_accept_greedy(const AcceptArgs& a, hipStream_t s);
 
 // Kernel launch that reports its own error (no reliance on the sticky
 // last-error state, which other libraries in the process also use).

@@ -881,7 +881,8 @@ __global__ __launch_bounds__(256) void tree_attn_combine_kernel(const AttnArgs a
 }
 
 // One workgroup per sequence: validate, find the accepted path, append its
-// K/V rows (root first) for every K/V head, advance the length.
+// K/V rows (root first) for every K/V head of every layer of the launch, then
+// advance the length.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_commit_kernel(const AttnCommitArgs a) {
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -934,20 +935,57 @@ __global__ __launch_bounds__(256) void tree_attn_commit_kernel(const AttnCommitA
   const int P = sInfo[1];
   const int L = sInfo[2];
   if (st != GDN_TREE_OK || P == 0) return;
-  const int work = 2 * a.Hkv * P * CPR;
-  for (int id = tid; id < work; id += 256) {
-    const int mat = id / (a.Hkv * P * CPR);
-    int rem = id - mat * a.Hkv * P * CPR;
-    const int kvh = rem / (P * CPR);
-    rem -= kvh * P * CPR;
-    const int pr = rem / CPR;
-    const int c = rem - pr * CPR;
-    const uint16_t* src = (mat ? a.v : a.k) + ((size_t)sPath[pr] * a.Hkv + kvh) * D + 8 * c;
-    uint16_t* dst = (mat ? a.vc : a.kc) + (((size_t)b * a.Hkv + kvh) * a.cap + L + pr) * D + 8 * c;
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  // the same rows of up to kGroup layers per pass: all their loads are in
+  // flight before the first store (a layer alone is one short dependent
+  // load-store round trip per thread)
+  constexpr int kGroup = 8;   // the named registers below
+  const int half = a.Hkv * P * CPR;            // chunks of K (then of V) per layer
+  if (a.layers == 1) {
+    const AttnCommitLayer& ly = a.L[0];
+    for (int id = tid; id < 2 * half; id += 256) {
+      const int mat = id / half;
+      const int rem0 = id - mat * half;
+      const int kvh = rem0 / (P * CPR);
+      const int rem = rem0 - kvh * P * CPR;
+      const int pr = rem / CPR;
+      const int c = rem - pr * CPR;
+      const uint16_t* src = (mat ? ly.v : ly.k) + ((size_t)sPath[pr] * a.Hkv + kvh) * D + 8 * c;
+      uint16_t* dst =
+          (mat ? ly.vc : ly.kc) + (((size_t)b * a.Hkv + kvh) * a.cap + L + pr) * D + 8 * c;
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+  for (int l0 = 0; a.layers > 1 && l0 < a.layers; l0 += kGroup) {
+    // layer pointers are wave-uniform: K first, then V, so that the choice
+    // between them is uniform too and the pointers stay in scalar registers
+    for (int mat = 0; mat < 2; ++mat) {
+      for (int id = tid; id < half; id += 256) {
+        const int kvh = id / (P * CPR);
+        const int rem = id - kvh * P * CPR;
+        const int pr = rem / CPR;
+        const int c = rem - pr * CPR;
+        const size_t src = ((size_t)sPath[pr] * a.Hkv + kvh) * D + 8 * c;
+        const size_t dst = (((size_t)b * a.Hkv + kvh) * a.cap + L + pr) * D + 8 * c;
+        // (past the last layer the last one repeats: the same bytes to the
+        // same place, so no branch is needed; named registers, not an array,
+        // which the compiler would keep in scratch)
+        auto in = [&](int j) {
+          const AttnCommitLayer& ly = a.L[min(l0 + j, a.layers - 1)];
+          return *reinterpret_cast<const uint4*>((mat ? ly.v : ly.k) + src);
+        };
+        auto out = [&](int j, const uint4& x) {
+          const AttnCommitLayer& ly = a.L[min(l0 + j, a.layers - 1)];
+          *reinterpret_cast<uint4*>((mat ? ly.vc : ly.kc) + dst) = x;
+        };
+        const uint4 x0 = in(0), x1 = in(1), x2 = in(2), x3 = in(3);
+        const uint4 x4 = in(4), x5 = in(5), x6 = in(6), x7 = in(7);
+        out(0, x0), out(1, x1), out(2, x2), out(3, x3);
+        out(4, x4), out(5, x5), out(6, x6), out(7, x7);
+      }
+    }
   }
   __syncthreads();
-  if (tid == 0) a.cache_len[b] = L + P;
+  if (tid == 0 && a.advance) a.cache_len[b] = L + P;
 }
 
 // Kernel from the most query rows a (sequence, K/V head) can have: up to 192

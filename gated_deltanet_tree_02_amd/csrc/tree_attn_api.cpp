@@ -9,6 +9,7 @@
 #include <cstdint>
 
 #include "gdn_tree_attn.h"
+#include "api_internal.h"
 #include "launch.h"
 
 namespace {
@@ -20,7 +21,11 @@ constexpr long long kTargetGroups = 256;  // one verify workgroup per CU (a CU h
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-gdn_status check_desc(const gdn_attn_desc* d) {
+}  // namespace
+
+namespace gdn {
+
+gdn_status check_attn_desc(const gdn_attn_desc* d) {
   if (d == nullptr) return GDN_ERR_NULL_PTR;
   if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->total_nodes < 0 ||
       d->max_nodes < 1 || d->max_nodes > GDN_TREE_MAX_NODES || d->cache_capacity < 0 ||
@@ -36,6 +41,12 @@ gdn_status check_desc(const gdn_attn_desc* d) {
     return GDN_ERR_BAD_SHAPE;
   return GDN_OK;
 }
+
+}  // namespace gdn
+
+namespace {
+
+gdn_status check_desc(const gdn_attn_desc* d) { return gdn::check_attn_desc(d); }
 
 // Split of each (sequence, KV head)'s cache rows over NS workgroups of CL
 // rows (CL a multiple of the key block), so that about kTargetGroups
@@ -61,6 +72,23 @@ size_t workspace_bytes(const gdn_attn_desc* d) {
 }
 
 gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+gdn::AttnCommitArgs commit_base(const gdn_attn_desc* d, const int32_t* offsets,
+                                const int32_t* parents, const int32_t* accepted,
+                                int32_t* cache_len, int32_t* tree_status) {
+  gdn::AttnCommitArgs a{};
+  a.B = d->num_seqs;
+  a.Hkv = d->num_kv_heads;
+  a.T = d->total_nodes;
+  a.max_nodes = d->max_nodes;
+  a.cap = d->cache_capacity;
+  a.offsets = offsets;
+  a.parents = parents;
+  a.accepted = accepted;
+  a.cache_len = cache_len;
+  a.status = tree_status;
+  return a;
+}
 
 }  // namespace
 
@@ -130,23 +158,47 @@ gdn_status gdn_tree_attn_commit(const gdn_attn_desc* desc, const int32_t* offset
   if (!offsets || !accepted || !cache_len || !tree_status) return GDN_ERR_NULL_PTR;
   if (desc->total_nodes > 0 && (!parents || !k || !v)) return GDN_ERR_NULL_PTR;
   if (desc->cache_capacity > 0 && (!k_cache || !v_cache)) return GDN_ERR_NULL_PTR;
-  gdn::AttnCommitArgs a{};
-  a.B = desc->num_seqs;
-  a.Hkv = desc->num_kv_heads;
-  a.T = desc->total_nodes;
-  a.max_nodes = desc->max_nodes;
-  a.cap = desc->cache_capacity;
-  a.offsets = offsets;
-  a.parents = parents;
-  a.accepted = accepted;
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.kc = static_cast<uint16_t*>(k_cache);
-  a.vc = static_cast<uint16_t*>(v_cache);
-  a.cache_len = cache_len;
-  a.status = tree_status;
+  gdn::AttnCommitArgs a = commit_base(desc, offsets, parents, accepted, cache_len, tree_status);
+  a.layers = 1;
+  a.advance = 1;
+  a.L[0] = {static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+            static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache)};
   return launched(
       gdn::launch_tree_attn_commit(desc->head_dim, a, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_tree_attn_commit_layers(const gdn_attn_desc* desc, int32_t n_layers,
+                                       const int32_t* offsets, const int32_t* parents,
+                                       const int32_t* accepted, const gdn_attn_layer_io* layers,
+                                       int32_t* cache_len, int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (desc->num_seqs == 0 || n_layers <= 0) return GDN_OK;
+  if (!offsets || !accepted || !cache_len || !tree_status || !layers) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && !parents) return GDN_ERR_NULL_PTR;
+  for (int l = 0; l < n_layers; ++l) {
+    if (desc->total_nodes > 0 && (!layers[l].k || !layers[l].v)) return GDN_ERR_NULL_PTR;
+    if (desc->cache_capacity > 0 && (!layers[l].k_cache || !layers[l].v_cache))
+      return GDN_ERR_NULL_PTR;
+  }
+  // every launch reads the same committed length; only the last advances it
+  for (int l0 = 0; l0 < n_layers; l0 += gdn::kMaxLayersPerLaunch) {
+    const int nl = n_layers - l0 < gdn::kMaxLayersPerLaunch ? n_layers - l0
+                                                            : gdn::kMaxLayersPerLaunch;
+    gdn::AttnCommitArgs a =
+        commit_base(desc, offsets, parents, accepted, cache_len, tree_status);
+    a.layers = nl;
+    a.advance = l0 + nl == n_layers;
+    for (int i = 0; i < nl; ++i) {
+      const gdn_attn_layer_io& ly = layers[l0 + i];
+      a.L[i] = {static_cast<const uint16_t*>(ly.k), static_cast<const uint16_t*>(ly.v),
+                static_cast<uint16_t*>(ly.k_cache), static_cast<uint16_t*>(ly.v_cache)};
+    }
+    st = launched(
+        gdn::launch_tree_attn_commit(desc->head_dim, a, static_cast<hipStream_t>(stream)));
+    if (st != GDN_OK) return st;
+  }
+  return GDN_OK;
 }
 
 }  // extern "C"

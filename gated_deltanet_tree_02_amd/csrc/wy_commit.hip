@@ -127,8 +127,17 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args ar
         st = GDN_TREE_BAD_ROOT;
       else if (__ballot(lane >= 1 && lane < n && (par < 0 || par >= lane)) != 0ull)
         st = GDN_TREE_BAD_PARENT;
-      else if (acc < -1 || acc >= n)
-        st = GDN_TREE_BAD_ACCEPTED;
+      if (st == GDN_TREE_OK && a.max_depth >= 0) {
+        // the depth limit of the level-by-level verify that wrote the workspace
+        uint64_t anc0;
+        float unused0;
+        path_scan(par, lane, n, 0.f, anc0, unused0);
+        int dep = lane < n ? __popcll(anc0) - 1 : 0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) dep = max(dep, __shfl_xor(dep, off, kWave));
+        if (dep > a.max_depth) st = GDN_TREE_TOO_DEEP;
+      }
+      if (st == GDN_TREE_OK && (acc < -1 || acc >= n)) st = GDN_TREE_BAD_ACCEPTED;
       if (st == GDN_TREE_OK && acc >= 0) {
         uint64_t anc;
         float unused;

@@ -417,3 +417,47 @@ def make_attn_config(name: str, seed: Optional[int] = None) -> AttnWorkload:
     else:
         lens = rng.integers(c["lens"][1], c["lens"][2] + 1, size=c["B"]).tolist()
     return make_attn_workload(trees, c["Hq"], c["Hkv"], c["d"], c["cap"], lens, seed=data_seed)
+
+
+# ---------------------------------------------------------------------------
+# Draft and target tokens for acceptance
+# ---------------------------------------------------------------------------
+
+
+def draft_target_tokens(rng: np.random.Generator, parents_list: Sequence[Sequence[int]],
+                        accepted: Sequence[int], vocab: int = 32000):
+    """Token ids for a batch of trees: draft tokens distinct among the
+    children of every node (a top-k expansion proposes distinct tokens), and
+    the target model's predicted next token at every node, drawn so that the
+    prediction names the next node of the given accepted path along it, and
+    names none of a node's children elsewhere (a prediction outside the tree).
+    Returns (draft [T], target [T]) int32; accepted[b] = -1 draws predictions
+    that match no child anywhere."""
+    drafts, targets = [], []
+    for parents, a in zip(parents_list, accepted):
+        n = len(parents)
+        children = [[] for _ in range(n)]
+        for c in range(1, n):
+            children[parents[c]].append(c)
+        draft = np.zeros(n, np.int64)
+        draft[0] = int(rng.integers(vocab))
+        for p in range(n):
+            if children[p]:
+                draft[children[p]] = rng.choice(vocab, size=len(children[p]), replace=False)
+        nxt = {}
+        if a >= 0:
+            path = path_to_root(parents, int(a))
+            nxt = {path[i]: path[i + 1] for i in range(len(path) - 1)}
+        target = np.zeros(n, np.int64)
+        for p in range(n):
+            if p in nxt:
+                target[p] = draft[nxt[p]]
+            else:
+                taken = {int(draft[c]) for c in children[p]}
+                t = int(rng.integers(vocab))
+                while t in taken:
+                    t = int(rng.integers(vocab))
+                target[p] = t
+        drafts.append(draft)
+        targets.append(target)
+    return (np.concatenate(drafts).astype(np.int32), np.concatenate(targets).astype(np.int32))

@@ -1,0 +1,165 @@
+/*
+ * gdn_round.h -- C ABI of libgdntree, one speculative round across the layers
+ * of a hybrid model: acceptance of the verified draft tree, one arena for the
+ * round's speculative state, tree sizing under a memory budget, and the whole
+ * round (verify -> accept -> commit) captured once as a HIP graph.
+ *
+ * A round of tree speculation runs every layer of the model on the same draft
+ * tree, picks the accepted path, and keeps the state of that path only
+ * (rainlin-top.pages.dev "Qwen3.5 tree spec", section 7: GDN layers verify the
+ * flattened tree, attention layers verify it under the tree mask, then the
+ * accepted path's state is restored in the GDN layers and its K/V rows are
+ * kept in the attention layers). The per-layer calls are in gdn_tree.h and
+ * gdn_tree_attn.h; this header composes them.
+ *
+ * Conventions follow gdn_tree.h: device pointers owned by the caller, no
+ * device allocation and no synchronisation, host-side checks reported by the
+ * gdn_status return value, data-dependent problems per sequence in
+ * tree_status (GDN_TREE_* codes).
+ */
+#ifndef GDN_ROUND_H
+#define GDN_ROUND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn_tree.h"
+#include "gdn_tree_attn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ acceptance */
+
+/* Greedy acceptance of a verified draft tree, per sequence (handbook
+ * anrans.github.io ai-infra-handbooks "speculative", implementation section,
+ * the generation loop): the walk starts at the root, which is always
+ * accepted; at the current node it takes the target model's prediction for
+ * the next token, looks for a child of the node whose draft token equals it,
+ * taking the first such child in node order, and moves there; it stops at the
+ * first node with no such child.
+ *   draft_tokens  [T] int32  token of every node (the root's is not read)
+ *   target_tokens [T] int32  the target model's predicted next token at every
+ *                            node (the argmax of its logits at that node)
+ *   accepted      [B] int32  out: last node of the accepted path (local
+ *                            index), the input of the commits
+ *   accept_len    [B] int32  out: nodes on the accepted path, root included
+ *   next_token    [B] int32  out: target_tokens at the last accepted node (the
+ *                            target's own next token, the next round's root)
+ *   tree_status   [B] int32  out: GDN_TREE_OK / BAD_SIZE / BAD_ROOT /
+ *                            BAD_PARENT; a rejected sequence gets accepted -1,
+ *                            accept_len 0 and next_token -1 (so every commit
+ *                            leaves it unchanged)
+ * Only num_seqs, total_nodes and max_nodes of `desc` are used. Integer work:
+ * results are exact. */
+gdn_status gdn_tree_accept_greedy(const gdn_tree_desc* desc, const int32_t* offsets,
+                                  const int32_t* parents, const int32_t* draft_tokens,
+                                  const int32_t* target_tokens, int32_t* accepted,
+                                  int32_t* accept_len, int32_t* next_token,
+                                  int32_t* tree_status, void* stream);
+
+/* ------------------------------------------------------------------ round shape and arena */
+
+/* The layers of one round. Every GDN layer has the shape `gdn` (WY or FORK
+ * mode) and every full-attention layer the shape `attn`; both describe the
+ * same batch of trees (num_seqs, total_nodes and max_nodes agree when both
+ * kinds are present). */
+typedef struct {
+  gdn_tree_desc gdn;
+  int32_t n_gdn_layers;     /* >= 0                                            */
+  gdn_attn_desc attn;       /* ignored when n_attn_layers == 0                 */
+  int32_t n_attn_layers;    /* >= 0                                            */
+} gdn_round_desc;
+
+/* Where each layer's scratch lives in one caller-owned arena (byte offsets;
+ * every slice 256-byte aligned). GDN layer l's workspace (gdn_ws_bytes, the
+ * speculative state its verify leaves for its commit) starts at
+ * l * gdn_ws_stride, attention layer l's at attn_ws_offset + l *
+ * attn_ws_stride. In GDN_MODE_FORK_DELTA the stride covers only the part
+ * commit reads (U and g); a layer's workspace runs on over the slices of the
+ * layers after it, whose verify-time states share that memory. This is
+ * valid when the GDN layers verify in increasing order, as a round does:
+ * every later layer writes its states past the kept part of every earlier
+ * one. */
+typedef struct {
+  size_t total_bytes;       /* arena size for the whole round                  */
+  size_t gdn_ws_bytes;      /* gdn_tree_workspace_bytes(&desc.gdn)             */
+  size_t gdn_ws_stride;
+  size_t attn_ws_bytes;     /* gdn_tree_attn_workspace_bytes(&desc.attn)       */
+  size_t attn_ws_offset;
+  size_t attn_ws_stride;
+} gdn_round_layout;
+
+/* Arena layout of a round. GDN_ERR_BAD_SHAPE when the two shapes disagree on
+ * the batch, or a layer count is negative; otherwise the per-layer
+ * descriptor checks of the per-layer calls. */
+gdn_status gdn_round_plan(const gdn_round_desc* desc, gdn_round_layout* layout);
+
+/* Tree sizing under a memory budget (fork page, section 8: the draft tree's
+ * width and depth are limited so that the speculative state fits the memory
+ * at hand). Among complete trees with branching factor k in [1, 8] and depth
+ * d in [1, max_depth] (1 + k + ... + k^d nodes, at most GDN_TREE_MAX_NODES),
+ * picks the one with the most nodes whose speculative state -- num_seqs
+ * sequences, n_gdn_layers layers: the GDN part of the round's arena
+ * (gdn_round_plan) in desc.gdn's mode -- fits budget_bytes; ties go to the
+ * wider tree. total_nodes and max_nodes of
+ * desc.gdn are ignored. When no tree with a draft node fits, the result is
+ * the root alone (branching 0, depth 0, nodes 1). state_bytes receives the
+ * chosen tree's bytes as the arena holds them (may be NULL). */
+gdn_status gdn_round_tree_for_budget(const gdn_round_desc* desc, size_t budget_bytes,
+                                     int32_t max_depth, int32_t* branching, int32_t* depth,
+                                     int32_t* nodes, size_t* state_bytes);
+
+/* ------------------------------------------------------------------ captured round */
+
+/* Everything one round reads and writes. Host arrays: gdn_layers
+ * [n_gdn_layers] (their workspace fields are ignored: the arena supplies
+ * them), attn_layers [n_attn_layers], layer_kinds [n_gdn_layers +
+ * n_attn_layers] (0 = the next GDN layer, 1 = the next attention layer, in
+ * model order; NULL = the GDN layers, then the attention layers). All other
+ * pointers are device pointers. cache_len is shared by the attention layers
+ * (one committed length per sequence); commit advances it once. */
+typedef struct {
+  const int32_t* offsets;
+  const int32_t* parents;
+  const gdn_layer_io* gdn_layers;
+  const gdn_attn_layer_io* attn_layers;
+  const int32_t* layer_kinds;
+  int32_t* cache_len;
+  float attn_scale;
+  void* arena;
+  size_t arena_bytes;
+  const int32_t* draft_tokens;
+  const int32_t* target_tokens;
+  int32_t* accepted;
+  int32_t* accept_len;
+  int32_t* next_token;
+  int32_t* tree_status;
+} gdn_round_io;
+
+typedef struct gdn_round_graph_s* gdn_round_graph;
+
+/* Record one round on `stream` (a non-null hipStream_t that is not already
+ * capturing) as a HIP graph: every layer's verify in model order, the greedy
+ * acceptance, the GDN commits of all layers, and the attention layers' KV
+ * append. Nothing runs during capture. The graph keeps the pointers of `io`:
+ * every buffer must stay allocated, at the same address, while the graph is
+ * used; their contents are read when the graph runs. GDN_ERR_GRAPH when the
+ * HIP runtime refuses capture or instantiation (the stream is left out of
+ * capture). *out is set only on success. */
+gdn_status gdn_round_capture(const gdn_round_desc* desc, const gdn_round_io* io, void* stream,
+                             gdn_round_graph* out);
+
+/* Run a captured round on `stream` (any stream of the same device). Runs of
+ * one graph must not overlap. */
+gdn_status gdn_round_launch(gdn_round_graph graph, void* stream);
+
+/* Free a captured round (host-side objects only). NULL is a no-op. */
+void gdn_round_destroy(gdn_round_graph graph);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_ROUND_H */

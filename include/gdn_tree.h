@@ -35,6 +35,13 @@
  *    starts from its parent's checkpoint and stores its own full state
  *    (fork page section 4, depth-by-depth subsection); commit copies the
  *    accepted node's checkpoint (section 5).
+ *  - GDN_MODE_FORK_DELTA: the same depth-by-depth fork with delta-compressed
+ *    checkpoints (fork page section 8, checkpoint compression): a node keeps
+ *    only what its update adds to its parent's state, the rank-one term
+ *    u_t k_t^T with u_t = beta_t (v_t - alpha_t S_parent k_t), and its gate.
+ *    These u_t are exactly the WY pseudo-values, so the kept part of the
+ *    workspace has the WY layout and commit is the WY commit; full states are
+ *    kept only for nodes with children, while verify runs.
  *
  * Conventions (all entry points)
  * ------------------------------
@@ -80,13 +87,14 @@ typedef enum {
   GDN_ERR_BAD_SHAPE = 2,      /* negative/zero sizes, max_nodes outside [1,64], ... */
   GDN_ERR_UNSUPPORTED = 3,    /* dk/dv/io dtype/mode combination not built          */
   GDN_ERR_WORKSPACE = 4,      /* workspace smaller than gdn_tree_workspace_bytes()  */
-  GDN_ERR_LAUNCH = 5          /* the HIP runtime refused a launch                   */
+  GDN_ERR_LAUNCH = 5,         /* the HIP runtime refused a launch                   */
+  GDN_ERR_GRAPH = 6           /* the HIP runtime refused graph capture or launch    */
 } gdn_status;
 
 /* Element type of q, k, v and o. State, gates and accumulation are fp32. */
 typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
 
-typedef enum { GDN_MODE_WY = 0, GDN_MODE_FORK = 1 } gdn_mode;
+typedef enum { GDN_MODE_WY = 0, GDN_MODE_FORK = 1, GDN_MODE_FORK_DELTA = 2 } gdn_mode;
 
 /* Per-sequence codes written to tree_status (checked in this order). */
 enum {
@@ -95,11 +103,11 @@ enum {
   GDN_TREE_BAD_PARENT = 2,    /* a non-root node's parent is < 0 or >= its index    */
   GDN_TREE_BAD_SIZE = 3,      /* N_b outside [1, max_nodes] or range outside [0,T]  */
   GDN_TREE_BAD_ACCEPTED = 4,  /* commit: accepted[b] outside [-1, N_b)              */
-  GDN_TREE_TOO_DEEP = 5,      /* FORK mode: a node deeper than desc.max_depth       */
+  GDN_TREE_TOO_DEEP = 5,      /* FORK modes: a node deeper than desc.max_depth      */
   GDN_TREE_CACHE_FULL = 6     /* attention commit: the path would overflow the cache */
 };
 /* Precedence: BAD_SIZE, then BAD_ROOT, then BAD_PARENT, then TOO_DEEP (FORK
- * verify) or BAD_ACCEPTED (commit). */
+ * modes), then BAD_ACCEPTED (commit). */
 
 typedef struct {
   int32_t num_seqs;     /* B >= 0                                                   */
@@ -107,7 +115,7 @@ typedef struct {
   int32_t dk, dv;       /* supported: dk == dv in {32, 64, 128}                     */
   int32_t total_nodes;  /* T = offsets[B] (host copy; sizes outputs and workspace)  */
   int32_t max_nodes;    /* upper bound on every N_b, in [1, 64]; sizes on-chip tiles */
-  int32_t max_depth;    /* FORK mode: number of levels - 1 to run (root = depth 0);
+  int32_t max_depth;    /* FORK modes: number of levels - 1 to run (root = depth 0);
                            0 or negative means max_nodes - 1. Ignored in WY mode.    */
   int32_t io_dtype;     /* gdn_dtype                                                */
   int32_t mode;         /* gdn_mode                                                 */
@@ -117,7 +125,11 @@ typedef struct {
  * workspace size:
  *   WY:   T*H*(dv + 1)*4 bytes -- pseudo-values U [T,H,dv] fp32, then the
  *         base-2 gate prefixes g [T,H] fp32 (each part 256-byte aligned);
- *   FORK: T*H*dv*dk*4 bytes    -- one fp32 checkpoint [T,H,dv,dk] per node-head.
+ *   FORK: T*H*dv*dk*4 bytes    -- one fp32 checkpoint [T,H,dv,dk] per node-head;
+ *   FORK_DELTA: the WY part (U, then g), then T*H*dv*dk*4 bytes of node
+ *         states [T,H,dv,dk] (256-byte aligned). Commit reads only the WY
+ *         part: the states are verify's working memory (only nodes with
+ *         children are written) and may be reused once verify has run.
  * Returns 0 for an invalid descriptor. */
 size_t gdn_tree_workspace_bytes(const gdn_tree_desc* desc);
 
@@ -148,9 +160,9 @@ gdn_status gdn_tree_verify(const gdn_tree_desc* desc, const int32_t* offsets,
  * (the last node of the accepted root-to-node path), or S0[b] when
  * accepted[b] == -1. S_out may equal S0 (in place); partial overlap is not
  * allowed. `workspace` is the one written by gdn_tree_verify with the same
- * descriptor, inputs and mode, and must not have been modified since. WY mode
- * also reads k and the same offsets/parents (k may be NULL in FORK mode);
- * FORK mode ignores k. tree_status receives the GDN_TREE_* code of every
+ * descriptor, inputs and mode, and its U and g parts must not have been
+ * modified since. WY and FORK_DELTA modes also read k and the same
+ * offsets/parents (k may be NULL in FORK mode); FORK mode ignores k. tree_status receives the GDN_TREE_* code of every
  * sequence; sequences with a nonzero code are left unwritten. */
 gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
                            const int32_t* parents, const int32_t* accepted, const void* k,

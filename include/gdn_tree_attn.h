@@ -92,6 +92,31 @@ gdn_status gdn_tree_attn_commit(const gdn_attn_desc* desc, const int32_t* offset
                                 const void* v, void* k_cache, void* v_cache, int32_t* cache_len,
                                 int32_t* tree_status, void* stream);
 
+/* One attention layer's buffers for the layer-batched commit below and for a
+ * captured round (gdn_round.h); layouts as above. */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* k_cache;
+  void* v_cache;
+  void* o;
+} gdn_attn_layer_io;
+
+/* Layer-batched commit: the accepted-path K/V append of n_layers attention
+ * layers of one model, which share the trees, the accepted nodes and the
+ * committed length of every sequence (all layers of a model hold the same
+ * prefix). Every layer's path rows go to cache rows cache_len[b] .. of its
+ * own caches, then cache_len[b] advances once by the path length. `layers` is
+ * a HOST array (q and o are not read). Per-sequence status and the
+ * unchanged-on-error rule are those of gdn_tree_attn_commit; the rows written
+ * are identical to n_layers single-layer commits that each start from the
+ * same length. n_layers <= 0 is a no-op. */
+gdn_status gdn_tree_attn_commit_layers(const gdn_attn_desc* desc, int32_t n_layers,
+                                       const int32_t* offsets, const int32_t* parents,
+                                       const int32_t* accepted, const gdn_attn_layer_io* layers,
+                                       int32_t* cache_len, int32_t* tree_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

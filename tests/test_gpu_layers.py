@@ -84,6 +84,20 @@ def test_fork_mode_layers_match():
         assert torch.equal(a.S_out, b.S_out)
 
 
+def test_fork_delta_layers_match():
+    """FORK_DELTA: per-layer verify launches, then the layer-batched WY commit
+    over the kept deltas: identical to the per-layer calls."""
+    _say("fork-delta layers")
+    w = gi.make_config("c3", layers=2)
+    single, batched, status = _run_both(w, mode=gt.MODE_FORK_DELTA, max_depth=3)
+    for a, b in zip(single, batched):
+        assert torch.equal(a.o, b.o)
+        assert torch.equal(a.S_out, b.S_out)
+    o, _, S, _ = oracle_layer(w, layer=1)
+    assert rel_err_rows(batched[1].o_np(), o) <= TOL[w.io]
+    assert rel_err_states(batched[1].S_out.cpu().numpy(), S) <= TOL[w.io]
+
+
 def test_layers_status_codes():
     _say("status")
     trees = [gi.chain_parents(5), [0, 0, 1], [-1, 1, 0], [-1, 0]]

@@ -239,6 +239,70 @@ def test_fork_too_deep_status():
     assert np.all(o[:8] == 0)
 
 
+# ------------------------------------------------------------------ FORK_DELTA mode
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_fork_delta_mode(name):
+    """Delta-compressed fork checkpoints: outputs and committed states meet the
+    oracle bar, the kept deltas are the dense WY pseudo-values, outputs are
+    bit-identical to FORK mode's (the same level kernel) and the gate prefixes
+    to WY mode's (the same path sum)."""
+    w = gi.make_config(name)
+    md = w.max_depth()
+    dd = _check_layer(w, mode=gt.MODE_FORK_DELTA, max_depth=md, check_wy_parts=True)
+    df = DeviceLayer(w, 0, mode=gt.MODE_FORK, max_depth=md)
+    dw = DeviceLayer(w, 0, mode=gt.MODE_WY)
+    df.verify()
+    dw.verify()
+    torch.cuda.synchronize()
+    assert torch.equal(dd.o, df.o)
+    U_d, g_d = dd.wy_parts()
+    U_w, g_w = dw.wy_parts()
+    np.testing.assert_array_equal(g_d, g_w)
+    e_u = rel_err_rows(U_d, U_w)
+    _say(f"{name}: FORK_DELTA deltas vs WY pseudo-values {e_u:.3e}")
+    assert e_u <= TOL[w.io]
+
+
+def test_fork_delta_c4_layer_and_wy_agree():
+    w = gi.make_config("c4", layers=1)
+    dw = DeviceLayer(w, 0, mode=gt.MODE_WY)
+    dd = DeviceLayer(w, 0, mode=gt.MODE_FORK_DELTA, max_depth=3)
+    for dl in (dw, dd):
+        dl.verify()
+        dl.commit()
+    torch.cuda.synchronize()
+    assert (dd.status.cpu().numpy() == 0).all()
+    e_o = rel_err_rows(dd.o_np(), dw.o_np())
+    e_s = rel_err_states(dd.S_out.cpu().numpy(), dw.S_out.cpu().numpy())
+    _say(f"c4 WY vs FORK_DELTA on GPU: o {e_o:.3e}, S {e_s:.3e}")
+    assert e_o <= TOL["bf16"] and e_s <= 1e-4
+    seqs = [0, 31, 63]
+    sub = sub_workload(w, seqs)
+    o_ref, _, S_ref, _ = oracle_layer(sub, 0)
+    rows = np.concatenate([np.arange(w.offsets[b], w.offsets[b + 1]) for b in seqs])
+    assert rel_err_rows(dd.o_np()[rows], o_ref) <= TOL["bf16"]
+    assert rel_err_states(dd.S_out.cpu().numpy()[seqs], S_ref) <= TOL["bf16"]
+
+
+def test_fork_delta_too_deep_status_at_verify_and_commit():
+    w = gi.make_workload([gi.chain_parents(8), gi.kary_parents(2, 2)], H=2, dk=32, dv=32,
+                         io="f32", seed=81, accepted=[7, 5])
+    dl = DeviceLayer(w, 0, mode=gt.MODE_FORK_DELTA, max_depth=3)
+    dl.verify()
+    torch.cuda.synchronize()
+    assert dl.status.cpu().numpy().tolist() == [5, 0]
+    assert np.all(dl.o_np()[:8] == 0)
+    dl.commit()
+    torch.cuda.synchronize()
+    assert dl.status.cpu().numpy().tolist() == [5, 0]
+    S = dl.S_out.cpu().numpy()
+    assert np.isnan(S[0]).all()                  # the rejected sequence is not written
+    _, _, S_ref, _ = oracle_layer(w, 0)         # the oracle has no depth limit
+    assert rel_err_states(S[1:], S_ref[1:]) <= TOL["f32"]
+
+
 # ------------------------------------------------------------- isolation, aliasing, errors
 
 

@@ -19,7 +19,7 @@ def _declared_functions():
     for f in sorted(os.listdir(INCLUDE)):
         if f.endswith(".h"):
             text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
-            names.update(re.findall(r"\b(gdn_tree_\w+)\s*\(", text))
+            names.update(re.findall(r"\b(gdn_(?:tree|round)_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -30,7 +30,10 @@ def test_library_exports_every_declared_symbol():
                             "gdn_tree_commit", "gdn_tree_status_string",
                             "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
                             "gdn_tree_attn_commit", "gdn_tree_verify_layers",
-                            "gdn_tree_commit_layers"])
+                            "gdn_tree_commit_layers", "gdn_tree_attn_commit_layers",
+                            "gdn_tree_accept_greedy", "gdn_round_plan",
+                            "gdn_round_tree_for_budget", "gdn_round_capture",
+                            "gdn_round_launch", "gdn_round_destroy"])
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -53,6 +56,9 @@ def test_workspace_bytes_wy_and_fork():
     assert gt.gdn_tree_workspace_bytes(d) == u + g
     d.mode = gt.MODE_FORK
     assert gt.gdn_tree_workspace_bytes(d) == th * 128 * 128 * 4
+    # FORK_DELTA: the WY part, then one state per node-head (verify's working memory)
+    d.mode = gt.MODE_FORK_DELTA
+    assert gt.gdn_tree_workspace_bytes(d) == u + g + th * 128 * 128 * 4
     # WY speculative state per node-head is (dv + 1) * 4 bytes
     d1 = gt.make_desc(1, 1, 128, 128, 64, 64)
     assert gt.gdn_tree_workspace_bytes(d1) == 64 * 128 * 4 + 256
@@ -75,7 +81,7 @@ def test_fork_workspace_reproduces_page_checkpoint_table():
 
 @pytest.mark.parametrize("field,value,code", [
     ("num_seqs", -1, 2), ("num_heads", 0, 2), ("total_nodes", -5, 2), ("max_nodes", 0, 2),
-    ("max_nodes", 65, 2), ("dk", 96, 3), ("dv", 64, 3), ("io_dtype", 7, 3), ("mode", 2, 3),
+    ("max_nodes", 65, 2), ("dk", 96, 3), ("dv", 64, 3), ("io_dtype", 7, 3), ("mode", 3, 3),
 ])
 def test_bad_descriptors_rejected_before_launch(field, value, code):
     lib = gt.load_library()
@@ -221,3 +227,189 @@ def test_layers_calls_check_before_launch():
                                       None) == 1
     d.dk = 96
     assert lib.gdn_tree_verify_layers(ctypes.byref(d), 2, fake, fake, ly, need, fake, None) == 3
+
+
+# ------------------------------------------------------------------ rounds (gdn_round.h)
+
+ROUND_HEADER = os.path.join(ROOT, "include", "gdn_round.h")
+ATTN_HEADER = os.path.join(ROOT, "include", "gdn_tree_attn.h")
+
+
+def _struct_fields(path, name):
+    text = open(path).read()
+    body = re.search(r"typedef struct \{([^{}]*)\} " + name + ";", text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return re.findall(r"\b(\w+)\s*;", body)
+
+
+def test_round_structs_match_headers():
+    assert _struct_fields(ROUND_HEADER, "gdn_round_desc") == [
+        f for f, _ in gt.GdnRoundDesc._fields_]
+    assert _struct_fields(ROUND_HEADER, "gdn_round_layout") == [
+        f for f, _ in gt.GdnRoundLayout._fields_]
+    assert _struct_fields(ROUND_HEADER, "gdn_round_io") == [f for f, _ in gt.GdnRoundIO._fields_]
+    assert _struct_fields(ATTN_HEADER, "gdn_attn_layer_io") == [
+        f for f, _ in gt.GdnAttnLayerIO._fields_]
+    assert ctypes.sizeof(gt.GdnRoundDesc) == 4 * (9 + 1 + 8 + 1)
+    assert ctypes.sizeof(gt.GdnRoundLayout) == 8 * 6
+    assert ctypes.sizeof(gt.GdnAttnLayerIO) == 8 * 6
+
+
+def test_round_plan_places_every_layer_in_one_arena():
+    gd = gt.make_desc(64, 16, 128, 128, 2560, 40)
+    ad = gt.make_attn_desc(4, 16, 4, 128, 2560, 40, 4160, 3000)     # few pairs: split cache
+    ad.num_seqs = 64
+    ad.max_cache_len = 4096
+    r = gt.make_round_desc(gd, 24, ad, 8)
+    L = gt.gdn_round_plan(r)
+    assert L.gdn_ws_bytes == gt.gdn_tree_workspace_bytes(gd)
+    assert L.gdn_ws_stride % 256 == 0 and L.gdn_ws_stride >= L.gdn_ws_bytes
+    assert L.attn_ws_offset == 24 * L.gdn_ws_stride
+    assert L.attn_ws_bytes == gt.gdn_tree_attn_workspace_bytes(ad)
+    assert L.total_bytes == L.attn_ws_offset + 8 * L.attn_ws_stride
+    # a split cache needs attention scratch
+    ad2 = gt.make_attn_desc(2, 8, 2, 128, 12, 6, 4096, 4096)
+    gd2 = gt.make_desc(2, 16, 128, 128, 12, 6)
+    L2 = gt.gdn_round_plan(gt.make_round_desc(gd2, 3, ad2, 2))
+    assert L2.attn_ws_bytes > 0 and L2.attn_ws_stride % 256 == 0
+    assert L2.total_bytes == 3 * L2.gdn_ws_stride + 2 * L2.attn_ws_stride
+    # no attention layers: the attention descriptor is not read
+    L3 = gt.gdn_round_plan(gt.make_round_desc(gd, 2))
+    assert L3.total_bytes == 2 * L3.gdn_ws_stride and L3.attn_ws_bytes == 0
+    # FORK_DELTA: slices of the kept part (U, g); the verify-time states of
+    # layers verified in order share the memory past them
+    gdd = gt.make_desc(64, 16, 128, 128, 2560, 40, mode=gt.MODE_FORK_DELTA, max_depth=3)
+    L4 = gt.gdn_round_plan(gt.make_round_desc(gdd, 24))
+    wy_part = gt.gdn_tree_workspace_bytes(gd)
+    assert L4.gdn_ws_stride == wy_part
+    assert L4.gdn_ws_bytes == wy_part + 2560 * 16 * 128 * 128 * 4
+    assert L4.total_bytes == 23 * wy_part + L4.gdn_ws_bytes
+    for l in range(24):
+        kept_end = l * L4.gdn_ws_stride + wy_part
+        later_states = [(l2 * L4.gdn_ws_stride + wy_part) for l2 in range(l + 1, 24)]
+        assert all(kept_end <= x for x in later_states)    # later verifies leave it alone
+        assert l * L4.gdn_ws_stride + L4.gdn_ws_bytes <= L4.total_bytes
+
+
+def test_round_plan_rejects_mismatched_or_bad_shapes():
+    lib = gt.load_library()
+    gd = gt.make_desc(8, 16, 128, 128, 80, 10)
+    ad = gt.make_attn_desc(8, 16, 4, 128, 80, 10, 256)
+    out = gt.GdnRoundLayout()
+    for field, value, code in [("num_seqs", 7, 2), ("total_nodes", 81, 2), ("max_nodes", 11, 2)]:
+        a2 = gt.GdnAttnDesc.from_buffer_copy(ad)
+        setattr(a2, field, value)
+        r = gt.make_round_desc(gd, 2, a2, 1)
+        assert lib.gdn_round_plan(ctypes.byref(r), ctypes.byref(out)) == code, field
+    assert lib.gdn_round_plan(ctypes.byref(gt.make_round_desc(gd, -1)), ctypes.byref(out)) == 2
+    bad = gt.GdnTreeDesc.from_buffer_copy(gd)
+    bad.dk = 96
+    assert lib.gdn_round_plan(ctypes.byref(gt.make_round_desc(bad, 1)), ctypes.byref(out)) == 3
+    # a bad GDN descriptor is ignored when the round has no GDN layer
+    assert lib.gdn_round_plan(ctypes.byref(gt.make_round_desc(bad, 0, ad, 1)),
+                              ctypes.byref(out)) == 0
+    assert lib.gdn_round_plan(None, ctypes.byref(out)) == 1
+    assert lib.gdn_round_plan(ctypes.byref(gt.make_round_desc(gd, 1)), None) == 1
+
+
+def test_tree_for_budget_reproduces_the_page_tree_sizes():
+    """Fork page, section 6 table and section 8: at the page's checkpoint
+    memory (rescaled to fp32 state) the budget sizing of FORK mode gives back
+    the page's node counts; WY fits far larger trees into the same budget."""
+    rows = {r[0]: r[1:] for r in read_golden("checkpoint_memory.txt")}
+    layers = int(rows["layers"][0])
+    fork = gt.make_round_desc(gt.make_desc(1, int(rows["heads"][0]), 128, 128, 1, 1,
+                                           mode=gt.MODE_FORK), layers)
+    wy = gt.make_round_desc(gt.make_desc(1, int(rows["heads"][0]), 128, 128, 1, 1), layers)
+    for name, depth, kk in (("tree_k2_d3", 3, 2), ("tree_k3_d3", 3, 3)):
+        n_ckpt, mib = int(rows[name][0]), int(rows[name][1])
+        budget = 2 * mib << 20                                   # 2-byte -> fp32 state
+        k, d, n, nb = gt.gdn_round_tree_for_budget(fork, budget, depth)
+        assert (k, d, n) == (kk, depth, n_ckpt)
+        assert nb == n_ckpt * layers * 16 * 128 * 128 * 4 <= budget
+        # one byte less: the next smaller tree
+        k2, d2, n2, _ = gt.gdn_round_tree_for_budget(fork, budget - 1, depth)
+        assert n2 < n_ckpt
+        kw, dw, nw, nbw = gt.gdn_round_tree_for_budget(wy, budget, depth)
+        assert nw > n_ckpt and nbw <= budget
+    # k=2 d=2: 7 nodes at the page's 84 MB; the 7-node star (k=6, d=1) ties and is wider
+    k, d, n, _ = gt.gdn_round_tree_for_budget(fork, 2 * int(rows["tree_k2_d2"][1]) << 20, 2)
+    assert n == int(rows["tree_k2_d2"][0]) and (k, d) == (6, 1)
+
+
+def test_tree_for_budget_closed_cases():
+    wy = gt.make_round_desc(gt.make_desc(4, 16, 128, 128, 1, 1), 24)
+    # no budget: the root alone
+    k, d, n, nb = gt.gdn_round_tree_for_budget(wy, 0, 3)
+    assert (k, d, n) == (0, 0, 1) and nb > 0
+    # unlimited budget, depth 3: the most nodes under 64 with k <= 8 and d <= 3 is 7^2 -> 57
+    assert gt.gdn_round_tree_for_budget(wy, 1 << 60, 3)[:3] == (7, 2, 57)
+    # depth up to 63: the 64-node chain
+    assert gt.gdn_round_tree_for_budget(wy, 1 << 60, 63)[:3] == (1, 63, 64)
+    # depth 1: the widest star, 8 children
+    assert gt.gdn_round_tree_for_budget(wy, 1 << 60, 1)[:3] == (8, 1, 9)
+    # every answer is the largest complete tree that fits (enumerated here)
+    sizes = sorted({sum(k ** i for i in range(d + 1)) for k in range(1, 9) for d in range(1, 5)
+                    if sum(k ** i for i in range(d + 1)) <= 64})
+
+    def state(n):
+        g = gt.make_desc(4, 16, 128, 128, 4 * n, 64)
+        return 24 * (-(-gt.gdn_tree_workspace_bytes(g) // 256) * 256)
+
+    for budget in (1 << 20, 5 << 20, 20 << 20, 60 << 20, 200 << 20):
+        k, d, n, nb = gt.gdn_round_tree_for_budget(wy, budget, 4)
+        fits = [m for m in sizes if state(m) <= budget]
+        assert n == (max(fits) if fits else 1)
+        assert nb == state(n)
+        assert n == 1 or sum(k ** i for i in range(d + 1)) == n
+
+
+def test_accept_and_round_calls_check_before_launch():
+    lib = gt.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = gt.make_desc(2, 1, 128, 128, 10, 8)
+    acc = lambda desc, *p: lib.gdn_tree_accept_greedy(ctypes.byref(desc), *p, None)
+    assert acc(d, fake, fake, fake, fake, None, fake, fake, fake) == 1
+    assert acc(d, fake, None, fake, fake, fake, fake, fake, fake) == 1
+    d0 = gt.make_desc(0, 1, 128, 128, 0, 8)
+    assert acc(d0, None, None, None, None, None, None, None, None) == 0
+    d.max_nodes = 65
+    assert acc(d, *([fake] * 8)) == 2
+    # dk / io / mode are not read by the acceptance
+    d2 = gt.make_desc(0, 1, 96, 96, 0, 8)
+    assert acc(d2, *([None] * 8)) == 0
+    # attention layer-batched commit
+    ad = gt.make_attn_desc(2, 4, 2, 64, 10, 8, 32)
+    assert lib.gdn_tree_attn_commit_layers(ctypes.byref(ad), 0, None, None, None, None, None,
+                                           None, None) == 0
+    assert lib.gdn_tree_attn_commit_layers(ctypes.byref(ad), 2, fake, fake, fake, None, fake,
+                                           fake, None) == 1
+    lys = (gt.GdnAttnLayerIO * 2)(*[gt.GdnAttnLayerIO(*([0x1000] * 6)) for _ in range(2)])
+    lys[1].v_cache = None
+    assert lib.gdn_tree_attn_commit_layers(ctypes.byref(ad), 2, fake, fake, fake, lys, fake,
+                                           fake, None) == 1
+    # capture: host checks come first (no GPU is touched)
+    gd = gt.make_desc(2, 16, 128, 128, 10, 8)
+    r = gt.make_round_desc(gd, 2, ad, 0)
+    L = gt.gdn_round_plan(r)
+    ly = (gt.GdnLayerIO * 2)(*[gt.GdnLayerIO(*([0x1000] * 9)) for _ in range(2)])
+    io = gt.GdnRoundIO()
+    for f in ("offsets", "parents", "draft_tokens", "target_tokens", "accepted", "accept_len",
+              "next_token", "tree_status", "arena"):
+        setattr(io, f, 0x1000)
+    io.gdn_layers = ctypes.cast(ly, ctypes.POINTER(gt.GdnLayerIO))
+    io.arena_bytes = L.total_bytes - 1
+    h = ctypes.c_void_p()
+    cap = lambda: lib.gdn_round_capture(ctypes.byref(r), ctypes.byref(io), fake, ctypes.byref(h))
+    assert cap() == 4
+    io.arena_bytes = L.total_bytes
+    kinds = (ctypes.c_int32 * 2)(0, 1)
+    io.layer_kinds = ctypes.cast(kinds, ctypes.POINTER(ctypes.c_int32))
+    assert cap() == 2
+    kinds[1] = 0
+    assert lib.gdn_round_capture(ctypes.byref(r), ctypes.byref(io), None, ctypes.byref(h)) == 6
+    assert not h.value
+    assert lib.gdn_round_capture(ctypes.byref(r), None, fake, ctypes.byref(h)) == 1
+    assert lib.gdn_round_launch(None, None) == 1
+    lib.gdn_round_destroy(None)
+    assert "graph" in gt.gdn_tree_status_string(6)

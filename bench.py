@@ -317,6 +317,75 @@ def fork_delta_leg(args, gt, gi, w, layers, offsets, parents, accepted, status, 
     return out
 
 
+def sampling_accept_leg(args, gt, gi, w, offsets, parents, dev, V=151936):
+    """Sampling-mode acceptance (gdn_tree_accept_sampling) on the GDN workload's
+    trees over a Qwen-sized vocabulary: per node a target and a draft
+    distribution from peaked logits (a few favoured tokens over a spread),
+    the draft's logits the target's plus noise, children drawn from the
+    parent's draft distribution without replacement; seeded, drawn on the GPU."""
+    import numpy as np
+    import torch
+    B, T = w.B, w.T
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+
+    def peaked(noise_from=None):
+        if noise_from is None:
+            z = 1.5 * torch.randn(T, V, generator=g, device=dev)
+            idx = torch.randint(0, V, (T, 4), generator=g, device=dev)
+            boost = 8.0 + 6.0 * torch.rand(T, 4, generator=g, device=dev)
+            z.scatter_add_(1, idx, boost)
+            return z
+        return noise_from + 0.7 * torch.randn(T, V, generator=g, device=dev)
+
+    zt = peaked()
+    zd = peaked(zt)
+    P = torch.softmax(zt, dim=-1)
+    del zt
+    Q = torch.softmax(zd, dim=-1)
+    del zd
+    draft = torch.zeros(T, dtype=torch.int32, device=dev)
+    for b, tree in enumerate(w.parents_list):
+        lo = int(w.offsets[b])
+        kids = {}
+        for c in range(1, len(tree)):
+            kids.setdefault(tree[c], []).append(c)
+        for u, cs in kids.items():
+            tok = torch.multinomial(Q[lo + u], len(cs), replacement=False, generator=g)
+            draft[lo + torch.tensor(cs, device=dev)] = tok.to(torch.int32)
+    U = torch.rand(T, 2, generator=g, device=dev)
+    desc = gt.make_desc(B, 1, 128, 128, T, w.max_nodes)
+    acc, alen, nxt, status = (torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(4))
+    call = lambda: gt.gdn_tree_accept_sampling(desc, offsets, parents, draft, P, Q, U, acc, alen,
+                                               nxt, status)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    steps = 20
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    stream = torch.cuda.current_stream(dev)
+    for s_ in range(steps):
+        ev[s_][0].record(stream)
+        call()
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    if np.any(status.cpu().numpy() != 0):
+        raise RuntimeError("nonzero status in the sampling acceptance")
+    times = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+    lens = alen.cpu().numpy()
+    # rows every walk must read: the two rows of each node it visits
+    rows_bytes = int(lens.sum()) * 2 * V * 4
+    med = times[steps // 2]
+    out = {"vocab": V, "steps": steps, "us_per_call_median": round(med, 2),
+           "mean_accept_len": round(float(lens.mean()), 3),
+           "visited_rows_bytes": rows_bytes,
+           "visited_rows_GBs": round(rows_bytes / med / 1e3, 1)}
+    log(f"sampling acceptance: {out}")
+    del P, Q
+    torch.cuda.empty_cache()
+    return out
+
+
 def round_leg(args, gt, gi, w, layers, offsets, parents, dev):
     """One whole speculative round of the 32-layer hybrid stack, in model
     order (three GDN layers, then one full-attention layer, eight times):
@@ -671,6 +740,8 @@ def main():
     rnd = None
     if args.round_steps > 0 and args.mode == "wy" and w.io == "bf16":
         rnd = round_leg(args, gt, gi, w, layers, offsets, parents, dev)
+        torch.cuda.empty_cache()
+        rnd["sampling_acceptance"] = sampling_accept_leg(args, gt, gi, w, offsets, parents, dev)
 
     out = {
         "metric": METRIC, "value": round(nodes_per_s, 1), "unit": "nodes/s/layer", "n_gpus": 1,

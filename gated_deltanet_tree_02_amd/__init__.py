@@ -28,7 +28,7 @@ __all__ = [
     "prepare_verify_layers", "prepare_commit_layers",
     "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
     "prepare_attn_commit_layers",
-    "gdn_tree_accept_greedy", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
+    "gdn_tree_accept_greedy", "gdn_tree_accept_sampling", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
     "gdn_round_plan", "gdn_round_tree_for_budget", "RoundGraph",
 ]
 
@@ -38,7 +38,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE_WY, MODE_FORK, MODE_FORK_DELTA = 0, 1, 2
 MAX_NODES = 64
 TREE_STATUS = {0: "ok", 1: "bad root", 2: "bad parent", 3: "bad size", 4: "bad accepted",
-               5: "too deep", 6: "cache full"}
+               5: "too deep", 6: "cache full", 7: "bad token"}
 
 
 class GdnError(RuntimeError):
@@ -139,6 +139,9 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_attn_commit_layers.restype = I
             lib.gdn_tree_accept_greedy.argtypes = [D, P, P, P, P, P, P, P, P, P]
             lib.gdn_tree_accept_greedy.restype = I
+            lib.gdn_tree_accept_sampling.argtypes = [D, P, P, P, P, P, ctypes.c_int32, P, P, P,
+                                                     P, P, P]
+            lib.gdn_tree_accept_sampling.restype = I
             R = ctypes.POINTER(GdnRoundDesc)
             lib.gdn_round_plan.argtypes = [R, ctypes.POINTER(GdnRoundLayout)]
             lib.gdn_round_plan.restype = I
@@ -596,6 +599,30 @@ def gdn_tree_accept_greedy(desc, offsets, parents, draft_tokens, target_tokens, 
         _check(load_library().gdn_tree_accept_greedy(ctypes.byref(desc), *args,
                                                      _stream(stream, dev)),
                "gdn_tree_accept_greedy")
+
+
+def gdn_tree_accept_sampling(desc, offsets, parents, draft_tokens, target_probs, draft_probs,
+                             uniforms, accepted, accept_len, next_token, tree_status,
+                             stream=None):
+    """Rejection-sampling acceptance of every tree: target_probs and
+    draft_probs [T, V] fp32, uniforms [T, 2] fp32; int32 outputs per sequence."""
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    i32, f32 = torch.int32, torch.float32
+    V = int(target_probs.shape[-1])
+    args = [_ptr(offsets, "offsets", i32, (B + 1,), dev), _ptr(parents, "parents", i32, (T,), dev),
+            _ptr(draft_tokens, "draft_tokens", i32, (T,), dev),
+            _ptr(target_probs, "target_probs", f32, (T, V), dev),
+            _ptr(draft_probs, "draft_probs", f32, (T, V), dev), ctypes.c_int32(V),
+            _ptr(uniforms, "uniforms", f32, (T, 2), dev),
+            _ptr(accepted, "accepted", i32, (B,), dev), _ptr(accept_len, "accept_len", i32, (B,), dev),
+            _ptr(next_token, "next_token", i32, (B,), dev),
+            _ptr(tree_status, "tree_status", i32, (B,), dev)]
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_accept_sampling(ctypes.byref(desc), *args,
+                                                       _stream(stream, dev)),
+               "gdn_tree_accept_sampling")
 
 
 def make_round_desc(gdn_desc=None, n_gdn_layers=0, attn_desc=None, n_attn_layers=0) -> GdnRoundDesc:

@@ -51,7 +51,368 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
   }
 }
 
+// ---------------------------------------------------------------- sampling mode
+//
+// Multi-candidate rejection sampling down the tree (handbook, same chapter,
+// exercise on sampling with a tree). At the current node with target p and
+// draft q (the distribution its children were drawn from, without
+// replacement, in node order), candidate x is accepted iff u q_k(x) < p_k(x);
+// after rejecting it the target becomes p_{k+1} = norm(max(0, p_k - q_k))
+// (unchanged when that has no mass) and the proposal q_{k+1} = q without the
+// rejected tokens, renormalised. An accepted child starts afresh with its own
+// rows; when no candidate is accepted, one token is drawn from p_k by inverse
+// CDF and the walk ends.
+//
+// One workgroup per sequence. p_k and q_k are never stored: for any token
+// they follow from p(j), q(j) and the per-stage scalars (1/Z_i, the rejected
+// tokens, the renormalisation of q). A rejection costs one pass over the
+// node's two rows, which yields the normaliser Z as a sum of per-tile sums of
+// max(0, p_k - q_k); those tile sums, scaled by 1/Z, are the tile sums of the
+// next p, so a final draw after a rejection needs no further pass (a draw
+// with no rejection at the node takes one pass over p). The draw then finds
+// the tile where the cumulative mass crosses the target and re-reads that
+// tile alone. Each wave works on whole 256-token tiles, four tiles' loads in
+// flight at a time. Decisions are taken in fp32; sums run in a fixed order.
+
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleWaves = kSampleThreads / 64;
+constexpr int kTile = 256;                       // tokens per tile (64 lanes x 4)
+constexpr int kTilesInFlight = 4;
+constexpr int kMaxTiles = (1 << 20) / kTile;     // vocabularies up to 2^20 tokens
+
+struct Stages {
+  int k;                  // rejections so far at this node
+  const int* rem;         // rejected tokens x_0 .. x_{k-1}
+  const float* zinv;      // 1 / Z_{i+1}, or 0 when that residual had no mass
+  const float* qscale;    // q_i = q restricted to tokens not in x_0..x_{i-1}, times qscale[i]
+};
+
+__device__ __forceinline__ bool removed(int j, const int* rem, int upto) {
+  bool r = false;
+  for (int i = 0; i < upto; ++i) r |= rem[i] == j;
+  return r;
+}
+
+// (p_k(j), q_k(j)) from the row values p(j), q(j)
+__device__ __forceinline__ float2 stage_pq(float pj, float qj, int j, const Stages& s) {
+  float pk = pj;
+  for (int i = 0; i < s.k; ++i) {
+    const float qi = removed(j, s.rem, i) ? 0.f : qj * s.qscale[i];
+    if (s.zinv[i] > 0.f) pk = fmaxf(pk - qi, 0.f) * s.zinv[i];
+  }
+  const float qk = removed(j, s.rem, s.k) ? 0.f : qj * s.qscale[s.k];
+  return make_float2(pk, qk);
+}
+
+// The same for exactly K stages, their scalars in scalar registers: a pass
+// evaluates it for every token of a row. A token is in the removed set of
+// stage i when it is one of x_0 .. x_{i-1}.
+template <int K>
+struct StageRegs {
+  int rem[K > 0 ? K : 1];
+  float zinv[K > 0 ? K : 1];
+  float qscale[K + 1];
+};
+
+__device__ __forceinline__ float uniform_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+template <int K>
+__device__ __forceinline__ StageRegs<K> stage_regs(const Stages& s) {
+  StageRegs<K> r;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    r.rem[i] = __builtin_amdgcn_readfirstlane(s.rem[i]);
+    r.zinv[i] = uniform_f(s.zinv[i]);
+  }
+#pragma unroll
+  for (int i = 0; i <= K; ++i) r.qscale[i] = uniform_f(s.qscale[i]);
+  return r;
+}
+
+template <int K>
+__device__ __forceinline__ float2 stage_pq_reg(float pj, float qj, int j, const StageRegs<K>& r) {
+  float pk = pj;
+  bool gone = false;          // j in the removed set of the stage at hand
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const float qi = gone ? 0.f : qj * r.qscale[i];
+    if (r.zinv[i] > 0.f) pk = fmaxf(pk - qi, 0.f) * r.zinv[i];
+    gone |= j == r.rem[i];
+  }
+  return make_float2(pk, gone ? 0.f : qj * r.qscale[K]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// Sum over the workgroup, in a fixed order; every thread gets the result.
+__device__ __forceinline__ float block_sum(float x, float* red) {
+  x = wave_sum(x);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();                      // red is free
+  if ((threadIdx.x & 63) == 0) red[wave] = x;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kSampleWaves; ++w) t += red[w];
+  return t;
+}
+
+// What a tile pass sums per token.
+enum TileSum { kResidual, kTarget };
+
+// One pass over a node's rows: sTile[t] = sum over tile t of
+// max(0, p_k - q_k) (kResidual) or of p_k (kTarget); the thread's share of
+// the row's q mass is added to *qs. Tiles go to waves round-robin, four at a
+// time with all their loads issued first. K >= 0: exactly K rejections so far,
+// the stage scalars in registers; K < 0: any number, read from LDS.
+template <TileSum WHAT, int K>
+__device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
+                                            const float* __restrict__ qrow, int V,
+                                            const Stages& s, float* sTile, float* qs) {
+  const StageRegs<K < 0 ? 0 : K> r = stage_regs<K < 0 ? 0 : K>(s);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ntiles = (V + kTile - 1) / kTile;
+  // p_0 needs no q: a draw with no rejection reads the target row alone
+  constexpr bool need_q = WHAT == kResidual || K != 0;
+  for (int t0 = wave; t0 < ntiles; t0 += kSampleWaves * kTilesInFlight) {
+    float4 pv[kTilesInFlight], qv[kTilesInFlight];
+#pragma unroll
+    for (int u = 0; u < kTilesInFlight; ++u) {
+      const int j = (t0 + u * kSampleWaves) * kTile + 4 * lane;
+      pv[u] = qv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < V) {
+        pv[u] = *reinterpret_cast<const float4*>(prow + j);
+        if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + j);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTilesInFlight; ++u) {
+      const int t = t0 + u * kSampleWaves;
+      const int j = t * kTile + 4 * lane;
+      const float pe[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+      const float qe[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 pq = K >= 0 ? stage_pq_reg<K < 0 ? 0 : K>(pe[e], qe[e], j + e, r)
+                                 : stage_pq(pe[e], qe[e], j + e, s);
+        m += WHAT == kResidual ? fmaxf(pq.x - pq.y, 0.f) : pq.x;
+        *qs += qe[e];
+      }
+      m = wave_sum(m);
+      if (lane == 0 && t < ntiles) sTile[t] = m;
+    }
+  }
+}
+
+template <TileSum WHAT>
+__device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
+                                          const float* __restrict__ qrow, int V,
+                                          const Stages& s, float* sTile, float* qs) {
+  switch (s.k) {
+    case 0: return tile_pass_t<WHAT, 0>(prow, qrow, V, s, sTile, qs);
+    case 1: return tile_pass_t<WHAT, 1>(prow, qrow, V, s, sTile, qs);
+    case 2: return tile_pass_t<WHAT, 2>(prow, qrow, V, s, sTile, qs);
+    case 3: return tile_pass_t<WHAT, 3>(prow, qrow, V, s, sTile, qs);
+    case 4: return tile_pass_t<WHAT, 4>(prow, qrow, V, s, sTile, qs);
+    default: return tile_pass_t<WHAT, -1>(prow, qrow, V, s, sTile, qs);
+  }
+}
+
+__global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const AcceptSampleArgs a) {
+  __shared__ int sPar[64];
+  __shared__ int sTok[64];
+  __shared__ int sRem[64];
+  __shared__ float sZinv[64];
+  __shared__ float sQscale[65];
+  __shared__ float sRed[kSampleWaves];
+  __shared__ float sTile[kMaxTiles];
+  __shared__ int sInfo[4];              // status, lo, n, decision / crossing tile
+  __shared__ float sF[2];               // crossing: mass before the tile, draw target
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (tid < 64) {
+    const TreeLane tl = load_tree(b, a.T, a.max_nodes, a.offsets, a.parents, lane);
+    sPar[lane] = tl.parent;
+    const int tok = (tl.status != GDN_TREE_BAD_SIZE && lane < tl.n) ? a.draft[tl.lo + lane] : 0;
+    sTok[lane] = tok;
+    // a candidate's token indexes the probability rows: it must be a token
+    const bool bad_tok = lane >= 1 && lane < tl.n && (tok < 0 || tok >= a.V);
+    const int st = tl.status == GDN_TREE_OK && __ballot(bad_tok) != 0ull ? GDN_TREE_BAD_TOKEN
+                                                                           : tl.status;
+    if (lane == 0) {
+      sInfo[0] = st;
+      sInfo[1] = tl.lo;
+      sInfo[2] = tl.n;
+    }
+  }
+  if (tid == 0) sQscale[0] = 1.f;
+  __syncthreads();
+  const int st = sInfo[0], lo = sInfo[1], n = sInfo[2];
+  if (st != GDN_TREE_OK) {
+    if (tid == 0) {
+      a.status[b] = st;
+      a.accepted[b] = -1;
+      a.accept_len[b] = 0;
+      a.next_token[b] = -1;
+    }
+    return;
+  }
+  const int V = a.V;
+  const int ntiles = (V + kTile - 1) / kTile;
+  int cur = 0, len = 1, token = V - 1;
+  for (;;) {
+    const float* __restrict__ prow = a.p + (size_t)(lo + cur) * V;
+    const float* __restrict__ qrow = a.q + (size_t)(lo + cur) * V;
+    Stages s{0, sRem, sZinv, sQscale};
+    float qtot = 0.f, qrem = 0.f;
+    bool tiles_ready = false;             // sTile holds the current p's tile sums / Z
+    int next = -1;
+    for (int c = cur + 1; c < n; ++c) {   // children have larger indices, in node order
+      if (sPar[c] != cur) continue;       // uniform
+      const int x = sTok[c];
+      if (tid == 0) {
+        const float2 pq = stage_pq(prow[x], qrow[x], x, s);
+        sInfo[3] = a.u[2 * (size_t)(lo + c)] * pq.y < pq.x;
+      }
+      __syncthreads();
+      const bool take = sInfo[3] != 0;
+      __syncthreads();                    // sInfo[3] is read by all before reuse
+      if (take) {
+        next = c;
+        break;
+      }
+      // rejected: tile sums of the residual max(0, p_k - q_k), and its mass Z
+      float qs = 0.f;
+      tile_pass<kResidual>(prow, qrow, V, s, sTile, &qs);
+      if (s.k == 0) qtot = block_sum(qs, sRed);     // (its barriers also publish sTile)
+      else __syncthreads();
+      if (wave == 0) {
+        const int per = (ntiles + 63) / 64;
+        const int t0 = min(lane * per, ntiles), t1 = min(t0 + per, ntiles);
+        float ls = 0.f;
+        for (int t = t0; t < t1; ++t) ls += sTile[t];
+        const float z = wave_sum(ls);
+        qrem += qrow[x];
+        if (lane == 0) {
+          sZinv[s.k] = z > 0.f ? 1.f / z : 0.f;
+          sRem[s.k] = x;
+          const float left = qtot - qrem;
+          sQscale[s.k + 1] = left > 0.f ? 1.f / left : 1.f;
+        }
+      }
+      __syncthreads();
+      tiles_ready = sZinv[s.k] > 0.f;     // else p is unchanged and has no tile sums here
+      s.k += 1;
+    }
+    if (next >= 0) {
+      cur = next;
+      ++len;
+      continue;
+    }
+    // final draw from p_k: tile sums (from the last rejection's pass, scaled,
+    // or from one pass over p), the crossing tile, then the token in it
+    float scale = 1.f;
+    if (tiles_ready) {
+      scale = sZinv[s.k - 1];
+    } else {
+      float unused = 0.f;
+      tile_pass<kTarget>(prow, qrow, V, s, sTile, &unused);
+      __syncthreads();
+    }
+    if (wave == 0) {
+      // lane l owns tiles [l*per, (l+1)*per)
+      const int per = (ntiles + 63) / 64;
+      const int t0 = min(lane * per, ntiles), t1 = min(t0 + per, ntiles);
+      float ls = 0.f;
+      for (int t = t0; t < t1; ++t) ls += sTile[t] * scale;
+      float incl = ls;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
+      }
+      const float total = __shfl(incl, 63, kWave);
+      const float target = a.u[2 * (size_t)(lo + cur) + 1] * total;
+      const uint64_t over = __ballot(incl > target && t1 > t0);
+      const int L = over ? __builtin_ctzll(over) : -1;
+      if (lane == (L < 0 ? 63 : L)) {
+        float run = incl - ls;
+        int tile = t1 > t0 ? t1 - 1 : ntiles - 1;
+        float before = run;
+        for (int t = t0; t < t1; ++t) {
+          if (run + sTile[t] * scale > target) {
+            tile = t;
+            before = run;
+            break;
+          }
+          run += sTile[t] * scale;
+          before = run;
+        }
+        sInfo[3] = tile;
+        sF[0] = before;
+        sF[1] = target;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int tile = sInfo[3];
+      const float before = sF[0], target = sF[1];
+      const int j0 = tile * kTile + 4 * lane;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (j0 < V) {
+        const float4 p4 = *reinterpret_cast<const float4*>(prow + j0);
+        const float4 q4 = *reinterpret_cast<const float4*>(qrow + j0);
+        v[0] = stage_pq(p4.x, q4.x, j0, s).x;
+        v[1] = stage_pq(p4.y, q4.y, j0 + 1, s).x;
+        v[2] = stage_pq(p4.z, q4.z, j0 + 2, s).x;
+        v[3] = stage_pq(p4.w, q4.w, j0 + 3, s).x;
+      }
+      const float ls = v[0] + v[1] + v[2] + v[3];
+      float incl = ls;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
+      }
+      float run = before + incl - ls;
+      int hit = -1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        run += v[e];
+        if (hit < 0 && j0 + e < V && run > target) hit = j0 + e;
+      }
+      const uint64_t any = __ballot(hit >= 0);
+      const int first = any ? __builtin_ctzll(any) : -1;
+      const int hit_first = __shfl(hit, first < 0 ? 0 : first, kWave);
+      if (lane == 0) token = first >= 0 ? hit_first : min(tile * kTile + kTile, V) - 1;
+    }
+    break;
+  }
+  if (tid == 0) {
+    a.status[b] = GDN_TREE_OK;
+    a.accepted[b] = cur;
+    a.accept_len[b] = len;
+    a.next_token[b] = token;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_accept_sampling(const AcceptSampleArgs& a, hipStream_t s) {
+  return launch_kernel(reinterpret_cast<const void*>(&accept_sampling_kernel), (unsigned)a.B,
+                       (unsigned)kSampleThreads, s, a);
+}
 
 hipError_t launch_accept_greedy(const AcceptArgs& a, hipStream_t s) {
   return launch_kernel(reinterpret_cast<const void*>(&accept_greedy_kernel),

@@ -123,6 +123,22 @@ struct AttnCommitArgs {
   AttnCommitLayer L[kMaxLayersPerLaunch];
 };
 
+// Sampling-mode acceptance: rejection sampling of the candidates down the
+// tree against the target's and the draft's distributions per node.
+struct AcceptSampleArgs {
+  int B, T, max_nodes, V;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* draft;
+  const float* p;        // [T, V] target distribution after each node
+  const float* q;        // [T, V] draft distribution the node's children were drawn from
+  const float* u;        // [T, 2] uniforms: as a candidate, for the final draw
+  int32_t* accepted;
+  int32_t* accept_len;
+  int32_t* next_token;
+  int32_t* status;
+};
+
 // Greedy acceptance of the verified trees.
 struct AcceptArgs {
   int B, T, max_nodes;
@@ -209,6 +225,7 @@ hipError_t launch_wy_commit_layers(int io, int d, const CommitLayersArgs& a, hip
 hipError_t launch_fork_level(int io, int d, const ForkArgs& a, hipStream_t s);
 hipError_t launch_fork_commit(int d, const ForkCommitArgs& a, hipStream_t s);
 hipError_t launch_accept_greedy(const AcceptArgs& a, hipStream_t s);
+hipError_t launch_accept_sampling(const AcceptSampleArgs& a, hipStream_t s);
 
 // Kernel launch that reports its own error (no reliance on the sticky
 // last-error state, which other libraries in the process also use).

@@ -155,6 +155,31 @@ gdn_status gdn_tree_accept_greedy(const gdn_tree_desc* desc, const int32_t* offs
              : GDN_ERR_LAUNCH;
 }
 
+gdn_status gdn_tree_accept_sampling(const gdn_tree_desc* desc, const int32_t* offsets,
+                                    const int32_t* parents, const int32_t* draft_tokens,
+                                    const float* target_probs, const float* draft_probs,
+                                    int32_t vocab, const float* uniforms, int32_t* accepted,
+                                    int32_t* accept_len, int32_t* next_token,
+                                    int32_t* tree_status, void* stream) {
+  if (desc == nullptr) return GDN_ERR_NULL_PTR;
+  if (desc->num_seqs < 0 || desc->total_nodes < 0 || desc->max_nodes < 1 ||
+      desc->max_nodes > GDN_TREE_MAX_NODES)
+    return GDN_ERR_BAD_SHAPE;
+  if (vocab < 4 || vocab > (1 << 20) || vocab % 4 != 0) return GDN_ERR_UNSUPPORTED;
+  if (desc->num_seqs == 0) return GDN_OK;
+  if (!offsets || !accepted || !accept_len || !next_token || !tree_status)
+    return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 &&
+      (!parents || !draft_tokens || !target_probs || !draft_probs || !uniforms))
+    return GDN_ERR_NULL_PTR;
+  gdn::AcceptSampleArgs a{desc->num_seqs, desc->total_nodes, desc->max_nodes, vocab, offsets,
+                          parents, draft_tokens, target_probs, draft_probs, uniforms,
+                          accepted, accept_len, next_token, tree_status};
+  return gdn::launch_accept_sampling(a, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? GDN_OK
+             : GDN_ERR_LAUNCH;
+}
+
 gdn_status gdn_round_plan(const gdn_round_desc* desc, gdn_round_layout* layout) {
   if (layout == nullptr) return GDN_ERR_NULL_PTR;
   const gdn_status st = check_round(desc);

@@ -59,6 +59,39 @@ gdn_status gdn_tree_accept_greedy(const gdn_tree_desc* desc, const int32_t* offs
                                   int32_t* accept_len, int32_t* next_token,
                                   int32_t* tree_status, void* stream);
 
+/* Sampling-mode acceptance: multi-candidate rejection sampling down the tree
+ * (handbook, same chapter, exercise on sampling with a tree). The walk starts
+ * at the root. At the current node, with the target's distribution p and the
+ * draft's distribution q from which the node's children were drawn (without
+ * replacement, in node order), each child's token x is tried in node order:
+ * it is accepted iff u * q(x) < p(x), u being the child's first uniform; the
+ * walk then moves to it and starts afresh with its rows. After a rejection p
+ * becomes max(0, p - q) normalised (left unchanged if that has no mass) and
+ * q loses the rejected token and is renormalised. When no child is accepted
+ * (or the node has none), one token is drawn from the current p by inverse
+ * CDF with the node's second uniform (the first token whose cumulative mass
+ * exceeds u times the total) and the walk ends. The emitted tokens then have
+ * the target's distribution.
+ *   draft_tokens  [T] int32   token of every node (the root's is not read)
+ *   target_probs  [T, vocab]  fp32, row t: the target's distribution of the
+ *                             token after node t (softmax already applied)
+ *   draft_probs   [T, vocab]  fp32, row t: the draft's distribution t's
+ *                             children were drawn from (rows of leaves unread)
+ *   uniforms      [T, 2]      fp32 in [0, 1): node t's draw as a candidate,
+ *                             and its draw for the final token
+ *   accepted, accept_len, next_token, tree_status: as for the greedy walk;
+ *                             next_token is the drawn token; status adds
+ *                             GDN_TREE_BAD_TOKEN for a draft token outside
+ *                             [0, vocab)
+ * vocab must be a multiple of 4 in [4, 2^20] (GDN_ERR_UNSUPPORTED otherwise).
+ * Decisions are taken in fp32. */
+gdn_status gdn_tree_accept_sampling(const gdn_tree_desc* desc, const int32_t* offsets,
+                                    const int32_t* parents, const int32_t* draft_tokens,
+                                    const float* target_probs, const float* draft_probs,
+                                    int32_t vocab, const float* uniforms, int32_t* accepted,
+                                    int32_t* accept_len, int32_t* next_token,
+                                    int32_t* tree_status, void* stream);
+
 /* ------------------------------------------------------------------ round shape and arena */
 
 /* The layers of one round. Every GDN layer has the shape `gdn` (WY or FORK

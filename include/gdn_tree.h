@@ -104,7 +104,8 @@ enum {
   GDN_TREE_BAD_SIZE = 3,      /* N_b outside [1, max_nodes] or range outside [0,T]  */
   GDN_TREE_BAD_ACCEPTED = 4,  /* commit: accepted[b] outside [-1, N_b)              */
   GDN_TREE_TOO_DEEP = 5,      /* FORK modes: a node deeper than desc.max_depth      */
-  GDN_TREE_CACHE_FULL = 6     /* attention commit: the path would overflow the cache */
+  GDN_TREE_CACHE_FULL = 6,    /* attention commit: the path would overflow the cache */
+  GDN_TREE_BAD_TOKEN = 7      /* sampling acceptance: a draft token outside [0, V)  */
 };
 /* Precedence: BAD_SIZE, then BAD_ROOT, then BAD_PARENT, then TOO_DEEP (FORK
  * modes), then BAD_ACCEPTED (commit). */

@@ -271,3 +271,138 @@ def test_round_graph_replays_equal_eager_calls(mode):
             ao_ref, _ = oracle_attn(aws[0])
             assert rel_err_rows(from_dev_io(G.ao[0]).astype(np.float64), ao_ref) <= TOL["bf16"]
     graph.close()
+
+
+# ------------------------------------------------------------------ sampling-mode acceptance
+
+
+def _softmax(z):
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _sampling_case(rng, trees, V, noise=0.7):
+    """Target and draft distributions per node from peaked logits (a few
+    favoured tokens per row over a spread of small ones, as a language model's
+    next-token distribution), the draft's logits the target's plus noise;
+    draft tokens drawn from the parent's draft distribution without
+    replacement."""
+    offsets, parents = _flat(trees)
+    T = len(parents)
+    zt = 1.5 * rng.standard_normal((T, V))
+    for t in range(T):
+        top = rng.choice(V, size=4, replace=False)
+        zt[t, top] += rng.uniform(8.0, 14.0, size=4)
+    zd = zt + noise * rng.standard_normal((T, V))
+    P = _softmax(zt).astype(np.float32)
+    Q = _softmax(zd).astype(np.float32)
+    draft = np.zeros(T, np.int32)
+    for b, tr in enumerate(trees):
+        lo = offsets[b]
+        for u in range(len(tr)):
+            kids = [c for c in range(len(tr)) if tr[c] == u]
+            if kids:
+                qu = Q[lo + u].astype(np.float64)
+                draft[lo + np.array(kids)] = rng.choice(V, size=len(kids), replace=False,
+                                                        p=qu / qu.sum())
+    return offsets, parents, draft, P, Q
+
+
+def _uniforms_clear_of_thresholds(rng, offsets, parents, draft, P, Q, tries=60):
+    """Uniforms whose every decision is at least 1e-5 from its threshold in
+    the fp64 oracle (relative to the total mass for a draw): fp32 sums and
+    quotients on the GPU are within about 1e-6 of it, so both take the same
+    decisions."""
+    for _ in range(tries):
+        U = rng.random((len(parents), 2)).astype(np.float32)
+        m = []
+        oacc.accept_sampling(offsets, parents, draft, P, Q, U, margins=m)
+        if not m or min(m) >= 1e-5:
+            return U
+    raise RuntimeError("no uniforms clear of the thresholds")
+
+
+def _sampling_gpu(offsets, parents, draft, P, Q, U, max_nodes=64):
+    B, T = len(offsets) - 1, len(parents)
+    desc = gt.make_desc(B, 1, 128, 128, T, max_nodes)
+    outs = [torch.full((B,), -9, dtype=torch.int32, device="cuda") for _ in range(4)]
+    gt.gdn_tree_accept_sampling(desc, i32(offsets), i32(parents), i32(draft), f32(P), f32(Q),
+                                f32(U), *outs)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+@pytest.mark.parametrize("V", [1000, 5000])
+def test_accept_sampling_matches_oracle(V):
+    _say("accept sampling, V", V)
+    rng = np.random.default_rng(V)
+    trees = [gi.random_tree_parents(rng, 5, 30) for _ in range(20)] + [[-1], gi.chain_parents(7),
+                                                                       gi.kary_parents(8, 1)]
+    offsets, parents, draft, P, Q = _sampling_case(rng, trees, V)
+    U = _uniforms_clear_of_thresholds(rng, offsets, parents, draft, P, Q)
+    got = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    ref = oacc.accept_sampling(offsets, parents, draft, P, Q, U)
+    for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, ref):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+    _say("mean accepted length", float(ref[1].mean()))
+
+
+def test_accept_sampling_full_vocabulary():
+    """A Qwen-sized vocabulary (151,936 tokens), k=3 d=3 trees."""
+    V = 151936
+    _say("accept sampling, V", V)
+    rng = np.random.default_rng(77)
+    trees = [gi.kary_parents(3, 3)] * 6
+    offsets, parents, draft, P, Q = _sampling_case(rng, trees, V)
+    U = _uniforms_clear_of_thresholds(rng, offsets, parents, draft, P, Q)
+    got = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    ref = oacc.accept_sampling(offsets, parents, draft, P, Q, U)
+    for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, ref):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+
+
+def test_accept_sampling_status_codes():
+    _say("accept sampling status")
+    rng = np.random.default_rng(5)
+    trees = [[0, 0], [-1, 0, 1], [-1, 1], [-1], gi.kary_parents(2, 2)]
+    offsets, parents = _flat(trees)
+    V = 64
+    T = len(parents)
+    P = _softmax(rng.standard_normal((T, V))).astype(np.float32)
+    Q = _softmax(rng.standard_normal((T, V))).astype(np.float32)
+    draft = rng.integers(0, V, T).astype(np.int32)
+    draft[offsets[1] + 2] = V                 # sequence 1: a token outside the vocabulary
+    U = _uniforms_clear_of_thresholds(rng, offsets, parents, draft, P, Q)
+    got = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    ref = oacc.accept_sampling(offsets, parents, draft, P, Q, U)
+    assert got[3].tolist() == [1, 7, 2, 0, 0]
+    for g, r in zip(got, ref):
+        np.testing.assert_array_equal(g, r)
+
+
+def test_accept_sampling_emits_the_target_distribution():
+    """Many independent one-level trees (root + 3 candidates drawn from q
+    without replacement): the first emitted token -- the accepted candidate,
+    else the drawn token -- follows the root's target distribution."""
+    _say("accept sampling distribution")
+    rng = np.random.default_rng(9)
+    V, N = 8, 20000
+    p = rng.dirichlet(np.ones(V) * 0.8)
+    q = rng.dirichlet(np.ones(V) * 0.8)
+    trees = [[-1, 0, 0, 0]] * N
+    offsets, parents = _flat(trees)
+    T = len(parents)
+    P = np.tile(p.astype(np.float32), (T, 1))
+    Q = np.tile(q.astype(np.float32), (T, 1))
+    draft = np.zeros(T, np.int32)
+    for b in range(N):
+        draft[4 * b + 1:4 * b + 4] = rng.choice(V, size=3, replace=False, p=q / q.sum())
+    U = rng.random((T, 2)).astype(np.float32)
+    acc, alen, nxt, st = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    assert (st == 0).all()
+    first = np.where(alen >= 2, draft[offsets[:-1] + np.maximum(acc, 0)], nxt)
+    emp = np.bincount(first, minlength=V) / N
+    sigma = np.sqrt(p * (1 - p) / N)
+    _say("max |emp - p| / sigma", float(np.max(np.abs(emp - p) / sigma)))
+    assert np.all(np.abs(emp - p) <= 5 * sigma + 1e-12)

@@ -31,7 +31,8 @@ def test_library_exports_every_declared_symbol():
                             "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
                             "gdn_tree_attn_commit", "gdn_tree_verify_layers",
                             "gdn_tree_commit_layers", "gdn_tree_attn_commit_layers",
-                            "gdn_tree_accept_greedy", "gdn_round_plan",
+                            "gdn_tree_accept_greedy", "gdn_tree_accept_sampling",
+                            "gdn_round_plan",
                             "gdn_round_tree_for_budget", "gdn_round_capture",
                             "gdn_round_launch", "gdn_round_destroy"])
     for name in names:
@@ -378,6 +379,20 @@ def test_accept_and_round_calls_check_before_launch():
     # dk / io / mode are not read by the acceptance
     d2 = gt.make_desc(0, 1, 96, 96, 0, 8)
     assert acc(d2, *([None] * 8)) == 0
+    # sampling mode: vocabulary limits, then pointers
+    samp = lambda desc, V, *p: lib.gdn_tree_accept_sampling(ctypes.byref(desc), *p[:5], V,
+                                                            *p[5:], None)
+    d3 = gt.make_desc(2, 1, 128, 128, 10, 8)
+    ok = [fake] * 10
+    for V in (0, 2, 6, (1 << 20) + 4):
+        assert samp(d3, V, *ok) == 3, V
+    p = list(ok)
+    p[3] = None                                     # target_probs
+    assert samp(d3, 8, *p) == 1
+    p = list(ok)
+    p[6] = None                                     # accepted
+    assert samp(d3, 8, *p) == 1
+    assert samp(gt.make_desc(0, 1, 128, 128, 0, 8), 8, *([None] * 10)) == 0
     # attention layer-batched commit
     ad = gt.make_attn_desc(2, 4, 2, 64, 10, 8, 32)
     assert lib.gdn_tree_attn_commit_layers(ctypes.byref(ad), 0, None, None, None, None, None,

@@ -651,8 +651,11 @@ class RoundGraph:
     """One speculative round (every layer's verify in model order, greedy
     acceptance, every layer's commit) recorded once with gdn_round_capture on
     `stream` (a torch.cuda.Stream, not the null stream) and replayed with
-    launch(). Tensors are checked here and kept alive by the object; the graph
-    reads their contents at each launch."""
+    launch(). The tensors passed here are checked and kept alive by the
+    object; the layer descriptions (GdnLayerIO, GdnAttnLayerIO) hold raw
+    pointers only, so the tensors behind them must be passed in `keep` (or
+    otherwise outlive the object). The graph reads every buffer's contents
+    at each launch."""
 
     def __init__(self, rdesc, offsets, parents, gdn_layers, attn_layers, arena, draft_tokens,
                  target_tokens, accepted, accept_len, next_token, tree_status, cache_len=None,

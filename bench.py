@@ -88,6 +88,8 @@ def parse():
     p.add_argument("--launch", default="layers", choices=["layers", "per-layer"],
                    help="WY leg: every layer in one launch per kernel (gdn_tree_*_layers) or one "
                         "launch per layer")
+    p.add_argument("--fused-steps", type=int, default=20,
+                   help="timed rounds of the fused previous-commit + verify call (0 = skip)")
     p.add_argument("--per-layer-steps", type=int, default=5,
                    help="after a layer-batched WY leg, timed steps with one launch per layer "
                         "(0 = skip)")
@@ -275,6 +277,65 @@ def attention_leg(args, gt, gi, w_trees, dev):
     return out
 
 
+def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev):
+    """Consecutive rounds through gdn_tree_commit_verify_layers: each step
+    commits the previous round's accepted paths into the state and verifies
+    this round's trees against it, in one launch over all layers (one pass
+    over the state per round instead of verify's read plus commit's read and
+    write). Two workspaces per layer alternate between rounds; the trees and
+    inputs of every round are the workload's, the state evolves in place."""
+    import numpy as np
+    import torch
+    L = len(layers)
+    desc = gt.make_desc(w.B, w.H, w.dk, w.dv, w.T, w.max_nodes,
+                        gt.DTYPE_BF16 if w.io == "bf16" else gt.DTYPE_F32, gt.MODE_WY)
+    nbytes = gt.gdn_tree_workspace_bytes(desc)
+    ws = [[torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(L)]
+          for _ in range(2)]
+    outs = [torch.empty_like(ly["v"]) for ly in layers]
+    ios = [[gt.make_layer_io(desc, q=ly["q"], k=ly["k"], v=ly["v"], alpha=ly["alpha"],
+                             beta=ly["beta"], S0=ly["S"], o=o, S_out=ly["S"], workspace=wl)
+            for ly, o, wl in zip(layers, outs, ws[i])] for i in range(2)]
+    first = gt.prepare_verify_layers(desc, offsets, parents, ios[0], nbytes, status,
+                                     keep=(layers, ws, outs))
+    # step i commits from workspace i % 2 and verifies into the other one
+    calls = [gt.prepare_commit_verify_layers(desc, desc, offsets, parents, accepted, offsets,
+                                             parents, ios[i], nbytes, ios[1 - i], nbytes, status,
+                                             keep=(layers, ws, outs)) for i in range(2)]
+    first()
+    for i in range(args.warmup):
+        calls[i % 2]()
+    torch.cuda.synchronize()
+    steps = args.fused_steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        calls[(args.warmup + i) % 2]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    if np.any(status.cpu().numpy() != 0):
+        raise RuntimeError("nonzero status in the fused leg")
+    times = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)        # us per launch
+    med = times[steps // 2]
+    per_layer = med / L
+    fb = vb + cb - w.B * w.H * 4 * w.dv * w.dk                       # state read once
+    out = {"steps": steps, "layers_per_launch": L,
+           "launch_us_median": round(med, 2),
+           "launch_us_p10_p90": [round(times[steps // 10], 2), round(times[(9 * steps) // 10], 2)],
+           "us_per_layer": round(per_layer, 3),
+           "alg_bytes_per_layer": int(fb),
+           "achieved_GBs": round(fb / per_layer / 1e3, 1),
+           "frac_hbm": round(fb / per_layer / 1e3 / HBM_PEAK_GBS, 4),
+           "nodes_per_s_per_layer": round(w.T * L * steps / el, 1)}
+    log(f"fused previous commit + verify: {out}")
+    del ws, outs, ios, calls, first
+    torch.cuda.empty_cache()
+    return out
+
+
 def fork_delta_leg(args, gt, gi, w, layers, offsets, parents, accepted, status, max_depth, run,
                    dev):
     """The fork baseline with delta-compressed checkpoints (GDN_MODE_FORK_DELTA):
@@ -284,7 +345,8 @@ def fork_delta_leg(args, gt, gi, w, layers, offsets, parents, accepted, status, 
     region of a round arena (gdn_round_plan)."""
     import torch
     L = len(layers)
-    desc = gt.make_desc(w.B, w.H, w.dk, w.dv, w.T, w.max_nodes, gt.DTYPE_BF16,
+    desc = gt.make_desc(w.B, w.H, w.dk, w.dv, w.T, w.max_nodes,
+                        gt.DTYPE_BF16 if w.io == "bf16" else gt.DTYPE_F32,
                         gt.MODE_FORK_DELTA, max_depth)
     plan = gt.gdn_round_plan(gt.make_round_desc(desc, L))
     arena = torch.empty(plan.total_bytes, dtype=torch.uint8, device=dev)
@@ -673,6 +735,15 @@ def main():
         pver = pcom = None
         torch.cuda.empty_cache()
 
+    # ---------------------------------------- previous commit fused into verify
+    fused = None
+    if batched and args.fused_steps > 0 and L <= 24:
+        for ly in layers:
+            ly.pop("o_wy", None), ly.pop("ws_wy", None)
+        ver = com = None
+        torch.cuda.empty_cache()
+        fused = fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev)
+
     # ------------------------------------------------------------- fork baseline
     fork = None
     if args.mode == "wy" and args.fork_steps > 0:
@@ -754,7 +825,8 @@ def main():
                    "launch": "all layers per launch" if batched else "one launch per layer",
                    "parallelism": "single-gpu"},
         "roofline": roof, "kernels": kern, "cpu_baseline": cpu, "fork_baseline": fork,
-        "per_layer_launches": per_layer, "spec_state_per_request": spec, "fa_layers": fa,
+        "per_layer_launches": per_layer, "fused_rounds": fused,
+        "spec_state_per_request": spec, "fa_layers": fa,
         "round": rnd,
     }
     print(json.dumps(out), flush=True)

@@ -26,6 +26,7 @@ __all__ = [
     "gdn_tree_attn_commit", "prepare_attn_verify", "prepare_attn_commit",
     "GdnLayerIO", "make_layer_io", "gdn_tree_verify_layers", "gdn_tree_commit_layers",
     "prepare_verify_layers", "prepare_commit_layers",
+    "gdn_tree_commit_verify", "gdn_tree_commit_verify_layers", "prepare_commit_verify_layers",
     "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
     "prepare_attn_commit_layers",
     "gdn_tree_accept_greedy", "gdn_tree_accept_sampling", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
@@ -134,6 +135,12 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_verify_layers.restype = I
             lib.gdn_tree_commit_layers.argtypes = [D, ctypes.c_int32, P, P, P, LY, S, P, P]
             lib.gdn_tree_commit_layers.restype = I
+            lib.gdn_tree_commit_verify.argtypes = [D, P, P, P, P, P, S, D, P, P, P, P, P, P, P,
+                                                   P, P, P, P, S, P, P]
+            lib.gdn_tree_commit_verify.restype = I
+            lib.gdn_tree_commit_verify_layers.argtypes = [D, D, ctypes.c_int32, P, P, P, P, P,
+                                                          LY, S, LY, S, P, P]
+            lib.gdn_tree_commit_verify_layers.restype = I
             AL = ctypes.POINTER(GdnAttnLayerIO)
             lib.gdn_tree_attn_commit_layers.argtypes = [A, ctypes.c_int32, P, P, P, AL, P, P, P]
             lib.gdn_tree_attn_commit_layers.restype = I
@@ -517,6 +524,93 @@ def prepare_commit_layers(desc, offsets, parents, accepted, layers, workspace_by
             _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
     return PreparedCall("gdn_tree_commit_layers", desc, args, _stream(stream, dev),
                         (offsets, parents, accepted, tree_status, arr, tuple(keep)))
+
+
+# ------------------------------------------------- previous commit fused into verify
+
+
+def _prev_args(prev_desc, desc, prev_offsets, prev_parents, accepted, dev):
+    torch = _torch()
+    if prev_desc.num_seqs != desc.num_seqs:
+        raise ValueError("prev_desc and desc must have the same num_seqs")
+    B, pT = desc.num_seqs, prev_desc.total_nodes
+    return [_ptr(prev_offsets, "prev_offsets", torch.int32, (B + 1,), dev),
+            _ptr(prev_parents, "prev_parents", torch.int32, (pT,), dev),
+            _ptr(accepted, "accepted", torch.int32, (B,), dev)]
+
+
+def gdn_tree_commit_verify(prev_desc, prev_offsets, prev_parents, accepted, prev_k,
+                           prev_workspace, desc, offsets, parents, q, k, v, alpha, beta, S0,
+                           S_out, o, workspace, tree_status, stream=None):
+    """The previous round's commit (accepted path of the previous tree into
+    S_out, from S0) and this round's verify against S_out, in one pass over
+    the state."""
+    torch = _torch()
+    dev, va = _verify_args(desc, offsets, parents, q, k, v, alpha, beta, S0, o, workspace,
+                           tree_status)
+    B, H, dk, dv = desc.num_seqs, desc.num_heads, desc.dk, desc.dv
+    pa = _prev_args(prev_desc, desc, prev_offsets, prev_parents, accepted, dev)
+    pa += [_ptr(prev_k, "prev_k", _io_dtype(prev_desc), (prev_desc.total_nodes, H, dk), dev),
+           _ptr(prev_workspace, "prev_workspace", torch.uint8, None, dev),
+           ctypes.c_size_t(prev_workspace.numel())]
+    s_out = _ptr(S_out, "S_out", torch.float32, (B, H, dv, dk), dev)
+    # va: offsets, parents, q, k, v, alpha, beta, S0, o, workspace, bytes, tree_status
+    args = pa + [ctypes.byref(desc)] + va[:8] + [s_out] + va[8:]
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_commit_verify(ctypes.byref(prev_desc), *args,
+                                                     _stream(stream, dev)),
+               "gdn_tree_commit_verify")
+
+
+def _commit_verify_layers_args(prev_desc, desc, prev_offsets, prev_parents, accepted, offsets,
+                               parents, prev_layers, prev_workspace_bytes, layers,
+                               workspace_bytes, tree_status):
+    torch = _torch()
+    if len(prev_layers) != len(layers):
+        raise ValueError("prev_layers and layers must have the same length")
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    desc_copy = type(desc).from_buffer_copy(desc)
+    pa = _prev_args(prev_desc, desc, prev_offsets, prev_parents, accepted, dev)
+    parr, arr = _layers_array(prev_layers), _layers_array(layers)
+    args = [ctypes.byref(desc_copy), ctypes.c_int32(len(layers))] + pa + [
+        _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+        _ptr(parents, "parents", torch.int32, (T,), dev), parr,
+        ctypes.c_size_t(prev_workspace_bytes), arr, ctypes.c_size_t(workspace_bytes),
+        _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
+    return dev, args, (desc_copy, parr, arr)
+
+
+def gdn_tree_commit_verify_layers(prev_desc, desc, prev_offsets, prev_parents, accepted,
+                                  offsets, parents, prev_layers, prev_workspace_bytes, layers,
+                                  workspace_bytes, tree_status, stream=None):
+    """gdn_tree_commit_verify for every layer: `prev_layers` (GdnLayerIO made
+    with prev_desc: k and workspace) and `layers` (GdnLayerIO made with desc:
+    q, k, v, alpha, beta, S0, o, S_out, workspace)."""
+    torch = _torch()
+    dev, args, _ = _commit_verify_layers_args(prev_desc, desc, prev_offsets, prev_parents,
+                                              accepted, offsets, parents, prev_layers,
+                                              prev_workspace_bytes, layers, workspace_bytes,
+                                              tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_commit_verify_layers(ctypes.byref(prev_desc), *args,
+                                                            _stream(stream, dev)),
+               "gdn_tree_commit_verify_layers")
+
+
+def prepare_commit_verify_layers(prev_desc, desc, prev_offsets, prev_parents, accepted, offsets,
+                                 parents, prev_layers, prev_workspace_bytes, layers,
+                                 workspace_bytes, tree_status, keep=(),
+                                 stream=None) -> PreparedCall:
+    """Marshalled gdn_tree_commit_verify_layers; `keep` holds the tensors
+    behind `prev_layers` and `layers`."""
+    dev, args, held = _commit_verify_layers_args(prev_desc, desc, prev_offsets, prev_parents,
+                                                 accepted, offsets, parents, prev_layers,
+                                                 prev_workspace_bytes, layers, workspace_bytes,
+                                                 tree_status)
+    return PreparedCall("gdn_tree_commit_verify_layers", prev_desc, args, _stream(stream, dev),
+                        (prev_offsets, prev_parents, accepted, offsets, parents, tree_status,
+                         held, tuple(keep)))
 
 
 # ------------------------------------------------------------------ attention layers, batched

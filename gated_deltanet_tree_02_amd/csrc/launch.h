@@ -184,8 +184,48 @@ struct CommitLayersArgs {
   CommitLayer L[kMaxLayersPerLaunch];
 };
 
+// Commit of the previous round fused into this round's verify: before a
+// workgroup verifies its (b, h), it applies the previous round's accepted
+// path to S0 in registers (the commit's rank-|path| update), writes that
+// committed state to S_out and verifies against it, so the state is read
+// once per round instead of twice. `prev` is the previous round's tree.
+struct PendingTree {
+  int T, max_nodes;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* accepted;
+};
+struct PendingLayer {
+  const void* k;     // previous round's k [T', H, dk]
+  const float* U;    // previous round's pseudo-values [T', H, dv]
+  const float* g2;   // previous round's base-2 gate prefixes [T', H]
+  float* S_out;      // committed state (may equal the layer's S0)
+};
+constexpr int kMaxFusedLayersPerLaunch = 24;
+struct CommitVerifyLayersArgs {
+  VerifyArgs base;
+  PendingTree prev;
+  int layers;
+  VerifyLayer L[kMaxFusedLayersPerLaunch];
+  PendingLayer P[kMaxFusedLayersPerLaunch];
+};
+
 __device__ __forceinline__ VerifyArgs layer_args(const VerifyArgs& a, int) { return a; }
 __device__ __forceinline__ VerifyArgs layer_args(const VerifyLayersArgs& la, int layer) {
+  VerifyArgs a = la.base;
+  const VerifyLayer& l = la.L[layer];
+  a.q = l.q;
+  a.k = l.k;
+  a.v = l.v;
+  a.alpha = l.alpha;
+  a.beta = l.beta;
+  a.S0 = l.S0;
+  a.o = l.o;
+  a.U = l.U;
+  a.g2 = l.g2;
+  return a;
+}
+__device__ __forceinline__ VerifyArgs layer_args(const CommitVerifyLayersArgs& la, int layer) {
   VerifyArgs a = la.base;
   const VerifyLayer& l = la.L[layer];
   a.q = l.q;
@@ -212,12 +252,17 @@ __device__ __forceinline__ CommitArgs layer_args(const CommitLayersArgs& la, int
 }
 __device__ __forceinline__ const VerifyArgs& base_args(const VerifyArgs& a) { return a; }
 __device__ __forceinline__ const VerifyArgs& base_args(const VerifyLayersArgs& a) { return a.base; }
+__device__ __forceinline__ const VerifyArgs& base_args(const CommitVerifyLayersArgs& a) {
+  return a.base;
+}
 __device__ __forceinline__ const CommitArgs& base_args(const CommitArgs& a) { return a; }
 __device__ __forceinline__ const CommitArgs& base_args(const CommitLayersArgs& a) { return a.base; }
 
 hipError_t launch_wy_verify(int io, int d, int mt, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_wy_verify_layers(int io, int d, int mt, const VerifyLayersArgs& a,
                                    hipStream_t s);
+hipError_t launch_wy_commit_verify_layers(int io, int d, int mt, const CommitVerifyLayersArgs& a,
+                                          hipStream_t s);
 hipError_t launch_tree_attn(int d, const AttnArgs& a, hipStream_t s);
 hipError_t launch_tree_attn_commit(int d, const AttnCommitArgs& a, hipStream_t s);
 hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s);

@@ -200,33 +200,50 @@ __device__ __forceinline__ void t_row_in_registers(uint64_t anc, int d, const fl
       *reinterpret_cast<uint32_t*>(Tbase + (p[s2] >> 4) * TTS + (p[s2] & 15)) = pack_hi_lo(y[s2]);
 }
 
+// Path rows of the previous round staged at once when its commit is fused
+// into this verify (longer paths are applied in rounds of this many).
+constexpr int kFusedPathRows = 4;
+template <class Args>
+constexpr bool fused_args() {
+  return std::is_same<Args, CommitVerifyLayersArgs>::value;
+}
+
 // LDS bytes of one workgroup with the v staging rows unpadded (the layout
 // declared in the kernel below).
-template <class IO, int DK, int DV, int MT>
+template <class IO, int DK, int DV, int MT, bool kFused>
 constexpr int verify_lds_bytes() {
   constexpr int NP = MT * 16, EPC = 16 / (int)sizeof(IO), CPR = DK / EPC, CPV = DV / EPC;
   constexpr int st1 = 16 * (2 * NP * (CPR + 1) + NP * CPV);
   constexpr int st2 = NP * DV * (4 + (int)sizeof(IO));
   constexpr int nqt = MT * (MT + 1) / 2;
+  constexpr int path = kFused ? kFusedPathRows * (16 * CPR + 4 * DV) : 0;
   return (st1 > st2 ? st1 : st2) + 4 * (NP * (NP + 1) / 2) + 4 * 256 * nqt +
-         (int)sizeof(IO) * 256 * nqt + 16 * NP;
+         (int)sizeof(IO) * 256 * nqt + 16 * NP + path;
 }
 // Three workgroups per CU (6 waves per SIMD, at most 80 VGPRs, the v rows
 // staged unpadded) where the LDS allows three; else the default register
 // budget and padded v rows, which read faster at the same occupancy.
-template <class IO, int DK, int DV, int MT>
+template <class IO, int DK, int DV, int MT, bool kFused>
 constexpr bool verify_three_per_cu() {
-  return verify_lds_bytes<IO, DK, DV, MT>() <= 52 * 1024;
+  return verify_lds_bytes<IO, DK, DV, MT, kFused>() <= 52 * 1024;
 }
-template <class IO, int DK, int DV, int MT>
+template <class IO, int DK, int DV, int MT, bool kFused>
 constexpr int verify_waves_per_simd() {
-  return verify_three_per_cu<IO, DK, DV, MT>() ? 6 : 1;
+  return verify_three_per_cu<IO, DK, DV, MT, kFused>() ? 6 : 1;
+}
+
+// Rank p (0 = the root) of a path given as a node bit set: its p-th lowest bit.
+__device__ __forceinline__ int nth_path_node(uint64_t path, int p) {
+  for (int j = 0; j < p; ++j) path &= path - 1ull;
+  return path ? __builtin_ctzll(path) : 0;
 }
 
 // Args: VerifyArgs (one layer) or VerifyLayersArgs (workgroup i takes layer
-// i / (B * H) of a layer-batched launch).
+// i / (B * H) of a layer-batched launch), or CommitVerifyLayersArgs (the same,
+// with the previous round's commit applied to S0 first).
 template <class IO, int DK, int DV, int MT, class Args>
-__global__ __launch_bounds__(64 * kVerifyWaves, (verify_waves_per_simd<IO, DK, DV, MT>()))
+__global__ __launch_bounds__(64 * kVerifyWaves,
+                             (verify_waves_per_simd<IO, DK, DV, MT, fused_args<Args>()>()))
 void wy_verify_kernel(const Args args) {
   constexpr int NW = kVerifyWaves;
   constexpr int NT = 64 * NW;                 // threads
@@ -243,7 +260,7 @@ void wy_verify_kernel(const Args args) {
   constexpr int SWZ = DV >= 64 ? 1 : 0;
   // v rows: unpadded with the swizzle above when that buys the third
   // workgroup per CU, else one spare chunk per row (like the k / q rows)
-  constexpr bool kVSwz = verify_three_per_cu<IO, DK, DV, MT>();
+  constexpr bool kVSwz = verify_three_per_cu<IO, DK, DV, MT, fused_args<Args>()>();
   constexpr int kVPad = kVSwz ? 0 : 1;
   constexpr int TTW = 16;                     // row of a stored 16x16 tile
   constexpr int TTS = 16 * TTW;               // stored tile size
@@ -252,8 +269,13 @@ void wy_verify_kernel(const Args args) {
   constexpr int NSTAGE = NP * (2 * CPR + CPV);  // staged q, k, v chunks
   constexpr int NLD = (NSTAGE + NT - 1) / NT;   // per thread (a spare one repeats the last)
   constexpr bool kF32 = std::is_same<IO, float>::value;
+  constexpr bool kFused = fused_args<Args>();
+  constexpr int PCH = kFusedPathRows;
+  constexpr int PKC = PCH * CPR;              // io chunks of the staged path k rows
+  constexpr int PUC = PCH * DV / 4;           // float4 of their scaled pseudo-values
   using io = io_traits<IO>;
   static_assert(DVT <= NW, "one 16-column dv tile per wave");
+  static_assert(PKC + PUC <= NT, "one staged path piece per thread");
 
   struct Stage1 {             // until the state products are done
     uint4 k[NP * (CPR + 1)];
@@ -283,6 +305,10 @@ void wy_verify_kernel(const Args args) {
   __shared__ uint64_t sAnc[NP];
   __shared__ float sG2[NP];
   __shared__ float sBeta[NP];
+  // previous round's path (fused commit): k rows as io chunks, and the
+  // pseudo-values scaled by their path coefficients
+  __shared__ __align__(16) uint4 sPK[kFused ? PKC : 1];
+  __shared__ __align__(16) float sPW[kFused ? PCH * DV : 4];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -310,6 +336,33 @@ void wy_verify_kernel(const Args args) {
   }
   const int n = hi - lo;
   const int mt = (n + 15) >> 4;
+
+  // 1z. (fused commit) the previous round's node range and accepted node,
+  // and one lane per previous node: its parent and gate prefix.
+  int plo = 0, pn = 1, pacc = -1, pst = GDN_TREE_OK, ppar_raw = -1;
+  float pg2_raw = 0.f;
+  const IO* __restrict__ pk = nullptr;
+  const float* __restrict__ pU = nullptr;
+  float* __restrict__ S_out = nullptr;
+  if constexpr (kFused) {
+    const PendingTree& pt = args.prev;
+    const PendingLayer& pl = args.P[layer];
+    pk = static_cast<const IO*>(pl.k);
+    pU = pl.U;
+    S_out = pl.S_out;
+    const int plo_r = pt.offsets[b];
+    const int phi_r = pt.offsets[b + 1];
+    pacc = pt.accepted[b];
+    if (plo_r < 0 || phi_r > pt.T || phi_r - plo_r < 1 || phi_r - plo_r > pt.max_nodes) {
+      pst = GDN_TREE_BAD_SIZE;
+    } else {
+      plo = plo_r;
+      pn = phi_r - plo_r;
+    }
+    const int pl_lane = lane < pn ? lane : 0;
+    ppar_raw = pt.parents[plo + pl_lane];
+    pg2_raw = pl.g2[(size_t)(plo + pl_lane) * H + h];
+  }
 
   // ---- 1. every global read of the workgroup, issued before any is used
   // (addresses clamped into the sequence, so the issue is unconditional).
@@ -372,6 +425,32 @@ void wy_verify_kernel(const Args args) {
   float g2;
   // (on a bad tree the scan still terminates; its results are not used)
   path_scan(par, lane, n, lane < n ? gate_log2(alpha_l) : 0.f, anc, g2);
+  // (fused commit) the previous tree's checks, then the accepted node's path
+  // (root first), its gate prefix and the path coefficients 2^(gA - g2_i)
+  uint64_t ppath = 0ull;
+  float pgA = 0.f, pcoef = 0.f;
+  if constexpr (kFused) {
+    const int ppar = lane < pn ? ppar_raw : -1;
+    int ps = pst;
+    if (ps == GDN_TREE_OK) {
+      if (__shfl(ppar, 0, kWave) != -1)
+        ps = GDN_TREE_BAD_ROOT;
+      else if (__ballot(lane >= 1 && lane < pn && (ppar < 0 || ppar >= lane)) != 0ull)
+        ps = GDN_TREE_BAD_PARENT;
+      else if (pacc < -1 || pacc >= pn)
+        ps = GDN_TREE_BAD_ACCEPTED;
+    }
+    ps = __builtin_amdgcn_readfirstlane(ps);
+    if (st == GDN_TREE_OK) st = ps;
+    if (st == GDN_TREE_OK && pacc >= 0) {
+      uint64_t panc;
+      float unused;
+      path_scan(ppar, lane, pn, 0.f, panc, unused);
+      ppath = shfl_u64(panc, pacc);
+      pgA = __shfl(pg2_raw, pacc, kWave);
+      pcoef = exp2f(pgA - pg2_raw);
+    }
+  }
   if (wave == 0 && lane < NP) {
     sAnc[lane] = anc;
     sG2[lane] = g2;
@@ -382,6 +461,24 @@ void wy_verify_kernel(const Args args) {
   // now, once the q, k, v rows have arrived: when every resident workgroup
   // loads at once, the rows that the first phases need are not queued behind
   // the state, which then streams in while the node products are computed.
+  // 1d. (fused commit) the first PCH path rows: one 16-byte piece per thread
+  // (a k chunk, or four pseudo-values), issued before the state so that
+  // waiting for them does not wait for the state.
+  const int P = kFused ? __popcll(ppath) : 0;
+  const int pidx = tid < PKC ? tid / CPR : (tid - PKC) / (DV / 4);
+  uint4 pld = make_uint4(0u, 0u, 0u, 0u);
+  float pcf = 0.f;
+  if constexpr (kFused) {
+    const int pnode = nth_path_node(ppath, pidx < P ? pidx : 0);
+    pcf = __shfl(pcoef, pnode, kWave);
+    if (pidx < P && tid < PKC + PUC) {
+      const size_t prow = (size_t)(plo + pnode) * H + h;
+      pld = tid < PKC
+                ? *reinterpret_cast<const uint4*>(pk + prow * DK + (tid - pidx * CPR) * EPC)
+                : *reinterpret_cast<const uint4*>(pU + prow * DV +
+                                                  4 * (tid - PKC - pidx * (DV / 4)));
+    }
+  }
   float4 sraw[KS][2];
   {
     const float* rowp = a.S0 + (size_t)bh * DV * DK + (size_t)(16 * jt + l16) * DK + 8 * g;
@@ -452,6 +549,20 @@ void wy_verify_kernel(const Args args) {
       }
     }
   }
+  if constexpr (kFused) {
+    if (pidx < P && tid < PKC + PUC) {
+      if (tid < PKC) {
+        sPK[tid] = pld;
+      } else {
+        float4 u = __builtin_bit_cast(float4, pld);
+        u.x *= pcf;
+        u.y *= pcf;
+        u.z *= pcf;
+        u.w *= pcf;
+        reinterpret_cast<float4*>(sPW)[tid - PKC] = u;
+      }
+    }
+  }
   __syncthreads();
 
   // ---- 4. wave 0: T = (I + A_kk)^-1, one lane per row. Row t is nonzero only
@@ -511,6 +622,69 @@ void wy_verify_kernel(const Args args) {
   // wave's 16 dv columns (A = staged k / q rows, B = S0 hi/lo); result lane
   // holds column r = 16w + lane%16 of nodes t = 16m + 4g + e. Then
   // R = diag(beta)(V - diag(G) X) and G*Y.
+  // ---- 4b. (fused commit) S0 <- G_a S0 + sum over the accepted path of
+  // (G_a/G_i) u_i k_i^T on this wave's fragment (row 16w + lane%16, columns
+  // 32s + 8g .. +7), written out as the committed state and verified against.
+  if constexpr (kFused) {
+    const float GA = pacc >= 0 ? exp2f(pgA) : 1.f;
+    if (owns) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sraw[s][0].x *= GA; sraw[s][0].y *= GA; sraw[s][0].z *= GA; sraw[s][0].w *= GA;
+        sraw[s][1].x *= GA; sraw[s][1].y *= GA; sraw[s][1].z *= GA; sraw[s][1].w *= GA;
+      }
+    }
+    for (int p0 = 0; p0 < P; p0 += PCH) {
+      const int pc = P - p0 < PCH ? P - p0 : PCH;
+      if (p0 > 0) {
+        // a path longer than PCH rows (deep chains): the next rows, staged
+        // by the whole workgroup once the previous ones are consumed
+        __syncthreads();
+        const int pnode = nth_path_node(ppath, p0 + (pidx < pc ? pidx : 0));
+        const float cf = __shfl(pcoef, pnode, kWave);
+        if (pidx < pc && tid < PKC + PUC) {
+          const size_t prow = (size_t)(plo + pnode) * H + h;
+          if (tid < PKC) {
+            sPK[tid] = *reinterpret_cast<const uint4*>(pk + prow * DK + (tid - pidx * CPR) * EPC);
+          } else {
+            float4 u = *reinterpret_cast<const float4*>(pU + prow * DV +
+                                                        4 * (tid - PKC - pidx * (DV / 4)));
+            u.x *= cf;
+            u.y *= cf;
+            u.z *= cf;
+            u.w *= cf;
+            reinterpret_cast<float4*>(sPW)[tid - PKC] = u;
+          }
+        }
+        __syncthreads();
+      }
+      if (owns) {
+        const int r = 16 * jt + l16;
+        for (int p = 0; p < pc; ++p) {
+          const float w = sPW[p * DV + r];
+          const IO* krow = reinterpret_cast<const IO*>(sPK) + p * DK + 8 * g;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const float4 k0 = io::load4(krow + 32 * s);
+            const float4 k1 = io::load4(krow + 32 * s + 4);
+            sraw[s][0].x += w * k0.x; sraw[s][0].y += w * k0.y;
+            sraw[s][0].z += w * k0.z; sraw[s][0].w += w * k0.w;
+            sraw[s][1].x += w * k1.x; sraw[s][1].y += w * k1.y;
+            sraw[s][1].z += w * k1.z; sraw[s][1].w += w * k1.w;
+          }
+        }
+      }
+    }
+    if (owns && !(pacc < 0 && S_out == a.S0)) {
+      float* rowo = S_out + (size_t)bh * DV * DK + (size_t)(16 * jt + l16) * DK + 8 * g;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        *reinterpret_cast<float4*>(rowo + 32 * s) = sraw[s][0];
+        *reinterpret_cast<float4*>(rowo + 32 * s + 4) = sraw[s][1];
+      }
+    }
+  }
+
   f32x4 rX[MT], rY[MT];
   if (owns) {
 #pragma unroll
@@ -631,6 +805,9 @@ inline unsigned grid_of(const VerifyArgs& a) { return (unsigned)(a.B * a.H); }
 inline unsigned grid_of(const VerifyLayersArgs& a) {
   return (unsigned)(a.base.B * a.base.H * a.layers);
 }
+inline unsigned grid_of(const CommitVerifyLayersArgs& a) {
+  return (unsigned)(a.base.B * a.base.H * a.layers);
+}
 
 template <class IO, int D, int MT, class Args>
 hipError_t launch_t(const Args& a, hipStream_t s) {
@@ -667,6 +844,11 @@ hipError_t launch_wy_verify(int io, int d, int mt, const VerifyArgs& a, hipStrea
 
 hipError_t launch_wy_verify_layers(int io, int d, int mt, const VerifyLayersArgs& a,
                                    hipStream_t s) {
+  return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, mt, a, s) : launch_d<float>(d, mt, a, s);
+}
+
+hipError_t launch_wy_commit_verify_layers(int io, int d, int mt, const CommitVerifyLayersArgs& a,
+                                          hipStream_t s) {
   return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, mt, a, s) : launch_d<float>(d, mt, a, s);
 }
 

@@ -204,6 +204,58 @@ gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
                                   const int32_t* accepted, const gdn_layer_io* layers,
                                   size_t workspace_bytes, int32_t* tree_status, void* stream);
 
+/* Fused round boundary: the previous round's commit followed by this round's
+ * verify, in one pass over the state.
+ *
+ * A serving loop runs, per GDN layer, gdn_tree_commit for round r (the
+ * accepted path of r's tree, fork page section 5; TreeWY abstract: only the
+ * accepted state is rebuilt) and later gdn_tree_verify for round r+1 on the
+ * committed state (fork page section 7, steps 4 then 2 of the next round).
+ * Both read the (B,H,dv,dk) state; this call reads it once: every
+ * workgroup applies the previous commit's update
+ *     S = G_a S0 + sum_{i in path(a)} (G_a/G_i) u_i k_i^T
+ * to its slice of S0 in registers, writes S to S_out and verifies this
+ * round's tree against S. The results are those of
+ *     gdn_tree_commit(prev_desc, prev_offsets, prev_parents, accepted,
+ *                     prev_k, S0, S_out, prev_workspace, ...)
+ *     gdn_tree_verify(desc, offsets, parents, q, k, v, alpha, beta,
+ *                     S_out, o, workspace, ...)
+ * up to fp32 rounding order, with these differences:
+ *  - prev_desc describes the previous round (its own total_nodes and
+ *    max_nodes); num_seqs, num_heads, dk, dv and io_dtype must equal desc's,
+ *    and both modes must be GDN_MODE_WY (else GDN_ERR_BAD_SHAPE /
+ *    GDN_ERR_UNSUPPORTED). prev_desc->total_nodes must be >= 1 when
+ *    num_seqs > 0.
+ *  - prev_workspace is the previous verify's workspace (U and g unchanged
+ *    since), prev_k its k rows [T',H,dk]. The two workspaces must not overlap
+ *    (checked: GDN_ERR_BAD_SHAPE); callers alternate two buffers.
+ *  - S_out may equal S0 (in place) or must not overlap it; S_out must not
+ *    overlap any other argument.
+ *  - tree_status [B] receives one code per sequence: this round's tree checks
+ *    (BAD_SIZE, BAD_ROOT, BAD_PARENT), then the previous tree's and
+ *    BAD_ACCEPTED for accepted[b] outside [-1, N'_b). A sequence with a
+ *    nonzero code gets zero o rows and a zero workspace (when its node range
+ *    is valid) and its S_out is not written.
+ *  - accepted[b] == -1 keeps S0 (S_out = S0; nothing is written in place).
+ * The layer-batched form takes HOST arrays of n_layers entries: prev_layers
+ * (fields k and workspace used) and layers (q, k, v, alpha, beta, S0, o,
+ * S_out, workspace). All layers share both trees and accepted. */
+gdn_status gdn_tree_commit_verify(const gdn_tree_desc* prev_desc, const int32_t* prev_offsets,
+                                  const int32_t* prev_parents, const int32_t* accepted,
+                                  const void* prev_k, const void* prev_workspace,
+                                  size_t prev_workspace_bytes, const gdn_tree_desc* desc,
+                                  const int32_t* offsets, const int32_t* parents, const void* q,
+                                  const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* S0, float* S_out, void* o,
+                                  void* workspace, size_t workspace_bytes, int32_t* tree_status,
+                                  void* stream);
+gdn_status gdn_tree_commit_verify_layers(
+    const gdn_tree_desc* prev_desc, const gdn_tree_desc* desc, int32_t n_layers,
+    const int32_t* prev_offsets, const int32_t* prev_parents, const int32_t* accepted,
+    const int32_t* offsets, const int32_t* parents, const gdn_layer_io* prev_layers,
+    size_t prev_workspace_bytes, const gdn_layer_io* layers, size_t workspace_bytes,
+    int32_t* tree_status, void* stream);
+
 /* Static text for a gdn_status value. */
 const char* gdn_tree_status_string(int status);
 

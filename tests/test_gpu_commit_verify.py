@@ -1,0 +1,239 @@
+"""GPU parity of the fused round boundary, gdn_tree_commit_verify[_layers]: the
+previous round's commit and this round's verify in one pass over the state.
+
+Reference: the oracle's commit of the previous tree's accepted path (fp64 path
+replay from S0), then the oracle's verify of this round's tree from that
+committed state. Agreement bar as for the separate calls: 1e-4 (fp32 io) or
+2e-2 (bf16 io) normwise relative error per output vector and per (sequence,
+head) state; status codes bit-exact. The fused results are also compared with
+the library's own separate commit + verify, and the layer-batched, in-place
+and out-of-place forms with each other (bit-identical)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_tree_02_amd as gt
+import gdn_inputs as gi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # the -m gpu suite only runs on a GPU machine
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_util import (TOL, DeviceLayer, rel_err_rows, rel_err_states,  # noqa: E402
+                      sub_workload)
+
+
+def _say(*a):
+    print("[gpu-commit-verify]", *a, flush=True)
+
+
+def _fused(P, C, S0, S_out):
+    """One fused call: commit P's accepted paths (S0 -> S_out), verify C on S_out."""
+    gt.gdn_tree_commit_verify(P.desc, P.offsets, P.parents, P.accepted, P.k, P.ws, C.desc,
+                              C.offsets, C.parents, C.q, C.k, C.v, C.alpha, C.beta, S0, S_out,
+                              C.o, C.ws, C.status)
+
+
+def _oracle_rounds(wp, wc, layer=0):
+    S_ref, stc = oracle.commit(wp.offsets, wp.parents, wp.accepted, wp.k[layer], wp.v[layer],
+                               wp.alpha[layer], wp.beta[layer], wp.S0[layer])
+    o_ref, st = oracle.verify(wc.offsets, wc.parents, wc.q[layer], wc.k[layer], wc.v[layer],
+                              wc.alpha[layer], wc.beta[layer], S_ref)
+    return S_ref, stc, o_ref, st
+
+
+def _case(prev_trees, cur_trees, H, d, io, seed, force_acc=None):
+    wp = gi.make_workload(prev_trees, H, d, d, io=io, seed=seed)
+    wc = gi.make_workload(cur_trees, H, d, d, io=io, seed=seed + 1000)
+    for b, a in (force_acc or {}).items():   # -1: the state is kept as it is
+        wp.accepted[b] = a
+    return wp, wc
+
+
+CASES = {
+    # previous k=3 d=3 trees (three 16-node tiles), this round ragged up to 64 nodes
+    "kary_then_ragged": lambda: _case(
+        [gi.kary_parents(3, 3)] * 8,
+        [gi.random_tree_parents(np.random.default_rng(7 + i)) for i in range(8)],
+        4, 128, "bf16", 11, force_acc={2: -1}),
+    # a deep previous chain: accepted paths longer than one staging round
+    "deep_chain_then_kary": lambda: _case(
+        [gi.chain_parents(n) for n in (12, 9, 5, 1, 30)], [gi.kary_parents(2, 2)] * 5,
+        4, 64, "bf16", 12, force_acc={0: 11, 1: 6, 4: 29}),
+    "tiny_fp32": lambda: _case([[-1, 0, 0, 1, 1, 2, 2]] * 2, [gi.kary_parents(2, 3)] * 2,
+                               2, 32, "f32", 13, force_acc={0: 3, 1: -1}),
+    "ragged_fp32_d128": lambda: _case(
+        [gi.random_tree_parents(np.random.default_rng(30 + i), 16, 40) for i in range(4)],
+        [gi.random_tree_parents(np.random.default_rng(40 + i), 2, 20) for i in range(4)],
+        2, 128, "f32", 14),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_commit_verify_matches_oracle(name):
+    wp, wc = CASES[name]()
+    deep = max(len(gi.path_to_root(p, a)) if a >= 0 else 0
+               for p, a in zip(wp.parents_list, wp.accepted))
+    _say(f"{name}: B={wp.B} H={wp.H} d={wp.dk} io={wp.io} prev T={wp.T} cur T={wc.T} "
+         f"longest accepted path {deep}")
+    P, C = DeviceLayer(wp, 0), DeviceLayer(wc, 0)
+    P.verify()
+    S0 = P.S0.clone()
+    S_out = torch.full_like(S0, float("nan"))
+    _fused(P, C, S0, S_out)
+    torch.cuda.synchronize()
+    S_ref, stc, o_ref, st = _oracle_rounds(wp, wc)
+    assert np.all(stc == 0) and np.all(st == 0)
+    assert np.all(C.status.cpu().numpy() == 0)
+    tol = TOL[wp.io]
+    e_s = rel_err_states(S_out.cpu().numpy(), S_ref)
+    e_o = rel_err_rows(C.o_np(), o_ref)
+    _say(f"{name}: S err {e_s:.3e}, o err {e_o:.3e} (tol {tol})")
+    assert e_s <= tol and e_o <= tol
+    # accepted = -1 keeps the state bit for bit
+    for b in np.nonzero(wp.accepted < 0)[0]:
+        assert torch.equal(S_out[b], S0[b])
+    # the library's separate commit, then verify on the committed state
+    S_sep = torch.full_like(S0, float("nan"))
+    P.commit(S_out=S_sep)
+    C2 = DeviceLayer(wc, 0)
+    C2.S0 = S_sep
+    C2.verify()
+    torch.cuda.synchronize()
+    e_ss = rel_err_states(S_out.cpu().numpy(), S_sep.cpu().numpy())
+    e_oo = rel_err_rows(C.o_np(), C2.o_np())
+    _say(f"{name}: fused vs separate calls: S {e_ss:.3e}, o {e_oo:.3e}")
+    assert e_ss <= 1e-6
+    assert e_oo <= (1e-6 if wp.io == "f32" else 8e-3)
+    U, g2 = C.wy_parts()
+    U2, g22 = C2.wy_parts()
+    assert rel_err_rows(U, U2) <= 1e-5 and np.array_equal(g2, g22)
+
+
+def test_commit_verify_in_place_equals_out_of_place():
+    wp, wc = CASES["kary_then_ragged"]()
+    P, C1, C2 = DeviceLayer(wp, 0), DeviceLayer(wc, 0), DeviceLayer(wc, 0)
+    P.verify()
+    S_keep = P.S0.clone()
+    S_out = torch.full_like(S_keep, float("nan"))
+    _fused(P, C1, P.S0, S_out)
+    S_in = S_keep.clone()
+    _fused(P, C2, S_in, S_in)
+    torch.cuda.synchronize()
+    assert torch.equal(P.S0, S_keep)            # out of place leaves S0 alone
+    assert torch.equal(S_in, S_out)
+    assert torch.equal(C1.o, C2.o)
+    for x, y in zip(C1.wy_parts(), C2.wy_parts()):
+        assert np.array_equal(x, y)
+
+
+def test_commit_verify_layers_bit_identical_to_single_calls():
+    L = 3
+    rng = np.random.default_rng(5)
+    prev_trees = [gi.random_tree_parents(rng, 8, 48) for _ in range(6)]
+    cur_trees = [gi.random_tree_parents(rng, 8, 48) for _ in range(6)]
+    wp = gi.make_workload(prev_trees, 4, 128, 128, io="bf16", layers=L, seed=21)
+    wc = gi.make_workload(cur_trees, 4, 128, 128, io="bf16", layers=L, seed=22)
+    Ps = [DeviceLayer(wp, l) for l in range(L)]
+    Cs = [DeviceLayer(wc, l) for l in range(L)]
+    Cb = [DeviceLayer(wc, l) for l in range(L)]
+    for P in Ps:
+        P.verify()
+    S_single = [P.S0.clone() for P in Ps]
+    S_batch = [P.S0.clone() for P in Ps]
+    for P, C, S in zip(Ps, Cs, S_single):
+        _fused(P, C, S, S)
+    pio = [gt.make_layer_io(P.desc, k=P.k, workspace=P.ws) for P in Ps]
+    cio = [gt.make_layer_io(C.desc, q=C.q, k=C.k, v=C.v, alpha=C.alpha, beta=C.beta, S0=S,
+                            o=C.o, S_out=S, workspace=C.ws) for C, S in zip(Cb, S_batch)]
+    status = torch.full((wp.B,), -7, dtype=torch.int32, device="cuda")
+    gt.gdn_tree_commit_verify_layers(Ps[0].desc, Cb[0].desc, Ps[0].offsets, Ps[0].parents,
+                                     Ps[0].accepted, Cb[0].offsets, Cb[0].parents, pio,
+                                     Ps[0].ws.numel(), cio, Cb[0].ws.numel(), status)
+    torch.cuda.synchronize()
+    assert np.all(status.cpu().numpy() == 0)
+    for l in range(L):
+        assert torch.equal(S_single[l], S_batch[l]), l
+        assert torch.equal(Cs[l].o, Cb[l].o), l
+        for x, y in zip(Cs[l].wy_parts(), Cb[l].wy_parts()):
+            assert np.array_equal(x, y), l
+
+
+def test_commit_verify_status_codes():
+    """Previous-tree and accepted-node failures are reported in this round's
+    status; the sequence's o rows and workspace are zero and its state is not
+    written. Other sequences are unaffected."""
+    prev_trees = [gi.kary_parents(2, 2)] * 5
+    cur_trees = [gi.kary_parents(2, 2)] * 5
+    wp = gi.make_workload(prev_trees, 2, 64, 64, io="bf16", seed=31)
+    wc = gi.make_workload(cur_trees, 2, 64, 64, io="bf16", seed=32)
+    wp.accepted[:] = [3, 9, 4, 5, -1]        # seq 1: outside [-1, 7)
+    P, C = DeviceLayer(wp, 0), DeviceLayer(wc, 0)
+    P.verify()
+    torch.cuda.synchronize()
+    assert np.all(P.status.cpu().numpy() == 0)
+    # seq 2: the previous tree is rewritten with a bad parent after its verify
+    par = P.parents.cpu().numpy()
+    par[wp.offsets[2] + 3] = 5
+    P.parents.copy_(torch.from_numpy(par))
+    # seq 3: this round's tree has a bad root
+    cpar = C.parents.cpu().numpy()
+    cpar[wc.offsets[3]] = 0
+    C.parents.copy_(torch.from_numpy(cpar))
+    S0 = P.S0.clone()
+    S_out = torch.full_like(S0, float("nan"))
+    _fused(P, C, S0, S_out)
+    torch.cuda.synchronize()
+    st = C.status.cpu().numpy()
+    # codes: 4 accepted out of range, 2 bad parent, 1 bad root
+    assert st.tolist() == [0, 4, 2, 1, 0]
+    o = C.o_np()
+    U, g2 = C.wy_parts()
+    for b in (1, 2, 3):
+        rows = slice(wc.offsets[b], wc.offsets[b + 1])
+        assert np.all(o[rows] == 0) and np.all(U[rows] == 0) and np.all(g2[rows] == 0)
+        assert torch.isnan(S_out[b]).all()
+    assert torch.equal(S_out[4], S0[4])
+    # sequences 0 and 4 against the oracle
+    keep = [0, 4]
+    sp, sc = sub_workload(wp, keep), sub_workload(wc, keep)
+    S_ref, _, o_ref, _ = _oracle_rounds(sp, sc)
+    rows = np.concatenate([np.arange(wc.offsets[b], wc.offsets[b + 1]) for b in keep])
+    assert rel_err_states(S_out.cpu().numpy()[keep], S_ref) <= TOL["bf16"]
+    assert rel_err_rows(o[rows], o_ref) <= TOL["bf16"]
+
+
+def test_commit_verify_c4_full_size_sampled():
+    """Two consecutive rounds of the k=3 d=3, B=64, 16-head, 128x128 workload
+    over all 24 GDN layers in one layer-batched launch (the benchmark's
+    configuration); the oracle recomputes sampled (layer, sequence) units."""
+    wp = gi.make_config("c4")
+    wc = gi.make_config("c4", seed=104)
+    L = wp.layers
+    Ps = [DeviceLayer(wp, l) for l in range(L)]
+    for P in Ps:
+        P.verify()
+    Cs = [DeviceLayer(wc, l) for l in range(L)]
+    pio = [gt.make_layer_io(P.desc, k=P.k, workspace=P.ws) for P in Ps]
+    cio = [gt.make_layer_io(C.desc, q=C.q, k=C.k, v=C.v, alpha=C.alpha, beta=C.beta, S0=P.S0,
+                            o=C.o, S_out=P.S0, workspace=C.ws) for P, C in zip(Ps, Cs)]
+    status = torch.full((wp.B,), -7, dtype=torch.int32, device="cuda")
+    gt.gdn_tree_commit_verify_layers(Ps[0].desc, Cs[0].desc, Ps[0].offsets, Ps[0].parents,
+                                     Ps[0].accepted, Cs[0].offsets, Cs[0].parents, pio,
+                                     Ps[0].ws.numel(), cio, Cs[0].ws.numel(), status)
+    torch.cuda.synchronize()
+    assert np.all(status.cpu().numpy() == 0)
+    rng = np.random.default_rng(41)
+    layers = sorted(rng.choice(L, 2, replace=False).tolist())
+    seqs = sorted(rng.choice(wp.B, 5, replace=False).tolist())
+    rows = np.concatenate([np.arange(wc.offsets[b], wc.offsets[b + 1]) for b in seqs])
+    for layer in layers:
+        sp = sub_workload(wp, seqs, layers=[layer])
+        sc = sub_workload(wc, seqs, layers=[layer])
+        S_ref, _, o_ref, _ = _oracle_rounds(sp, sc)
+        e_s = rel_err_states(Ps[layer].S0.cpu().numpy()[seqs], S_ref)
+        e_o = rel_err_rows(Cs[layer].o_np()[rows], o_ref)
+        _say(f"c4 layer {layer} seqs {seqs}: S err {e_s:.3e}, o err {e_o:.3e}")
+        assert e_s <= TOL["bf16"] and e_o <= TOL["bf16"]

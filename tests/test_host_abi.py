@@ -31,6 +31,7 @@ def test_library_exports_every_declared_symbol():
                             "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
                             "gdn_tree_attn_commit", "gdn_tree_verify_layers",
                             "gdn_tree_commit_layers", "gdn_tree_attn_commit_layers",
+                            "gdn_tree_commit_verify", "gdn_tree_commit_verify_layers",
                             "gdn_tree_accept_greedy", "gdn_tree_accept_sampling",
                             "gdn_round_plan",
                             "gdn_round_tree_for_budget", "gdn_round_capture",
@@ -228,6 +229,48 @@ def test_layers_calls_check_before_launch():
                                       None) == 1
     d.dk = 96
     assert lib.gdn_tree_verify_layers(ctypes.byref(d), 2, fake, fake, ly, need, fake, None) == 3
+
+
+def test_commit_verify_checks_before_launch():
+    """The fused commit + verify entry points reject mismatched descriptors,
+    modes, missing pointers, small or overlapping workspaces on the host."""
+    lib = gt.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    prev = gt.make_desc(4, 2, 64, 64, 20, 8)
+    cur = gt.make_desc(4, 2, 64, 64, 30, 12)
+    pneed, need = gt.gdn_tree_workspace_bytes(prev), gt.gdn_tree_workspace_bytes(cur)
+    ly = (gt.GdnLayerIO * 2)(*[gt.GdnLayerIO(*([0x1000] * 9)) for _ in range(2)])
+    ply = (gt.GdnLayerIO * 2)(*[gt.GdnLayerIO(*([0x1000] * 9)) for _ in range(2)])
+    for i in range(2):   # disjoint workspaces
+        ly[i].workspace = 0x100000
+        ply[i].workspace = 0x100000 + need
+
+    def call(p=prev, c=cur, n=2, a=ply, b=ly, pw=pneed, w=need):
+        return lib.gdn_tree_commit_verify_layers(ctypes.byref(p), ctypes.byref(c), n, fake, fake,
+                                                 fake, fake, fake, a, pw, b, w, fake, None)
+
+    assert call(n=0) == 0
+    assert call(b=None) == 1
+    assert call(pw=pneed - 1) == 4
+    assert call(w=need - 1) == 4
+    ply[1].k = None
+    assert call() == 1
+    ply[1].k = 0x1000
+    ply[0].workspace = 0x100000 + need - 256          # overlaps this round's workspace
+    assert call() == 2
+    ply[0].workspace = 0x100000 + need
+    other = gt.make_desc(4, 2, 64, 64, 20, 8, gt.DTYPE_F32)
+    assert call(p=other) == 2                          # io dtype differs
+    other = gt.make_desc(5, 2, 64, 64, 20, 8)
+    assert call(p=other) == 2                          # batch differs
+    other = gt.make_desc(4, 2, 64, 64, 20, 8, gt.DTYPE_BF16, gt.MODE_FORK)
+    assert call(p=other) == 3                          # the previous workspace must be WY
+    other = gt.make_desc(4, 2, 64, 64, 0, 8)
+    assert call(p=other) == 2                          # a previous batch without nodes
+    # the single-layer form goes through the same checks
+    assert lib.gdn_tree_commit_verify(ctypes.byref(prev), fake, fake, fake, fake, fake,
+                                      pneed - 1, ctypes.byref(cur), fake, fake, fake, fake, fake,
+                                      fake, fake, fake, fake, fake, fake, need, fake, None) == 4
 
 
 # ------------------------------------------------------------------ rounds (gdn_round.h)

@@ -62,6 +62,11 @@ CASES = {
     "deep_chain_then_kary": lambda: _case(
         [gi.chain_parents(n) for n in (12, 9, 5, 1, 30)], [gi.kary_parents(2, 2)] * 5,
         4, 64, "bf16", 12, force_acc={0: 11, 1: 6, 4: 29}),
+    # bf16 rows of 128 with this round's trees in three node tiles: the path
+    # rows stay in registers; deep chains need several rounds of them
+    "deep_chain_then_kary3_d128": lambda: _case(
+        [gi.chain_parents(n) for n in (12, 30, 3, 7, 1, 5)], [gi.kary_parents(3, 3)] * 6,
+        4, 128, "bf16", 15, force_acc={0: 11, 1: 29, 2: 2, 3: 4, 4: 0, 5: -1}),
     "tiny_fp32": lambda: _case([[-1, 0, 0, 1, 1, 2, 2]] * 2, [gi.kary_parents(2, 3)] * 2,
                                2, 32, "f32", 13, force_acc={0: 3, 1: -1}),
     "ragged_fp32_d128": lambda: _case(

@@ -1,10 +1,16 @@
 #!/usr/bin/env python3
 """Tree-GDN verify + commit throughput on one MI355X.
 
-One step = every GDN layer of the workload verified and then committed in
-place: the whole hot path over one batch. By default the layers go out as one
-launch per kernel (gdn_tree_verify_layers, gdn_tree_commit_layers);
-`--launch per-layer` issues gdn_tree_verify / gdn_tree_commit per layer.
+One step = one round of the whole hot path over one batch on every GDN layer
+of the workload: each layer's state takes the previous round's commit (the
+accepted paths) and this round's trees are verified against it. By default
+(`--step fused`) a step is one gdn_tree_commit_verify_layers launch, which
+applies the commit and verifies in one pass over the states; the first
+round's verify is issued before timing starts, so K timed steps do K commits
+and K verifies per layer. `--step separate` times the separate calls instead:
+every layer verified and then committed in place, as one launch per kernel
+(gdn_tree_verify_layers, gdn_tree_commit_layers), or one launch per layer
+with `--launch per-layer`. The JSON line reports both schedules.
 Default workload: k=3 d=3 draft trees (40 nodes incl. root), 24 GDN layers
 with independent inputs and states, batch 64, 16 heads, 128x128 fp32 state,
 bf16 q/k/v (Qwen3.5-9B GDN shape). Inputs are seeded synthetic data resident
@@ -38,10 +44,11 @@ METRIC = "tree-GDN verified draft nodes/s per layer (1 GPU) + % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "gated_deltanet_tree_02_amd", "csrc")
-TRAFFIC_FILES = [os.path.join(ROOT, "profiles", "wy_verify_commit_c4_hbm_traffic.md"),
+TRAFFIC_FILES = [os.path.join(ROOT, "profiles", "gdn_wy_c4_hbm_traffic.md"),
                  os.path.join(ROOT, "profiles", "tree_attn_fa_c4_hbm_traffic.md")]
 # sources whose hash ties a recorded counter measurement to the kernels it measured
 KERNEL_SOURCES = {"verify": ["wy_verify.hip", "device_common.h", "launch.h"],
+                  "commit_verify": ["wy_verify.hip", "device_common.h", "launch.h"],
                   "commit": ["wy_commit.hip", "device_common.h", "launch.h"],
                   "attn_verify": ["tree_attn.hip", "device_common.h", "launch.h",
                                   "tree_attn_api.cpp"]}
@@ -88,8 +95,11 @@ def parse():
     p.add_argument("--launch", default="layers", choices=["layers", "per-layer"],
                    help="WY leg: every layer in one launch per kernel (gdn_tree_*_layers) or one "
                         "launch per layer")
-    p.add_argument("--fused-steps", type=int, default=20,
-                   help="timed rounds of the fused previous-commit + verify call (0 = skip)")
+    p.add_argument("--step", default="fused", choices=["fused", "separate"],
+                   help="what a timed step is: one fused previous-commit + verify launch, or "
+                        "the separate verify and commit launches (WY, layer-batched)")
+    p.add_argument("--secondary-steps", type=int, default=20,
+                   help="timed steps of the schedule that is not the headline (0 = skip)")
     p.add_argument("--per-layer-steps", type=int, default=5,
                    help="after a layer-batched WY leg, timed steps with one launch per layer "
                         "(0 = skip)")
@@ -277,7 +287,8 @@ def attention_leg(args, gt, gi, w_trees, dev):
     return out
 
 
-def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev):
+def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev, steps,
+              warmup):
     """Consecutive rounds through gdn_tree_commit_verify_layers: each step
     commits the previous round's accepted paths into the state and verifies
     this round's trees against it, in one launch over all layers (one pass
@@ -303,16 +314,15 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
                                              parents, ios[i], nbytes, ios[1 - i], nbytes, status,
                                              keep=(layers, ws, outs)) for i in range(2)]
     first()
-    for i in range(args.warmup):
+    for i in range(warmup):
         calls[i % 2]()
     torch.cuda.synchronize()
-    steps = args.fused_steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
-        calls[(args.warmup + i) % 2]()
+        calls[(warmup + i) % 2]()
         ev[i][1].record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
@@ -320,12 +330,15 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
         raise RuntimeError("nonzero status in the fused leg")
     times = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)        # us per launch
     med = times[steps // 2]
-    per_layer = med / L
+    per_layer = sum(times) / steps / L                              # mean launch, per layer
     fb = vb + cb - w.B * w.H * 4 * w.dv * w.dk                       # state read once
-    out = {"steps": steps, "layers_per_launch": L,
+    out = {"steps": steps, "warmup": warmup, "layers_per_launch": L,
+           "ms_per_step": round(1e3 * el / steps, 4),
+           "launch_us_mean": round(sum(times) / steps, 2),
            "launch_us_median": round(med, 2),
            "launch_us_p10_p90": [round(times[steps // 10], 2), round(times[(9 * steps) // 10], 2)],
            "us_per_layer": round(per_layer, 3),
+           "us_per_layer_median": round(med / L, 3),
            "alg_bytes_per_layer": int(fb),
            "achieved_GBs": round(fb / per_layer / 1e3, 1),
            "frac_hbm": round(fb / per_layer / 1e3 / HBM_PEAK_GBS, 4),
@@ -668,15 +681,18 @@ def main():
 
     # ------------------------------------------------------------------ main leg
     batched = args.mode == "wy" and args.launch == "layers"
+    # the fused round is the headline step where it applies (WY, layer-batched)
+    headline_fused = args.step == "fused" and batched
+    sep_steps = max(1, args.secondary_steps) if headline_fused else args.steps
     desc, nbytes, ver, com = make_calls(args.mode, batched)
     log(f"mode {args.mode}: workspace {nbytes / 2**20:.1f} MiB per layer, "
         f"{'all layers per launch' if batched else 'one launch per layer'}")
-    elapsed, v_ms, c_ms = run(ver, com, args.steps, args.warmup)
+    elapsed, v_ms, c_ms = run(ver, com, sep_steps, args.warmup)
     st = status.cpu().numpy()
     if np.any(st != 0):
         raise RuntimeError(f"nonzero tree status {np.unique(st)}")
-    ms_step = 1e3 * elapsed / args.steps
-    nodes_per_s = w.T * L * args.steps / elapsed
+    ms_step = 1e3 * elapsed / sep_steps
+    nodes_per_s = w.T * L * sep_steps / elapsed
     vb, cb, fvb, fcb = algorithmic_bytes(w, io_bytes, gi)
     if args.mode == "fork":
         vb, cb = fvb, fcb
@@ -737,12 +753,35 @@ def main():
 
     # ---------------------------------------- previous commit fused into verify
     fused = None
-    if batched and args.fused_steps > 0 and L <= 24:
+    f_steps = args.steps if headline_fused else args.secondary_steps
+    if batched and f_steps > 0:
         for ly in layers:
             ly.pop("o_wy", None), ly.pop("ws_wy", None)
         ver = com = None
         torch.cuda.empty_cache()
-        fused = fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev)
+        fused = fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev,
+                          f_steps, args.warmup)
+        t = recorded_traffic("commit_verify", args.config)     # per layer
+        fused["traffic_bytes"] = t
+        fused["traffic_over_alg"] = round(t / fused["alg_bytes_per_layer"], 3) if t else None
+    separate = None
+    if headline_fused:
+        # the separate calls become the secondary figures; the fused kernel is
+        # the headline step's only (and so dominant) kernel
+        separate = {"value": round(nodes_per_s, 1), "ms_per_step": round(ms_step, 4),
+                    "steps": sep_steps, "roofline": roof}
+        kern["commit_verify"] = {
+            "avg_us": fused["us_per_layer"], "alg_bytes": fused["alg_bytes_per_layer"],
+            "achieved_GBs": fused["achieved_GBs"], "frac_hbm": fused["frac_hbm"],
+            "layers_per_launch": L, "launch_us": fused["launch_us_mean"],
+            "alg_bytes_per_launch": fused["alg_bytes_per_layer"] * L,
+            "traffic_bytes": fused["traffic_bytes"], "traffic_over_alg": fused["traffic_over_alg"]}
+        roof = {"kernel": "wy_commit_verify", "bound": "hbm", "achieved": fused["achieved_GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fused["frac_hbm"],
+                "traffic": fused["traffic_bytes"] * L if fused["traffic_bytes"] else None,
+                "layers_per_launch": L}
+        nodes_per_s = fused["nodes_per_s_per_layer"]
+        ms_step = fused["ms_per_step"]
 
     # ------------------------------------------------------------- fork baseline
     fork = None
@@ -817,15 +856,18 @@ def main():
     out = {
         "metric": METRIC, "value": round(nodes_per_s, 1), "unit": "nodes/s/layer", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.io == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": gi.CONFIGS[args.config]["desc"], "config_id": args.config,
                    "layers": L, "batch": w.B, "total_nodes": w.T, "heads": w.H, "dk": w.dk,
                    "dv": w.dv, "io": w.io, "state": "fp32", "mode": args.mode,
+                   "step": ("previous commit + verify, fused" if headline_fused
+                            else "verify then commit"),
                    "launch": "all layers per launch" if batched else "one launch per layer",
                    "parallelism": "single-gpu"},
         "roofline": roof, "kernels": kern, "cpu_baseline": cpu, "fork_baseline": fork,
-        "per_layer_launches": per_layer, "fused_rounds": fused,
+        "per_layer_launches": per_layer, "fused_rounds": fused, "separate_calls": separate,
         "spec_state_per_request": spec, "fa_layers": fa,
         "round": rnd,
     }

@@ -392,6 +392,16 @@ void wy_verify_kernel(const Args args) {
   const bool owns = wave < DVT;                 // dv < 128: the last waves own no columns
   const int jt = owns ? wave : DVT - 1;
 
+  float4 sraw[KS][2];
+  auto load_S0 = [&]() {
+    const float* rowp = a.S0 + (size_t)bh * DV * DK + (size_t)(16 * jt + l16) * DK + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sraw[s][0] = *reinterpret_cast<const float4*>(rowp + 32 * s);
+      sraw[s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
+    }
+  };
+  if constexpr (kFused) load_S0();
   // ---- 2. staged chunks to LDS (swizzled), then the tree prologue, computed
   // by every wave so that no branch separates the loads from their first use.
 #pragma unroll
@@ -479,15 +489,7 @@ void wy_verify_kernel(const Args args) {
                                                   4 * (tid - PKC - pidx * (DV / 4)));
     }
   }
-  float4 sraw[KS][2];
-  {
-    const float* rowp = a.S0 + (size_t)bh * DV * DK + (size_t)(16 * jt + l16) * DK + 8 * g;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sraw[s][0] = *reinterpret_cast<const float4*>(rowp + 32 * s);
-      sraw[s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
-    }
-  }
+  if constexpr (!kFused) load_S0();
   if (st != GDN_TREE_OK) {
     for (int idx = tid; idx < n * (DV / 4); idx += NT) {
       const int t = idx / (DV / 4);

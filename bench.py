@@ -87,7 +87,9 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # after an idle period the first ~25 launches of a leg run up to 20% slower
+    # (per-launch times fall steadily, then stay flat); 30 untimed steps settle it
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--mode", default="wy", choices=["wy", "fork"])
     p.add_argument("--fork-steps", type=int, default=3, help="timed steps of the fork baseline (0 = skip)")

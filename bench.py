@@ -290,7 +290,7 @@ def attention_leg(args, gt, gi, w_trees, dev):
 
 
 def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev, steps,
-              warmup):
+              warmup, per_layer=False):
     """Consecutive rounds through gdn_tree_commit_verify_layers: each step
     commits the previous round's accepted paths into the state and verifies
     this round's trees against it, in one launch over all layers (one pass
@@ -311,20 +311,28 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
             for ly, o, wl in zip(layers, outs, ws[i])] for i in range(2)]
     first = gt.prepare_verify_layers(desc, offsets, parents, ios[0], nbytes, status,
                                      keep=(layers, ws, outs))
-    # step i commits from workspace i % 2 and verifies into the other one
-    calls = [gt.prepare_commit_verify_layers(desc, desc, offsets, parents, accepted, offsets,
-                                             parents, ios[i], nbytes, ios[1 - i], nbytes, status,
-                                             keep=(layers, ws, outs)) for i in range(2)]
+    # step i commits from workspace i % 2 and verifies into the other one; with
+    # per_layer, one launch per layer (as a model forward issues them)
+    groups = [[l] for l in range(L)] if per_layer else [list(range(L))]
+    calls = [[gt.prepare_commit_verify_layers(desc, desc, offsets, parents, accepted, offsets,
+                                              parents, [ios[i][l] for l in grp], nbytes,
+                                              [ios[1 - i][l] for l in grp], nbytes, status,
+                                              keep=(layers, ws, outs)) for grp in groups]
+             for i in range(2)]
+
+    def step(i):
+        for c in calls[i % 2]:
+            c()
     first()
     for i in range(warmup):
-        calls[i % 2]()
+        step(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
-        calls[(warmup + i) % 2]()
+        step(warmup + i)
         ev[i][1].record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
@@ -334,7 +342,7 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
     med = times[steps // 2]
     per_layer = sum(times) / steps / L                              # mean launch, per layer
     fb = vb + cb - w.B * w.H * 4 * w.dv * w.dk                       # state read once
-    out = {"steps": steps, "warmup": warmup, "layers_per_launch": L,
+    out = {"steps": steps, "warmup": warmup, "layers_per_launch": 1 if per_layer else L,
            "ms_per_step": round(1e3 * el / steps, 4),
            "launch_us_mean": round(sum(times) / steps, 2),
            "launch_us_median": round(med, 2),
@@ -345,7 +353,7 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
            "achieved_GBs": round(fb / per_layer / 1e3, 1),
            "frac_hbm": round(fb / per_layer / 1e3 / HBM_PEAK_GBS, 4),
            "nodes_per_s_per_layer": round(w.T * L * steps / el, 1)}
-    log(f"fused previous commit + verify: {out}")
+    log(f"fused previous commit + verify{' (one launch per layer)' if per_layer else ''}: {out}")
     del ws, outs, ios, calls, first
     torch.cuda.empty_cache()
     return out
@@ -747,11 +755,18 @@ def main():
             # verify per layer (as a forward issues it), commit of all layers batched
             "model_order_nodes_per_s_per_layer": round(w.T / ((pv_us + c_us) * 1e-6), 1),
             "steps": args.per_layer_steps}
-        log(f"one launch per layer: {per_layer}")
         for ly in layers:
             ly.pop("o_wy"), ly.pop("ws_wy")
         pver = pcom = None
         torch.cuda.empty_cache()
+        # the fused previous commit + verify, one launch per layer: in model
+        # order every layer's commit rides on its next verify
+        pf = fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev,
+                       args.per_layer_steps, 5, per_layer=True)
+        per_layer["fused_us_per_layer"] = pf["us_per_layer"]
+        per_layer["fused_frac_hbm"] = pf["frac_hbm"]
+        per_layer["model_order_fused_nodes_per_s_per_layer"] = pf["nodes_per_s_per_layer"]
+        log(f"one launch per layer: {per_layer}")
 
     # ---------------------------------------- previous commit fused into verify
     fused = None

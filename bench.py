@@ -830,6 +830,9 @@ def main():
     wy_state = n_req * L * w.H * (4 * w.dv + 4 + io_bytes * w.dk)
     fork_state = n_req * L * w.H * 4 * w.dv * w.dk
     spec = {"wy_bytes": int(wy_state), "wy_bytes_without_keys": int(n_req * L * w.H * (4 * w.dv + 4)),
+            # the fused rounds keep two WY workspaces per layer at once (the
+            # previous round's until its commit has run, and this round's)
+            "wy_bytes_fused_rounds": int(2 * wy_state),
             "fork_fp32_bytes": int(fork_state), "fork_over_wy": round(fork_state / wy_state, 1),
             "nodes_per_request": n_req, "layers": L}
 

@@ -390,6 +390,37 @@ def test_bad_offsets_and_oversize():
     assert dl.status.cpu().numpy().tolist() == [0, 3]
 
 
+def test_mixed_tile_counts_and_statuses():
+    """bf16 rows of 128, trees of one to four 16-node tiles in one batch with
+    bad-root, bad-parent and oversize sequences among them: statuses, zero
+    rows and the valid sequences' outputs and states."""
+    rng = np.random.default_rng(77)
+    trees = [gi.random_tree_parents(rng, 49, 64), gi.random_tree_parents(rng, 2, 16),
+             gi.chain_parents(64), gi.random_tree_parents(rng, 33, 48), gi.kary_parents(2, 2),
+             gi.random_tree_parents(rng, 50, 64), gi.chain_parents(65)]
+    w = gi.make_workload(trees, H=2, dk=128, dv=128, io="bf16", seed=78)
+    dl = DeviceLayer(w, max_nodes=64)
+    par = w.parents.copy()
+    par[w.offsets[4]] = 0                  # one tile: bad root
+    par[w.offsets[5] + 40] = 45            # four tiles: bad parent
+    dl.parents = i32(par)
+    dl.verify()
+    torch.cuda.synchronize()
+    assert dl.status.cpu().numpy().tolist() == [0, 0, 0, 0, 1, 2, 3]
+    o = dl.o_np()
+    for b in (4, 5):
+        assert np.all(o[w.offsets[b]:w.offsets[b + 1]] == 0)
+    dl.commit()
+    torch.cuda.synchronize()
+    keep = [0, 1, 2, 3]
+    o_ref, _, S_ref, _ = oracle_layer(sub_workload(w, keep), 0)
+    rows = np.concatenate([np.arange(w.offsets[b], w.offsets[b + 1]) for b in keep])
+    e_o = rel_err_rows(o[rows], o_ref)
+    e_s = rel_err_states(dl.S_out.cpu().numpy()[keep], S_ref)
+    _say(f"mixed tiles: sizes {[len(t) for t in trees]}, o err {e_o:.3e}, S err {e_s:.3e}")
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+
+
 def test_empty_batch_and_empty_tree():
     desc = gt.make_desc(0, 16, 128, 128, 0, 8)
     e = torch.empty(0, device="cuda")

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / 64;
 constexpr int kTile = 256;                       // tokens per tile (64 lanes x 4)
-constexpr int kTilesInFlight = 4;
+constexpr int kTilesInFlight = 7;
 constexpr int kMaxTiles = (1 << 20) / kTile;     // vocabularies up to 2^20 tokens
 
 struct Stages {

@@ -168,7 +168,7 @@ enum TileSum { kResidual, kTarget };
 
 // One pass over a node's rows: sTile[t] = sum over tile t of
 // max(0, p_k - q_k) (kResidual) or of p_k (kTarget); the thread's share of
-// the row's q mass is added to *qs. Tiles go to waves round-robin, four at a
+// the row's q mass is added to *qs. Tiles go to waves round-robin, kTilesInFlight at a
 // time with all their loads issued first. K >= 0: exactly K rejections so far,
 // the stage scalars in registers; K < 0: any number, read from LDS.
 template <TileSum WHAT, int K>

@@ -401,7 +401,10 @@ void wy_verify_kernel(const Args args) {
       sraw[s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
     }
   };
-  if constexpr (kFused) load_S0();
+  // (fused) odd workgroups take the state first, even ones after their rows,
+  // so that the two workgroups of a CU do not load in step
+  const bool early_S0 = kFused && (blockIdx.x & 1);
+  if (early_S0) load_S0();
   // ---- 2. staged chunks to LDS (swizzled), then the tree prologue, computed
   // by every wave so that no branch separates the loads from their first use.
 #pragma unroll
@@ -489,7 +492,7 @@ void wy_verify_kernel(const Args args) {
                                                   4 * (tid - PKC - pidx * (DV / 4)));
     }
   }
-  if constexpr (!kFused) load_S0();
+  if (!early_S0) load_S0();
   if (st != GDN_TREE_OK) {
     for (int idx = tid; idx < n * (DV / 4); idx += NT) {
       const int t = idx / (DV / 4);

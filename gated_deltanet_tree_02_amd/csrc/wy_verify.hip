@@ -229,7 +229,8 @@ constexpr bool verify_three_per_cu() {
 }
 template <class IO, int DK, int DV, int MT, bool kFused>
 constexpr int verify_waves_per_simd() {
-  return verify_three_per_cu<IO, DK, DV, MT, kFused>() ? 6 : 1;
+  // (the fused kernel with 128-wide rows needs about 100 VGPRs: no cap)
+  return verify_three_per_cu<IO, DK, DV, MT, kFused>() && !(kFused && DK == 128) ? 6 : 1;
 }
 
 // The committed state is not read again in the round: non-temporal stores.

@@ -242,3 +242,38 @@ def test_commit_verify_c4_full_size_sampled():
         e_o = rel_err_rows(Cs[layer].o_np()[rows], o_ref)
         _say(f"c4 layer {layer} seqs {seqs}: S err {e_s:.3e}, o err {e_o:.3e}")
         assert e_s <= TOL["bf16"] and e_o <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,nseq", [("c3", 32), ("c5", 12)])
+def test_commit_verify_full_size_one_layer(name, nseq):
+    """The k=2 d=3 (B=32) and ragged (B=128, 16-64 nodes) workloads at full
+    size, two consecutive rounds with their own trees (ragged: the next
+    round's trees differ from the previous round's), in the benchmark's
+    launch; the oracle recomputes every sequence (c3) or a sample including
+    the largest and smallest trees (c5)."""
+    wp = gi.make_config(name)
+    wc = gi.make_config(name, seed=gi.CONFIGS[name]["seed"] + 100)
+    P, C = DeviceLayer(wp, 0, max_nodes=64), DeviceLayer(wc, 0, max_nodes=64)
+    P.verify()
+    io_p = [gt.make_layer_io(P.desc, k=P.k, workspace=P.ws)]
+    io_c = [gt.make_layer_io(C.desc, q=C.q, k=C.k, v=C.v, alpha=C.alpha, beta=C.beta, S0=P.S0,
+                             o=C.o, S_out=P.S0, workspace=C.ws)]
+    status = torch.full((wp.B,), -7, dtype=torch.int32, device="cuda")
+    gt.gdn_tree_commit_verify_layers(P.desc, C.desc, P.offsets, P.parents, P.accepted,
+                                     C.offsets, C.parents, io_p, P.ws.numel(), io_c,
+                                     C.ws.numel(), status)
+    torch.cuda.synchronize()
+    assert np.all(status.cpu().numpy() == 0)
+    if nseq >= wp.B:
+        seqs = list(range(wp.B))
+    else:
+        rng = np.random.default_rng(43)
+        sp, sc = np.diff(wp.offsets), np.diff(wc.offsets)
+        seqs = sorted(set([int(np.argmax(sp)), int(np.argmin(sp)), int(np.argmax(sc)),
+                           int(np.argmin(sc))] + rng.choice(wp.B, nseq, replace=False).tolist()))
+    rows = np.concatenate([np.arange(wc.offsets[b], wc.offsets[b + 1]) for b in seqs])
+    S_ref, _, o_ref, _ = _oracle_rounds(sub_workload(wp, seqs), sub_workload(wc, seqs))
+    e_s = rel_err_states(P.S0.cpu().numpy()[seqs], S_ref)
+    e_o = rel_err_rows(C.o_np()[rows], o_ref)
+    _say(f"{name} full size, {len(seqs)} sequences: S err {e_s:.3e}, o err {e_o:.3e}")
+    assert e_s <= TOL["bf16"] and e_o <= TOL["bf16"]

@@ -233,12 +233,6 @@ constexpr int verify_waves_per_simd() {
   return verify_three_per_cu<IO, DK, DV, MT, kFused>() && !(kFused && DK == 128) ? 6 : 1;
 }
 
-// The committed state is not read again in the round: non-temporal stores.
-// (Non-temporal state loads were measured slower.)
-__device__ __forceinline__ void store_nt(float* p, const float4& x) {
-  __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4*>(p));
-}
-
 // Rank p (0 = the root) of a path given as a node bit set: its p-th lowest bit.
 __device__ __forceinline__ int nth_path_node(uint64_t path, int p) {
   for (int j = 0; j < p; ++j) path &= path - 1ull;
@@ -691,8 +685,8 @@ void wy_verify_kernel(const Args args) {
       float* rowo = S_out + (size_t)bh * DV * DK + (size_t)(16 * jt + l16) * DK + 8 * g;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        store_nt(rowo + 32 * s, sraw[s][0]);
-        store_nt(rowo + 32 * s + 4, sraw[s][1]);
+        *reinterpret_cast<float4*>(rowo + 32 * s) = sraw[s][0];
+        *reinterpret_cast<float4*>(rowo + 32 * s + 4) = sraw[s][1];
       }
     }
   }

@@ -27,6 +27,7 @@ __all__ = [
     "GdnLayerIO", "make_layer_io", "gdn_tree_verify_layers", "gdn_tree_commit_layers",
     "prepare_verify_layers", "prepare_commit_layers",
     "gdn_tree_commit_verify", "gdn_tree_commit_verify_layers", "prepare_commit_verify_layers",
+    "gdn_tree_replay_verify", "gdn_tree_replay_verify_layers", "prepare_replay_verify_layers",
     "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
     "prepare_attn_commit_layers",
     "gdn_tree_accept_greedy", "gdn_tree_accept_sampling", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
@@ -141,6 +142,12 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_commit_verify_layers.argtypes = [D, D, ctypes.c_int32, P, P, P, P, P,
                                                           LY, S, LY, S, P, P]
             lib.gdn_tree_commit_verify_layers.restype = I
+            lib.gdn_tree_replay_verify.argtypes = [D, P, P, P, P, P, P, P, D, P, P, P, P, P, P,
+                                                   P, P, P, P, P, P]
+            lib.gdn_tree_replay_verify.restype = I
+            lib.gdn_tree_replay_verify_layers.argtypes = [D, D, ctypes.c_int32, P, P, P, P, P,
+                                                          LY, LY, P, P]
+            lib.gdn_tree_replay_verify_layers.restype = I
             AL = ctypes.POINTER(GdnAttnLayerIO)
             lib.gdn_tree_attn_commit_layers.argtypes = [A, ctypes.c_int32, P, P, P, AL, P, P, P]
             lib.gdn_tree_attn_commit_layers.restype = I
@@ -609,6 +616,81 @@ def prepare_commit_verify_layers(prev_desc, desc, prev_offsets, prev_parents, ac
                                                  prev_workspace_bytes, layers, workspace_bytes,
                                                  tree_status)
     return PreparedCall("gdn_tree_commit_verify_layers", prev_desc, args, _stream(stream, dev),
+                        (prev_offsets, prev_parents, accepted, offsets, parents, tree_status,
+                         held, tuple(keep)))
+
+
+def gdn_tree_replay_verify(prev_desc, prev_offsets, prev_parents, accepted, prev_k, prev_v,
+                           prev_alpha, prev_beta, desc, offsets, parents, q, k, v, alpha, beta,
+                           S0, S_out, o, tree_status, stream=None):
+    """The previous round's accepted path replayed on the state (S0 -> S_out)
+    and this round's verify against S_out, in one pass over the state and
+    with no workspace."""
+    torch = _torch()
+    B, H, T, dk, dv = desc.num_seqs, desc.num_heads, desc.total_nodes, desc.dk, desc.dv
+    pT = prev_desc.total_nodes
+    dev = offsets.device
+    io, pio = _io_dtype(desc), _io_dtype(prev_desc)
+    pa = _prev_args(prev_desc, desc, prev_offsets, prev_parents, accepted, dev)
+    pa += [_ptr(prev_k, "prev_k", pio, (pT, H, dk), dev), _ptr(prev_v, "prev_v", pio, (pT, H, dv), dev),
+           _ptr(prev_alpha, "prev_alpha", torch.float32, (pT, H), dev),
+           _ptr(prev_beta, "prev_beta", torch.float32, (pT, H), dev)]
+    ca = [ctypes.byref(desc), _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+          _ptr(parents, "parents", torch.int32, (T,), dev), _ptr(q, "q", io, (T, H, dk), dev),
+          _ptr(k, "k", io, (T, H, dk), dev), _ptr(v, "v", io, (T, H, dv), dev),
+          _ptr(alpha, "alpha", torch.float32, (T, H), dev),
+          _ptr(beta, "beta", torch.float32, (T, H), dev),
+          _ptr(S0, "S0", torch.float32, (B, H, dv, dk), dev),
+          _ptr(S_out, "S_out", torch.float32, (B, H, dv, dk), dev), _ptr(o, "o", io, (T, H, dv), dev),
+          _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_replay_verify(ctypes.byref(prev_desc), *pa, *ca,
+                                                     _stream(stream, dev)),
+               "gdn_tree_replay_verify")
+
+
+def _replay_verify_layers_args(prev_desc, desc, prev_offsets, prev_parents, accepted, offsets,
+                               parents, prev_layers, layers, tree_status):
+    torch = _torch()
+    if len(prev_layers) != len(layers):
+        raise ValueError("prev_layers and layers must have the same length")
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    desc_copy = type(desc).from_buffer_copy(desc)
+    pa = _prev_args(prev_desc, desc, prev_offsets, prev_parents, accepted, dev)
+    parr, arr = _layers_array(prev_layers), _layers_array(layers)
+    args = [ctypes.byref(desc_copy), ctypes.c_int32(len(layers))] + pa + [
+        _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+        _ptr(parents, "parents", torch.int32, (T,), dev), parr, arr,
+        _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
+    return dev, args, (desc_copy, parr, arr)
+
+
+def gdn_tree_replay_verify_layers(prev_desc, desc, prev_offsets, prev_parents, accepted,
+                                  offsets, parents, prev_layers, layers, tree_status,
+                                  stream=None):
+    """gdn_tree_replay_verify for every layer: `prev_layers` (GdnLayerIO made
+    with prev_desc: k, v, alpha, beta) and `layers` (GdnLayerIO made with desc:
+    q, k, v, alpha, beta, S0, o, S_out)."""
+    torch = _torch()
+    dev, args, _ = _replay_verify_layers_args(prev_desc, desc, prev_offsets, prev_parents,
+                                              accepted, offsets, parents, prev_layers, layers,
+                                              tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_replay_verify_layers(ctypes.byref(prev_desc), *args,
+                                                            _stream(stream, dev)),
+               "gdn_tree_replay_verify_layers")
+
+
+def prepare_replay_verify_layers(prev_desc, desc, prev_offsets, prev_parents, accepted, offsets,
+                                 parents, prev_layers, layers, tree_status, keep=(),
+                                 stream=None) -> PreparedCall:
+    """Marshalled gdn_tree_replay_verify_layers; `keep` holds the tensors
+    behind `prev_layers` and `layers`."""
+    dev, args, held = _replay_verify_layers_args(prev_desc, desc, prev_offsets, prev_parents,
+                                                 accepted, offsets, parents, prev_layers, layers,
+                                                 tree_status)
+    return PreparedCall("gdn_tree_replay_verify_layers", prev_desc, args, _stream(stream, dev),
                         (prev_offsets, prev_parents, accepted, offsets, parents, tree_status,
                          held, tuple(keep)))
 

@@ -319,7 +319,7 @@ gdn_status gdn_tree_commit_verify_layers(
       const float* pU = static_cast<const float*>(p.workspace);
       const float* pg2 = reinterpret_cast<const float*>(static_cast<const char*>(p.workspace) +
                                                         wy_u_bytes(prev_desc));
-      a.P[i] = gdn::PendingLayer{p.k, pU, pg2, y.S_out};
+      a.P[i] = gdn::PendingLayer{p.k, pU, pg2, nullptr, nullptr, nullptr, y.S_out};
     }
     st = launched(gdn::launch_wy_commit_verify_layers(desc->io_dtype, desc->dk, mt, a, s));
     if (st != GDN_OK) return st;
@@ -343,6 +343,76 @@ gdn_status gdn_tree_commit_verify(const gdn_tree_desc* prev_desc, const int32_t*
   return gdn_tree_commit_verify_layers(prev_desc, desc, 1, prev_offsets, prev_parents, accepted,
                                        offsets, parents, &prev, prev_ws_bytes, &cur, ws_bytes,
                                        tree_status, stream);
+}
+
+gdn_status gdn_tree_replay_verify_layers(
+    const gdn_tree_desc* prev_desc, const gdn_tree_desc* desc, int32_t n_layers,
+    const int32_t* prev_offsets, const int32_t* prev_parents, const int32_t* accepted,
+    const int32_t* offsets, const int32_t* parents, const gdn_layer_io* prev_layers,
+    const gdn_layer_io* layers, int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(prev_desc);
+  if (st != GDN_OK) return st;
+  st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (prev_desc->mode != GDN_MODE_WY || desc->mode != GDN_MODE_WY) return GDN_ERR_UNSUPPORTED;
+  if (prev_desc->num_seqs != desc->num_seqs || prev_desc->num_heads != desc->num_heads ||
+      prev_desc->dk != desc->dk || prev_desc->dv != desc->dv ||
+      prev_desc->io_dtype != desc->io_dtype)
+    return GDN_ERR_BAD_SHAPE;
+  if (n_layers <= 0 || desc->num_seqs == 0) return GDN_OK;
+  if (prev_desc->total_nodes < 1) return GDN_ERR_BAD_SHAPE;
+  if (!layers || !prev_layers || !prev_offsets || !prev_parents || !accepted || !offsets ||
+      !tree_status)
+    return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && !parents) return GDN_ERR_NULL_PTR;
+  for (int l = 0; l < n_layers; ++l) {
+    const gdn_layer_io& y = layers[l];
+    const gdn_layer_io& p = prev_layers[l];
+    if (!y.S0 || !y.S_out || !p.k || !p.v || !p.alpha || !p.beta) return GDN_ERR_NULL_PTR;
+    if (desc->total_nodes > 0 && (!y.q || !y.k || !y.v || !y.alpha || !y.beta || !y.o))
+      return GDN_ERR_NULL_PTR;
+  }
+  if ((long long)desc->num_seqs * desc->num_heads * gdn::kMaxFusedLayersPerLaunch > INT_MAX)
+    return GDN_ERR_BAD_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int mt = (desc->max_nodes + 15) / 16;
+  gdn::ReplayVerifyLayersArgs a{};
+  a.base = gdn::VerifyArgs{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                           offsets, parents, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, nullptr, nullptr, tree_status};
+  a.prev = gdn::PendingTree{prev_desc->total_nodes, prev_desc->max_nodes, prev_offsets,
+                            prev_parents, accepted};
+  for (int l0 = 0; l0 < n_layers; l0 += gdn::kMaxFusedLayersPerLaunch) {
+    a.layers = std::min(n_layers - l0, gdn::kMaxFusedLayersPerLaunch);
+    for (int i = 0; i < a.layers; ++i) {
+      const gdn_layer_io& y = layers[l0 + i];
+      const gdn_layer_io& p = prev_layers[l0 + i];
+      a.L[i] = gdn::VerifyLayer{y.q, y.k, y.v, y.alpha, y.beta, y.S0, y.o, nullptr, nullptr};
+      a.P[i] = gdn::PendingLayer{p.k, nullptr, nullptr, p.v, p.alpha, p.beta, y.S_out};
+    }
+    st = launched(gdn::launch_wy_replay_verify_layers(desc->io_dtype, desc->dk, mt, a, s));
+    if (st != GDN_OK) return st;
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_tree_replay_verify(const gdn_tree_desc* prev_desc, const int32_t* prev_offsets,
+                                  const int32_t* prev_parents, const int32_t* accepted,
+                                  const void* prev_k, const void* prev_v,
+                                  const float* prev_alpha, const float* prev_beta,
+                                  const gdn_tree_desc* desc, const int32_t* offsets,
+                                  const int32_t* parents, const void* q, const void* k,
+                                  const void* v, const float* alpha, const float* beta,
+                                  const float* S0, float* S_out, void* o, int32_t* tree_status,
+                                  void* stream) {
+  gdn_layer_io prev{};
+  prev.k = prev_k;
+  prev.v = prev_v;
+  prev.alpha = prev_alpha;
+  prev.beta = prev_beta;
+  gdn_layer_io cur{q, k, v, alpha, beta, S0, o, S_out, nullptr};
+  return gdn_tree_replay_verify_layers(prev_desc, desc, 1, prev_offsets, prev_parents, accepted,
+                                       offsets, parents, &prev, &cur, tree_status, stream);
 }
 
 const char* gdn_tree_status_string(int status) {

@@ -197,8 +197,11 @@ struct PendingTree {
 };
 struct PendingLayer {
   const void* k;     // previous round's k [T', H, dk]
-  const float* U;    // previous round's pseudo-values [T', H, dv]
-  const float* g2;   // previous round's base-2 gate prefixes [T', H]
+  const float* U;    // previous round's pseudo-values [T', H, dv] (commit from U)
+  const float* g2;   // previous round's base-2 gate prefixes [T', H] (commit from U)
+  const void* v;     // previous round's v [T', H, dv] (replay)
+  const float* alpha;  // previous round's gates [T', H] (replay)
+  const float* beta;
   float* S_out;      // committed state (may equal the layer's S0)
 };
 constexpr int kMaxFusedLayersPerLaunch = 24;
@@ -209,6 +212,10 @@ struct CommitVerifyLayersArgs {
   VerifyLayer L[kMaxFusedLayersPerLaunch];
   PendingLayer P[kMaxFusedLayersPerLaunch];
 };
+// The same, with the previous round's accepted path replayed on the state
+// (the gated delta rule step by step from its k, v, alpha, beta) instead of
+// rebuilt from pseudo-values; this round's verify then writes no workspace.
+struct ReplayVerifyLayersArgs : CommitVerifyLayersArgs {};
 
 __device__ __forceinline__ VerifyArgs layer_args(const VerifyArgs& a, int) { return a; }
 __device__ __forceinline__ VerifyArgs layer_args(const VerifyLayersArgs& la, int layer) {
@@ -239,6 +246,9 @@ __device__ __forceinline__ VerifyArgs layer_args(const CommitVerifyLayersArgs& l
   a.g2 = l.g2;
   return a;
 }
+__device__ __forceinline__ VerifyArgs layer_args(const ReplayVerifyLayersArgs& la, int layer) {
+  return layer_args(static_cast<const CommitVerifyLayersArgs&>(la), layer);
+}
 __device__ __forceinline__ CommitArgs layer_args(const CommitArgs& a, int) { return a; }
 __device__ __forceinline__ CommitArgs layer_args(const CommitLayersArgs& la, int layer) {
   CommitArgs a = la.base;
@@ -255,6 +265,9 @@ __device__ __forceinline__ const VerifyArgs& base_args(const VerifyLayersArgs& a
 __device__ __forceinline__ const VerifyArgs& base_args(const CommitVerifyLayersArgs& a) {
   return a.base;
 }
+__device__ __forceinline__ const VerifyArgs& base_args(const ReplayVerifyLayersArgs& a) {
+  return a.base;
+}
 __device__ __forceinline__ const CommitArgs& base_args(const CommitArgs& a) { return a; }
 __device__ __forceinline__ const CommitArgs& base_args(const CommitLayersArgs& a) { return a.base; }
 
@@ -262,6 +275,8 @@ hipError_t launch_wy_verify(int io, int d, int mt, const VerifyArgs& a, hipStrea
 hipError_t launch_wy_verify_layers(int io, int d, int mt, const VerifyLayersArgs& a,
                                    hipStream_t s);
 hipError_t launch_wy_commit_verify_layers(int io, int d, int mt, const CommitVerifyLayersArgs& a,
+                                          hipStream_t s);
+hipError_t launch_wy_replay_verify_layers(int io, int d, int mt, const ReplayVerifyLayersArgs& a,
                                           hipStream_t s);
 hipError_t launch_tree_attn(int d, const AttnArgs& a, hipStream_t s);
 hipError_t launch_tree_attn_commit(int d, const AttnCommitArgs& a, hipStream_t s);

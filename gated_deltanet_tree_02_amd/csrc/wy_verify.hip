@@ -204,8 +204,12 @@ __device__ __forceinline__ void t_row_in_registers(uint64_t anc, int d, const fl
 // into this verify (longer paths are applied in rounds of this many).
 constexpr int kFusedPathRows = 4;
 template <class Args>
+constexpr bool replay_args() {
+  return std::is_same<Args, ReplayVerifyLayersArgs>::value;
+}
+template <class Args>
 constexpr bool fused_args() {
-  return std::is_same<Args, CommitVerifyLayersArgs>::value;
+  return std::is_same<Args, CommitVerifyLayersArgs>::value || replay_args<Args>();
 }
 
 // LDS bytes of one workgroup with the v staging rows unpadded (the layout
@@ -271,9 +275,12 @@ void wy_verify_kernel(const Args args) {
   constexpr int NLD = (NSTAGE + NT - 1) / NT;   // per thread (a spare one repeats the last)
   constexpr bool kF32 = std::is_same<IO, float>::value;
   constexpr bool kFused = fused_args<Args>();
+  constexpr bool kReplay = replay_args<Args>();
   constexpr int PCH = kFusedPathRows;
   constexpr int PKC = PCH * CPR;              // io chunks of the staged path k rows
-  constexpr int PUC = PCH * DV / 4;           // float4 of their scaled pseudo-values
+  // then per path row: its scaled pseudo-values (float4), or its v row (io chunks, replay)
+  constexpr int SEC = kReplay ? CPV : DV / 4;
+  constexpr int PUC = PCH * SEC;
   using io = io_traits<IO>;
   static_assert(DVT <= NW, "one 16-column dv tile per wave");
   static_assert(PKC + PUC <= NT, "one staged path piece per thread");
@@ -341,14 +348,16 @@ void wy_verify_kernel(const Args args) {
   // 1z. (fused commit) the previous round's node range and accepted node,
   // and one lane per previous node: its parent and gate prefix.
   int plo = 0, pn = 1, pacc = -1, pst = GDN_TREE_OK, ppar_raw = -1;
-  float pg2_raw = 0.f;
+  float pg2_raw = 0.f, palpha = 1.f, pbeta = 0.f;
   const IO* __restrict__ pk = nullptr;
+  const IO* __restrict__ pv = nullptr;
   const float* __restrict__ pU = nullptr;
   float* __restrict__ S_out = nullptr;
   if constexpr (kFused) {
     const PendingTree& pt = args.prev;
     const PendingLayer& pl = args.P[layer];
     pk = static_cast<const IO*>(pl.k);
+    pv = static_cast<const IO*>(pl.v);
     pU = pl.U;
     S_out = pl.S_out;
     const int plo_r = pt.offsets[b];
@@ -362,7 +371,13 @@ void wy_verify_kernel(const Args args) {
     }
     const int pl_lane = lane < pn ? lane : 0;
     ppar_raw = pt.parents[plo + pl_lane];
-    pg2_raw = pl.g2[(size_t)(plo + pl_lane) * H + h];
+    const size_t pgl = (size_t)(plo + pl_lane) * H + h;
+    if constexpr (kReplay) {
+      palpha = pl.alpha[pgl];
+      pbeta = pl.beta[pgl];
+    } else {
+      pg2_raw = pl.g2[pgl];
+    }
   }
 
   // ---- 1. every global read of the workgroup, issued before any is used
@@ -461,8 +476,10 @@ void wy_verify_kernel(const Args args) {
       float unused;
       path_scan(ppar, lane, pn, 0.f, panc, unused);
       ppath = shfl_u64(panc, pacc);
-      pgA = __shfl(pg2_raw, pacc, kWave);
-      pcoef = exp2f(pgA - pg2_raw);
+      if constexpr (!kReplay) {
+        pgA = __shfl(pg2_raw, pacc, kWave);
+        pcoef = exp2f(pgA - pg2_raw);
+      }
     }
   }
   if (wave == 0 && lane < NP) {
@@ -479,7 +496,7 @@ void wy_verify_kernel(const Args args) {
   // (a k chunk, or four pseudo-values), issued before the state so that
   // waiting for them does not wait for the state.
   const int P = kFused ? __popcll(ppath) : 0;
-  const int pidx = tid < PKC ? tid / CPR : (tid - PKC) / (DV / 4);
+  const int pidx = tid < PKC ? tid / CPR : (tid - PKC) / SEC;
   uint4 pld = make_uint4(0u, 0u, 0u, 0u);
   float pcf = 0.f;
   if constexpr (kFused) {
@@ -487,10 +504,12 @@ void wy_verify_kernel(const Args args) {
     pcf = __shfl(pcoef, pnode, kWave);
     if (pidx < P && tid < PKC + PUC) {
       const size_t prow = (size_t)(plo + pnode) * H + h;
-      pld = tid < PKC
-                ? *reinterpret_cast<const uint4*>(pk + prow * DK + (tid - pidx * CPR) * EPC)
-                : *reinterpret_cast<const uint4*>(pU + prow * DV +
-                                                  4 * (tid - PKC - pidx * (DV / 4)));
+      if (tid < PKC)
+        pld = *reinterpret_cast<const uint4*>(pk + prow * DK + (tid - pidx * CPR) * EPC);
+      else if constexpr (kReplay)
+        pld = *reinterpret_cast<const uint4*>(pv + prow * DV + (tid - PKC - pidx * CPV) * EPC);
+      else
+        pld = *reinterpret_cast<const uint4*>(pU + prow * DV + 4 * (tid - PKC - pidx * (DV / 4)));
     }
   }
   if (!early_S0) load_S0();
@@ -500,9 +519,10 @@ void wy_verify_kernel(const Args args) {
       const int r = 4 * (idx - t * (DV / 4));
       const size_t row = ((size_t)(lo + t) * H + h) * DV + r;
       io::store4(o + row, make_float4(0.f, 0.f, 0.f, 0.f));
-      *reinterpret_cast<float4*>(a.U + row) = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (!kReplay) *reinterpret_cast<float4*>(a.U + row) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int t = tid; t < n; t += NT) a.g2[(size_t)(lo + t) * H + h] = 0.f;
+    if constexpr (!kReplay)
+      for (int t = tid; t < n; t += NT) a.g2[(size_t)(lo + t) * H + h] = 0.f;
     if (h == 0 && tid == 0) a.status[b] = st;
     return;
   }
@@ -559,6 +579,8 @@ void wy_verify_kernel(const Args args) {
     if (pidx < P && tid < PKC + PUC) {
       if (tid < PKC) {
         sPK[tid] = pld;
+      } else if constexpr (kReplay) {
+        reinterpret_cast<uint4*>(sPW)[tid - PKC] = pld;
       } else {
         float4 u = __builtin_bit_cast(float4, pld);
         u.x *= pcf;
@@ -624,16 +646,14 @@ void wy_verify_kernel(const Args args) {
     }
   }
 
-  // ---- 5. per wave: X = K S0^T and Y = Q S0^T for node tiles m, with the
-  // wave's 16 dv columns (A = staged k / q rows, B = S0 hi/lo); result lane
-  // holds column r = 16w + lane%16 of nodes t = 16m + 4g + e. Then
-  // R = diag(beta)(V - diag(G) X) and G*Y.
   // ---- 4b. (fused commit) S0 <- G_a S0 + sum over the accepted path of
   // (G_a/G_i) u_i k_i^T on this wave's fragment (row 16w + lane%16, columns
   // 32s + 8g .. +7), written out as the committed state and verified against.
+  // Replay instead runs the gated delta rule along the path, root first:
+  // w = S k_j, S <- alpha_j S + beta_j (v_j - alpha_j w) k_j^T.
   if constexpr (kFused) {
     const float GA = pacc >= 0 ? exp2f(pgA) : 1.f;
-    if (owns) {
+    if (owns && !kReplay) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         sraw[s][0].x *= GA; sraw[s][0].y *= GA; sraw[s][0].z *= GA; sraw[s][0].w *= GA;
@@ -652,6 +672,9 @@ void wy_verify_kernel(const Args args) {
           const size_t prow = (size_t)(plo + pnode) * H + h;
           if (tid < PKC) {
             sPK[tid] = *reinterpret_cast<const uint4*>(pk + prow * DK + (tid - pidx * CPR) * EPC);
+          } else if constexpr (kReplay) {
+            reinterpret_cast<uint4*>(sPW)[tid - PKC] = *reinterpret_cast<const uint4*>(
+                pv + prow * DV + (tid - PKC - pidx * CPV) * EPC);
           } else {
             float4 u = *reinterpret_cast<const float4*>(pU + prow * DV +
                                                         4 * (tid - PKC - pidx * (DV / 4)));
@@ -664,7 +687,42 @@ void wy_verify_kernel(const Args args) {
         }
         __syncthreads();
       }
-      if (owns) {
+      if (owns && kReplay) {
+        const int r = 16 * jt + l16;
+        for (int p = 0; p < pc; ++p) {
+          const int node = nth_path_node(ppath, p0 + p);
+          const float al = __shfl(palpha, node, kWave);
+          const float be = __shfl(pbeta, node, kWave);
+          const IO* krow = reinterpret_cast<const IO*>(sPK) + p * DK + 8 * g;
+          float4 kk[KS][2];
+          float dot = 0.f;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            kk[s][0] = io::load4(krow + 32 * s);
+            kk[s][1] = io::load4(krow + 32 * s + 4);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              dot += sraw[s][hh].x * kk[s][hh].x + sraw[s][hh].y * kk[s][hh].y +
+                     sraw[s][hh].z * kk[s][hh].z + sraw[s][hh].w * kk[s][hh].w;
+          }
+          // the row's 128 columns are spread over the lanes l16 + 16g
+          dot += __shfl_xor(dot, 16, kWave);
+          dot += __shfl_xor(dot, 32, kWave);
+          const float vr = io::load1(reinterpret_cast<const IO*>(sPW) + p * DV + r);
+          const float c = be * (vr - al * dot);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              sraw[s][hh].x = al * sraw[s][hh].x + c * kk[s][hh].x;
+              sraw[s][hh].y = al * sraw[s][hh].y + c * kk[s][hh].y;
+              sraw[s][hh].z = al * sraw[s][hh].z + c * kk[s][hh].z;
+              sraw[s][hh].w = al * sraw[s][hh].w + c * kk[s][hh].w;
+            }
+          }
+        }
+      }
+      if (owns && !kReplay) {
         const int r = 16 * jt + l16;
         for (int p = 0; p < pc; ++p) {
           const float w = sPW[p * DV + r];
@@ -691,6 +749,10 @@ void wy_verify_kernel(const Args args) {
     }
   }
 
+  // ---- 5. per wave: X = K S0^T and Y = Q S0^T for node tiles m, with the
+  // wave's 16 dv columns (A = staged k / q rows, B = S0 hi/lo); result lane
+  // holds column r = 16w + lane%16 of nodes t = 16m + 4g + e. Then
+  // R = diag(beta)(V - diag(G) X) and G*Y.
   f32x4 rX[MT], rY[MT];
   if (owns) {
 #pragma unroll
@@ -781,7 +843,7 @@ void wy_verify_kernel(const Args args) {
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * m + 4 * g + e;
         const int rs = r ^ (SWZ * 16 * ((t >> 2) & 3));
-        sm.s2.u[t * DV + rs] = uu[m][e];
+        if constexpr (!kReplay) sm.s2.u[t * DV + rs] = uu[m][e];
         io::store1(sm.s2.o + t * DV + rs, oo[e]);
       }
     }
@@ -796,14 +858,15 @@ void wy_verify_kernel(const Args args) {
     *reinterpret_cast<uint4*>(o + ((size_t)(lo + t) * H + h) * DV + c * EPC) =
         *reinterpret_cast<const uint4*>(sm.s2.o + t * DV + cs);
   }
-  for (int idx = tid; idx < n * (DV / 4); idx += NT) {
+  // (replay: the next round replays from this round's inputs; no workspace)
+  for (int idx = tid; !kReplay && idx < n * (DV / 4); idx += NT) {
     const int t = idx / (DV / 4);
     const int c = idx - t * (DV / 4);
     const int cs = (4 * c) ^ (SWZ * 16 * ((t >> 2) & 3));
     *reinterpret_cast<float4*>(a.U + ((size_t)(lo + t) * H + h) * DV + 4 * c) =
         *reinterpret_cast<const float4*>(sm.s2.u + t * DV + cs);
   }
-  if (wave == 0 && lane < n) a.g2[(size_t)(lo + lane) * H + h] = g2;
+  if (!kReplay && wave == 0 && lane < n) a.g2[(size_t)(lo + lane) * H + h] = g2;
   if (h == 0 && tid == 0) a.status[b] = GDN_TREE_OK;
 }
 
@@ -812,6 +875,9 @@ inline unsigned grid_of(const VerifyLayersArgs& a) {
   return (unsigned)(a.base.B * a.base.H * a.layers);
 }
 inline unsigned grid_of(const CommitVerifyLayersArgs& a) {
+  return (unsigned)(a.base.B * a.base.H * a.layers);
+}
+inline unsigned grid_of(const ReplayVerifyLayersArgs& a) {
   return (unsigned)(a.base.B * a.base.H * a.layers);
 }
 
@@ -854,6 +920,11 @@ hipError_t launch_wy_verify_layers(int io, int d, int mt, const VerifyLayersArgs
 }
 
 hipError_t launch_wy_commit_verify_layers(int io, int d, int mt, const CommitVerifyLayersArgs& a,
+                                          hipStream_t s) {
+  return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, mt, a, s) : launch_d<float>(d, mt, a, s);
+}
+
+hipError_t launch_wy_replay_verify_layers(int io, int d, int mt, const ReplayVerifyLayersArgs& a,
                                           hipStream_t s) {
   return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, mt, a, s) : launch_d<float>(d, mt, a, s);
 }

@@ -256,6 +256,41 @@ gdn_status gdn_tree_commit_verify_layers(
     size_t prev_workspace_bytes, const gdn_layer_io* layers, size_t workspace_bytes,
     int32_t* tree_status, void* stream);
 
+/* Fused round boundary by replay: the same round boundary as
+ * gdn_tree_commit_verify, but the previous round's accepted path is committed
+ * by running the gated delta rule along it (root first) on each workgroup's
+ * slice of S0,
+ *     w = S k_j,   S <- alpha_j S + beta_j (v_j - alpha_j w) k_j^T,
+ * from that path's own k, v, alpha, beta (fork page section 5: the kept state
+ * is the last accepted token's; the update is the one every node's output is
+ * defined by), and this round's verify writes no workspace: the next round
+ * replays from this round's inputs. The results are those of
+ *     gdn_tree_commit(...) of the previous round, then
+ *     gdn_tree_verify(desc, ..., S_out, o, ...)
+ * up to fp32 rounding order (the path is applied as a recurrence instead of
+ * through pseudo-values), without the workspace. Arguments, checks and status
+ * codes as for gdn_tree_commit_verify, except:
+ *  - prev_k, prev_v [T',H,dk|dv] (io dtype) and prev_alpha, prev_beta [T',H]
+ *    are the previous round's verify inputs, unchanged since;
+ *  - there is no workspace argument; desc's workspace size is not used.
+ * The layer-batched form takes HOST arrays of n_layers entries: prev_layers
+ * (fields k, v, alpha, beta used) and layers (q, k, v, alpha, beta, S0, o,
+ * S_out used). All layers share both trees and accepted. */
+gdn_status gdn_tree_replay_verify(const gdn_tree_desc* prev_desc, const int32_t* prev_offsets,
+                                  const int32_t* prev_parents, const int32_t* accepted,
+                                  const void* prev_k, const void* prev_v,
+                                  const float* prev_alpha, const float* prev_beta,
+                                  const gdn_tree_desc* desc, const int32_t* offsets,
+                                  const int32_t* parents, const void* q, const void* k,
+                                  const void* v, const float* alpha, const float* beta,
+                                  const float* S0, float* S_out, void* o, int32_t* tree_status,
+                                  void* stream);
+gdn_status gdn_tree_replay_verify_layers(
+    const gdn_tree_desc* prev_desc, const gdn_tree_desc* desc, int32_t n_layers,
+    const int32_t* prev_offsets, const int32_t* prev_parents, const int32_t* accepted,
+    const int32_t* offsets, const int32_t* parents, const gdn_layer_io* prev_layers,
+    const gdn_layer_io* layers, int32_t* tree_status, void* stream);
+
 /* Static text for a gdn_status value. */
 const char* gdn_tree_status_string(int status);
 

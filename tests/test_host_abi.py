@@ -32,6 +32,7 @@ def test_library_exports_every_declared_symbol():
                             "gdn_tree_attn_commit", "gdn_tree_verify_layers",
                             "gdn_tree_commit_layers", "gdn_tree_attn_commit_layers",
                             "gdn_tree_commit_verify", "gdn_tree_commit_verify_layers",
+                            "gdn_tree_replay_verify", "gdn_tree_replay_verify_layers",
                             "gdn_tree_accept_greedy", "gdn_tree_accept_sampling",
                             "gdn_round_plan",
                             "gdn_round_tree_for_budget", "gdn_round_capture",
@@ -271,6 +272,35 @@ def test_commit_verify_checks_before_launch():
     assert lib.gdn_tree_commit_verify(ctypes.byref(prev), fake, fake, fake, fake, fake,
                                       pneed - 1, ctypes.byref(cur), fake, fake, fake, fake, fake,
                                       fake, fake, fake, fake, fake, fake, need, fake, None) == 4
+
+
+def test_replay_verify_checks_before_launch():
+    """The replay form takes no workspace; it rejects mismatched descriptors,
+    non-WY modes and missing previous-round inputs on the host."""
+    lib = gt.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    prev = gt.make_desc(4, 2, 64, 64, 20, 8)
+    cur = gt.make_desc(4, 2, 64, 64, 30, 12)
+    ly = (gt.GdnLayerIO * 2)(*[gt.GdnLayerIO(*([0x1000] * 9)) for _ in range(2)])
+    ply = (gt.GdnLayerIO * 2)(*[gt.GdnLayerIO(*([0x1000] * 9)) for _ in range(2)])
+
+    def call(p=prev, c=cur, n=2, a=ply, b=ly):
+        return lib.gdn_tree_replay_verify_layers(ctypes.byref(p), ctypes.byref(c), n, fake, fake,
+                                                 fake, fake, fake, a, b, fake, None)
+
+    assert call(n=0) == 0
+    assert call(a=None) == 1
+    for field in ("k", "v", "alpha", "beta"):
+        setattr(ply[1], field, None)
+        assert call() == 1, field
+        setattr(ply[1], field, 0x1000)
+    ly[0].workspace = None                              # no workspace is needed
+    ly[0].S_out = None
+    assert call() == 1
+    ly[0].S_out = 0x1000
+    assert call(p=gt.make_desc(4, 2, 64, 64, 20, 8, gt.DTYPE_F32)) == 2
+    assert call(c=gt.make_desc(4, 2, 64, 64, 30, 12, gt.DTYPE_BF16, gt.MODE_FORK)) == 3
+    assert call(p=gt.make_desc(4, 2, 64, 64, 0, 8)) == 2
 
 
 # ------------------------------------------------------------------ rounds (gdn_round.h)

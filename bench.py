@@ -49,6 +49,7 @@ TRAFFIC_FILES = [os.path.join(ROOT, "profiles", "gdn_wy_c4_hbm_traffic.md"),
 # sources whose hash ties a recorded counter measurement to the kernels it measured
 KERNEL_SOURCES = {"verify": ["wy_verify.hip", "device_common.h", "launch.h"],
                   "commit_verify": ["wy_verify.hip", "device_common.h", "launch.h"],
+                  "replay_verify": ["wy_verify.hip", "device_common.h", "launch.h"],
                   "commit": ["wy_commit.hip", "device_common.h", "launch.h"],
                   "attn_verify": ["tree_attn.hip", "device_common.h", "launch.h",
                                   "tree_attn_api.cpp"]}
@@ -97,9 +98,11 @@ def parse():
     p.add_argument("--launch", default="layers", choices=["layers", "per-layer"],
                    help="WY leg: every layer in one launch per kernel (gdn_tree_*_layers) or one "
                         "launch per layer")
-    p.add_argument("--step", default="fused", choices=["fused", "separate"],
-                   help="what a timed step is: one fused previous-commit + verify launch, or "
-                        "the separate verify and commit launches (WY, layer-batched)")
+    p.add_argument("--step", default="replay", choices=["replay", "fused", "separate"],
+                   help="what a timed step is: one launch that replays the previous round's "
+                        "accepted path on the state and verifies (no workspace), one launch "
+                        "that commits the previous round from its pseudo-values and verifies, "
+                        "or the separate verify and commit launches (WY, layer-batched)")
     p.add_argument("--secondary-steps", type=int, default=20,
                    help="timed steps of the schedule that is not the headline (0 = skip)")
     p.add_argument("--per-layer-steps", type=int, default=5,
@@ -290,7 +293,7 @@ def attention_leg(args, gt, gi, w_trees, dev):
 
 
 def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev, steps,
-              warmup, per_layer=False):
+              warmup, per_layer=False, replay=False):
     """Consecutive rounds through gdn_tree_commit_verify_layers: each step
     commits the previous round's accepted paths into the state and verifies
     this round's trees against it, in one launch over all layers (one pass
@@ -314,11 +317,24 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
     # step i commits from workspace i % 2 and verifies into the other one; with
     # per_layer, one launch per layer (as a model forward issues them)
     groups = [[l] for l in range(L)] if per_layer else [list(range(L))]
-    calls = [[gt.prepare_commit_verify_layers(desc, desc, offsets, parents, accepted, offsets,
-                                              parents, [ios[i][l] for l in grp], nbytes,
-                                              [ios[1 - i][l] for l in grp], nbytes, status,
-                                              keep=(layers, ws, outs)) for grp in groups]
-             for i in range(2)]
+    if replay:
+        # the previous round's inputs are this workload's (same trees and
+        # inputs every round); no workspace
+        pio = [gt.make_layer_io(desc, k=ly["k"], v=ly["v"], alpha=ly["alpha"], beta=ly["beta"])
+               for ly in layers]
+        cio = [gt.make_layer_io(desc, q=ly["q"], k=ly["k"], v=ly["v"], alpha=ly["alpha"],
+                                beta=ly["beta"], S0=ly["S"], o=o, S_out=ly["S"])
+               for ly, o in zip(layers, outs)]
+        calls = [[gt.prepare_replay_verify_layers(desc, desc, offsets, parents, accepted, offsets,
+                                                  parents, [pio[l] for l in grp],
+                                                  [cio[l] for l in grp], status,
+                                                  keep=(layers, outs)) for grp in groups]] * 2
+    else:
+        calls = [[gt.prepare_commit_verify_layers(desc, desc, offsets, parents, accepted,
+                                                  offsets, parents, [ios[i][l] for l in grp],
+                                                  nbytes, [ios[1 - i][l] for l in grp], nbytes,
+                                                  status, keep=(layers, ws, outs))
+                  for grp in groups] for i in range(2)]
 
     def step(i):
         for c in calls[i % 2]:
@@ -342,6 +358,15 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
     med = times[steps // 2]
     per_layer = sum(times) / steps / L                              # mean launch, per layer
     fb = vb + cb - w.B * w.H * 4 * w.dv * w.dk                       # state read once
+    if replay:
+        # no pseudo-values or gate prefixes written; the path's k, v, alpha,
+        # beta read instead of its U, k, g
+        io_b = 2 if w.io == "bf16" else 4
+        import gdn_inputs as gi
+        path = sum(len(gi.path_to_root(p, int(a))) if a >= 0 else 0
+                   for p, a in zip(w.parents_list, w.accepted))
+        fb -= w.T * w.H * (4 * w.dv + 4)
+        fb += path * w.H * (io_b * w.dv + 8 - 4 * w.dv - 4)
     out = {"steps": steps, "warmup": warmup, "layers_per_launch": 1 if per_layer else L,
            "ms_per_step": round(1e3 * el / steps, 4),
            "launch_us_mean": round(sum(times) / steps, 2),
@@ -353,7 +378,8 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
            "achieved_GBs": round(fb / per_layer / 1e3, 1),
            "frac_hbm": round(fb / per_layer / 1e3 / HBM_PEAK_GBS, 4),
            "nodes_per_s_per_layer": round(w.T * L * steps / el, 1)}
-    log(f"fused previous commit + verify{' (one launch per layer)' if per_layer else ''}: {out}")
+    log(f"fused previous {'replay' if replay else 'commit'} + verify"
+        f"{' (one launch per layer)' if per_layer else ''}: {out}")
     del ws, outs, ios, calls, first
     torch.cuda.empty_cache()
     return out
@@ -691,8 +717,8 @@ def main():
 
     # ------------------------------------------------------------------ main leg
     batched = args.mode == "wy" and args.launch == "layers"
-    # the fused round is the headline step where it applies (WY, layer-batched)
-    headline_fused = args.step == "fused" and batched
+    # a fused round is the headline step where it applies (WY, layer-batched)
+    headline_fused = args.step in ("fused", "replay") and batched
     sep_steps = max(1, args.secondary_steps) if headline_fused else args.steps
     desc, nbytes, ver, com = make_calls(args.mode, batched)
     log(f"mode {args.mode}: workspace {nbytes / 2**20:.1f} MiB per layer, "
@@ -766,39 +792,56 @@ def main():
         per_layer["fused_us_per_layer"] = pf["us_per_layer"]
         per_layer["fused_frac_hbm"] = pf["frac_hbm"]
         per_layer["model_order_fused_nodes_per_s_per_layer"] = pf["nodes_per_s_per_layer"]
+        pr = fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev,
+                       args.per_layer_steps, 5, per_layer=True, replay=True)
+        per_layer["replay_us_per_layer"] = pr["us_per_layer"]
+        per_layer["replay_frac_hbm"] = pr["frac_hbm"]
+        per_layer["model_order_replay_nodes_per_s_per_layer"] = pr["nodes_per_s_per_layer"]
         log(f"one launch per layer: {per_layer}")
 
     # ---------------------------------------- previous commit fused into verify
-    fused = None
-    f_steps = args.steps if headline_fused else args.secondary_steps
-    if batched and f_steps > 0:
+    fused = replay = None
+    for kind in ("fused", "replay"):
+        f_steps = args.steps if headline_fused and args.step == kind else args.secondary_steps
+        if not batched or f_steps <= 0:
+            continue
         for ly in layers:
             ly.pop("o_wy", None), ly.pop("ws_wy", None)
         ver = com = None
         torch.cuda.empty_cache()
-        fused = fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev,
-                          f_steps, args.warmup)
-        t = recorded_traffic("commit_verify", args.config)     # per layer
-        fused["traffic_bytes"] = t
-        fused["traffic_over_alg"] = round(t / fused["alg_bytes_per_layer"], 3) if t else None
+        leg = fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, dev,
+                        f_steps, args.warmup, replay=kind == "replay")
+        t = recorded_traffic("commit_verify" if kind == "fused" else "replay_verify",
+                             args.config)                      # per layer
+        leg["traffic_bytes"] = t
+        leg["traffic_over_alg"] = round(t / leg["alg_bytes_per_layer"], 3) if t else None
+        if kind == "fused":
+            fused = leg
+        else:
+            replay = leg
     separate = None
     if headline_fused:
+        head = fused if args.step == "fused" else replay
+        kname = "commit_verify" if args.step == "fused" else "replay_verify"
         # the separate calls become the secondary figures; the fused kernel is
         # the headline step's only (and so dominant) kernel
         separate = {"value": round(nodes_per_s, 1), "ms_per_step": round(ms_step, 4),
                     "steps": sep_steps, "roofline": roof}
-        kern["commit_verify"] = {
-            "avg_us": fused["us_per_layer"], "alg_bytes": fused["alg_bytes_per_layer"],
-            "achieved_GBs": fused["achieved_GBs"], "frac_hbm": fused["frac_hbm"],
-            "layers_per_launch": L, "launch_us": fused["launch_us_mean"],
-            "alg_bytes_per_launch": fused["alg_bytes_per_layer"] * L,
-            "traffic_bytes": fused["traffic_bytes"], "traffic_over_alg": fused["traffic_over_alg"]}
-        roof = {"kernel": "wy_commit_verify", "bound": "hbm", "achieved": fused["achieved_GBs"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fused["frac_hbm"],
-                "traffic": fused["traffic_bytes"] * L if fused["traffic_bytes"] else None,
+    for kn, leg in (("commit_verify", fused), ("replay_verify", replay)):
+        if leg is not None:
+            kern[kn] = {
+                "avg_us": leg["us_per_layer"], "alg_bytes": leg["alg_bytes_per_layer"],
+                "achieved_GBs": leg["achieved_GBs"], "frac_hbm": leg["frac_hbm"],
+                "layers_per_launch": L, "launch_us": leg["launch_us_mean"],
+                "alg_bytes_per_launch": leg["alg_bytes_per_layer"] * L,
+                "traffic_bytes": leg["traffic_bytes"], "traffic_over_alg": leg["traffic_over_alg"]}
+    if headline_fused:
+        roof = {"kernel": "wy_" + kname, "bound": "hbm", "achieved": head["achieved_GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["frac_hbm"],
+                "traffic": head["traffic_bytes"] * L if head["traffic_bytes"] else None,
                 "layers_per_launch": L}
-        nodes_per_s = fused["nodes_per_s_per_layer"]
-        ms_step = fused["ms_per_step"]
+        nodes_per_s = head["nodes_per_s_per_layer"]
+        ms_step = head["ms_per_step"]
 
     # ------------------------------------------------------------- fork baseline
     fork = None
@@ -882,12 +925,15 @@ def main():
         "config": {"workload": gi.CONFIGS[args.config]["desc"], "config_id": args.config,
                    "layers": L, "batch": w.B, "total_nodes": w.T, "heads": w.H, "dk": w.dk,
                    "dv": w.dv, "io": w.io, "state": "fp32", "mode": args.mode,
-                   "step": ("previous commit + verify, fused" if headline_fused
+                   "step": ("previous round's accepted path replayed + verify, fused"
+                            if headline_fused and args.step == "replay" else
+                            "previous commit + verify, fused" if headline_fused
                             else "verify then commit"),
                    "launch": "all layers per launch" if batched else "one launch per layer",
                    "parallelism": "single-gpu"},
         "roofline": roof, "kernels": kern, "cpu_baseline": cpu, "fork_baseline": fork,
-        "per_layer_launches": per_layer, "fused_rounds": fused, "separate_calls": separate,
+        "per_layer_launches": per_layer, "fused_rounds": fused, "replay_rounds": replay,
+        "separate_calls": separate,
         "spec_state_per_request": spec, "fa_layers": fa,
         "round": rnd,
     }

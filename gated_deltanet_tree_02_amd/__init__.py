@@ -31,7 +31,7 @@ __all__ = [
     "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
     "prepare_attn_commit_layers",
     "gdn_tree_accept_greedy", "gdn_tree_accept_sampling", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
-    "gdn_round_plan", "gdn_round_tree_for_budget", "RoundGraph",
+    "gdn_round_plan", "gdn_round_tree_for_budget", "RoundGraph", "GdnRoundPrev",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdntree.so")
@@ -96,6 +96,13 @@ class GdnRoundIO(ctypes.Structure):
         ("draft_tokens", ctypes.c_void_p), ("target_tokens", ctypes.c_void_p),
         ("accepted", ctypes.c_void_p), ("accept_len", ctypes.c_void_p),
         ("next_token", ctypes.c_void_p), ("tree_status", ctypes.c_void_p),
+    ]
+
+
+class GdnRoundPrev(ctypes.Structure):
+    _fields_ = [
+        ("gdn", GdnTreeDesc), ("offsets", ctypes.c_void_p), ("parents", ctypes.c_void_p),
+        ("accepted", ctypes.c_void_p), ("gdn_layers", ctypes.POINTER(GdnLayerIO)),
     ]
 
 
@@ -166,6 +173,10 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_round_capture.argtypes = [R, ctypes.POINTER(GdnRoundIO), P,
                                               ctypes.POINTER(ctypes.c_void_p)]
             lib.gdn_round_capture.restype = I
+            lib.gdn_round_capture_replay.argtypes = [R, ctypes.POINTER(GdnRoundIO),
+                                                     ctypes.POINTER(GdnRoundPrev), P,
+                                                     ctypes.POINTER(ctypes.c_void_p)]
+            lib.gdn_round_capture_replay.restype = I
             lib.gdn_round_launch.argtypes = [P, P]
             lib.gdn_round_launch.restype = I
             lib.gdn_round_destroy.argtypes = [P]
@@ -835,7 +846,11 @@ class RoundGraph:
 
     def __init__(self, rdesc, offsets, parents, gdn_layers, attn_layers, arena, draft_tokens,
                  target_tokens, accepted, accept_len, next_token, tree_status, cache_len=None,
-                 layer_kinds=None, attn_scale=None, stream=None, keep=()):
+                 layer_kinds=None, attn_scale=None, stream=None, keep=(), prev=None):
+        """prev: None, or a dict for gdn_round_capture_replay (the previous
+        round committed by replay inside this round's GDN verifies): "desc"
+        (its GdnTreeDesc), "offsets", "parents", "accepted" (tensors) and
+        "gdn_layers" (GdnLayerIO list with k, v, alpha, beta)."""
         torch = _torch()
         g, a = rdesc.gdn, rdesc.attn
         B = g.num_seqs if rdesc.n_gdn_layers > 0 else a.num_seqs
@@ -874,11 +889,31 @@ class RoundGraph:
         self._lib = load_library()
         self._handle = ctypes.c_void_p()
         s = torch.cuda.current_stream(dev) if stream is None else stream
+        self._prev = None
+        if prev is not None:
+            pd = prev["desc"]
+            if len(prev["gdn_layers"]) != rdesc.n_gdn_layers:
+                raise ValueError("prev gdn_layers do not match the round descriptor")
+            pr = GdnRoundPrev()
+            pr.gdn = type(pd).from_buffer_copy(pd)
+            pr.offsets = _ptr(prev["offsets"], "prev offsets", i32, (pd.num_seqs + 1,), dev)
+            pr.parents = _ptr(prev["parents"], "prev parents", i32, (pd.total_nodes,), dev)
+            pr.accepted = _ptr(prev["accepted"], "prev accepted", i32, (pd.num_seqs,), dev)
+            self._prev_layers = _layers_array(prev["gdn_layers"])
+            pr.gdn_layers = ctypes.cast(self._prev_layers, ctypes.POINTER(GdnLayerIO))
+            self._prev = pr
+            self._keep = self._keep + ((prev["offsets"], prev["parents"], prev["accepted"]),)
         with torch.cuda.device(dev):
-            _check(self._lib.gdn_round_capture(ctypes.byref(self._rdesc), ctypes.byref(io),
-                                               ctypes.c_void_p(s.cuda_stream),
-                                               ctypes.byref(self._handle)),
-                   "gdn_round_capture")
+            if self._prev is None:
+                _check(self._lib.gdn_round_capture(ctypes.byref(self._rdesc), ctypes.byref(io),
+                                                   ctypes.c_void_p(s.cuda_stream),
+                                                   ctypes.byref(self._handle)),
+                       "gdn_round_capture")
+            else:
+                _check(self._lib.gdn_round_capture_replay(
+                    ctypes.byref(self._rdesc), ctypes.byref(io), ctypes.byref(self._prev),
+                    ctypes.c_void_p(s.cuda_stream), ctypes.byref(self._handle)),
+                    "gdn_round_capture_replay")
         self._dev = dev
 
     def launch(self, stream=None):

@@ -86,7 +86,7 @@ gdn_tree_desc tree_shape(const gdn_round_desc* d) {
 
 // Every call of one round, in order, on `stream`.
 gdn_status enqueue_round(const gdn_round_desc* d, const gdn_round_io* io,
-                         const gdn_round_layout& L, void* stream) {
+                         const gdn_round_layout& L, const gdn_round_prev* prev, void* stream) {
   const int ng = d->n_gdn_layers, na = d->n_attn_layers;
   char* base = static_cast<char*>(io->arena);
   int gi = 0, ai = 0;
@@ -95,9 +95,17 @@ gdn_status enqueue_round(const gdn_round_desc* d, const gdn_round_io* io,
     const int kind = io->layer_kinds ? io->layer_kinds[pos] : (pos < ng ? 0 : 1);
     if (kind == 0) {
       const gdn_layer_io& ly = io->gdn_layers[gi];
-      void* ws = L.gdn_ws_bytes ? base + (size_t)gi * L.gdn_ws_stride : nullptr;
-      st = gdn_tree_verify(&d->gdn, io->offsets, io->parents, ly.q, ly.k, ly.v, ly.alpha,
-                           ly.beta, ly.S0, ly.o, ws, L.gdn_ws_bytes, io->tree_status, stream);
+      if (prev) {
+        const gdn_layer_io& p = prev->gdn_layers[gi];
+        st = gdn_tree_replay_verify(&prev->gdn, prev->offsets, prev->parents, prev->accepted,
+                                    p.k, p.v, p.alpha, p.beta, &d->gdn, io->offsets,
+                                    io->parents, ly.q, ly.k, ly.v, ly.alpha, ly.beta, ly.S0,
+                                    ly.S_out, ly.o, io->tree_status, stream);
+      } else {
+        void* ws = L.gdn_ws_bytes ? base + (size_t)gi * L.gdn_ws_stride : nullptr;
+        st = gdn_tree_verify(&d->gdn, io->offsets, io->parents, ly.q, ly.k, ly.v, ly.alpha,
+                             ly.beta, ly.S0, ly.o, ws, L.gdn_ws_bytes, io->tree_status, stream);
+      }
       ++gi;
     } else {
       const gdn_attn_layer_io& ly = io->attn_layers[ai];
@@ -115,7 +123,7 @@ gdn_status enqueue_round(const gdn_round_desc* d, const gdn_round_io* io,
                               io->target_tokens, io->accepted, io->accept_len, io->next_token,
                               io->tree_status, stream);
   if (st != GDN_OK) return st;
-  if (ng > 0) {
+  if (ng > 0 && !prev) {
     std::vector<gdn_layer_io> layers(io->gdn_layers, io->gdn_layers + ng);
     for (int l = 0; l < ng; ++l)
       layers[l].workspace = L.gdn_ws_bytes ? base + (size_t)l * L.gdn_ws_stride : nullptr;
@@ -236,8 +244,12 @@ gdn_status gdn_round_tree_for_budget(const gdn_round_desc* desc, size_t budget_b
   return GDN_OK;
 }
 
-gdn_status gdn_round_capture(const gdn_round_desc* desc, const gdn_round_io* io, void* stream,
-                             gdn_round_graph* out) {
+}  // extern "C"
+
+namespace {
+
+gdn_status capture_round(const gdn_round_desc* desc, const gdn_round_io* io,
+                         const gdn_round_prev* prev, void* stream, gdn_round_graph* out) {
   if (desc == nullptr || io == nullptr || out == nullptr) return GDN_ERR_NULL_PTR;
   gdn_status st = check_round(desc);
   if (st != GDN_OK) return st;
@@ -256,6 +268,23 @@ gdn_status gdn_round_capture(const gdn_round_desc* desc, const gdn_round_io* io,
   plan(desc, &L);
   if (io->arena_bytes < L.total_bytes) return GDN_ERR_WORKSPACE;
   if (L.total_bytes > 0 && io->arena == nullptr) return GDN_ERR_NULL_PTR;
+  if (prev && ng > 0) {
+    // the replay's host checks, before capture starts (enqueueing repeats them)
+    if (!prev->gdn_layers) return GDN_ERR_NULL_PTR;
+    for (int l = 0; l < ng; ++l) {
+      const gdn_layer_io& y = io->gdn_layers[l];
+      st = gdn_tree_replay_verify_layers(&prev->gdn, &desc->gdn, 0, prev->offsets,
+                                         prev->parents, prev->accepted, io->offsets,
+                                         io->parents, &prev->gdn_layers[l], &y,
+                                         io->tree_status, nullptr);
+      if (st != GDN_OK) return st;
+      const gdn_layer_io& p = prev->gdn_layers[l];
+      if (!y.S0 || !y.S_out || !p.k || !p.v || !p.alpha || !p.beta || !prev->offsets ||
+          !prev->parents || !prev->accepted)
+        return GDN_ERR_NULL_PTR;
+      if (desc->gdn.num_seqs > 0 && prev->gdn.total_nodes < 1) return GDN_ERR_BAD_SHAPE;
+    }
+  }
   if (stream == nullptr) return GDN_ERR_GRAPH;  // the null stream cannot be captured
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -263,7 +292,7 @@ gdn_status gdn_round_capture(const gdn_round_desc* desc, const gdn_round_io* io,
     return GDN_ERR_GRAPH;
   if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess)
     return GDN_ERR_GRAPH;
-  st = enqueue_round(desc, io, L, stream);
+  st = enqueue_round(desc, io, L, prev, stream);
   hipGraph_t graph = nullptr;
   const hipError_t e = hipStreamEndCapture(s, &graph);
   if (st != GDN_OK || e != hipSuccess) {
@@ -281,6 +310,22 @@ gdn_status gdn_round_capture(const gdn_round_desc* desc, const gdn_round_io* io,
   }
   *out = g;
   return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_round_capture(const gdn_round_desc* desc, const gdn_round_io* io, void* stream,
+                             gdn_round_graph* out) {
+  return capture_round(desc, io, nullptr, stream, out);
+}
+
+gdn_status gdn_round_capture_replay(const gdn_round_desc* desc, const gdn_round_io* io,
+                                    const gdn_round_prev* prev, void* stream,
+                                    gdn_round_graph* out) {
+  if (prev == nullptr) return GDN_ERR_NULL_PTR;
+  return capture_round(desc, io, prev, stream, out);
 }
 
 gdn_status gdn_round_launch(gdn_round_graph graph, void* stream) {

@@ -184,6 +184,34 @@ typedef struct gdn_round_graph_s* gdn_round_graph;
 gdn_status gdn_round_capture(const gdn_round_desc* desc, const gdn_round_io* io, void* stream,
                              gdn_round_graph* out);
 
+/* The previous round, for a round whose GDN layers commit it inside their
+ * verify by replay (gdn_tree_replay_verify, gdn_tree.h): its GDN shape
+ * (num_seqs, num_heads, dk, dv and io_dtype as the round's; its own
+ * total_nodes and max_nodes), its tree, its accepted nodes, and per GDN
+ * layer its k, v, alpha and beta (gdn_layers: HOST array of the round's
+ * n_gdn_layers entries, fields k, v, alpha, beta used). Device pointers
+ * otherwise. */
+typedef struct {
+  gdn_tree_desc gdn;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* accepted;
+  const gdn_layer_io* gdn_layers;
+} gdn_round_prev;
+
+/* gdn_round_capture for a round that also commits the previous one: every
+ * GDN layer's verify is gdn_tree_replay_verify (the previous round's accepted
+ * path replayed on the layer's state, S0 -> S_out, then this round's tree
+ * verified against it, fork page section 7 step 4 of one round joined to step
+ * 2 of the next), and the round ends after the attention layers' KV append:
+ * its own GDN commit is left to the next round's graph. The GDN layers' S0
+ * and S_out are used, their workspace fields are ignored and the arena's GDN
+ * part is not written. The buffers of the previous round must be other than
+ * this round's (callers alternate two sets and capture one graph each way). */
+gdn_status gdn_round_capture_replay(const gdn_round_desc* desc, const gdn_round_io* io,
+                                    const gdn_round_prev* prev, void* stream,
+                                    gdn_round_graph* out);
+
 /* Run a captured round on `stream` (any stream of the same device). Runs of
  * one graph must not overlap. */
 gdn_status gdn_round_launch(gdn_round_graph graph, void* stream);

@@ -16,6 +16,7 @@ import torch
 
 import gated_deltanet_tree_02_amd as gt
 import gdn_inputs as gi
+import oracle
 from oracle import accept as oacc
 
 pytestmark = pytest.mark.gpu
@@ -270,6 +271,109 @@ def test_round_graph_replays_equal_eager_calls(mode):
             assert rel_err_rows(from_dev_io(G.o[0]).astype(np.float64), o_ref) <= TOL["bf16"]
             ao_ref, _ = oracle_attn(aws[0])
             assert rel_err_rows(from_dev_io(G.ao[0]).astype(np.float64), ao_ref) <= TOL["bf16"]
+    graph.close()
+
+
+def test_replay_round_graph_equals_eager_calls_and_the_oracle():
+    """A round captured with gdn_round_capture_replay: every GDN layer replays
+    the previous round's accepted paths on its state and verifies this round's
+    trees (another tree set), then acceptance and the attention KV append; no
+    GDN commit. Replays equal the same calls issued eagerly, and the first
+    one equals the oracle's commit of the previous round then its verify."""
+    rng = np.random.default_rng(21)
+    trees_p = [gi.kary_parents(3, 2), gi.chain_parents(6), gi.random_tree_parents(rng, 8, 30),
+               [-1], gi.kary_parents(2, 3)]
+    trees = [gi.kary_parents(2, 2), gi.chain_parents(5), gi.branching_parents([3, 2]), [-1],
+             gi.random_tree_parents(rng, 10, 40)]
+    n_gdn, n_attn = 3, 2
+    kinds = [0, 1, 0, 0, 1]
+    wp = gi.make_workload(trees_p, H=4, dk=128, dv=128, io="bf16", layers=n_gdn, seed=22)
+    w = gi.make_workload(trees, H=4, dk=128, dv=128, io="bf16", layers=n_gdn, seed=23)
+    lens = [10, 0, 40, 5, 63]
+    cap = 128
+    aws = [gi.make_attn_workload(trees, 8, 2, 128, cap, lens, seed=90 + l) for l in range(n_attn)]
+    pdesc = gt.make_desc(wp.B, 4, 128, 128, wp.T, 64, gt.DTYPE_BF16)
+    gdesc = gt.make_desc(w.B, 4, 128, 128, w.T, 64, gt.DTYPE_BF16)
+    adesc = gt.make_attn_desc(w.B, 8, 2, 128, w.T, 64, cap, cap)
+    rdesc = gt.make_round_desc(gdesc, n_gdn, adesc, n_attn)
+    layout = gt.gdn_round_plan(rdesc)
+    p_off, p_par, p_acc = i32(wp.offsets), i32(wp.parents), i32(wp.accepted)
+    offsets, parents = i32(w.offsets), i32(w.parents)
+    pins = [dict(k=to_dev_io(wp.k[l], "bf16"), v=to_dev_io(wp.v[l], "bf16"),
+                 alpha=f32(wp.alpha[l]), beta=f32(wp.beta[l])) for l in range(n_gdn)]
+    ins = [dict(q=to_dev_io(w.q[l], "bf16"), k=to_dev_io(w.k[l], "bf16"),
+                v=to_dev_io(w.v[l], "bf16"), alpha=f32(w.alpha[l]), beta=f32(w.beta[l]))
+           for l in range(n_gdn)]
+    ains = [dict(q=to_dev_io(a.q, "bf16"), k=to_dev_io(a.k, "bf16"), v=to_dev_io(a.v, "bf16"))
+            for a in aws]
+    draft = torch.zeros(w.T, dtype=torch.int32, device="cuda")
+    target = torch.zeros(w.T, dtype=torch.int32, device="cuda")
+    E = _RoundState(w, aws, lens)
+    G = _RoundState(w, aws, lens)
+    for X in (E, G):                      # the states the previous round left
+        X.S = [f32(wp.S0[l]) for l in range(n_gdn)]
+    arena = torch.empty(max(1, layout.total_bytes), dtype=torch.uint8, device="cuda")
+    gdn_io = [gt.make_layer_io(gdesc, q=ins[l]["q"], k=ins[l]["k"], v=ins[l]["v"],
+                               alpha=ins[l]["alpha"], beta=ins[l]["beta"], S0=G.S[l], o=G.o[l],
+                               S_out=G.S[l]) for l in range(n_gdn)]
+    attn_io = [gt.make_attn_layer_io(adesc, q=ains[l]["q"], k=ains[l]["k"], v=ains[l]["v"],
+                                     k_cache=G.kc[l], v_cache=G.vc[l], o=G.ao[l])
+               for l in range(n_attn)]
+    prev_io = [gt.make_layer_io(pdesc, k=x["k"], v=x["v"], alpha=x["alpha"], beta=x["beta"])
+               for x in pins]
+    stream = torch.cuda.Stream()
+    graph = gt.RoundGraph(rdesc, offsets, parents, gdn_io, attn_io, arena, draft, target, G.acc,
+                          G.alen, G.nxt, G.st, cache_len=G.cache_len, layer_kinds=kinds,
+                          stream=stream, keep=(ins, ains, pins, G),
+                          prev=dict(desc=pdesc, offsets=p_off, parents=p_par, accepted=p_acc,
+                                    gdn_layers=prev_io))
+    anb = gt.gdn_tree_attn_workspace_bytes(adesc)
+    aws_e = [torch.empty(anb, dtype=torch.uint8, device="cuda") if anb else None
+             for _ in range(n_attn)]
+    e_attn_io = [gt.make_attn_layer_io(adesc, k=ains[l]["k"], v=ains[l]["v"], k_cache=E.kc[l],
+                                       v_cache=E.vc[l]) for l in range(n_attn)]
+    for rnd in range(3):
+        acc = [gi.pick_accepted(rng, t) for t in trees]
+        d_np, t_np = gi.draft_target_tokens(rng, trees, acc)
+        draft.copy_(torch.from_numpy(d_np))
+        target.copy_(torch.from_numpy(t_np))
+        torch.cuda.synchronize()
+        gi_, ai_ = 0, 0
+        for kind in kinds:
+            if kind == 0:
+                x, px = ins[gi_], pins[gi_]
+                gt.gdn_tree_replay_verify(pdesc, p_off, p_par, p_acc, px["k"], px["v"],
+                                          px["alpha"], px["beta"], gdesc, offsets, parents,
+                                          x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                                          E.S[gi_], E.S[gi_], E.o[gi_], E.st)
+                gi_ += 1
+            else:
+                x = ains[ai_]
+                gt.gdn_tree_attn_verify(adesc, offsets, parents, x["q"], x["k"], x["v"],
+                                        E.kc[ai_], E.vc[ai_], E.cache_len, E.ao[ai_], aws_e[ai_],
+                                        E.st)
+                ai_ += 1
+        gt.gdn_tree_accept_greedy(gdesc, offsets, parents, draft, target, E.acc, E.alen, E.nxt,
+                                  E.st)
+        gt.gdn_tree_attn_commit_layers(adesc, offsets, parents, E.acc, e_attn_io, E.cache_len,
+                                       E.st)
+        torch.cuda.synchronize()
+        graph.launch(stream)
+        stream.synchronize()
+        e, g = E.snapshot(), G.snapshot()
+        _say("replay round", rnd, "accepted", g["acc"].tolist(), "status", g["st"].tolist())
+        np.testing.assert_array_equal(g["acc"], acc)
+        _same(e, g)
+        if rnd == 0:
+            for l in range(n_gdn):
+                S_ref, _ = oracle.commit(wp.offsets, wp.parents, wp.accepted, wp.k[l], wp.v[l],
+                                         wp.alpha[l], wp.beta[l], wp.S0[l])
+                o_ref, _ = oracle.verify(w.offsets, w.parents, w.q[l], w.k[l], w.v[l],
+                                         w.alpha[l], w.beta[l], S_ref)
+                g_s = G.S[l].cpu().numpy().astype(np.float64)
+                assert rel_err_rows(g_s.reshape(w.B * 4, -1), S_ref.reshape(w.B * 4, -1)) \
+                    <= TOL["bf16"]
+                assert rel_err_rows(from_dev_io(G.o[l]).astype(np.float64), o_ref) <= TOL["bf16"]
     graph.close()
 
 

@@ -36,6 +36,7 @@ def test_library_exports_every_declared_symbol():
                             "gdn_tree_accept_greedy", "gdn_tree_accept_sampling",
                             "gdn_round_plan",
                             "gdn_round_tree_for_budget", "gdn_round_capture",
+                            "gdn_round_capture_replay",
                             "gdn_round_launch", "gdn_round_destroy"])
     for name in names:
         assert hasattr(lib, name), name
@@ -322,6 +323,8 @@ def test_round_structs_match_headers():
     assert _struct_fields(ROUND_HEADER, "gdn_round_layout") == [
         f for f, _ in gt.GdnRoundLayout._fields_]
     assert _struct_fields(ROUND_HEADER, "gdn_round_io") == [f for f, _ in gt.GdnRoundIO._fields_]
+    assert _struct_fields(ROUND_HEADER, "gdn_round_prev") == [
+        f for f, _ in gt.GdnRoundPrev._fields_]
     assert _struct_fields(ATTN_HEADER, "gdn_attn_layer_io") == [
         f for f, _ in gt.GdnAttnLayerIO._fields_]
     assert ctypes.sizeof(gt.GdnRoundDesc) == 4 * (9 + 1 + 8 + 1)
@@ -498,6 +501,22 @@ def test_accept_and_round_calls_check_before_launch():
     assert lib.gdn_round_capture(ctypes.byref(r), ctypes.byref(io), None, ctypes.byref(h)) == 6
     assert not h.value
     assert lib.gdn_round_capture(ctypes.byref(r), None, fake, ctypes.byref(h)) == 1
+    # the replay form: the previous round is required and checked before capture
+    cap_r = lambda pr: lib.gdn_round_capture_replay(ctypes.byref(r), ctypes.byref(io),
+                                                    pr, None, ctypes.byref(h))
+    assert cap_r(None) == 1
+    pl = (gt.GdnLayerIO * 2)(*[gt.GdnLayerIO(*([0x1000] * 9)) for _ in range(2)])
+    prev = gt.GdnRoundPrev()
+    prev.gdn = gt.make_desc(2, 16, 128, 128, 14, 8)
+    prev.offsets = prev.parents = prev.accepted = 0x1000
+    prev.gdn_layers = ctypes.cast(pl, ctypes.POINTER(gt.GdnLayerIO))
+    assert cap_r(ctypes.byref(prev)) == 6             # checks pass; the null stream is refused
+    pl[1].v = None
+    assert cap_r(ctypes.byref(prev)) == 1
+    pl[1].v = 0x1000
+    prev.gdn = gt.make_desc(2, 8, 128, 128, 14, 8)      # head count differs
+    assert cap_r(ctypes.byref(prev)) == 2
+    assert not h.value
     assert lib.gdn_round_launch(None, None) == 1
     lib.gdn_round_destroy(None)
     assert "graph" in gt.gdn_tree_status_string(6)

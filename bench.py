@@ -606,6 +606,24 @@ def round_leg(args, gt, gi, w, layers, offsets, parents, dev):
     if not np.array_equal(got_len, expect):
         raise RuntimeError("round acceptance differs from the drawn accepted paths")
     graph.close()
+    # the same round with the previous round's GDN commit replayed inside the
+    # GDN verifies (gdn_round_capture_replay): the previous round is the same
+    # trees and inputs with the workload's accepted paths (a buffer of its own)
+    prev_acc = torch.from_numpy(np.ascontiguousarray(w.accepted, np.int32)).to(dev)
+    prev_io = [gt.make_layer_io(gdesc, k=ly["k"], v=ly["v"], alpha=ly["alpha"], beta=ly["beta"])
+               for ly in layers]
+    rgraph = gt.RoundGraph(rdesc, offsets, parents, gdn_io, attn_io, arena, draft, target, acc,
+                           alen, nxt, status, cache_len=cache_len, layer_kinds=kinds,
+                           stream=stream, keep=(layers, attn, outs),
+                           prev=dict(desc=gdesc, offsets=offsets, parents=parents,
+                                     accepted=prev_acc, gdn_layers=prev_io))
+    rlaunch = lambda: rgraph.launch(stream)
+    for _ in range(2):
+        rlaunch()
+        with torch.cuda.stream(stream):
+            cache_len.copy_(lens0)
+    r_wall, r_med, r_times = timed(rlaunch, steps)
+    rgraph.close()
     out = {
         "layers": {"gdn": n_gdn, "attention": n_attn,
                    "order": "3 GDN, 1 attention, x8" if kinds[:4] == [0, 0, 0, 1] else "GDN, attention"},
@@ -615,6 +633,11 @@ def round_leg(args, gt, gi, w, layers, offsets, parents, dev):
         "eager_ms_per_round_median": round(e_med, 4),
         "graph_wall_ms_per_round": round(g_wall, 4), "eager_wall_ms_per_round": round(e_wall, 4),
         "kernel_launches_per_round": n_gdn + n_attn + 3,
+        "replay_graph_ms_per_round_median": round(r_med, 4),
+        "replay_graph_ms_per_round_p10_p90": [round(r_times[steps // 10], 4),
+                                              round(r_times[(9 * steps) // 10], 4)],
+        "replay_nodes_per_s_all_layers": round(T / (r_med * 1e-3), 1),
+        "replay_kernel_launches_per_round": n_gdn + n_attn + 2,
         "nodes_per_s_all_layers": round(T / (g_med * 1e-3), 1),
         "mean_accept_len": round(float(got_len.mean()), 3),
         "arena_bytes": int(layout.total_bytes),

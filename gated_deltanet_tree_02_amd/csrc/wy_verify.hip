@@ -32,6 +32,16 @@
 //     fused with the output o_t = G_t Y_t + sum_{i in A(t)} A_qk[t,i] u_i.
 //  6. o (staged in LDS) and U leave as whole contiguous rows (16 bytes per
 //     lane), never as the 32-64 byte pieces the MFMA result layout would give.
+//
+// The same kernel also joins the previous round's commit to this round's
+// verify (the fork page's section 7: step 4 of one round, then step 2 of the
+// next), so a round reads each state once: once a wave's S0 fragment has
+// landed it applies the previous accepted path to it in registers (phase 4b),
+// writes the committed fragment out and verifies against it. The path is
+// applied either from the previous round's pseudo-values and gate prefixes
+// (CommitVerifyLayersArgs: S = G_a S0 + sum_i (G_a/G_i) u_i k_i^T), or by
+// replaying the gated delta rule along it from its own k, v, alpha, beta
+// (ReplayVerifyLayersArgs), in which case this round writes no U and no g.
 #include <type_traits>
 
 #include "device_common.h"

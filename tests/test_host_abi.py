@@ -302,6 +302,13 @@ def test_replay_verify_checks_before_launch():
     assert call(p=gt.make_desc(4, 2, 64, 64, 20, 8, gt.DTYPE_F32)) == 2
     assert call(c=gt.make_desc(4, 2, 64, 64, 30, 12, gt.DTYPE_BF16, gt.MODE_FORK)) == 3
     assert call(p=gt.make_desc(4, 2, 64, 64, 0, 8)) == 2
+    # an empty batch enqueues nothing, whatever the pointers
+    e0, e1 = gt.make_desc(0, 2, 64, 64, 0, 8), gt.make_desc(0, 2, 64, 64, 0, 8)
+    assert lib.gdn_tree_replay_verify_layers(ctypes.byref(e0), ctypes.byref(e1), 2, None, None,
+                                             None, None, None, None, None, None, None) == 0
+    assert lib.gdn_tree_commit_verify_layers(ctypes.byref(e0), ctypes.byref(e1), 2, None, None,
+                                             None, None, None, None, 0, None, 0, None,
+                                             None) == 0
 
 
 # ------------------------------------------------------------------ rounds (gdn_round.h)

@@ -80,6 +80,18 @@ def recorded_traffic(kind, config):
     return None
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -921,7 +933,8 @@ def main():
         cpu = {"value": round(done_nodes / spent, 1), "unit": "nodes/s/layer", "cores": threads,
                "kind": "oracle",
                "sample": f"{used_layers} of {L} layers x {w.B} seqs x {w.H} heads, verify+commit, "
-                         f"fp64 per-path replay, {spent:.1f} s"}
+                         f"fp64 per-path replay, {spent:.1f} s",
+               "cpu_model": cpu_model()}
         log(f"cpu oracle: {cpu}")
 
     fa = None

@@ -935,6 +935,21 @@ def main():
                "sample": f"{used_layers} of {L} layers x {w.B} seqs x {w.H} heads, verify+commit, "
                          f"fp64 per-path replay, {spent:.1f} s",
                "cpu_model": cpu_model()}
+        # the k=2 d=3 batch (32 sequences, one layer) on one host thread
+        w3 = gi.make_config("c3")
+        x3 = [np.ascontiguousarray(a[0], np.float64)
+              for a in (w3.q, w3.k, w3.v, w3.alpha, w3.beta, w3.S0)]
+        oracle.set_threads(1)
+        try:
+            t1 = time.perf_counter()
+            oracle.verify(w3.offsets, w3.parents, *x3)
+            oracle.commit(w3.offsets, w3.parents, w3.accepted, x3[1], x3[2], x3[3], x3[4], x3[5])
+            one = time.perf_counter() - t1
+        finally:
+            oracle.set_threads(threads)
+        cpu["single_thread_k2d3"] = {"value": round(w3.T / one, 1), "unit": "nodes/s/layer",
+                                     "seconds": round(one, 3),
+                                     "sample": "tree k=2 d=3, 32 seqs x 16 heads, one layer"}
         log(f"cpu oracle: {cpu}")
 
     fa = None

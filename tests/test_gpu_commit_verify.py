@@ -304,3 +304,52 @@ def test_commit_verify_full_size_one_layer(name, nseq, mode):
     e_o = rel_err_rows(C.o_np()[rows], o_ref)
     _say(f"{name} ({mode}) full size, {len(seqs)} sequences: S err {e_s:.3e}, o err {e_o:.3e}")
     assert e_s <= TOL["bf16"] and e_o <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_multi_round_pipeline_against_the_oracle(mode):
+    """Six rounds, each with its own random trees, inputs and accepted paths:
+    round r's fused call commits round r-1 and verifies round r (in place on
+    the state); every round's outputs, and the state after the last round's
+    separate commit, follow the oracle's sequence of commits and verifies."""
+    rng = np.random.default_rng(99)
+    B, H, d, R = 4, 2, 128, 6
+    rounds = []
+    for r in range(R):
+        trees = [gi.random_tree_parents(rng, 2, 48, max_depth=5) for _ in range(B)]
+        w = gi.make_workload(trees, H, d, d, io="bf16", seed=500 + r)
+        if r == 1:
+            w.accepted[0] = -1                     # one sequence keeps its state once
+        rounds.append(w)
+    layers = [DeviceLayer(w, 0, max_nodes=64) for w in rounds]
+    S = layers[0].S0                               # the state, updated in place
+    S_ref = np.asarray(rounds[0].S0[0], np.float64)
+    for r, (w, C) in enumerate(zip(rounds, layers)):
+        if r == 0:
+            C.S0 = S
+            C.verify()
+        else:
+            _fused(layers[r - 1], C, S, S, mode)
+            P = rounds[r - 1]
+            S_ref, _ = oracle.commit(P.offsets, P.parents, P.accepted, P.k[0], P.v[0],
+                                     P.alpha[0], P.beta[0], S_ref)
+        torch.cuda.synchronize()
+        assert np.all(C.status.cpu().numpy() == 0), r
+        o_ref, _ = oracle.verify(w.offsets, w.parents, w.q[0], w.k[0], w.v[0], w.alpha[0],
+                                 w.beta[0], S_ref)
+        e_o = rel_err_rows(C.o_np(), o_ref)
+        e_s = rel_err_states(S.cpu().numpy(), S_ref)
+        _say(f"multi-round ({mode}) round {r}: o err {e_o:.3e}, state err {e_s:.3e}")
+        assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"], r
+    # the last round committed with the separate call (from its workspace)
+    last, L = rounds[-1], layers[-1]
+    L.S0 = S.clone()                                # the state the last round verified against
+    if mode == "replay":                            # replay verifies write no workspace
+        L.verify()
+    L.commit(S_out=S)
+    torch.cuda.synchronize()
+    S_ref, _ = oracle.commit(last.offsets, last.parents, last.accepted, last.k[0], last.v[0],
+                             last.alpha[0], last.beta[0], S_ref)
+    e_s = rel_err_states(S.cpu().numpy(), S_ref)
+    _say(f"multi-round ({mode}) final commit: state err {e_s:.3e}")
+    assert e_s <= TOL["bf16"]

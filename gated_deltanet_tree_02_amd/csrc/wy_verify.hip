@@ -427,9 +427,10 @@ void wy_verify_kernel(const Args args) {
       sraw[s][1] = *reinterpret_cast<const float4*>(rowp + 32 * s + 4);
     }
   };
-  // (fused) odd workgroups take the state first, even ones after their rows,
-  // so that the two workgroups of a CU do not load in step
-  const bool early_S0 = kFused && (blockIdx.x & 1);
+  // (fused from pseudo-values) odd workgroups take the state first, even ones
+  // after their rows, so that the two workgroups of a CU do not load in step;
+  // the replay kernel, which writes less at its end, does best with all late
+  const bool early_S0 = kFused && !kReplay && (blockIdx.x & 1);
   if (early_S0) load_S0();
   // ---- 2. staged chunks to LDS (swizzled), then the tree prologue, computed
   // by every wave so that no branch separates the loads from their first use.

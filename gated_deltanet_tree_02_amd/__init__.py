@@ -28,6 +28,8 @@ __all__ = [
     "prepare_verify_layers", "prepare_commit_layers",
     "gdn_tree_commit_verify", "gdn_tree_commit_verify_layers", "prepare_commit_verify_layers",
     "gdn_tree_replay_verify", "gdn_tree_replay_verify_layers", "prepare_replay_verify_layers",
+    "gdn_tree_replay_commit", "gdn_tree_replay_commit_layers", "prepare_replay_commit_layers",
+    "PREV_SHIFT", "prev_code",
     "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
     "prepare_attn_commit_layers",
     "gdn_tree_accept_greedy", "gdn_tree_accept_sampling", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
@@ -41,6 +43,13 @@ MODE_WY, MODE_FORK, MODE_FORK_DELTA = 0, 1, 2
 MAX_NODES = 64
 TREE_STATUS = {0: "ok", 1: "bad root", 2: "bad parent", 3: "bad size", 4: "bad accepted",
                5: "too deep", 6: "cache full", 7: "bad token"}
+# fused round-boundary calls: the previous round's commit code sits above this shift
+PREV_SHIFT = 4
+
+
+def prev_code(code: int) -> int:
+    """A previous-round code in the position the fused calls report it."""
+    return code << PREV_SHIFT
 
 
 class GdnError(RuntimeError):
@@ -155,6 +164,10 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_replay_verify_layers.argtypes = [D, D, ctypes.c_int32, P, P, P, P, P,
                                                           LY, LY, P, P]
             lib.gdn_tree_replay_verify_layers.restype = I
+            lib.gdn_tree_replay_commit.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
+            lib.gdn_tree_replay_commit.restype = I
+            lib.gdn_tree_replay_commit_layers.argtypes = [D, ctypes.c_int32, P, P, P, LY, P, P]
+            lib.gdn_tree_replay_commit_layers.restype = I
             AL = ctypes.POINTER(GdnAttnLayerIO)
             lib.gdn_tree_attn_commit_layers.argtypes = [A, ctypes.c_int32, P, P, P, AL, P, P, P]
             lib.gdn_tree_attn_commit_layers.restype = I
@@ -704,6 +717,63 @@ def prepare_replay_verify_layers(prev_desc, desc, prev_offsets, prev_parents, ac
     return PreparedCall("gdn_tree_replay_verify_layers", prev_desc, args, _stream(stream, dev),
                         (prev_offsets, prev_parents, accepted, offsets, parents, tree_status,
                          held, tuple(keep)))
+
+
+def gdn_tree_replay_commit(desc, offsets, parents, accepted, k, v, alpha, beta, S0, S_out,
+                           tree_status, stream=None):
+    """Commit by replaying the accepted path from its own k, v, alpha, beta
+    (no workspace): S_out = the accepted node's state, or S0 for -1."""
+    torch = _torch()
+    B, H, T, dk, dv = desc.num_seqs, desc.num_heads, desc.total_nodes, desc.dk, desc.dv
+    dev = offsets.device
+    io = _io_dtype(desc)
+    args = [_ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+            _ptr(parents, "parents", torch.int32, (T,), dev),
+            _ptr(accepted, "accepted", torch.int32, (B,), dev),
+            _ptr(k, "k", io, (T, H, dk), dev), _ptr(v, "v", io, (T, H, dv), dev),
+            _ptr(alpha, "alpha", torch.float32, (T, H), dev),
+            _ptr(beta, "beta", torch.float32, (T, H), dev),
+            _ptr(S0, "S0", torch.float32, (B, H, dv, dk), dev),
+            _ptr(S_out, "S_out", torch.float32, (B, H, dv, dk), dev),
+            _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_replay_commit(ctypes.byref(desc), *args,
+                                                     _stream(stream, dev)),
+               "gdn_tree_replay_commit")
+
+
+def _replay_commit_layers_args(desc, offsets, parents, accepted, layers, tree_status):
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    arr = _layers_array(layers)
+    args = [ctypes.c_int32(len(layers)), _ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+            _ptr(parents, "parents", torch.int32, (T,), dev),
+            _ptr(accepted, "accepted", torch.int32, (B,), dev), arr,
+            _ptr(tree_status, "tree_status", torch.int32, (B,), dev)]
+    return dev, args, arr
+
+
+def gdn_tree_replay_commit_layers(desc, offsets, parents, accepted, layers, tree_status,
+                                  stream=None):
+    """gdn_tree_replay_commit for every layer in `layers` (GdnLayerIO: k, v,
+    alpha, beta, S0, S_out) on the shared tree."""
+    torch = _torch()
+    dev, args, _ = _replay_commit_layers_args(desc, offsets, parents, accepted, layers,
+                                              tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_replay_commit_layers(ctypes.byref(desc), *args,
+                                                            _stream(stream, dev)),
+               "gdn_tree_replay_commit_layers")
+
+
+def prepare_replay_commit_layers(desc, offsets, parents, accepted, layers, tree_status, keep=(),
+                                 stream=None) -> PreparedCall:
+    """Marshalled gdn_tree_replay_commit_layers; `keep` holds the tensors behind `layers`."""
+    dev, args, arr = _replay_commit_layers_args(desc, offsets, parents, accepted, layers,
+                                                tree_status)
+    return PreparedCall("gdn_tree_replay_commit_layers", desc, args, _stream(stream, dev),
+                        (offsets, parents, accepted, tree_status, arr, tuple(keep)))
 
 
 # ------------------------------------------------------------------ attention layers, batched

@@ -20,9 +20,12 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
   const int b = blockIdx.x * 4 + wave;
   if (b >= a.B) return;  // wave-uniform
   const TreeLane tl = load_tree(b, a.T, a.max_nodes, a.offsets, a.parents, lane);
-  if (tl.status != GDN_TREE_OK) {
+  // in a captured round, a sequence an earlier step rejected keeps its code
+  // and accepts nothing, so that no commit changes its state
+  const int earlier = a.merge ? a.status[b] : GDN_TREE_OK;
+  if (tl.status != GDN_TREE_OK || earlier != GDN_TREE_OK) {
     if (lane == 0) {
-      a.status[b] = tl.status;
+      put_status(a.status, b, tl.status, a.merge);
       a.accepted[b] = -1;
       a.accept_len[b] = 0;
       a.next_token[b] = -1;
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
   }
   const int next = __shfl(tgt, cur, kWave);
   if (lane == 0) {
-    a.status[b] = GDN_TREE_OK;
+    put_status(a.status, b, GDN_TREE_OK, a.merge);
     a.accepted[b] = cur;
     a.accept_len[b] = len;
     a.next_token[b] = next;
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
 // next p, so a final draw after a rejection needs no further pass (a draw
 // with no rejection at the node takes one pass over p). The draw then finds
 // the tile where the cumulative mass crosses the target and re-reads that
-// tile alone. Each wave works on whole 256-token tiles, four tiles' loads in
+// tile alone. Each wave works on whole 256-token tiles, kTilesInFlight (seven) tiles' loads in
 // flight at a time. Decisions are taken in fp32; sums run in a fixed order.
 
 constexpr int kSampleThreads = 1024;

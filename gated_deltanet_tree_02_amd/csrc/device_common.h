@@ -79,6 +79,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Per-sequence result code. merge == 0: the code is written. merge != 0 (a
+// later step of a captured round): a code already set by an earlier step of
+// the round is kept, so the round reports the first failure of a sequence.
+__device__ __forceinline__ void put_status(int32_t* status, int b, int code, int merge) {
+  if (!merge)
+    status[b] = code;
+  else if (code != GDN_TREE_OK && status[b] == GDN_TREE_OK)
+    status[b] = code;
+}
+
 // Base-2 logarithm of a decay gate, clamped so that a gate of 0 (or a
 // denormal) stays finite: 2^-64 is far below fp32 resolution of any other
 // term, so the clamp does not change a result.

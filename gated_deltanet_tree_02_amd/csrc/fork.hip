@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void fork_level_kernel(const ForkArgs a) {
       sInfo[1] = tl.lo;
       sInfo[2] = tl.n;
       sLevel = lvl;
-      if (a.level == 0 && h == 0 && ch == 0) a.status[b] = st;
+      if (a.level == 0 && h == 0 && ch == 0) put_status(a.status, b, st, a.merge);
     }
   }
   __syncthreads();
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void fork_commit_kernel(const ForkCommitArgs a
       sInfo[0] = st;
       sInfo[1] = acc;
       sInfo[2] = tl.lo;
-      if (h == 0 && ch == 0) a.status[b] = st;
+      if (h == 0 && ch == 0) put_status(a.status, b, st, a.merge);
     }
   }
   __syncthreads();

@@ -95,11 +95,15 @@ gdn_status gdn_tree_build(const gdn_tree_desc* desc, const int32_t* offsets,
   return launched(gdn::launch_tree_build(a, static_cast<hipStream_t>(stream)));
 }
 
-gdn_status gdn_tree_verify(const gdn_tree_desc* desc, const int32_t* offsets,
-                           const int32_t* parents, const void* q, const void* k,
-                           const void* v, const float* alpha, const float* beta,
-                           const float* S0, void* o, void* workspace, size_t ws_bytes,
-                           int32_t* tree_status, void* stream) {
+}  // extern "C"
+
+namespace gdn {
+
+gdn_status verify_impl(const gdn_tree_desc* desc, const int32_t* offsets,
+                       const int32_t* parents, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, const float* S0, void* o,
+                       void* workspace, size_t ws_bytes, int32_t* tree_status, void* stream,
+                       int merge) {
   gdn_status st = check_desc(desc);
   if (st != GDN_OK) return st;
   if (desc->num_seqs == 0) return GDN_OK;
@@ -115,6 +119,7 @@ gdn_status gdn_tree_verify(const gdn_tree_desc* desc, const int32_t* offsets,
     float* g2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wy_u_bytes(desc));
     gdn::VerifyArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
                       offsets, parents, q, k, v, alpha, beta, S0, o, U, g2, tree_status};
+    a.merge = merge;
     const int mt = (desc->max_nodes + 15) / 16;
     return launched(gdn::launch_wy_verify(desc->io_dtype, d, mt, a, s));
   }
@@ -128,16 +133,34 @@ gdn_status gdn_tree_verify(const gdn_tree_desc* desc, const int32_t* offsets,
     gdn::ForkArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
                     L - 1, level, offsets, parents, q, k, v, alpha, beta, S0, o,
                     ckpt, tree_status, U, g2};
+    a.merge = merge;
     st = launched(gdn::launch_fork_level(desc->io_dtype, d, a, s));
     if (st != GDN_OK) return st;
   }
   return GDN_OK;
 }
 
-gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
-                           const int32_t* parents, const int32_t* accepted, const void* k,
-                           const float* S0, float* S_out, const void* workspace,
-                           size_t ws_bytes, int32_t* tree_status, void* stream) {
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_tree_verify(const gdn_tree_desc* desc, const int32_t* offsets,
+                           const int32_t* parents, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta,
+                           const float* S0, void* o, void* workspace, size_t ws_bytes,
+                           int32_t* tree_status, void* stream) {
+  return gdn::verify_impl(desc, offsets, parents, q, k, v, alpha, beta, S0, o, workspace,
+                          ws_bytes, tree_status, stream, 0);
+}
+
+}  // extern "C"
+
+namespace gdn {
+
+gdn_status commit_impl(const gdn_tree_desc* desc, const int32_t* offsets,
+                       const int32_t* parents, const int32_t* accepted, const void* k,
+                       const float* S0, float* S_out, const void* workspace, size_t ws_bytes,
+                       int32_t* tree_status, void* stream, int merge) {
   gdn_status st = check_desc(desc);
   if (st != GDN_OK) return st;
   if (desc->num_seqs == 0) return GDN_OK;
@@ -155,12 +178,26 @@ gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
     gdn::CommitArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
                       offsets, parents, accepted, k, S0, S_out, U, g2, tree_status,
                       commit_depth_limit(desc)};
+    a.merge = merge;
     return launched(gdn::launch_wy_commit(desc->io_dtype, d, a, s));
   }
   gdn::ForkCommitArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
                         levels(desc) - 1, offsets, parents, accepted, S0, S_out,
                         static_cast<const float*>(workspace), tree_status};
+  a.merge = merge;
   return launched(gdn::launch_fork_commit(d, a, s));
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_tree_commit(const gdn_tree_desc* desc, const int32_t* offsets,
+                           const int32_t* parents, const int32_t* accepted, const void* k,
+                           const float* S0, float* S_out, const void* workspace,
+                           size_t ws_bytes, int32_t* tree_status, void* stream) {
+  return gdn::commit_impl(desc, offsets, parents, accepted, k, S0, S_out, workspace, ws_bytes,
+                          tree_status, stream, 0);
 }
 
 gdn_status gdn_tree_verify_layers(const gdn_tree_desc* desc, int32_t n_layers,
@@ -212,10 +249,14 @@ gdn_status gdn_tree_verify_layers(const gdn_tree_desc* desc, int32_t n_layers,
   return GDN_OK;
 }
 
-gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
-                                  const int32_t* offsets, const int32_t* parents,
-                                  const int32_t* accepted, const gdn_layer_io* layers,
-                                  size_t ws_bytes, int32_t* tree_status, void* stream) {
+}  // extern "C"
+
+namespace gdn {
+
+gdn_status commit_layers_impl(const gdn_tree_desc* desc, int32_t n_layers,
+                              const int32_t* offsets, const int32_t* parents,
+                              const int32_t* accepted, const gdn_layer_io* layers,
+                              size_t ws_bytes, int32_t* tree_status, void* stream, int merge) {
   gdn_status st = check_desc(desc);
   if (st != GDN_OK) return st;
   if (n_layers <= 0 || desc->num_seqs == 0) return GDN_OK;
@@ -223,8 +264,8 @@ gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
   if (desc->mode == GDN_MODE_FORK) {
     for (int l = 0; l < n_layers; ++l) {
       const gdn_layer_io& y = layers[l];
-      st = gdn_tree_commit(desc, offsets, parents, accepted, y.k, y.S0, y.S_out, y.workspace,
-                           ws_bytes, tree_status, stream);
+      st = commit_impl(desc, offsets, parents, accepted, y.k, y.S0, y.S_out, y.workspace,
+                       ws_bytes, tree_status, stream, merge);
       if (st != GDN_OK) return st;
     }
     return GDN_OK;
@@ -244,6 +285,7 @@ gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
   a.base = gdn::CommitArgs{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
                            offsets, parents, accepted, nullptr, nullptr, nullptr, nullptr,
                            nullptr, tree_status, commit_depth_limit(desc)};
+  a.base.merge = merge;
   for (int l0 = 0; l0 < n_layers; l0 += gdn::kMaxLayersPerLaunch) {
     a.layers = std::min(n_layers - l0, gdn::kMaxLayersPerLaunch);
     for (int i = 0; i < a.layers; ++i) {
@@ -257,6 +299,18 @@ gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
     if (st != GDN_OK) return st;
   }
   return GDN_OK;
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
+                                  const int32_t* offsets, const int32_t* parents,
+                                  const int32_t* accepted, const gdn_layer_io* layers,
+                                  size_t ws_bytes, int32_t* tree_status, void* stream) {
+  return gdn::commit_layers_impl(desc, n_layers, offsets, parents, accepted, layers, ws_bytes,
+                                 tree_status, stream, 0);
 }
 
 gdn_status gdn_tree_commit_verify_layers(
@@ -345,11 +399,15 @@ gdn_status gdn_tree_commit_verify(const gdn_tree_desc* prev_desc, const int32_t*
                                        tree_status, stream);
 }
 
-gdn_status gdn_tree_replay_verify_layers(
+}  // extern "C"
+
+namespace gdn {
+
+gdn_status replay_verify_layers_impl(
     const gdn_tree_desc* prev_desc, const gdn_tree_desc* desc, int32_t n_layers,
     const int32_t* prev_offsets, const int32_t* prev_parents, const int32_t* accepted,
     const int32_t* offsets, const int32_t* parents, const gdn_layer_io* prev_layers,
-    const gdn_layer_io* layers, int32_t* tree_status, void* stream) {
+    const gdn_layer_io* layers, int32_t* tree_status, void* stream, int merge) {
   gdn_status st = check_desc(prev_desc);
   if (st != GDN_OK) return st;
   st = check_desc(desc);
@@ -380,6 +438,7 @@ gdn_status gdn_tree_replay_verify_layers(
   a.base = gdn::VerifyArgs{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
                            offsets, parents, nullptr, nullptr, nullptr, nullptr, nullptr,
                            nullptr, nullptr, nullptr, nullptr, tree_status};
+  a.base.merge = merge;
   a.prev = gdn::PendingTree{prev_desc->total_nodes, prev_desc->max_nodes, prev_offsets,
                             prev_parents, accepted};
   for (int l0 = 0; l0 < n_layers; l0 += gdn::kMaxFusedLayersPerLaunch) {
@@ -394,6 +453,20 @@ gdn_status gdn_tree_replay_verify_layers(
     if (st != GDN_OK) return st;
   }
   return GDN_OK;
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_tree_replay_verify_layers(
+    const gdn_tree_desc* prev_desc, const gdn_tree_desc* desc, int32_t n_layers,
+    const int32_t* prev_offsets, const int32_t* prev_parents, const int32_t* accepted,
+    const int32_t* offsets, const int32_t* parents, const gdn_layer_io* prev_layers,
+    const gdn_layer_io* layers, int32_t* tree_status, void* stream) {
+  return gdn::replay_verify_layers_impl(prev_desc, desc, n_layers, prev_offsets, prev_parents,
+                                        accepted, offsets, parents, prev_layers, layers,
+                                        tree_status, stream, 0);
 }
 
 gdn_status gdn_tree_replay_verify(const gdn_tree_desc* prev_desc, const int32_t* prev_offsets,
@@ -413,6 +486,55 @@ gdn_status gdn_tree_replay_verify(const gdn_tree_desc* prev_desc, const int32_t*
   gdn_layer_io cur{q, k, v, alpha, beta, S0, o, S_out, nullptr};
   return gdn_tree_replay_verify_layers(prev_desc, desc, 1, prev_offsets, prev_parents, accepted,
                                        offsets, parents, &prev, &cur, tree_status, stream);
+}
+
+gdn_status gdn_tree_replay_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
+                                         const int32_t* offsets, const int32_t* parents,
+                                         const int32_t* accepted, const gdn_layer_io* layers,
+                                         int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (n_layers <= 0 || desc->num_seqs == 0) return GDN_OK;
+  if (!layers || !offsets || !accepted || !tree_status) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && !parents) return GDN_ERR_NULL_PTR;
+  for (int l = 0; l < n_layers; ++l) {
+    const gdn_layer_io& y = layers[l];
+    if (!y.S0 || !y.S_out) return GDN_ERR_NULL_PTR;
+    if (desc->total_nodes > 0 && (!y.k || !y.v || !y.alpha || !y.beta)) return GDN_ERR_NULL_PTR;
+  }
+  if ((long long)desc->num_seqs * desc->num_heads * gdn::kMaxLayersPerLaunch > INT_MAX)
+    return GDN_ERR_BAD_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  gdn::CommitLayersArgs a{};
+  a.base = gdn::CommitArgs{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                           offsets, parents, accepted, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, tree_status, -1};
+  for (int l0 = 0; l0 < n_layers; l0 += gdn::kMaxLayersPerLaunch) {
+    a.layers = std::min(n_layers - l0, gdn::kMaxLayersPerLaunch);
+    for (int i = 0; i < a.layers; ++i) {
+      const gdn_layer_io& y = layers[l0 + i];
+      a.L[i] = gdn::CommitLayer{y.k, y.S0, y.S_out, nullptr, nullptr, y.v, y.alpha, y.beta};
+    }
+    st = launched(gdn::launch_replay_commit_layers(desc->io_dtype, desc->dk, a, s));
+    if (st != GDN_OK) return st;
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_tree_replay_commit(const gdn_tree_desc* desc, const int32_t* offsets,
+                                  const int32_t* parents, const int32_t* accepted,
+                                  const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* S0, float* S_out,
+                                  int32_t* tree_status, void* stream) {
+  gdn_layer_io y{};
+  y.k = k;
+  y.v = v;
+  y.alpha = alpha;
+  y.beta = beta;
+  y.S0 = S0;
+  y.S_out = S_out;
+  return gdn_tree_replay_commit_layers(desc, 1, offsets, parents, accepted, &y, tree_status,
+                                       stream);
 }
 
 const char* gdn_tree_status_string(int status) {

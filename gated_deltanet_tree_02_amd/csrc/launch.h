@@ -30,6 +30,7 @@ struct VerifyArgs {
   float* U;      // [T,H,dv] pseudo-values
   float* g2;     // [T,H] base-2 gate prefixes
   int32_t* status;
+  int merge = 0;  // keep a code an earlier step of the round set (put_status)
 };
 
 struct CommitArgs {
@@ -44,6 +45,11 @@ struct CommitArgs {
   const float* g2;
   int32_t* status;
   int max_depth;   // >= 0: a tree deeper than this is rejected (FORK_DELTA); -1: no limit
+  // commit by replay: the path's own inputs instead of U and g2
+  const void* v = nullptr;          // [T,H,dv] io
+  const float* alpha = nullptr;     // [T,H]
+  const float* beta = nullptr;      // [T,H]
+  int merge = 0;
 };
 
 struct ForkArgs {
@@ -61,6 +67,7 @@ struct ForkArgs {
   int32_t* status;
   float* U;      // FORK_DELTA: [T,H,dv] the per-node deltas, else null
   float* g2;     // FORK_DELTA: [T,H] base-2 gate prefixes, else null
+  int merge = 0;
 };
 
 struct ForkCommitArgs {
@@ -72,6 +79,7 @@ struct ForkCommitArgs {
   float* S_out;
   const float* ckpt;
   int32_t* status;
+  int merge = 0;
 };
 
 // io: 0 = fp32, 1 = bf16 (gdn_dtype); d = dk = dv; mt = ceil(max_nodes / 16).
@@ -94,6 +102,7 @@ struct AttnArgs {
   float* part_o;     // [T, Hq, NS, d] (NS > 1)
   float* part_ml;    // [T, Hq, NS, 2] (NS > 1)
   int32_t* status;
+  int merge = 0;
 };
 
 // Layer-batched verify / commit: one launch covers several layers that share
@@ -121,6 +130,7 @@ struct AttnCommitArgs {
   int32_t* cache_len;
   int32_t* status;
   AttnCommitLayer L[kMaxLayersPerLaunch];
+  int merge = 0;
 };
 
 // Sampling-mode acceptance: rejection sampling of the candidates down the
@@ -150,6 +160,9 @@ struct AcceptArgs {
   int32_t* accept_len;
   int32_t* next_token;
   int32_t* status;
+  // a later step of a captured round: a sequence whose status an earlier step
+  // set keeps it and accepts nothing (accepted -1)
+  int merge = 0;
 };
 
 struct VerifyLayer {
@@ -176,6 +189,9 @@ struct CommitLayer {
   float* S_out;
   const float* U;
   const float* g2;
+  const void* v = nullptr;          // commit by replay
+  const float* alpha = nullptr;
+  const float* beta = nullptr;
 };
 
 struct CommitLayersArgs {
@@ -258,6 +274,9 @@ __device__ __forceinline__ CommitArgs layer_args(const CommitLayersArgs& la, int
   a.S_out = l.S_out;
   a.U = l.U;
   a.g2 = l.g2;
+  a.v = l.v;
+  a.alpha = l.alpha;
+  a.beta = l.beta;
   return a;
 }
 __device__ __forceinline__ const VerifyArgs& base_args(const VerifyArgs& a) { return a; }
@@ -282,6 +301,9 @@ hipError_t launch_tree_attn(int d, const AttnArgs& a, hipStream_t s);
 hipError_t launch_tree_attn_commit(int d, const AttnCommitArgs& a, hipStream_t s);
 hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s);
 hipError_t launch_wy_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s);
+// commit by replaying the accepted path (CommitArgs v, alpha, beta set; U, g2 unused)
+hipError_t launch_replay_commit(int io, int d, const CommitArgs& a, hipStream_t s);
+hipError_t launch_replay_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s);
 hipError_t launch_fork_level(int io, int d, const ForkArgs& a, hipStream_t s);
 hipError_t launch_fork_commit(int d, const ForkCommitArgs& a, hipStream_t s);
 hipError_t launch_accept_greedy(const AcceptArgs& a, hipStream_t s);

@@ -84,68 +84,12 @@ gdn_tree_desc tree_shape(const gdn_round_desc* d) {
   return t;
 }
 
-// Every call of one round, in order, on `stream`.
-gdn_status enqueue_round(const gdn_round_desc* d, const gdn_round_io* io,
-                         const gdn_round_layout& L, const gdn_round_prev* prev, void* stream) {
-  const int ng = d->n_gdn_layers, na = d->n_attn_layers;
-  char* base = static_cast<char*>(io->arena);
-  int gi = 0, ai = 0;
-  gdn_status st = GDN_OK;
-  for (int pos = 0; pos < ng + na; ++pos) {
-    const int kind = io->layer_kinds ? io->layer_kinds[pos] : (pos < ng ? 0 : 1);
-    if (kind == 0) {
-      const gdn_layer_io& ly = io->gdn_layers[gi];
-      if (prev) {
-        const gdn_layer_io& p = prev->gdn_layers[gi];
-        st = gdn_tree_replay_verify(&prev->gdn, prev->offsets, prev->parents, prev->accepted,
-                                    p.k, p.v, p.alpha, p.beta, &d->gdn, io->offsets,
-                                    io->parents, ly.q, ly.k, ly.v, ly.alpha, ly.beta, ly.S0,
-                                    ly.S_out, ly.o, io->tree_status, stream);
-      } else {
-        void* ws = L.gdn_ws_bytes ? base + (size_t)gi * L.gdn_ws_stride : nullptr;
-        st = gdn_tree_verify(&d->gdn, io->offsets, io->parents, ly.q, ly.k, ly.v, ly.alpha,
-                             ly.beta, ly.S0, ly.o, ws, L.gdn_ws_bytes, io->tree_status, stream);
-      }
-      ++gi;
-    } else {
-      const gdn_attn_layer_io& ly = io->attn_layers[ai];
-      void* ws = L.attn_ws_bytes ? base + L.attn_ws_offset + (size_t)ai * L.attn_ws_stride
-                                 : nullptr;
-      st = gdn_tree_attn_verify(&d->attn, io->offsets, io->parents, ly.q, ly.k, ly.v,
-                                ly.k_cache, ly.v_cache, io->cache_len, io->attn_scale, ly.o, ws,
-                                L.attn_ws_bytes, io->tree_status, stream);
-      ++ai;
-    }
-    if (st != GDN_OK) return st;
-  }
-  const gdn_tree_desc ts = tree_shape(d);
-  st = gdn_tree_accept_greedy(&ts, io->offsets, io->parents, io->draft_tokens,
-                              io->target_tokens, io->accepted, io->accept_len, io->next_token,
-                              io->tree_status, stream);
-  if (st != GDN_OK) return st;
-  if (ng > 0 && !prev) {
-    std::vector<gdn_layer_io> layers(io->gdn_layers, io->gdn_layers + ng);
-    for (int l = 0; l < ng; ++l)
-      layers[l].workspace = L.gdn_ws_bytes ? base + (size_t)l * L.gdn_ws_stride : nullptr;
-    st = gdn_tree_commit_layers(&d->gdn, ng, io->offsets, io->parents, io->accepted,
-                                layers.data(), L.gdn_ws_bytes, io->tree_status, stream);
-    if (st != GDN_OK) return st;
-  }
-  if (na > 0)
-    st = gdn_tree_attn_commit_layers(&d->attn, na, io->offsets, io->parents, io->accepted,
-                                     io->attn_layers, io->cache_len, io->tree_status, stream);
-  return st;
-}
-
-}  // namespace
-
-extern "C" {
-
-gdn_status gdn_tree_accept_greedy(const gdn_tree_desc* desc, const int32_t* offsets,
-                                  const int32_t* parents, const int32_t* draft_tokens,
-                                  const int32_t* target_tokens, int32_t* accepted,
-                                  int32_t* accept_len, int32_t* next_token,
-                                  int32_t* tree_status, void* stream) {
+// Greedy acceptance; merge != 0 inside a captured round (see enqueue_round).
+gdn_status accept_greedy_impl(const gdn_tree_desc* desc, const int32_t* offsets,
+                              const int32_t* parents, const int32_t* draft_tokens,
+                              const int32_t* target_tokens, int32_t* accepted,
+                              int32_t* accept_len, int32_t* next_token, int32_t* tree_status,
+                              void* stream, int merge) {
   if (desc == nullptr) return GDN_ERR_NULL_PTR;
   if (desc->num_seqs < 0 || desc->total_nodes < 0 || desc->max_nodes < 1 ||
       desc->max_nodes > GDN_TREE_MAX_NODES || desc->num_seqs > INT_MAX - 3)
@@ -158,9 +102,82 @@ gdn_status gdn_tree_accept_greedy(const gdn_tree_desc* desc, const int32_t* offs
   gdn::AcceptArgs a{desc->num_seqs, desc->total_nodes, desc->max_nodes, offsets, parents,
                     draft_tokens, target_tokens, accepted, accept_len, next_token,
                     tree_status};
+  a.merge = merge;
   return gdn::launch_accept_greedy(a, static_cast<hipStream_t>(stream)) == hipSuccess
              ? GDN_OK
              : GDN_ERR_LAUNCH;
+}
+
+// Every call of one round, in order, on `stream`. The round's first step
+// writes tree_status; every later step keeps a code an earlier one set (a
+// verify that rejected the sequence in one layer, or the previous round's
+// commit that could not be applied), and the acceptance then accepts nothing
+// for such a sequence, so no commit changes its state.
+gdn_status enqueue_round(const gdn_round_desc* d, const gdn_round_io* io,
+                         const gdn_round_layout& L, const gdn_round_prev* prev, void* stream) {
+  const int ng = d->n_gdn_layers, na = d->n_attn_layers;
+  char* base = static_cast<char*>(io->arena);
+  int gi = 0, ai = 0;
+  gdn_status st = GDN_OK;
+  for (int pos = 0; pos < ng + na; ++pos) {
+    const int kind = io->layer_kinds ? io->layer_kinds[pos] : (pos < ng ? 0 : 1);
+    const int merge = pos > 0;
+    if (kind == 0) {
+      const gdn_layer_io& ly = io->gdn_layers[gi];
+      if (prev) {
+        st = gdn::replay_verify_layers_impl(&prev->gdn, &d->gdn, 1, prev->offsets,
+                                            prev->parents, prev->accepted, io->offsets,
+                                            io->parents, &prev->gdn_layers[gi], &ly,
+                                            io->tree_status, stream, merge);
+      } else {
+        void* ws = L.gdn_ws_bytes ? base + (size_t)gi * L.gdn_ws_stride : nullptr;
+        st = gdn::verify_impl(&d->gdn, io->offsets, io->parents, ly.q, ly.k, ly.v, ly.alpha,
+                              ly.beta, ly.S0, ly.o, ws, L.gdn_ws_bytes, io->tree_status, stream,
+                              merge);
+      }
+      ++gi;
+    } else {
+      const gdn_attn_layer_io& ly = io->attn_layers[ai];
+      void* ws = L.attn_ws_bytes ? base + L.attn_ws_offset + (size_t)ai * L.attn_ws_stride
+                                 : nullptr;
+      st = gdn::attn_verify_impl(&d->attn, io->offsets, io->parents, ly.q, ly.k, ly.v,
+                                 ly.k_cache, ly.v_cache, io->cache_len, io->attn_scale, ly.o, ws,
+                                 L.attn_ws_bytes, io->tree_status, stream, merge);
+      ++ai;
+    }
+    if (st != GDN_OK) return st;
+  }
+  const gdn_tree_desc ts = tree_shape(d);
+  st = accept_greedy_impl(&ts, io->offsets, io->parents, io->draft_tokens, io->target_tokens,
+                          io->accepted, io->accept_len, io->next_token, io->tree_status, stream,
+                          ng + na > 0);
+  if (st != GDN_OK) return st;
+  if (ng > 0 && !prev) {
+    std::vector<gdn_layer_io> layers(io->gdn_layers, io->gdn_layers + ng);
+    for (int l = 0; l < ng; ++l)
+      layers[l].workspace = L.gdn_ws_bytes ? base + (size_t)l * L.gdn_ws_stride : nullptr;
+    st = gdn::commit_layers_impl(&d->gdn, ng, io->offsets, io->parents, io->accepted,
+                                 layers.data(), L.gdn_ws_bytes, io->tree_status, stream, 1);
+    if (st != GDN_OK) return st;
+  }
+  if (na > 0)
+    st = gdn::attn_commit_layers_impl(&d->attn, na, io->offsets, io->parents, io->accepted,
+                                      io->attn_layers, io->cache_len, io->tree_status, stream,
+                                      1);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_tree_accept_greedy(const gdn_tree_desc* desc, const int32_t* offsets,
+                                  const int32_t* parents, const int32_t* draft_tokens,
+                                  const int32_t* target_tokens, int32_t* accepted,
+                                  int32_t* accept_len, int32_t* next_token,
+                                  int32_t* tree_status, void* stream) {
+  return accept_greedy_impl(desc, offsets, parents, draft_tokens, target_tokens, accepted,
+                            accept_len, next_token, tree_status, stream, 0);
 }
 
 gdn_status gdn_tree_accept_sampling(const gdn_tree_desc* desc, const int32_t* offsets,

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(const AttnArgs a) {
   }
   __syncthreads();
   const int st = __builtin_amdgcn_readfirstlane(sStatus);
-  if (split == 0 && kvh == 0 && tid == 0) a.status[b] = st;
+  if (split == 0 && kvh == 0 && tid == 0) put_status(a.status, b, st, a.merge);
 
   // ---- query rows: wave w owns tiles w, w + waves, ... (rows 16 tile + l16
   // of the G * n rows of the K/V head, query-head-major, node inner)
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(64 * W) void tree_attn32_kernel(const AttnArgs a) {
   }
   __syncthreads();
   const int st = __builtin_amdgcn_readfirstlane(sStatus);
-  if (split == 0 && kvh == 0 && tid == 0) a.status[b] = st;
+  if (split == 0 && kvh == 0 && tid == 0) put_status(a.status, b, st, a.merge);
 
   // ---- this wave's tile: rows 32 wave + l % 32 of the G * n rows of the
   // K/V head (query-head-major, node inner)
@@ -927,7 +927,7 @@ __global__ __launch_bounds__(256) void tree_attn_commit_kernel(const AttnCommitA
       sInfo[0] = st;
       sInfo[1] = P;
       sInfo[2] = L;
-      a.status[b] = st;
+      put_status(a.status, b, st, a.merge);
     }
   }
   __syncthreads();

@@ -99,12 +99,15 @@ size_t gdn_tree_attn_workspace_bytes(const gdn_attn_desc* desc) {
   return workspace_bytes(desc);
 }
 
-gdn_status gdn_tree_attn_verify(const gdn_attn_desc* desc, const int32_t* offsets,
-                                const int32_t* parents, const void* q, const void* k,
-                                const void* v, const void* k_cache, const void* v_cache,
-                                const int32_t* cache_len, float scale, void* o,
-                                void* workspace, size_t ws_bytes, int32_t* tree_status,
-                                void* stream) {
+}  // extern "C"
+
+namespace gdn {
+
+gdn_status attn_verify_impl(const gdn_attn_desc* desc, const int32_t* offsets,
+                            const int32_t* parents, const void* q, const void* k, const void* v,
+                            const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                            float scale, void* o, void* workspace, size_t ws_bytes,
+                            int32_t* tree_status, void* stream, int merge) {
   gdn_status st = check_desc(desc);
   if (st != GDN_OK) return st;
   if (desc->num_seqs == 0) return GDN_OK;
@@ -145,7 +148,22 @@ gdn_status gdn_tree_attn_verify(const gdn_attn_desc* desc, const int32_t* offset
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.status = tree_status;
+  a.merge = merge;
   return launched(gdn::launch_tree_attn(desc->head_dim, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_tree_attn_verify(const gdn_attn_desc* desc, const int32_t* offsets,
+                                const int32_t* parents, const void* q, const void* k,
+                                const void* v, const void* k_cache, const void* v_cache,
+                                const int32_t* cache_len, float scale, void* o,
+                                void* workspace, size_t ws_bytes, int32_t* tree_status,
+                                void* stream) {
+  return gdn::attn_verify_impl(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len,
+                               scale, o, workspace, ws_bytes, tree_status, stream, 0);
 }
 
 gdn_status gdn_tree_attn_commit(const gdn_attn_desc* desc, const int32_t* offsets,
@@ -167,10 +185,15 @@ gdn_status gdn_tree_attn_commit(const gdn_attn_desc* desc, const int32_t* offset
       gdn::launch_tree_attn_commit(desc->head_dim, a, static_cast<hipStream_t>(stream)));
 }
 
-gdn_status gdn_tree_attn_commit_layers(const gdn_attn_desc* desc, int32_t n_layers,
-                                       const int32_t* offsets, const int32_t* parents,
-                                       const int32_t* accepted, const gdn_attn_layer_io* layers,
-                                       int32_t* cache_len, int32_t* tree_status, void* stream) {
+}  // extern "C"
+
+namespace gdn {
+
+gdn_status attn_commit_layers_impl(const gdn_attn_desc* desc, int32_t n_layers,
+                                   const int32_t* offsets, const int32_t* parents,
+                                   const int32_t* accepted, const gdn_attn_layer_io* layers,
+                                   int32_t* cache_len, int32_t* tree_status, void* stream,
+                                   int merge) {
   gdn_status st = check_desc(desc);
   if (st != GDN_OK) return st;
   if (desc->num_seqs == 0 || n_layers <= 0) return GDN_OK;
@@ -189,6 +212,7 @@ gdn_status gdn_tree_attn_commit_layers(const gdn_attn_desc* desc, int32_t n_laye
         commit_base(desc, offsets, parents, accepted, cache_len, tree_status);
     a.layers = nl;
     a.advance = l0 + nl == n_layers;
+    a.merge = merge;
     for (int i = 0; i < nl; ++i) {
       const gdn_attn_layer_io& ly = layers[l0 + i];
       a.L[i] = {static_cast<const uint16_t*>(ly.k), static_cast<const uint16_t*>(ly.v),
@@ -199,6 +223,18 @@ gdn_status gdn_tree_attn_commit_layers(const gdn_attn_desc* desc, int32_t n_laye
     if (st != GDN_OK) return st;
   }
   return GDN_OK;
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_tree_attn_commit_layers(const gdn_attn_desc* desc, int32_t n_layers,
+                                       const int32_t* offsets, const int32_t* parents,
+                                       const int32_t* accepted, const gdn_attn_layer_io* layers,
+                                       int32_t* cache_len, int32_t* tree_status, void* stream) {
+  return gdn::attn_commit_layers_impl(desc, n_layers, offsets, parents, accepted, layers,
+                                      cache_len, tree_status, stream, 0);
 }
 
 }  // extern "C"

@@ -23,6 +23,14 @@
 // (kPathFirst = false), which keeps workgroups short and their reads and
 // writes in long runs. In-place
 // (S_out == S0) is safe: every element is read and written by the same thread.
+//
+// The same kernel commits by replay (kReplay) when verify kept no
+// pseudo-values: the gated delta rule is run along the accepted path, root
+// first, on every state row the thread holds,
+//     w = S_r . k_j,   S_r <- alpha_j S_r + beta_j (v_j[r] - alpha_j w) k_j^T,
+// from the path's own k, v, alpha and beta (fork page, section 5: the kept
+// state is the last accepted token's). A row is spread over DK/4 consecutive
+// lanes, so its dot product is a butterfly over those lanes.
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -38,7 +46,7 @@ constexpr int kCommitThreads = 256;
 
 // Args: CommitArgs (one layer) or CommitLayersArgs (workgroup i takes layer
 // i / (B * H) of a layer-batched launch).
-template <class IO, int DK, int DV, bool kPathFirst, class Args>
+template <class IO, int DK, int DV, bool kPathFirst, bool kReplay, class Args>
 __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args args) {
   constexpr int NT = kCommitThreads;
   constexpr int CPROW = DK / 4;             // float4 per state row
@@ -55,9 +63,11 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args ar
   using io = io_traits<IO>;
 
   __shared__ __align__(16) float sK[PCH * DK];
+  // scaled pseudo-values, or (replay) the path's v rows
   __shared__ __align__(16) float sW[PCH * DV];
   __shared__ int sPath[64];
-  __shared__ float sCoef[64];
+  __shared__ float sCoef[64];     // path coefficients, or (replay) alpha
+  __shared__ float sBeta[kReplay ? 64 : 1];
   __shared__ int sInfo[4];
   __shared__ float sGA;
 
@@ -87,14 +97,18 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args ar
     for (int idx = t; idx < pc * (DV / 4); idx += nthr) {
       const int p = idx / (DV / 4);
       const int r = 4 * (idx - p * (DV / 4));
-      const float cf = sCoef[p0 + p];
-      float4 u = *reinterpret_cast<const float4*>(
-          a.U + ((size_t)(lo + sPath[p0 + p]) * H + h) * DV + r);
-      u.x *= cf;
-      u.y *= cf;
-      u.z *= cf;
-      u.w *= cf;
-      *reinterpret_cast<float4*>(sW + p * DV + r) = u;
+      const size_t row = ((size_t)(lo + sPath[p0 + p]) * H + h) * DV + r;
+      if constexpr (kReplay) {
+        *reinterpret_cast<float4*>(sW + p * DV + r) = io::load4(static_cast<const IO*>(a.v) + row);
+      } else {
+        const float cf = sCoef[p0 + p];
+        float4 u = *reinterpret_cast<const float4*>(a.U + row);
+        u.x *= cf;
+        u.y *= cf;
+        u.z *= cf;
+        u.w *= cf;
+        *reinterpret_cast<float4*>(sW + p * DV + r) = u;
+      }
     }
   };
 
@@ -120,7 +134,10 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args ar
     } else {
       const int nl = lane < n ? lane : 0;
       const int par_raw = a.parents[lo + nl];
-      const float g2_raw = a.g2[(size_t)(lo + nl) * H + h];
+      // the gate prefix (pseudo-values), or (replay) the node's gates
+      const float g2_raw = kReplay ? a.alpha[(size_t)(lo + nl) * H + h]
+                                   : a.g2[(size_t)(lo + nl) * H + h];
+      const float beta_raw = kReplay ? a.beta[(size_t)(lo + nl) * H + h] : 0.f;
       acc = a.accepted[b];
       const int par = lane < n ? par_raw : -1;
       if (__shfl(par, 0, kWave) != -1)
@@ -143,11 +160,16 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args ar
         float unused;
         path_scan(par, lane, n, 0.f, anc, unused);
         const uint64_t path = shfl_u64(anc, acc);
-        gA = __shfl(g2_raw, acc, kWave);
+        if (!kReplay) gA = __shfl(g2_raw, acc, kWave);
         if ((path >> lane) & 1ull) {
           const int rank = __popcll(path & ((1ull << lane) - 1ull));
           sPath[rank] = lane;
-          sCoef[rank] = exp2f(gA - g2_raw);
+          if constexpr (kReplay) {
+            sCoef[rank] = g2_raw;
+            sBeta[rank] = beta_raw;
+          } else {
+            sCoef[rank] = exp2f(gA - g2_raw);
+          }
         }
         P = __popcll(path);
       }
@@ -158,7 +180,7 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args ar
       sInfo[2] = P;
       sInfo[3] = lo;
       sGA = exp2f(gA);
-      if (h == 0) a.status[b] = st;
+      if (h == 0) put_status(a.status, b, st, a.merge);
     }
     wave_lds_sync();   // sPath / sCoef written by other lanes of this wave
     if (kPathFirst && st == GDN_TREE_OK && P > 0) stage_path_rows(lo, 0, P < PCH ? P : PCH, lane, kWave);
@@ -175,7 +197,7 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args ar
   if (acc < 0 && a.S_out == a.S0) return;   // keep S0, in place: nothing to write
   float* __restrict__ dst = a.S_out + sbase;
   // accepted = -1 copies S0: factor 1 (exact) and an empty path (P = 0)
-  const float GA = acc < 0 ? 1.f : sGA;
+  const float GA = (acc < 0 || kReplay) ? 1.f : sGA;
   if constexpr (!kPathFirst) {
     // the whole workgroup stages the first round of path rows
     if (P > 0) stage_path_rows(lo, 0, P < PCH ? P : PCH, tid, NT);
@@ -208,7 +230,26 @@ __global__ __launch_bounds__(kCommitThreads) void wy_commit_kernel(const Args ar
         if (path_wave) stage_path_rows(lo, p0, pc, lane, kWave);
         __syncthreads();
       }
-      {
+      if constexpr (kReplay) {
+        for (int p = 0; p < pc; ++p) {
+          const float4 kk = *reinterpret_cast<const float4*>(sK + p * DK + 4 * c4);
+          const float al = sCoef[p0 + p];
+          const float be = sBeta[p0 + p];
+#pragma unroll
+          for (int j = 0; j < FPC; ++j) {
+            const int i = pcx * FPC + j;
+            float w = s[i].x * kk.x + s[i].y * kk.y + s[i].z * kk.z + s[i].w * kk.w;
+            // the row's DK/4 lanes are consecutive: a butterfly over them
+#pragma unroll
+            for (int off = CPROW / 2; off > 0; off >>= 1) w += __shfl_xor(w, off, kWave);
+            const float cf = be * (sW[p * DV + row0 + RSTEP * i] - al * w);
+            s[i].x = al * s[i].x + cf * kk.x;
+            s[i].y = al * s[i].y + cf * kk.y;
+            s[i].z = al * s[i].z + cf * kk.z;
+            s[i].w = al * s[i].w + cf * kk.w;
+          }
+        }
+      } else {
         for (int p = 0; p < pc; ++p) {
           const float4 kk = *reinterpret_cast<const float4*>(sK + p * DK + 4 * c4);
 #pragma unroll
@@ -257,11 +298,12 @@ hipError_t resident_workgroups(const void* kernel, int block, int* out) {
 inline int grid_of(const CommitArgs& a) { return a.B * a.H; }
 inline int grid_of(const CommitLayersArgs& a) { return a.base.B * a.base.H * a.layers; }
 
-template <class IO, int D, class Args>
+template <class IO, int D, bool kReplay, class Args>
 hipError_t launch_t(const Args& a, hipStream_t s) {
-  const void* first = reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, true, Args>);
+  const void* first =
+      reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, true, kReplay, Args>);
   const void* state_first =
-      reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, false, Args>);
+      reinterpret_cast<const void*>(&wy_commit_kernel<IO, D, D, false, kReplay, Args>);
   int slots = 0;
   const hipError_t e = resident_workgroups(first, kCommitThreads, &slots);
   if (e != hipSuccess) return e;
@@ -270,24 +312,38 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
                        (unsigned)kCommitThreads, s, a);
 }
 
-template <class IO, class Args>
+template <class IO, bool kReplay, class Args>
 hipError_t launch_d(int d, const Args& a, hipStream_t s) {
   switch (d) {
-    case 32: return launch_t<IO, 32>(a, s);
-    case 64: return launch_t<IO, 64>(a, s);
-    case 128: return launch_t<IO, 128>(a, s);
+    case 32: return launch_t<IO, 32, kReplay>(a, s);
+    case 64: return launch_t<IO, 64, kReplay>(a, s);
+    case 128: return launch_t<IO, 128, kReplay>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+template <bool kReplay, class Args>
+hipError_t launch_io(int io, int d, const Args& a, hipStream_t s) {
+  return io == GDN_DTYPE_BF16 ? launch_d<uint16_t, kReplay>(d, a, s)
+                              : launch_d<float, kReplay>(d, a, s);
 }
 
 }  // namespace
 
 hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s) {
-  return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, a, s) : launch_d<float>(d, a, s);
+  return launch_io<false>(io, d, a, s);
 }
 
 hipError_t launch_wy_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s) {
-  return io == GDN_DTYPE_BF16 ? launch_d<uint16_t>(d, a, s) : launch_d<float>(d, a, s);
+  return launch_io<false>(io, d, a, s);
+}
+
+hipError_t launch_replay_commit(int io, int d, const CommitArgs& a, hipStream_t s) {
+  return launch_io<true>(io, d, a, s);
+}
+
+hipError_t launch_replay_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s) {
+  return launch_io<true>(io, d, a, s);
 }
 
 }  // namespace gdn

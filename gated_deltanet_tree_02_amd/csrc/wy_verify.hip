@@ -253,6 +253,139 @@ __device__ __forceinline__ int nth_path_node(uint64_t path, int p) {
   return path ? __builtin_ctzll(path) : 0;
 }
 
+// The previous round's side of a fused round boundary, one lane per previous
+// node: the node range and accepted node (uniform), the lane's parent and
+// either its gates (replay) or its base-2 gate prefix (pseudo-values).
+struct PrevLane {
+  int lo, n, acc, size_status;
+  int par_raw;
+  float g2_raw, alpha, beta;
+};
+
+template <bool kReplay>
+__device__ __forceinline__ PrevLane load_prev(const PendingTree& pt, const PendingLayer& pl,
+                                              int b, int h, int H, int lane) {
+  PrevLane p;
+  p.lo = 0;
+  p.n = 1;
+  p.size_status = GDN_TREE_OK;
+  p.g2_raw = 0.f;
+  p.alpha = 1.f;
+  p.beta = 0.f;
+  const int lo_r = pt.offsets[b];
+  const int hi_r = pt.offsets[b + 1];
+  p.acc = pt.accepted[b];
+  if (lo_r < 0 || hi_r > pt.T || hi_r - lo_r < 1 || hi_r - lo_r > pt.max_nodes) {
+    p.size_status = GDN_TREE_BAD_SIZE;
+  } else {
+    p.lo = lo_r;
+    p.n = hi_r - lo_r;
+  }
+  const int nl = lane < p.n ? lane : 0;
+  p.par_raw = pt.parents[p.lo + nl];
+  const size_t gl = (size_t)(p.lo + nl) * H + h;
+  if constexpr (kReplay) {
+    p.alpha = pl.alpha[gl];
+    p.beta = pl.beta[gl];
+  } else {
+    p.g2_raw = pl.g2[gl];
+  }
+  return p;
+}
+
+// Checks of the previous round before its commit (uniform result): nothing
+// is committed and nothing is checked for accepted == -1; otherwise the
+// previous tree (size, root, parents) and then the accepted index. `path`
+// receives the accepted node's path (root first, as a node set), or 0.
+__device__ __forceinline__ int check_prev(const PrevLane& p, int lane, uint64_t& path) {
+  path = 0ull;
+  if (p.acc == -1) return GDN_TREE_OK;
+  int ps = p.size_status;
+  const int par = lane < p.n ? p.par_raw : -1;
+  if (ps == GDN_TREE_OK) {
+    if (__shfl(par, 0, kWave) != -1)
+      ps = GDN_TREE_BAD_ROOT;
+    else if (__ballot(lane >= 1 && lane < p.n && (par < 0 || par >= lane)) != 0ull)
+      ps = GDN_TREE_BAD_PARENT;
+    else if (p.acc < -1 || p.acc >= p.n)
+      ps = GDN_TREE_BAD_ACCEPTED;
+  }
+  ps = __builtin_amdgcn_readfirstlane(ps);
+  if (ps == GDN_TREE_OK) {
+    uint64_t anc;
+    float unused;
+    path_scan(par, lane, p.n, 0.f, anc, unused);
+    path = shfl_u64(anc, p.acc);
+  }
+  return ps;
+}
+
+// The previous round's commit alone, S0 -> S_out, for a sequence whose own
+// tree this round is rejected: the accepted tokens' update is kept all the
+// same (fork page, section 5: the state is the last accepted token's). A cold
+// path kept small in registers: 16 lanes per state row, DK/16 consecutive
+// elements per lane, 32 rows per pass; path rows are read straight from
+// memory. Returns the previous round's code.
+template <class IO, int DK, int DV, bool kReplay>
+__device__ int commit_prev_only(const CommitVerifyLayersArgs& args, int layer, int b, int h,
+                                int bh, const float* __restrict__ S0) {
+  constexpr int NT = 64 * kVerifyWaves;
+  constexpr int TPR = 16;                     // lanes per state row
+  constexpr int CPT = DK / TPR;               // columns per lane
+  constexpr int RPP = NT / TPR;               // rows per pass
+  static_assert(DV % RPP == 0 && DK % TPR == 0, "rows and columns tile the workgroup");
+  using io = io_traits<IO>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int H = args.base.H;
+  const PendingLayer& pl = args.P[layer];
+  const PrevLane p = load_prev<kReplay>(args.prev, pl, b, h, H, lane);
+  uint64_t path0;
+  const int ps = check_prev(p, lane, path0);
+  float* __restrict__ S_out = pl.S_out;
+  if (ps != GDN_TREE_OK || (p.acc < 0 && S_out == S0)) return ps;
+  const IO* __restrict__ pk = static_cast<const IO*>(pl.k);
+  const int rr = tid / TPR;
+  const int c0 = (tid - rr * TPR) * CPT;
+  const float gA = (!kReplay && p.acc >= 0) ? __shfl(p.g2_raw, p.acc, kWave) : 0.f;
+  const float GA = (!kReplay && p.acc >= 0) ? exp2f(gA) : 1.f;
+  for (int r = rr; r < DV; r += RPP) {
+    const size_t base = (size_t)bh * DV * DK + (size_t)r * DK + c0;
+    float s[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) s[c] = GA * S0[base + c];
+    uint64_t path = path0;
+    while (path) {   // root first (a parent's index is below its children's)
+      const int j = __builtin_ctzll(path);
+      path &= path - 1ull;
+      const size_t prow = (size_t)(p.lo + j) * H + h;
+      float kk[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) kk[c] = io::load1(pk + prow * DK + c0 + c);
+      if constexpr (kReplay) {
+        const float al = __shfl(p.alpha, j, kWave);
+        const float be = __shfl(p.beta, j, kWave);
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) dot += s[c] * kk[c];
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, kWave);
+        const float vr = io::load1(static_cast<const IO*>(pl.v) + prow * DV + r);
+        const float cf = be * (vr - al * dot);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) s[c] = al * s[c] + cf * kk[c];
+      } else {
+        const float w = exp2f(gA - __shfl(p.g2_raw, j, kWave)) * pl.U[prow * DV + r];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) s[c] += w * kk[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) S_out[base + c] = s[c];
+  }
+  return ps;
+}
+
 // Args: VerifyArgs (one layer) or VerifyLayersArgs (workgroup i takes layer
 // i / (B * H) of a layer-batched launch), or CommitVerifyLayersArgs (the same,
 // with the previous round's commit applied to S0 first).
@@ -349,7 +482,13 @@ void wy_verify_kernel(const Args args) {
   const int lo = a.offsets[b];
   const int hi = a.offsets[b + 1];
   if (lo < 0 || hi > a.T || hi - lo < 1 || hi - lo > a.max_nodes) {
-    if (h == 0 && tid == 0) a.status[b] = GDN_TREE_BAD_SIZE;
+    // (fused) the previous round's commit is applied all the same
+    int code = GDN_TREE_BAD_SIZE;
+    if constexpr (kFused) {
+      const int pcode = commit_prev_only<IO, DK, DV, kReplay>(args, layer, b, h, bh, a.S0);
+      code |= GDN_TREE_PREV(pcode);
+    }
+    if (h == 0 && tid == 0) put_status(a.status, b, code, a.merge);
     return;
   }
   const int n = hi - lo;
@@ -357,38 +496,21 @@ void wy_verify_kernel(const Args args) {
 
   // 1z. (fused commit) the previous round's node range and accepted node,
   // and one lane per previous node: its parent and gate prefix.
-  int plo = 0, pn = 1, pacc = -1, pst = GDN_TREE_OK, ppar_raw = -1;
-  float pg2_raw = 0.f, palpha = 1.f, pbeta = 0.f;
+  PrevLane prv{0, 1, -1, GDN_TREE_OK, -1, 0.f, 1.f, 0.f};
   const IO* __restrict__ pk = nullptr;
   const IO* __restrict__ pv = nullptr;
   const float* __restrict__ pU = nullptr;
   float* __restrict__ S_out = nullptr;
   if constexpr (kFused) {
-    const PendingTree& pt = args.prev;
     const PendingLayer& pl = args.P[layer];
     pk = static_cast<const IO*>(pl.k);
     pv = static_cast<const IO*>(pl.v);
     pU = pl.U;
     S_out = pl.S_out;
-    const int plo_r = pt.offsets[b];
-    const int phi_r = pt.offsets[b + 1];
-    pacc = pt.accepted[b];
-    if (plo_r < 0 || phi_r > pt.T || phi_r - plo_r < 1 || phi_r - plo_r > pt.max_nodes) {
-      pst = GDN_TREE_BAD_SIZE;
-    } else {
-      plo = plo_r;
-      pn = phi_r - plo_r;
-    }
-    const int pl_lane = lane < pn ? lane : 0;
-    ppar_raw = pt.parents[plo + pl_lane];
-    const size_t pgl = (size_t)(plo + pl_lane) * H + h;
-    if constexpr (kReplay) {
-      palpha = pl.alpha[pgl];
-      pbeta = pl.beta[pgl];
-    } else {
-      pg2_raw = pl.g2[pgl];
-    }
+    prv = load_prev<kReplay>(args.prev, pl, b, h, H, lane);
   }
+  const int plo = prv.lo, pacc = prv.acc;
+  const float pg2_raw = prv.g2_raw, palpha = prv.alpha, pbeta = prv.beta;
 
   // ---- 1. every global read of the workgroup, issued before any is used
   // (addresses clamped into the sequence, so the issue is unconditional).
@@ -469,25 +591,12 @@ void wy_verify_kernel(const Args args) {
   // (root first), its gate prefix and the path coefficients 2^(gA - g2_i)
   uint64_t ppath = 0ull;
   float pgA = 0.f, pcoef = 0.f;
+  int ps = GDN_TREE_OK;   // the previous round's commit (fused)
   if constexpr (kFused) {
-    const int ppar = lane < pn ? ppar_raw : -1;
-    int ps = pst;
-    if (ps == GDN_TREE_OK) {
-      if (__shfl(ppar, 0, kWave) != -1)
-        ps = GDN_TREE_BAD_ROOT;
-      else if (__ballot(lane >= 1 && lane < pn && (ppar < 0 || ppar >= lane)) != 0ull)
-        ps = GDN_TREE_BAD_PARENT;
-      else if (pacc < -1 || pacc >= pn)
-        ps = GDN_TREE_BAD_ACCEPTED;
-    }
-    ps = __builtin_amdgcn_readfirstlane(ps);
-    if (st == GDN_TREE_OK) st = ps;
-    if (st == GDN_TREE_OK && pacc >= 0) {
-      uint64_t panc;
-      float unused;
-      path_scan(ppar, lane, pn, 0.f, panc, unused);
-      ppath = shfl_u64(panc, pacc);
-      if constexpr (!kReplay) {
+    ps = check_prev(prv, lane, ppath);
+    if (st != GDN_TREE_OK) ppath = 0ull;   // (committed on the cold path below)
+    if constexpr (!kReplay) {
+      if (ppath) {
         pgA = __shfl(pg2_raw, pacc, kWave);
         pcoef = exp2f(pgA - pg2_raw);
       }
@@ -524,7 +633,12 @@ void wy_verify_kernel(const Args args) {
     }
   }
   if (!early_S0) load_S0();
-  if (st != GDN_TREE_OK) {
+  if (st != GDN_TREE_OK || ps != GDN_TREE_OK) {
+    // this round's tree, or the previous round's commit, is rejected: zero
+    // output rows (and workspace). With only this round's tree rejected, the
+    // previous commit is still applied (cold path); a rejected previous
+    // commit leaves S_out unwritten and nothing is verified against a state
+    // that lacks it.
     for (int idx = tid; idx < n * (DV / 4); idx += NT) {
       const int t = idx / (DV / 4);
       const int r = 4 * (idx - t * (DV / 4));
@@ -534,7 +648,13 @@ void wy_verify_kernel(const Args args) {
     }
     if constexpr (!kReplay)
       for (int t = tid; t < n; t += NT) a.g2[(size_t)(lo + t) * H + h] = 0.f;
-    if (h == 0 && tid == 0) a.status[b] = st;
+    int code = st;
+    if constexpr (kFused) {
+      if (st != GDN_TREE_OK && ps == GDN_TREE_OK)
+        ps = commit_prev_only<IO, DK, DV, kReplay>(args, layer, b, h, bh, a.S0);
+      code |= GDN_TREE_PREV(ps);
+    }
+    if (h == 0 && tid == 0) put_status(a.status, b, code, a.merge);
     return;
   }
 
@@ -878,7 +998,7 @@ void wy_verify_kernel(const Args args) {
         *reinterpret_cast<const float4*>(sm.s2.u + t * DV + cs);
   }
   if (!kReplay && wave == 0 && lane < n) a.g2[(size_t)(lo + lane) * H + h] = g2;
-  if (h == 0 && tid == 0) a.status[b] = GDN_TREE_OK;
+  if (h == 0 && tid == 0) put_status(a.status, b, GDN_TREE_OK, a.merge);
 }
 
 inline unsigned grid_of(const VerifyArgs& a) { return (unsigned)(a.B * a.H); }

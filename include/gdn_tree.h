@@ -110,6 +110,18 @@ enum {
 /* Precedence: BAD_SIZE, then BAD_ROOT, then BAD_PARENT, then TOO_DEEP (FORK
  * modes), then BAD_ACCEPTED (commit). */
 
+/* The fused round-boundary calls (gdn_tree_commit_verify, gdn_tree_replay_verify
+ * and their layer-batched forms) report two outcomes per sequence in one code:
+ *   tree_status & 0xF                    this round's tree (OK, BAD_SIZE,
+ *                                        BAD_ROOT, BAD_PARENT);
+ *   tree_status >> GDN_TREE_PREV_SHIFT   the previous round's commit (OK when
+ *                                        it was applied, else BAD_SIZE /
+ *                                        BAD_ROOT / BAD_PARENT of the previous
+ *                                        tree or BAD_ACCEPTED).
+ * GDN_TREE_PREV(code) forms the second part. */
+#define GDN_TREE_PREV_SHIFT 4
+#define GDN_TREE_PREV(code) ((code) << GDN_TREE_PREV_SHIFT)
+
 typedef struct {
   int32_t num_seqs;     /* B >= 0                                                   */
   int32_t num_heads;    /* H >= 1                                                   */
@@ -231,11 +243,17 @@ gdn_status gdn_tree_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
  *    (checked: GDN_ERR_BAD_SHAPE); callers alternate two buffers.
  *  - S_out may equal S0 (in place) or must not overlap it; S_out must not
  *    overlap any other argument.
- *  - tree_status [B] receives one code per sequence: this round's tree checks
- *    (BAD_SIZE, BAD_ROOT, BAD_PARENT), then the previous tree's and
- *    BAD_ACCEPTED for accepted[b] outside [-1, N'_b). A sequence with a
- *    nonzero code gets zero o rows and a zero workspace (when its node range
- *    is valid) and its S_out is not written.
+ *  - tree_status [B] receives two codes per sequence (GDN_TREE_PREV_SHIFT):
+ *    this round's tree checks (BAD_SIZE, BAD_ROOT, BAD_PARENT) in the low
+ *    bits, and GDN_TREE_PREV() of the previous round's (its tree's BAD_SIZE,
+ *    BAD_ROOT, BAD_PARENT, then BAD_ACCEPTED for accepted[b] outside
+ *    [-1, N'_b)). The previous tree is checked only when accepted[b] != -1.
+ *  - The previous commit is applied (S_out written) whenever its own part is
+ *    OK, also when this round's tree is rejected, so one malformed draft tree
+ *    never loses the accepted tokens' update. A sequence with any nonzero
+ *    part gets zero o rows and a zero workspace (none are written when this
+ *    round's part is BAD_SIZE); when the previous part is nonzero its S_out
+ *    is not written.
  *  - accepted[b] == -1 keeps S0 (S_out = S0; nothing is written in place).
  * The layer-batched form takes HOST arrays of n_layers entries: prev_layers
  * (fields k and workspace used) and layers (q, k, v, alpha, beta, S0, o,
@@ -290,6 +308,33 @@ gdn_status gdn_tree_replay_verify_layers(
     const int32_t* prev_offsets, const int32_t* prev_parents, const int32_t* accepted,
     const int32_t* offsets, const int32_t* parents, const gdn_layer_io* prev_layers,
     const gdn_layer_io* layers, int32_t* tree_status, void* stream);
+
+/* Commit by replay, with no workspace: for every sequence b, S_out[b] = the
+ * state of local node accepted[b] (or S0[b] when accepted[b] == -1), formed
+ * by running the gated delta rule along the accepted path, root first, on S0:
+ *     w = S k_j,   S <- alpha_j S + beta_j (v_j - alpha_j w) k_j^T
+ * (fork page section 5: the kept state is the last accepted token's; the
+ * update is the one every node's output is defined by). It is the commit of
+ * a round verified by gdn_tree_replay_verify, whose verify kept no
+ * pseudo-values: a sequence that leaves the batch, or the last round before
+ * a pause, is committed with it instead of with the next round's fused call.
+ *   k, v [T,H,dk|dv] (io dtype), alpha, beta [T,H] fp32: the round's verify
+ *     inputs, unchanged since; only the accepted path's rows are read.
+ * desc as for gdn_tree_commit (mode and max_depth are ignored). S_out may
+ * equal S0 (in place) or must not overlap it. tree_status receives BAD_SIZE,
+ * BAD_ROOT, BAD_PARENT or BAD_ACCEPTED (accepted[b] outside [-1, N_b));
+ * such a sequence is left unwritten. The layer-batched form takes a HOST array
+ * of n_layers entries (fields k, v, alpha, beta, S0, S_out used) sharing
+ * offsets, parents, accepted and tree_status; n_layers <= 0 is a no-op. */
+gdn_status gdn_tree_replay_commit(const gdn_tree_desc* desc, const int32_t* offsets,
+                                  const int32_t* parents, const int32_t* accepted,
+                                  const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* S0, float* S_out,
+                                  int32_t* tree_status, void* stream);
+gdn_status gdn_tree_replay_commit_layers(const gdn_tree_desc* desc, int32_t n_layers,
+                                         const int32_t* offsets, const int32_t* parents,
+                                         const int32_t* accepted, const gdn_layer_io* layers,
+                                         int32_t* tree_status, void* stream);
 
 /* Static text for a gdn_status value. */
 const char* gdn_tree_status_string(int status);

@@ -25,7 +25,7 @@ if not torch.cuda.is_available():  # the -m gpu suite only runs on a GPU machine
     pytest.skip("no GPU", allow_module_level=True)
 
 from gpu_util import (TOL, bits_to_dev, dev_to_bits, f32, from_dev_io, i32,  # noqa: E402
-                      oracle_attn, oracle_layer, rel_err_rows, to_dev_io)
+                      oracle_attn, oracle_layer, rel_err_rows, sub_workload, to_dev_io)
 
 
 def _say(*a):
@@ -374,6 +374,94 @@ def test_replay_round_graph_equals_eager_calls_and_the_oracle():
                 assert rel_err_rows(g_s.reshape(w.B * 4, -1), S_ref.reshape(w.B * 4, -1)) \
                     <= TOL["bf16"]
                 assert rel_err_rows(from_dev_io(G.o[l]).astype(np.float64), o_ref) <= TOL["bf16"]
+    graph.close()
+
+
+def test_replay_round_keeps_the_first_failure_and_commits_what_it_can():
+    """A captured replay round in which sequence 1's previous accepted index is
+    out of range, sequence 2's previous tree has a bad parent, sequence 3's
+    tree of this round has a bad root, and sequence 4 accepted nothing last
+    round (its previous tree is bad too, and is not checked). The round's
+    status keeps the first failure of each sequence (the previous round's
+    code above gt.PREV_SHIFT); a failed sequence accepts nothing, so neither
+    the attention caches nor the committed lengths move for it; sequence 3's
+    previous commit is applied although its own tree is rejected."""
+    rng = np.random.default_rng(31)
+    trees_p = [gi.kary_parents(2, 2), gi.chain_parents(6), gi.kary_parents(3, 2),
+               gi.random_tree_parents(rng, 8, 30), gi.kary_parents(2, 2)]
+    trees = [gi.kary_parents(2, 2), gi.chain_parents(5), gi.branching_parents([3, 2]),
+             gi.kary_parents(2, 3), gi.random_tree_parents(rng, 10, 40)]
+    n_gdn, n_attn, kinds = 2, 1, [0, 1, 0]
+    wp = gi.make_workload(trees_p, H=2, dk=128, dv=128, io="bf16", layers=n_gdn, seed=32)
+    w = gi.make_workload(trees, H=2, dk=128, dv=128, io="bf16", layers=n_gdn, seed=33)
+    wp.accepted[:] = [gi.pick_accepted(rng, trees_p[0]), 99, 3, 4, -1]
+    lens, cap = [10, 0, 40, 5, 63], 128
+    aw = gi.make_attn_workload(trees, 4, 2, 128, cap, lens, seed=34)
+    pdesc = gt.make_desc(wp.B, 2, 128, 128, wp.T, 64, gt.DTYPE_BF16)
+    gdesc = gt.make_desc(w.B, 2, 128, 128, w.T, 64, gt.DTYPE_BF16)
+    adesc = gt.make_attn_desc(w.B, 4, 2, 128, w.T, 64, cap, cap)
+    rdesc = gt.make_round_desc(gdesc, n_gdn, adesc, n_attn)
+    layout = gt.gdn_round_plan(rdesc)
+    ppar = wp.parents.copy()
+    for b in (2, 4):                            # bad parents after the previous round
+        ppar[wp.offsets[b] + 2] = 7
+    cpar = w.parents.copy()
+    cpar[w.offsets[3]] = 0                      # bad root this round
+    p_off, p_par, p_acc = i32(wp.offsets), i32(ppar), i32(wp.accepted)
+    offsets, parents = i32(w.offsets), i32(cpar)
+    pins = [dict(k=to_dev_io(wp.k[l], "bf16"), v=to_dev_io(wp.v[l], "bf16"),
+                 alpha=f32(wp.alpha[l]), beta=f32(wp.beta[l])) for l in range(n_gdn)]
+    ins = [dict(q=to_dev_io(w.q[l], "bf16"), k=to_dev_io(w.k[l], "bf16"),
+                v=to_dev_io(w.v[l], "bf16"), alpha=f32(w.alpha[l]), beta=f32(w.beta[l]))
+           for l in range(n_gdn)]
+    ain = dict(q=to_dev_io(aw.q, "bf16"), k=to_dev_io(aw.k, "bf16"), v=to_dev_io(aw.v, "bf16"))
+    acc_target = [gi.pick_accepted(rng, t) for t in trees]
+    d_np, t_np = gi.draft_target_tokens(rng, trees, acc_target)
+    draft, target = i32(d_np), i32(t_np)
+    G = _RoundState(w, [aw], lens)
+    G.S = [f32(wp.S0[l]) for l in range(n_gdn)]
+    kc0, vc0 = dev_to_bits(G.kc[0]), dev_to_bits(G.vc[0])
+    arena = torch.empty(max(1, layout.total_bytes), dtype=torch.uint8, device="cuda")
+    gdn_io = [gt.make_layer_io(gdesc, q=ins[l]["q"], k=ins[l]["k"], v=ins[l]["v"],
+                               alpha=ins[l]["alpha"], beta=ins[l]["beta"], S0=G.S[l], o=G.o[l],
+                               S_out=G.S[l]) for l in range(n_gdn)]
+    attn_io = [gt.make_attn_layer_io(adesc, q=ain["q"], k=ain["k"], v=ain["v"], k_cache=G.kc[0],
+                                     v_cache=G.vc[0], o=G.ao[0])]
+    prev_io = [gt.make_layer_io(pdesc, k=x["k"], v=x["v"], alpha=x["alpha"], beta=x["beta"])
+               for x in pins]
+    stream = torch.cuda.Stream()
+    graph = gt.RoundGraph(rdesc, offsets, parents, gdn_io, attn_io, arena, draft, target, G.acc,
+                          G.alen, G.nxt, G.st, cache_len=G.cache_len, layer_kinds=kinds,
+                          stream=stream, keep=(ins, ain, pins, G),
+                          prev=dict(desc=pdesc, offsets=p_off, parents=p_par, accepted=p_acc,
+                                    gdn_layers=prev_io))
+    graph.launch(stream)
+    stream.synchronize()
+    g = G.snapshot()
+    _say("failures round: status", g["st"].tolist(), "accepted", g["acc"].tolist())
+    prev = gt.prev_code
+    assert g["st"].tolist() == [0, prev(4), prev(2), 1, 0]
+    assert g["acc"].tolist() == [acc_target[0], -1, -1, -1, acc_target[4]]
+    assert g["alen"].tolist()[1:4] == [0, 0, 0] and g["nxt"].tolist()[1:4] == [-1, -1, -1]
+    plen = [len(gi.path_to_root(t, a)) for t, a in zip(trees, acc_target)]
+    assert g["len"].tolist() == [lens[0] + plen[0], lens[1], lens[2], lens[3], lens[4] + plen[4]]
+    kc, vc = g["kc"][0], g["vc"][0]
+    for b in (1, 2, 3):                          # caches of failed sequences untouched
+        assert np.array_equal(kc[b], kc0[b]) and np.array_equal(vc[b], vc0[b]), b
+    for l in range(n_gdn):
+        S = G.S[l].cpu().numpy().astype(np.float64)
+        # committed: sequences 0 and 3 (3's own tree is rejected); kept: 1, 2, 4
+        done = [0, 3]
+        sp = sub_workload(wp, done, layers=[l])
+        S_ref, stc = oracle.commit(sp.offsets, sp.parents, sp.accepted, sp.k[0], sp.v[0],
+                                   sp.alpha[0], sp.beta[0], sp.S0[0])
+        assert np.all(stc == 0)
+        assert rel_err_rows(S[done].reshape(4, -1), S_ref.reshape(4, -1)) <= TOL["bf16"]
+        for b in (1, 2, 4):
+            assert np.array_equal(S[b], wp.S0[l][b].astype(np.float32).astype(np.float64)), (l, b)
+        o = from_dev_io(G.o[l])
+        for b in (1, 2, 3):
+            assert np.all(o[w.offsets[b]:w.offsets[b + 1]] == 0), (l, b)
     graph.close()
 
 

@@ -33,6 +33,7 @@ def test_library_exports_every_declared_symbol():
                             "gdn_tree_commit_layers", "gdn_tree_attn_commit_layers",
                             "gdn_tree_commit_verify", "gdn_tree_commit_verify_layers",
                             "gdn_tree_replay_verify", "gdn_tree_replay_verify_layers",
+                            "gdn_tree_replay_commit", "gdn_tree_replay_commit_layers",
                             "gdn_tree_accept_greedy", "gdn_tree_accept_sampling",
                             "gdn_round_plan",
                             "gdn_round_tree_for_budget", "gdn_round_capture",
@@ -309,6 +310,36 @@ def test_replay_verify_checks_before_launch():
     assert lib.gdn_tree_commit_verify_layers(ctypes.byref(e0), ctypes.byref(e1), 2, None, None,
                                              None, None, None, None, 0, None, 0, None,
                                              None) == 0
+
+
+def test_replay_commit_checks_before_launch():
+    """Commit by replay takes no workspace; it needs the path's k, v, alpha and
+    beta, S0 and S_out, and rejects bad descriptors on the host."""
+    lib = gt.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = gt.make_desc(4, 2, 64, 64, 20, 8)
+    ly = (gt.GdnLayerIO * 2)(*[gt.GdnLayerIO(*([0x1000] * 9)) for _ in range(2)])
+
+    def call(desc=d, n=2, a=ly, acc=fake):
+        return lib.gdn_tree_replay_commit_layers(ctypes.byref(desc), n, fake, fake, acc, a, fake,
+                                                 None)
+
+    assert call(n=0) == 0
+    assert call(a=None) == 1
+    assert call(acc=None) == 1
+    for field in ("k", "v", "alpha", "beta", "S0", "S_out"):
+        setattr(ly[1], field, None)
+        assert call() == 1, field
+        setattr(ly[1], field, 0x1000)
+    for field in ("q", "o", "workspace"):                # not read by the commit
+        setattr(ly[0], field, None)
+    assert call(desc=gt.make_desc(4, 2, 48, 48, 20, 8)) == 3
+    assert call(desc=gt.make_desc(4, 2, 64, 64, 20, 65)) == 2
+    e = gt.make_desc(0, 2, 64, 64, 0, 8)
+    assert lib.gdn_tree_replay_commit(ctypes.byref(e), None, None, None, None, None, None, None,
+                                      None, None, None, None) == 0
+    assert lib.gdn_tree_replay_commit(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake,
+                                      fake, fake, fake, None) == 1
 
 
 # ------------------------------------------------------------------ rounds (gdn_round.h)

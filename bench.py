@@ -4,13 +4,19 @@
 One step = one round of the whole hot path over one batch on every GDN layer
 of the workload: each layer's state takes the previous round's commit (the
 accepted paths) and this round's trees are verified against it. By default
-(`--step fused`) a step is one gdn_tree_commit_verify_layers launch, which
-applies the commit and verifies in one pass over the states; the first
-round's verify is issued before timing starts, so K timed steps do K commits
-and K verifies per layer. `--step separate` times the separate calls instead:
-every layer verified and then committed in place, as one launch per kernel
-(gdn_tree_verify_layers, gdn_tree_commit_layers), or one launch per layer
-with `--launch per-layer`. The JSON line reports both schedules.
+(`--step replay`) a step is one gdn_tree_replay_verify_layers launch, which
+commits the previous round by replaying its accepted paths on the states and
+verifies in the same pass, keeping no workspace; `--step fused` commits from
+the previous round's pseudo-values instead (gdn_tree_commit_verify_layers).
+The first round's verify is issued before timing starts, so K timed steps do
+K commits and K verifies per layer. `--step separate` times the separate
+calls instead: every layer verified and then committed in place, as one
+launch per kernel (gdn_tree_verify_layers, gdn_tree_commit_layers), or one
+launch per layer with `--launch per-layer`. The JSON line reports every
+schedule, and per-launch records of the other workloads (`configs`: the tiny
+tree, the chain, the k=2 d=3 batch and the ragged batch), each timed while
+rotating through more than 1 GiB of independent copies so that no launch
+finds its state in L2 or the Infinity Cache.
 Default workload: k=3 d=3 draft trees (40 nodes incl. root), 24 GDN layers
 with independent inputs and states, batch 64, 16 heads, 128x128 fp32 state,
 bf16 q/k/v (Qwen3.5-9B GDN shape). Inputs are seeded synthetic data resident
@@ -81,7 +87,15 @@ def recorded_traffic(kind, config):
 
 
 def cpu_model():
-    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    """The host CPU's model name as lscpu reports it (else /proc/cpuinfo), or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
@@ -126,6 +140,13 @@ def parse():
                    help="timed steps of the full-attention leg (0 = skip)")
     p.add_argument("--attn-only", action="store_true",
                    help="run only the full-attention leg (profiling)")
+    p.add_argument("--config-steps", type=int, default=50,
+                   help="timed launches per schedule of the per-configuration records "
+                        "(c1, c2, c3, c5; 0 = skip)")
+    p.add_argument("--configs", default="c1,c2,c3,c5",
+                   help="workloads of the per-configuration records")
+    p.add_argument("--configs-only", action="store_true",
+                   help="run only the per-configuration records (profiling)")
     p.add_argument("--pmc-calibration", action="store_true",
                    help="after the timed legs, run a plain 256 MiB device copy three times "
                         "(reads and writes 256 MiB each): the known-size kernel that scales "
@@ -368,7 +389,7 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
         raise RuntimeError("nonzero status in the fused leg")
     times = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)        # us per launch
     med = times[steps // 2]
-    per_layer = sum(times) / steps / L                              # mean launch, per layer
+    us_layer = sum(times) / steps / L                               # mean launch, per layer
     fb = vb + cb - w.B * w.H * 4 * w.dv * w.dk                       # state read once
     if replay:
         # no pseudo-values or gate prefixes written; the path's k, v, alpha,
@@ -384,11 +405,11 @@ def fused_leg(args, gt, w, layers, offsets, parents, accepted, status, vb, cb, d
            "launch_us_mean": round(sum(times) / steps, 2),
            "launch_us_median": round(med, 2),
            "launch_us_p10_p90": [round(times[steps // 10], 2), round(times[(9 * steps) // 10], 2)],
-           "us_per_layer": round(per_layer, 3),
+           "us_per_layer": round(us_layer, 3),
            "us_per_layer_median": round(med / L, 3),
            "alg_bytes_per_layer": int(fb),
-           "achieved_GBs": round(fb / per_layer / 1e3, 1),
-           "frac_hbm": round(fb / per_layer / 1e3 / HBM_PEAK_GBS, 4),
+           "achieved_GBs": round(fb / us_layer / 1e3, 1),
+           "frac_hbm": round(fb / us_layer / 1e3 / HBM_PEAK_GBS, 4),
            "nodes_per_s_per_layer": round(w.T * L * steps / el, 1)}
     log(f"fused previous {'replay' if replay else 'commit'} + verify"
         f"{' (one launch per layer)' if per_layer else ''}: {out}")
@@ -505,6 +526,138 @@ def sampling_accept_leg(args, gt, gi, w, offsets, parents, dev, V=151936):
            "visited_rows_GBs": round(rows_bytes / med / 1e3, 1)}
     log(f"sampling acceptance: {out}")
     del P, Q
+    torch.cuda.empty_cache()
+    return out
+
+
+def config_legs(args, gt, gi, dev):
+    """Per-launch records of the other workloads, one GDN layer each (the
+    headline covers the 24-layer k=3 d=3 stack). For every workload, two
+    schedules, each timed launch by launch with HIP events on the launching
+    stream (median, p10/p90): the fused round boundary by replay
+    (gdn_tree_replay_verify_layers, one layer per launch: the previous
+    round's accepted paths replayed on the state, this round's tree verified),
+    and the separate verify and commit launches. Launches must not find their
+    data in the 4 MB L2 or the 256 MB Infinity Cache: the k=2 d=3 and ragged
+    batches rotate through independent copies of the layer totalling more
+    than 1 GiB (as the layers of a model do); the tiny tree and the chain are
+    a few hundred KiB per copy, so a 1 GiB buffer is read between timed
+    launches instead (outside the events)."""
+    import numpy as np
+    import torch
+    names = [c for c in args.configs.split(",") if c]
+    steps, warm = args.config_steps, 10
+    out = {}
+    flush = None
+    for name in names:
+        t0 = time.time()
+        w = gi.make_config(name, layers=1)
+        io_t = torch.bfloat16 if w.io == "bf16" else torch.float32
+        io_bytes = 2 if w.io == "bf16" else 4
+        B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+        desc = gt.make_desc(B, H, dk, dv, T, w.max_nodes,
+                            gt.DTYPE_BF16 if w.io == "bf16" else gt.DTYPE_F32, gt.MODE_WY)
+        nbytes = gt.gdn_tree_workspace_bytes(desc)
+        per_copy = B * H * dv * dk * 4 + T * H * (io_bytes * (2 * dk + 2 * dv) + 8) + nbytes
+        rotate = per_copy * 8 >= (1 << 30) // 4          # large enough to rotate
+        copies = max(2, -(-(1 << 30) // per_copy)) if rotate else 1
+        if not rotate and flush is None:
+            flush = torch.ones(1 << 28, device=dev)       # 1 GiB, read between launches
+
+        def put(x, io=False):
+            t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+            return t.to(io_t) if io else t
+        offsets, parents, accepted = put(w.offsets), put(w.parents), put(w.accepted)
+        status = torch.zeros(B, dtype=torch.int32, device=dev)
+        base = dict(q=put(w.q[0], True), k=put(w.k[0], True), v=put(w.v[0], True),
+                    alpha=put(w.alpha[0]), beta=put(w.beta[0]), S=put(w.S0[0]))
+        cps = [base] + [{k_: x.clone() for k_, x in base.items()} for _ in range(copies - 1)]
+        for c in cps:
+            c["o"] = torch.empty_like(c["v"])
+        replay_calls = []
+        for c in cps:
+            pio = gt.make_layer_io(desc, k=c["k"], v=c["v"], alpha=c["alpha"], beta=c["beta"])
+            cio = gt.make_layer_io(desc, q=c["q"], k=c["k"], v=c["v"], alpha=c["alpha"],
+                                   beta=c["beta"], S0=c["S"], o=c["o"], S_out=c["S"])
+            replay_calls.append(gt.prepare_replay_verify_layers(
+                desc, desc, offsets, parents, accepted, offsets, parents, [pio], [cio], status,
+                keep=(c,)))
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+
+        def timed(fns_per_launch, n):
+            """n launches (each a list of calls, one event interval per call)."""
+            k = len(fns_per_launch(0))
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(k + 1)] for _ in range(n)]
+            for i in range(warm + n):
+                if flush is not None and not rotate:
+                    flush.sum()
+                fns = fns_per_launch(i)
+                if i < warm:
+                    for f in fns:
+                        f()
+                    continue
+                e = ev[i - warm]
+                e[0].record(stream)
+                for j, f in enumerate(fns):
+                    f()
+                    e[j + 1].record(stream)
+            torch.cuda.synchronize()
+            if np.any(status.cpu().numpy() != 0):
+                raise RuntimeError(f"nonzero status in the {name} record")
+            return [sorted(e[j].elapsed_time(e[j + 1]) * 1e3 for e in ev) for j in range(k)]
+
+        def stats(times):
+            n = len(times)
+            return {"launch_us_median": round(times[n // 2], 3),
+                    "launch_us_p10_p90": [round(times[n // 10], 3), round(times[(9 * n) // 10], 3)],
+                    "launch_us_mean": round(sum(times) / n, 3)}
+
+        # the first round's verify, so that every timed launch commits a round
+        for c in cps:
+            gt.gdn_tree_verify(desc, offsets, parents, c["q"], c["k"], c["v"], c["alpha"],
+                               c["beta"], c["S"], c["o"],
+                               torch.empty(nbytes, dtype=torch.uint8, device=dev), status)
+        (rt,) = timed(lambda i: [replay_calls[i % copies]], steps)
+        vb, cb, _, _ = algorithmic_bytes(w, io_bytes, gi)
+        path = sum(len(gi.path_to_root(p, int(a))) if a >= 0 else 0
+                   for p, a in zip(w.parents_list, w.accepted))
+        rb = vb + cb - B * H * 4 * dv * dk - T * H * (4 * dv + 4) + path * H * (
+            io_bytes * dv + 8 - 4 * dv - 4)
+        rec = {"workload": gi.CONFIGS[name]["desc"], "batch": B, "total_nodes": T,
+               "copies": copies, "rotation_bytes": int(per_copy * copies) if rotate else None,
+               "cache_eviction": (f"rotation through {copies} copies" if rotate
+                                  else "1 GiB read between timed launches")}
+        r = stats(rt)
+        r.update({"alg_bytes": int(rb),
+                  "achieved_GBs_median": round(rb / r["launch_us_median"] / 1e3, 1),
+                  "frac_hbm_median": round(rb / r["launch_us_median"] / 1e3 / HBM_PEAK_GBS, 4),
+                  "nodes_per_s_per_layer": round(T / (r["launch_us_median"] * 1e-6), 1)})
+        rec["replay"] = r
+        del replay_calls
+        # the separate verify and commit launches (workspace per copy)
+        sep = []
+        for c in cps:
+            c["ws"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            sep.append([gt.prepare_verify(desc, offsets, parents, c["q"], c["k"], c["v"],
+                                          c["alpha"], c["beta"], c["S"], c["o"], c["ws"], status),
+                        gt.prepare_commit(desc, offsets, parents, accepted, c["k"], c["S"],
+                                          c["S"], c["ws"], status)])
+        vt, ct = timed(lambda i: sep[i % copies], steps)
+        sv, sc = stats(vt), stats(ct)
+        v_med, c_med = sv["launch_us_median"], sc["launch_us_median"]
+        rec["separate"] = {
+            "verify": dict(sv, alg_bytes=int(vb),
+                           frac_hbm_median=round(vb / v_med / 1e3 / HBM_PEAK_GBS, 4)),
+            "commit": dict(sc, alg_bytes=int(cb),
+                           frac_hbm_median=round(cb / c_med / 1e3 / HBM_PEAK_GBS, 4)),
+            "nodes_per_s_per_layer": round(T / ((v_med + c_med) * 1e-6), 1)}
+        rec["steps"] = steps
+        log(f"config {name} ({time.time() - t0:.1f}s): {rec}")
+        out[name] = rec
+        del sep, cps, base
+        torch.cuda.empty_cache()
+    del flush
     torch.cuda.empty_cache()
     return out
 
@@ -682,6 +835,9 @@ def main():
         if args.pmc_calibration:
             pmc_calibration(dev)
         print(json.dumps({"fa_layers": fa}), flush=True)
+        return
+    if args.configs_only:
+        print(json.dumps({"configs": config_legs(args, gt, gi, dev)}), flush=True)
         return
     io_t = torch.bfloat16 if w.io == "bf16" else torch.float32
     io_bytes = 2 if w.io == "bf16" else 4
@@ -907,12 +1063,23 @@ def main():
     n_req = w.T / w.B
     wy_state = n_req * L * w.H * (4 * w.dv + 4 + io_bytes * w.dk)
     fork_state = n_req * L * w.H * 4 * w.dv * w.dk
+    # the replay round (the headline step) keeps no workspace: between its
+    # acceptance and the next verify it retains the round's k, v, alpha, beta
+    # rows (all nodes, as the call takes them; only the accepted path's rows
+    # are read, so a caller that compacts them keeps the path alone)
+    replay_state = n_req * L * w.H * (io_bytes * (w.dk + w.dv) + 8)
+    mean_path = sum(len(gi.path_to_root(p, int(a))) if a >= 0 else 0
+                    for p, a in zip(w.parents_list, w.accepted)) / w.B
+    replay_path = mean_path * L * w.H * (io_bytes * (w.dk + w.dv) + 8)
     spec = {"wy_bytes": int(wy_state), "wy_bytes_without_keys": int(n_req * L * w.H * (4 * w.dv + 4)),
             # the fused rounds keep two WY workspaces per layer at once (the
             # previous round's until its commit has run, and this round's)
             "wy_bytes_fused_rounds": int(2 * wy_state),
+            "replay_retained_bytes": int(replay_state),
+            "replay_retained_path_bytes": int(replay_path),
             "fork_fp32_bytes": int(fork_state), "fork_over_wy": round(fork_state / wy_state, 1),
-            "nodes_per_request": n_req, "layers": L}
+            "fork_over_replay": round(fork_state / replay_state, 1),
+            "nodes_per_request": n_req, "mean_accepted_path": round(mean_path, 3), "layers": L}
 
     # --------------------------------------------------------------- CPU oracle
     cpu = None
@@ -958,6 +1125,7 @@ def main():
             ly.pop(key)
     ver = com = None
     torch.cuda.empty_cache()
+    cfgs = config_legs(args, gt, gi, dev) if args.config_steps > 0 else None
     if args.attn_steps > 0:
         fa = attention_leg(args, gt, gi, w, dev)
         torch.cuda.empty_cache()
@@ -985,7 +1153,7 @@ def main():
         "roofline": roof, "kernels": kern, "cpu_baseline": cpu, "fork_baseline": fork,
         "per_layer_launches": per_layer, "fused_rounds": fused, "replay_rounds": replay,
         "separate_calls": separate,
-        "spec_state_per_request": spec, "fa_layers": fa,
+        "spec_state_per_request": spec, "configs": cfgs, "fa_layers": fa,
         "round": rnd,
     }
     print(json.dumps(out), flush=True)

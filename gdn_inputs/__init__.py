@@ -424,6 +424,38 @@ def make_attn_config(name: str, seed: Optional[int] = None) -> AttnWorkload:
 # ---------------------------------------------------------------------------
 
 
+def draft_confidences(rng: np.random.Generator, parents_list: Sequence[Sequence[int]],
+                      p_dominant: float = 0.5) -> np.ndarray:
+    """The draft model's confidence in every node's token, as float32 [T]
+    (the input of a selective fork). Siblings are alternatives drawn from one
+    distribution, so their confidences share a unit of mass: with probability
+    p_dominant a node's first child takes U(0.95, 1] of it (a dominant token)
+    and the others split the rest (Dirichlet(1, ...)); otherwise the children
+    and the undrafted remainder split the unit uniformly (Dirichlet over
+    children + 1 parts). The root, the token the target itself emitted, has
+    confidence 1."""
+    out = []
+    for parents in parents_list:
+        n = len(parents)
+        conf = np.zeros(n, np.float64)
+        conf[0] = 1.0
+        children = [[] for _ in range(n)]
+        for c in range(1, n):
+            children[parents[c]].append(c)
+        for kids in children:
+            if not kids:
+                continue
+            if rng.random() < p_dominant:
+                top = 0.95 + 0.05 * (1.0 - rng.random())
+                conf[kids[0]] = top
+                if len(kids) > 1:
+                    conf[kids[1:]] = (1.0 - top) * rng.dirichlet(np.ones(len(kids)))[:-1]
+            else:
+                conf[kids] = rng.dirichlet(np.ones(len(kids) + 1))[:-1]
+        out.append(conf)
+    return np.concatenate(out).astype(np.float32)
+
+
 def draft_target_tokens(rng: np.random.Generator, parents_list: Sequence[Sequence[int]],
                         accepted: Sequence[int], vocab: int = 32000):
     """Token ids for a batch of trees: draft tokens distinct among the

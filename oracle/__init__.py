@@ -59,6 +59,11 @@ def _load():
             lib.oracle_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
             lib.oracle_fork_replay.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
             lib.oracle_chain.argtypes = [I, I, I, P, P, P, P, P, P, P, P]
+            D = ctypes.c_double
+            lib.oracle_selective_fork.argtypes = [I, I, I, I, I, I, P, P, P, D, P, P, P, P, P, P,
+                                                  P, P, P, P]
+            lib.oracle_selective_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P,
+                                                    P, P, P]
             lib.oracle_tree_attn.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
                                              ctypes.c_double, P, P]
             lib.oracle_tree_attn_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
@@ -145,6 +150,45 @@ def fork_replay(offsets, parents, q, k, v, alpha, beta, S0, max_nodes: int = 64)
     lib.oracle_fork_replay(B, H, dk, dv, T, max_nodes, _p(offsets), _p(parents), _p(q), _p(k),
                            _p(v), _p(alpha), _p(beta), _p(S0), _p(o), _p(ck), _p(status))
     return o, ck, status[:B]
+
+
+def selective_fork(offsets, parents, conf, threshold, q, k, v, alpha, beta, S0,
+                   max_nodes: int = 64):
+    """Depth-by-depth fork that saves a checkpoint only for nodes with
+    conf <= threshold: (o[T,H,dv], ckpt[T,H,dv,dk] (saved entries only, others
+    zero), kept[T] int32, status[B])."""
+    lib = _load()
+    offsets, parents = _i32(offsets), _i32(parents)
+    conf, q, k, v, alpha, beta, S0 = map(_f64, (conf, q, k, v, alpha, beta, S0))
+    B = len(offsets) - 1
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((T, H, dv), np.float64)
+    ck = np.zeros((T, H, dv, dk), np.float64)
+    kept = np.zeros(max(T, 1), np.int32)
+    status = np.zeros(max(B, 1), np.int32)
+    lib.oracle_selective_fork(B, H, dk, dv, T, max_nodes, _p(offsets), _p(parents), _p(conf),
+                              float(threshold), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(S0),
+                              _p(o), _p(ck), _p(kept), _p(status))
+    return o, ck, kept[:T], status[:B]
+
+
+def selective_commit(offsets, parents, kept, accepted, ckpt, k, v, alpha, beta, S0,
+                     max_nodes: int = 64):
+    """The accepted node's state after a selective-fork verify (its saved
+    checkpoint, or rebuilt from the nearest saved ancestor): (S_out, status)."""
+    lib = _load()
+    offsets, parents, kept, accepted = _i32(offsets), _i32(parents), _i32(kept), _i32(accepted)
+    ckpt, k, v, alpha, beta, S0 = map(_f64, (ckpt, k, v, alpha, beta, S0))
+    B = len(offsets) - 1
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    out = np.zeros((B, H, dv, dk), np.float64)
+    status = np.zeros(max(B, 1), np.int32)
+    lib.oracle_selective_commit(B, H, dk, dv, T, max_nodes, _p(offsets), _p(parents), _p(kept),
+                                _p(accepted), _p(ckpt), _p(k), _p(v), _p(alpha), _p(beta),
+                                _p(S0), _p(out), _p(status))
+    return out, status[:B]
 
 
 def chain(q, k, v, alpha, beta, S0):

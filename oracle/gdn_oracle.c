@@ -252,3 +252,122 @@ void oracle_chain(int n, int dk, int dv, const double* q, const double* k, const
     read_out(dk, dv, S_final, q + (size_t)t * dk, o + (size_t)t * dv);
   }
 }
+
+/* ---------------------------------------------------------------- selective fork
+ *
+ * Selective fork (rainlin-top section 8, "selective fork"): the draft's
+ * confidence in each node decides whether the depth-by-depth fork keeps a
+ * rollback point for it. A node whose confidence is above the threshold
+ * (the page: 0.95) is processed without saving a checkpoint; one at or below
+ * it forks and saves one, as in section 4. Reading taken here: a node whose
+ * state was not saved is never lost, only not stored; where it is needed
+ * later (as a parent during verify, or as the accepted node at commit) it is
+ * recomputed from the nearest saved ancestor (S0 above the root) by applying
+ * the delta steps of the unsaved nodes in between. */
+
+/* State of local node `node` of sequence b, head h, rebuilt from the saved
+ * checkpoints: start at the nearest saved node on its root path (the node
+ * itself included), or at S0 when none is saved, and apply the steps of the
+ * path nodes below that start. */
+static void rebuild_state(int H, int dk, int dv, int lo, const int32_t* parents,
+                          const int32_t* kept, const double* ckpt, int node, int b, int h,
+                          const double* k, const double* v, const double* alpha,
+                          const double* beta, const double* S0, double* S) {
+  const size_t SS = (size_t)dv * dk;
+  int path[ORC_MAX_NODES];
+  int len = 0;
+  int start = -1;                   /* a saved node on the path, or -1 */
+  for (int j = node; j != -1; j = parents[lo + j]) {
+    if (kept[lo + j]) {
+      start = j;
+      break;
+    }
+    path[len++] = j;                /* unsaved nodes, deepest first */
+  }
+  if (start >= 0)
+    memcpy(S, ckpt + ((size_t)(lo + start) * H + h) * SS, sizeof(double) * SS);
+  else
+    memcpy(S, S0 + ((size_t)b * H + h) * SS, sizeof(double) * SS);
+  for (int s = len - 1; s >= 0; --s) {
+    size_t g = (size_t)(lo + path[s]) * H + h;
+    delta_step(dk, dv, S, k + g * dk, v + g * dv, alpha[g], beta[g]);
+  }
+}
+
+/* Verify with selective fork, depth by depth: every node of level l starts
+ * from its parent's state (the saved checkpoint, or rebuilt as above; S0 for
+ * the root), takes its own delta step, emits o = S q, and saves its state
+ * iff conf <= threshold (kept[t] = 1). ckpt [T,H,dv,dk]: saved states at the
+ * node's own index, other entries untouched. */
+void oracle_selective_fork(int B, int H, int dk, int dv, int T, int max_nodes,
+                           const int32_t* offsets, const int32_t* parents, const double* conf,
+                           double threshold, const double* q, const double* k, const double* v,
+                           const double* alpha, const double* beta, const double* S0, double* o,
+                           double* ckpt, int32_t* kept, int32_t* status) {
+  for (int b = 0; b < B; ++b) status[b] = check_seq(b, T, max_nodes, offsets, parents);
+  const size_t SS = (size_t)dv * dk;
+  for (int b = 0; b < B; ++b) {
+    if (status[b] != ORC_OK) continue;
+    int lo = offsets[b], n = offsets[b + 1] - lo;
+    int level[ORC_MAX_NODES];
+    int maxlevel = 0;
+    for (int i = 0; i < n; ++i) {
+      int d = 0;
+      for (int j = parents[lo + i]; j != -1; j = parents[lo + j]) d++;
+      level[i] = d;
+      if (d > maxlevel) maxlevel = d;
+      kept[lo + i] = 0;
+    }
+    double* S = (double*)malloc(sizeof(double) * SS);
+    for (int l = 0; l <= maxlevel; ++l) {
+      for (int i = 0; i < n; ++i) {
+        if (level[i] != l) continue;
+        const int keep = conf[lo + i] <= threshold;
+        for (int h = 0; h < H; ++h) {
+          size_t g = (size_t)(lo + i) * H + h;
+          int p = parents[lo + i];
+          if (p == -1)
+            memcpy(S, S0 + ((size_t)b * H + h) * SS, sizeof(double) * SS);
+          else
+            rebuild_state(H, dk, dv, lo, parents, kept, ckpt, p, b, h, k, v, alpha, beta, S0, S);
+          delta_step(dk, dv, S, k + g * dk, v + g * dv, alpha[g], beta[g]);
+          read_out(dk, dv, S, q + g * dk, o + g * dv);
+          if (keep) memcpy(ckpt + g * SS, S, sizeof(double) * SS);
+        }
+        kept[lo + i] = keep;
+      }
+    }
+    free(S);
+  }
+}
+
+/* Commit after a selective-fork verify: the accepted node's state, from its
+ * saved checkpoint when it has one, else rebuilt from the nearest saved
+ * ancestor (S0 when none); -1 keeps S0. kept and ckpt as verify left them.
+ * Status as oracle_commit. */
+void oracle_selective_commit(int B, int H, int dk, int dv, int T, int max_nodes,
+                             const int32_t* offsets, const int32_t* parents, const int32_t* kept,
+                             const int32_t* accepted, const double* ckpt, const double* k,
+                             const double* v, const double* alpha, const double* beta,
+                             const double* S0, double* S_out, int32_t* status) {
+  for (int b = 0; b < B; ++b) {
+    int st = check_seq(b, T, max_nodes, offsets, parents);
+    if (st == ORC_OK) {
+      int n = offsets[b + 1] - offsets[b];
+      if (accepted[b] < -1 || accepted[b] >= n) st = ORC_BAD_ACCEPTED;
+    }
+    status[b] = st;
+  }
+  const size_t SS = (size_t)dv * dk;
+  for (int b = 0; b < B; ++b) {
+    if (status[b] != ORC_OK) continue;
+    for (int h = 0; h < H; ++h) {
+      size_t base = ((size_t)b * H + h) * SS;
+      if (accepted[b] == -1)
+        memcpy(S_out + base, S0 + base, sizeof(double) * SS);
+      else
+        rebuild_state(H, dk, dv, offsets[b], parents, kept, ckpt, accepted[b], b, h, k, v,
+                      alpha, beta, S0, S_out + base);
+    }
+  }
+}

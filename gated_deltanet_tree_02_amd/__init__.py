@@ -30,6 +30,9 @@ __all__ = [
     "gdn_tree_replay_verify", "gdn_tree_replay_verify_layers", "prepare_replay_verify_layers",
     "gdn_tree_replay_commit", "gdn_tree_replay_commit_layers", "prepare_replay_commit_layers",
     "PREV_SHIFT", "prev_code",
+    "gdn_tree_fork_selective_workspace_bytes", "gdn_tree_fork_selective_verify",
+    "gdn_tree_fork_selective_commit", "prepare_fork_selective_verify",
+    "prepare_fork_selective_commit",
     "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
     "prepare_attn_commit_layers",
     "gdn_tree_accept_greedy", "gdn_tree_accept_sampling", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
@@ -42,7 +45,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE_WY, MODE_FORK, MODE_FORK_DELTA = 0, 1, 2
 MAX_NODES = 64
 TREE_STATUS = {0: "ok", 1: "bad root", 2: "bad parent", 3: "bad size", 4: "bad accepted",
-               5: "too deep", 6: "cache full", 7: "bad token"}
+               5: "too deep", 6: "cache full", 7: "bad token", 8: "too many kept"}
 # fused round-boundary calls: the previous round's commit code sits above this shift
 PREV_SHIFT = 4
 
@@ -168,6 +171,15 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_replay_commit.restype = I
             lib.gdn_tree_replay_commit_layers.argtypes = [D, ctypes.c_int32, P, P, P, LY, P, P]
             lib.gdn_tree_replay_commit_layers.restype = I
+            F = ctypes.c_float
+            lib.gdn_tree_fork_selective_workspace_bytes.argtypes = [D, ctypes.c_int32]
+            lib.gdn_tree_fork_selective_workspace_bytes.restype = S
+            lib.gdn_tree_fork_selective_verify.argtypes = [D, P, P, P, F, ctypes.c_int32, P, P,
+                                                           P, P, P, P, P, P, S, P, P]
+            lib.gdn_tree_fork_selective_verify.restype = I
+            lib.gdn_tree_fork_selective_commit.argtypes = [D, P, P, P, F, ctypes.c_int32, P, P,
+                                                           P, P, P, P, P, P, S, P, P]
+            lib.gdn_tree_fork_selective_commit.restype = I
             AL = ctypes.POINTER(GdnAttnLayerIO)
             lib.gdn_tree_attn_commit_layers.argtypes = [A, ctypes.c_int32, P, P, P, AL, P, P, P]
             lib.gdn_tree_attn_commit_layers.restype = I
@@ -774,6 +786,113 @@ def prepare_replay_commit_layers(desc, offsets, parents, accepted, layers, tree_
                                                 tree_status)
     return PreparedCall("gdn_tree_replay_commit_layers", desc, args, _stream(stream, dev),
                         (offsets, parents, accepted, tree_status, arr, tuple(keep)))
+
+
+# ------------------------------------------------------------------ selective fork
+
+
+def gdn_tree_fork_selective_workspace_bytes(desc, max_kept: int) -> int:
+    return int(load_library().gdn_tree_fork_selective_workspace_bytes(ctypes.byref(desc),
+                                                                      int(max_kept)))
+
+
+def _selective_args(desc, offsets, parents, confidence, threshold, max_kept):
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    return dev, [_ptr(offsets, "offsets", torch.int32, (B + 1,), dev),
+                 _ptr(parents, "parents", torch.int32, (T,), dev),
+                 _ptr(confidence, "confidence", torch.float32, (T,), dev),
+                 ctypes.c_float(threshold), ctypes.c_int32(max_kept)]
+
+
+def _ws_args(workspace, dev):
+    torch = _torch()
+    if workspace is None:
+        return [None, ctypes.c_size_t(0)]
+    return [_ptr(workspace, "workspace", torch.uint8, None, dev),
+            ctypes.c_size_t(workspace.numel())]
+
+
+def _selective_verify_args(desc, offsets, parents, confidence, threshold, max_kept, q, k, v,
+                           alpha, beta, S0, o, workspace, tree_status):
+    torch = _torch()
+    B, H, T, dk, dv = desc.num_seqs, desc.num_heads, desc.total_nodes, desc.dk, desc.dv
+    io = _io_dtype(desc)
+    dev, args = _selective_args(desc, offsets, parents, confidence, threshold, max_kept)
+    args += [_ptr(q, "q", io, (T, H, dk), dev), _ptr(k, "k", io, (T, H, dk), dev),
+             _ptr(v, "v", io, (T, H, dv), dev), _ptr(alpha, "alpha", torch.float32, (T, H), dev),
+             _ptr(beta, "beta", torch.float32, (T, H), dev),
+             _ptr(S0, "S0", torch.float32, (B, H, dv, dk), dev), _ptr(o, "o", io, (T, H, dv), dev)]
+    args += _ws_args(workspace, dev)
+    args.append(_ptr(tree_status, "tree_status", torch.int32, (B,), dev))
+    return dev, args
+
+
+def _selective_commit_args(desc, offsets, parents, confidence, threshold, max_kept, accepted, k,
+                           v, alpha, beta, S0, S_out, workspace, tree_status):
+    torch = _torch()
+    B, H, T, dk, dv = desc.num_seqs, desc.num_heads, desc.total_nodes, desc.dk, desc.dv
+    io = _io_dtype(desc)
+    dev, args = _selective_args(desc, offsets, parents, confidence, threshold, max_kept)
+    args += [_ptr(accepted, "accepted", torch.int32, (B,), dev),
+             _ptr(k, "k", io, (T, H, dk), dev), _ptr(v, "v", io, (T, H, dv), dev),
+             _ptr(alpha, "alpha", torch.float32, (T, H), dev),
+             _ptr(beta, "beta", torch.float32, (T, H), dev),
+             _ptr(S0, "S0", torch.float32, (B, H, dv, dk), dev),
+             _ptr(S_out, "S_out", torch.float32, (B, H, dv, dk), dev)]
+    args += _ws_args(workspace, dev)
+    args.append(_ptr(tree_status, "tree_status", torch.int32, (B,), dev))
+    return dev, args
+
+
+def gdn_tree_fork_selective_verify(desc, offsets, parents, confidence, threshold, max_kept, q, k,
+                                   v, alpha, beta, S0, o, workspace, tree_status, stream=None):
+    """Depth-by-depth fork keeping checkpoints only for nodes with
+    confidence <= threshold (at most max_kept per sequence)."""
+    torch = _torch()
+    dev, args = _selective_verify_args(desc, offsets, parents, confidence, threshold, max_kept, q,
+                                       k, v, alpha, beta, S0, o, workspace, tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_fork_selective_verify(ctypes.byref(desc), *args,
+                                                             _stream(stream, dev)),
+               "gdn_tree_fork_selective_verify")
+
+
+def gdn_tree_fork_selective_commit(desc, offsets, parents, confidence, threshold, max_kept,
+                                   accepted, k, v, alpha, beta, S0, S_out, workspace, tree_status,
+                                   stream=None):
+    """The accepted node's state after a selective-fork verify."""
+    torch = _torch()
+    dev, args = _selective_commit_args(desc, offsets, parents, confidence, threshold, max_kept,
+                                       accepted, k, v, alpha, beta, S0, S_out, workspace,
+                                       tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_fork_selective_commit(ctypes.byref(desc), *args,
+                                                             _stream(stream, dev)),
+               "gdn_tree_fork_selective_commit")
+
+
+def prepare_fork_selective_verify(desc, offsets, parents, confidence, threshold, max_kept, q, k,
+                                  v, alpha, beta, S0, o, workspace, tree_status,
+                                  stream=None) -> PreparedCall:
+    tensors = (offsets, parents, confidence, q, k, v, alpha, beta, S0, o, workspace, tree_status)
+    dev, args = _selective_verify_args(desc, offsets, parents, confidence, threshold, max_kept, q,
+                                       k, v, alpha, beta, S0, o, workspace, tree_status)
+    return PreparedCall("gdn_tree_fork_selective_verify", desc, args, _stream(stream, dev),
+                        tensors)
+
+
+def prepare_fork_selective_commit(desc, offsets, parents, confidence, threshold, max_kept,
+                                  accepted, k, v, alpha, beta, S0, S_out, workspace, tree_status,
+                                  stream=None) -> PreparedCall:
+    tensors = (offsets, parents, confidence, accepted, k, v, alpha, beta, S0, S_out, workspace,
+               tree_status)
+    dev, args = _selective_commit_args(desc, offsets, parents, confidence, threshold, max_kept,
+                                       accepted, k, v, alpha, beta, S0, S_out, workspace,
+                                       tree_status)
+    return PreparedCall("gdn_tree_fork_selective_commit", desc, args, _stream(stream, dev),
+                        tensors)
 
 
 # ------------------------------------------------------------------ attention layers, batched

@@ -537,6 +537,70 @@ gdn_status gdn_tree_replay_commit(const gdn_tree_desc* desc, const int32_t* offs
                                        stream);
 }
 
+size_t gdn_tree_fork_selective_workspace_bytes(const gdn_tree_desc* desc, int32_t max_kept) {
+  if (check_desc(desc) != GDN_OK || max_kept < 0 || max_kept > desc->max_nodes) return 0;
+  return round_up((size_t)desc->num_seqs * max_kept * desc->num_heads * desc->dv * desc->dk *
+                  sizeof(float));
+}
+
+gdn_status gdn_tree_fork_selective_verify(const gdn_tree_desc* desc, const int32_t* offsets,
+                                          const int32_t* parents, const float* confidence,
+                                          float threshold, int32_t max_kept, const void* q,
+                                          const void* k, const void* v, const float* alpha,
+                                          const float* beta, const float* S0, void* o,
+                                          void* workspace, size_t ws_bytes,
+                                          int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (max_kept < 0 || max_kept > desc->max_nodes) return GDN_ERR_BAD_SHAPE;
+  if (desc->num_seqs == 0) return GDN_OK;
+  if (!offsets || !tree_status || !S0) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 &&
+      (!parents || !confidence || !q || !k || !v || !alpha || !beta || !o))
+    return GDN_ERR_NULL_PTR;
+  const size_t need = gdn_tree_fork_selective_workspace_bytes(desc, max_kept);
+  if (ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (need > 0 && !workspace) return GDN_ERR_NULL_PTR;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int L = levels(desc);
+  for (int level = 0; level < L; ++level) {
+    gdn::ForkArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes, desc->max_nodes,
+                    L - 1, level, offsets, parents, q, k, v, alpha, beta, S0, o,
+                    static_cast<float*>(workspace), tree_status, nullptr, nullptr};
+    a.conf = confidence;
+    a.threshold = threshold;
+    a.max_kept = max_kept;
+    st = launched(gdn::launch_fork_selective_level(desc->io_dtype, desc->dk, a, s));
+    if (st != GDN_OK) return st;
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_tree_fork_selective_commit(const gdn_tree_desc* desc, const int32_t* offsets,
+                                          const int32_t* parents, const float* confidence,
+                                          float threshold, int32_t max_kept,
+                                          const int32_t* accepted, const void* k, const void* v,
+                                          const float* alpha, const float* beta,
+                                          const float* S0, float* S_out, const void* workspace,
+                                          size_t ws_bytes, int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (max_kept < 0 || max_kept > desc->max_nodes) return GDN_ERR_BAD_SHAPE;
+  if (desc->num_seqs == 0) return GDN_OK;
+  if (!offsets || !accepted || !S0 || !S_out || !tree_status) return GDN_ERR_NULL_PTR;
+  if (desc->total_nodes > 0 && (!parents || !confidence || !k || !v || !alpha || !beta))
+    return GDN_ERR_NULL_PTR;
+  const size_t need = gdn_tree_fork_selective_workspace_bytes(desc, max_kept);
+  if (ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (need > 0 && !workspace) return GDN_ERR_NULL_PTR;
+  gdn::SelectiveCommitArgs a{desc->num_seqs, desc->num_heads, desc->total_nodes,
+                             desc->max_nodes, levels(desc) - 1, offsets, parents, accepted,
+                             confidence, threshold, max_kept, k, v, alpha, beta, S0, S_out,
+                             static_cast<const float*>(workspace), tree_status};
+  return launched(gdn::launch_fork_selective_commit(desc->io_dtype, desc->dk, a,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 const char* gdn_tree_status_string(int status) {
   switch (status) {
     case GDN_OK: return "ok";

@@ -68,6 +68,33 @@ struct ForkArgs {
   float* U;      // FORK_DELTA: [T,H,dv] the per-node deltas, else null
   float* g2;     // FORK_DELTA: [T,H] base-2 gate prefixes, else null
   int merge = 0;
+  // selective fork: a node saves its state iff conf <= threshold, in slot
+  // b * max_kept + (its rank among the sequence's saved nodes); ckpt is
+  // then [B * max_kept, H, dv, dk]
+  const float* conf = nullptr;
+  float threshold = 0.f;
+  int max_kept = 0;
+};
+
+// Commit after a selective-fork verify: the accepted node's saved state, or
+// the state rebuilt from its nearest saved ancestor (S0 when none) by
+// replaying the path's steps from k, v, alpha, beta.
+struct SelectiveCommitArgs {
+  int B, H, T, max_nodes, max_depth;
+  const int32_t* offsets;
+  const int32_t* parents;
+  const int32_t* accepted;
+  const float* conf;
+  float threshold;
+  int max_kept;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;
+  float* S_out;
+  const float* ckpt;     // [B * max_kept, H, dv, dk]
+  int32_t* status;
 };
 
 struct ForkCommitArgs {
@@ -306,6 +333,9 @@ hipError_t launch_replay_commit(int io, int d, const CommitArgs& a, hipStream_t 
 hipError_t launch_replay_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s);
 hipError_t launch_fork_level(int io, int d, const ForkArgs& a, hipStream_t s);
 hipError_t launch_fork_commit(int d, const ForkCommitArgs& a, hipStream_t s);
+hipError_t launch_fork_selective_level(int io, int d, const ForkArgs& a, hipStream_t s);
+hipError_t launch_fork_selective_commit(int io, int d, const SelectiveCommitArgs& a,
+                                        hipStream_t s);
 hipError_t launch_accept_greedy(const AcceptArgs& a, hipStream_t s);
 hipError_t launch_accept_sampling(const AcceptSampleArgs& a, hipStream_t s);
 

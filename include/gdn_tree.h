@@ -105,10 +105,11 @@ enum {
   GDN_TREE_BAD_ACCEPTED = 4,  /* commit: accepted[b] outside [-1, N_b)              */
   GDN_TREE_TOO_DEEP = 5,      /* FORK modes: a node deeper than desc.max_depth      */
   GDN_TREE_CACHE_FULL = 6,    /* attention commit: the path would overflow the cache */
-  GDN_TREE_BAD_TOKEN = 7      /* sampling acceptance: a draft token outside [0, V)  */
+  GDN_TREE_BAD_TOKEN = 7,     /* sampling acceptance: a draft token outside [0, V)  */
+  GDN_TREE_TOO_MANY_KEPT = 8  /* selective fork: more saved nodes than max_kept      */
 };
 /* Precedence: BAD_SIZE, then BAD_ROOT, then BAD_PARENT, then TOO_DEEP (FORK
- * modes), then BAD_ACCEPTED (commit). */
+ * modes), then TOO_MANY_KEPT (selective fork), then BAD_ACCEPTED (commit). */
 
 /* The fused round-boundary calls (gdn_tree_commit_verify, gdn_tree_replay_verify
  * and their layer-batched forms) report two outcomes per sequence in one code:
@@ -335,6 +336,49 @@ gdn_status gdn_tree_replay_commit_layers(const gdn_tree_desc* desc, int32_t n_la
                                          const int32_t* offsets, const int32_t* parents,
                                          const int32_t* accepted, const gdn_layer_io* layers,
                                          int32_t* tree_status, void* stream);
+
+/* Selective fork: the fork/checkpoint baseline (GDN_MODE_FORK's depth-by-
+ * depth scheme) keeping a rollback point only for nodes the draft is unsure
+ * of (fork page section 8, "selective fork": a branch whose draft confidence
+ * is above 0.95 is processed directly, without saving a checkpoint, because
+ * it is almost certainly accepted). Node t saves its state iff
+ * confidence[t] <= threshold (the page's 0.95 is the caller's threshold; a
+ * confidence exactly equal to it saves). A node whose state was not saved is
+ * rebuilt wherever it is needed: a node starts from its nearest saved proper
+ * ancestor (S0 when there is none) and applies the gated delta rule of every
+ * path node below it, its own last; the commit does the same for the accepted
+ * node (or copies its own saved state). Results are those of GDN_MODE_FORK.
+ *   confidence [T] fp32   the draft's confidence in each node's token
+ *   max_kept              saved nodes each sequence may hold, in [0, max_nodes]
+ *                         (GDN_ERR_BAD_SHAPE otherwise); a sequence that would
+ *                         save more gets GDN_TREE_TOO_MANY_KEPT
+ *   workspace             gdn_tree_fork_selective_workspace_bytes(desc,
+ *                         max_kept) bytes: checkpoints [B*max_kept, H, dv, dk]
+ *                         fp32, sequence b's saved nodes in node order from
+ *                         slot b*max_kept (may be NULL when the size is 0)
+ * desc as for GDN_MODE_FORK (desc.mode is ignored; desc.max_depth bounds the
+ * levels run, deeper trees get GDN_TREE_TOO_DEEP). Verify writes o and the
+ * saved states; commit reads them, the same confidence, threshold and
+ * max_kept, and the path's k, v, alpha, beta, and writes S_out (may equal
+ * S0). Status codes and zeroed rows as gdn_tree_verify / gdn_tree_commit.
+ * The workspace size function returns 0 for an invalid descriptor or
+ * max_kept. */
+size_t gdn_tree_fork_selective_workspace_bytes(const gdn_tree_desc* desc, int32_t max_kept);
+gdn_status gdn_tree_fork_selective_verify(const gdn_tree_desc* desc, const int32_t* offsets,
+                                          const int32_t* parents, const float* confidence,
+                                          float threshold, int32_t max_kept, const void* q,
+                                          const void* k, const void* v, const float* alpha,
+                                          const float* beta, const float* S0, void* o,
+                                          void* workspace, size_t workspace_bytes,
+                                          int32_t* tree_status, void* stream);
+gdn_status gdn_tree_fork_selective_commit(const gdn_tree_desc* desc, const int32_t* offsets,
+                                          const int32_t* parents, const float* confidence,
+                                          float threshold, int32_t max_kept,
+                                          const int32_t* accepted, const void* k, const void* v,
+                                          const float* alpha, const float* beta,
+                                          const float* S0, float* S_out, const void* workspace,
+                                          size_t workspace_bytes, int32_t* tree_status,
+                                          void* stream);
 
 /* Static text for a gdn_status value. */
 const char* gdn_tree_status_string(int status);

@@ -34,6 +34,8 @@ def test_library_exports_every_declared_symbol():
                             "gdn_tree_commit_verify", "gdn_tree_commit_verify_layers",
                             "gdn_tree_replay_verify", "gdn_tree_replay_verify_layers",
                             "gdn_tree_replay_commit", "gdn_tree_replay_commit_layers",
+                            "gdn_tree_fork_selective_workspace_bytes",
+                            "gdn_tree_fork_selective_verify", "gdn_tree_fork_selective_commit",
                             "gdn_tree_accept_greedy", "gdn_tree_accept_sampling",
                             "gdn_round_plan",
                             "gdn_round_tree_for_budget", "gdn_round_capture",
@@ -340,6 +342,41 @@ def test_replay_commit_checks_before_launch():
                                       None, None, None, None) == 0
     assert lib.gdn_tree_replay_commit(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake,
                                       fake, fake, fake, None) == 1
+
+
+def test_selective_fork_workspace_and_checks():
+    """Workspace = B * max_kept checkpoints; max_kept outside [0, max_nodes],
+    missing inputs and a small workspace are rejected before launch; with
+    max_kept = 0 no workspace is needed."""
+    lib = gt.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = gt.make_desc(4, 2, 64, 64, 40, 12)
+    per = 2 * 64 * 64 * 4
+    assert gt.gdn_tree_fork_selective_workspace_bytes(d, 5) == -(-4 * 5 * per // 256) * 256
+    assert gt.gdn_tree_fork_selective_workspace_bytes(d, 0) == 0
+    assert gt.gdn_tree_fork_selective_workspace_bytes(d, 13) == 0
+    assert gt.gdn_tree_fork_selective_workspace_bytes(d, -1) == 0
+    need = gt.gdn_tree_fork_selective_workspace_bytes(d, 3)
+
+    def verify(mk=3, conf=fake, ws=fake, wsb=need, desc=d):
+        return lib.gdn_tree_fork_selective_verify(ctypes.byref(desc), fake, fake, conf, 0.95, mk,
+                                                  fake, fake, fake, fake, fake, fake, fake, ws,
+                                                  wsb, fake, None)
+
+    def commit(mk=3, conf=fake, ws=fake, wsb=need, v=fake):
+        return lib.gdn_tree_fork_selective_commit(ctypes.byref(d), fake, fake, conf, 0.95, mk,
+                                                  fake, fake, v, fake, fake, fake, fake, ws, wsb,
+                                                  fake, None)
+
+    assert verify(mk=13) == 2 and verify(mk=-1) == 2 and commit(mk=13) == 2
+    assert verify(conf=None) == 1 and commit(conf=None) == 1 and commit(v=None) == 1
+    assert verify(wsb=need - 1) == 4 and commit(wsb=need - 1) == 4
+    assert verify(ws=None) == 1
+    assert verify(desc=gt.make_desc(4, 2, 48, 48, 40, 12)) == 3
+    e = gt.make_desc(0, 2, 64, 64, 0, 8)
+    assert lib.gdn_tree_fork_selective_verify(ctypes.byref(e), None, None, None, 0.95, 0, None,
+                                              None, None, None, None, None, None, None, 0, None,
+                                              None) == 0
 
 
 # ------------------------------------------------------------------ rounds (gdn_round.h)

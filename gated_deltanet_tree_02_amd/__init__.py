@@ -32,6 +32,7 @@ __all__ = [
     "PREV_SHIFT", "prev_code",
     "gdn_tree_fork_selective_workspace_bytes", "gdn_tree_fork_selective_verify",
     "gdn_tree_fork_selective_commit", "prepare_fork_selective_verify",
+    "gdn_tree_attn_verify_noalloc",
     "prepare_fork_selective_commit",
     "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
     "prepare_attn_commit_layers",
@@ -148,6 +149,9 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_attn_verify.argtypes = [A, P, P, P, P, P, P, P, P, ctypes.c_float, P, P,
                                                  S, P, P]
             lib.gdn_tree_attn_verify.restype = I
+            lib.gdn_tree_attn_verify_noalloc.argtypes = [A, P, P, P, P, P, P, P, P,
+                                                         ctypes.c_float, P, P, P]
+            lib.gdn_tree_attn_verify_noalloc.restype = I
             lib.gdn_tree_attn_commit.argtypes = [A, P, P, P, P, P, P, P, P, P, P]
             lib.gdn_tree_attn_commit.restype = I
             LY = ctypes.POINTER(GdnLayerIO)
@@ -451,6 +455,20 @@ def gdn_tree_attn_verify(desc, offsets, parents, q, k, v, k_cache, v_cache, cach
         _check(load_library().gdn_tree_attn_verify(ctypes.byref(desc), *args,
                                                    _stream(stream, dev)),
                "gdn_tree_attn_verify")
+
+
+def gdn_tree_attn_verify_noalloc(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len,
+                                 o, tree_status, scale=None, stream=None):
+    """gdn_tree_attn_verify with the library's fixed per-GPU scratch instead of
+    a workspace (no device allocation by the library)."""
+    torch = _torch()
+    dev, args = _attn_verify_args(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len,
+                                  scale, o, None, tree_status)
+    args = args[:-3] + args[-1:]            # no workspace pointer and size
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_attn_verify_noalloc(ctypes.byref(desc), *args,
+                                                           _stream(stream, dev)),
+               "gdn_tree_attn_verify_noalloc")
 
 
 def gdn_tree_attn_commit(desc, offsets, parents, accepted, k, v, k_cache, v_cache, cache_len,

@@ -610,6 +610,7 @@ const char* gdn_tree_status_string(int status) {
     case GDN_ERR_WORKSPACE: return "workspace smaller than the entry point's workspace_bytes()";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
     case GDN_ERR_GRAPH: return "graph capture, instantiation or launch failed";
+    case GDN_ERR_SCRATCH: return "the call needs more scratch than the library's fixed buffer";
   }
   return "unknown status";
 }

@@ -325,6 +325,11 @@ hipError_t launch_wy_commit_verify_layers(int io, int d, int mt, const CommitVer
 hipError_t launch_wy_replay_verify_layers(int io, int d, int mt, const ReplayVerifyLayersArgs& a,
                                           hipStream_t s);
 hipError_t launch_tree_attn(int d, const AttnArgs& a, hipStream_t s);
+// Bytes of the fixed per-GPU scratch of the no-allocation attention verify,
+// and its device address on the current device (taken once per device).
+constexpr size_t kAttnScratchBytes = size_t(32) << 20;
+constexpr int kMaxScratchDevices = 64;
+__attribute__((visibility("hidden"))) hipError_t attn_scratch(void** ptr);
 hipError_t launch_tree_attn_commit(int d, const AttnCommitArgs& a, hipStream_t s);
 hipError_t launch_wy_commit(int io, int d, const CommitArgs& a, hipStream_t s);
 hipError_t launch_wy_commit_layers(int io, int d, const CommitLayersArgs& a, hipStream_t s);

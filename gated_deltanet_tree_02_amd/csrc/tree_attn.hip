@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "gdn_tree_attn.h"
@@ -1013,6 +1014,31 @@ hipError_t launch_tree_attn(int d, const AttnArgs& a, hipStream_t s) {
     case 128: return launch_attn_d<128>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Scratch of the no-allocation verify (gdn_tree_attn_verify_noalloc): the
+// split-cache partials of one call, written and then read by that call's own
+// kernels. One array per GPU, held until the process ends; every call on a
+// GPU shares it, so calls that overlap on one GPU race. In host code the
+// name is a host-side stand-in: kernels get the device address taken below.
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+hipError_t attn_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* by_device[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (by_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));    // this device's copy
+    if (e != hipSuccess) return e;
+    by_device[dev] = p;
+  }
+  *ptr = by_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_tree_attn_commit(int d, const AttnCommitArgs& a, hipStream_t s) {

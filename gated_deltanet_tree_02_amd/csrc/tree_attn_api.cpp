@@ -166,6 +166,22 @@ gdn_status gdn_tree_attn_verify(const gdn_attn_desc* desc, const int32_t* offset
                                scale, o, workspace, ws_bytes, tree_status, stream, 0);
 }
 
+gdn_status gdn_tree_attn_verify_noalloc(const gdn_attn_desc* desc, const int32_t* offsets,
+                                        const int32_t* parents, const void* q, const void* k,
+                                        const void* v, const void* k_cache, const void* v_cache,
+                                        const int32_t* cache_len, float scale, void* o,
+                                        int32_t* tree_status, void* stream) {
+  gdn_status st = check_desc(desc);
+  if (st != GDN_OK) return st;
+  if (desc->num_seqs == 0) return GDN_OK;
+  const size_t need = workspace_bytes(desc);
+  if (need > gdn::kAttnScratchBytes) return GDN_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (need > 0 && gdn::attn_scratch(&scratch) != hipSuccess) return GDN_ERR_LAUNCH;
+  return gdn::attn_verify_impl(desc, offsets, parents, q, k, v, k_cache, v_cache, cache_len,
+                               scale, o, scratch, need, tree_status, stream, 0);
+}
+
 gdn_status gdn_tree_attn_commit(const gdn_attn_desc* desc, const int32_t* offsets,
                                 const int32_t* parents, const int32_t* accepted, const void* k,
                                 const void* v, void* k_cache, void* v_cache, int32_t* cache_len,

@@ -88,7 +88,8 @@ typedef enum {
   GDN_ERR_UNSUPPORTED = 3,    /* dk/dv/io dtype/mode combination not built          */
   GDN_ERR_WORKSPACE = 4,      /* workspace smaller than gdn_tree_workspace_bytes()  */
   GDN_ERR_LAUNCH = 5,         /* the HIP runtime refused a launch                   */
-  GDN_ERR_GRAPH = 6           /* the HIP runtime refused graph capture or launch    */
+  GDN_ERR_GRAPH = 6,          /* the HIP runtime refused graph capture or launch    */
+  GDN_ERR_SCRATCH = 7         /* the call needs more than the fixed scratch holds   */
 } gdn_status;
 
 /* Element type of q, k, v and o. State, gates and accumulation are fp32. */

@@ -80,6 +80,22 @@ gdn_status gdn_tree_attn_verify(const gdn_attn_desc* desc, const int32_t* offset
                                 void* workspace, size_t workspace_bytes, int32_t* tree_status,
                                 void* stream);
 
+/* gdn_tree_attn_verify without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The split-cache partials go to a scratch
+ * buffer of 32 MiB per GPU that the library holds in its code object until
+ * the process ends; its address is taken on the first call on each device.
+ * The call allocates nothing. A descriptor whose partials would exceed 32 MiB
+ * (gdn_tree_attn_workspace_bytes > 32 MiB) gets GDN_ERR_SCRATCH and nothing
+ * is enqueued. Every call on one GPU shares that GPU's scratch: calls that
+ * may overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller. Results are identical to gdn_tree_attn_verify. */
+gdn_status gdn_tree_attn_verify_noalloc(const gdn_attn_desc* desc, const int32_t* offsets,
+                                        const int32_t* parents, const void* q, const void* k,
+                                        const void* v, const void* k_cache, const void* v_cache,
+                                        const int32_t* cache_len, float scale, void* o,
+                                        int32_t* tree_status, void* stream);
+
 /* Commit: for every sequence b with accepted[b] = a >= 0, append the K/V rows
  * of the path root .. a (root first) at cache rows cache_len[b] .. and advance
  * cache_len[b] by the path length; accepted[b] = -1 leaves b unchanged.

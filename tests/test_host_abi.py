@@ -29,6 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["gdn_tree_workspace_bytes", "gdn_tree_build", "gdn_tree_verify",
                             "gdn_tree_commit", "gdn_tree_status_string",
                             "gdn_tree_attn_workspace_bytes", "gdn_tree_attn_verify",
+                            "gdn_tree_attn_verify_noalloc",
                             "gdn_tree_attn_commit", "gdn_tree_verify_layers",
                             "gdn_tree_commit_layers", "gdn_tree_attn_commit_layers",
                             "gdn_tree_commit_verify", "gdn_tree_commit_verify_layers",

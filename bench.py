@@ -461,6 +461,54 @@ def fork_delta_leg(args, gt, gi, w, layers, offsets, parents, accepted, status, 
     return out
 
 
+def selective_fork_leg(args, gt, gi, w, layers, offsets, parents, accepted, status, max_depth,
+                       run, dev, p_dominant=0.5, threshold=0.95):
+    """The fork baseline with selective fork (gdn_tree_fork_selective_*): a
+    node saves its checkpoint only when the draft's confidence in it is at
+    most 0.95. Confidences are drawn per node (gdn_inputs.draft_confidences:
+    siblings share one unit of mass, a dominant first child with probability
+    p_dominant, the root certain); every sequence gets the largest number of
+    saved nodes of the batch as its slot budget. Verify one layer at a time,
+    depth by depth; commit one layer at a time."""
+    import numpy as np
+    import torch
+    L = len(layers)
+    conf_np = gi.draft_confidences(np.random.default_rng(2026), w.parents_list, p_dominant)
+    conf = torch.from_numpy(conf_np).to(dev)
+    saved = [int((conf_np[w.offsets[b]:w.offsets[b + 1]] <= threshold).sum()) for b in range(w.B)]
+    max_kept = max(saved)
+    desc = gt.make_desc(w.B, w.H, w.dk, w.dv, w.T, w.max_nodes,
+                        gt.DTYPE_BF16 if w.io == "bf16" else gt.DTYPE_F32, gt.MODE_FORK, max_depth)
+    nbytes = gt.gdn_tree_fork_selective_workspace_bytes(desc, max_kept)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)[:nbytes] if nbytes else None
+    outs = [torch.empty_like(ly["v"]) for ly in layers]
+    ver = [gt.prepare_fork_selective_verify(desc, offsets, parents, conf, threshold, max_kept,
+                                            ly["q"], ly["k"], ly["v"], ly["alpha"], ly["beta"],
+                                            ly["S"], o, ws, status)
+           for ly, o in zip(layers, outs)]
+    com = [gt.prepare_fork_selective_commit(desc, offsets, parents, conf, threshold, max_kept,
+                                            accepted, ly["k"], ly["v"], ly["alpha"], ly["beta"],
+                                            ly["S"], ly["S"], ws, status) for ly in layers]
+    el, v_ms, c_ms = run(ver, com, args.fork_steps, 1)
+    if np.any(status.cpu().numpy() != 0):
+        raise RuntimeError("nonzero status in the selective-fork leg")
+    node_ckpt = w.H * w.dv * w.dk * 4
+    out = {"ms_per_step": round(1e3 * el / args.fork_steps, 3),
+           "nodes_per_s_per_layer": round(w.T * L * args.fork_steps / el, 1),
+           "verify_us_per_layer": round(1e3 * v_ms / L, 2),
+           "commit_us_per_layer": round(1e3 * c_ms / L, 2),
+           "threshold": threshold, "p_dominant": p_dominant,
+           "saved_nodes": int(sum(saved)), "nodes": int(w.T),
+           "saved_fraction": round(sum(saved) / w.T, 4), "max_kept": int(max_kept),
+           "workspace_bytes_per_layer": int(nbytes),
+           "saved_bytes_per_layer": int(sum(saved) * node_ckpt),
+           "steps": args.fork_steps}
+    log(f"selective fork: {out}")
+    del ws, outs, ver, com, conf
+    torch.cuda.empty_cache()
+    return out
+
+
 def sampling_accept_leg(args, gt, gi, w, offsets, parents, dev, V=151936):
     """Sampling-mode acceptance (gdn_tree_accept_sampling) on the GDN workload's
     trees over a Qwen-sized vocabulary: per node a target and a draft
@@ -1055,6 +1103,8 @@ def main():
         torch.cuda.empty_cache()
         fork["delta_checkpoints"] = fork_delta_leg(args, gt, gi, w, layers, offsets, parents,
                                                    accepted, status, max_depth, run, dev)
+        fork["selective"] = selective_fork_leg(args, gt, gi, w, layers, offsets, parents,
+                                               accepted, status, max_depth, run, dev)
 
     if args.pmc_calibration:
         pmc_calibration(dev)
@@ -1078,6 +1128,9 @@ def main():
             "replay_retained_bytes": int(replay_state),
             "replay_retained_path_bytes": int(replay_path),
             "fork_fp32_bytes": int(fork_state), "fork_over_wy": round(fork_state / wy_state, 1),
+            # selective fork: the saved checkpoints of an average request
+            "selective_fork_fp32_bytes": (int(fork["selective"]["saved_bytes_per_layer"] * L / w.B)
+                                          if fork and "selective" in fork else None),
             "fork_over_replay": round(fork_state / replay_state, 1),
             "nodes_per_request": n_req, "mean_accepted_path": round(mean_path, 3), "layers": L}
 

@@ -74,13 +74,14 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
 // next p, so a final draw after a rejection needs no further pass (a draw
 // with no rejection at the node takes one pass over p). The draw then finds
 // the tile where the cumulative mass crosses the target and re-reads that
-// tile alone. Each wave works on whole 256-token tiles, kTilesInFlight (seven) tiles' loads in
-// flight at a time. Decisions are taken in fp32; sums run in a fixed order.
+// tile alone. Each wave works on whole 256-token tiles and keeps
+// kTilesInFlight tiles' loads in flight. Decisions are taken in fp32; sums
+// run in a fixed order.
 
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / 64;
 constexpr int kTile = 256;                       // tokens per tile (64 lanes x 4)
-constexpr int kTilesInFlight = 7;
+constexpr int kTilesInFlight = 4;
 constexpr int kMaxTiles = (1 << 20) / kTile;     // vocabularies up to 2^20 tokens
 
 struct Stages {
@@ -147,10 +148,30 @@ __device__ __forceinline__ float2 stage_pq_reg(float pj, float qj, int j, const 
   return make_float2(pk, gone ? 0.f : qj * r.qscale[K]);
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+// Sum over the 64 lanes of a wave in DPP steps, with no LDS traffic: an
+// inclusive scan within each row of 16 lanes (shifts by 1, 2, 4, 8; lanes
+// shifted in from outside the row read 0), then lane 15 of rows 0 and 2
+// carried into rows 1 and 3, then lane 31 into rows 2 and 3. Lane 63 ends
+// with the total.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, kRowMask, 0xf,
+                                            true);
+  return x + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float wave_sum_lane63(float x) {
+  x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
   return x;
+}
+// The same total in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_lane63(x)), 63));
 }
 
 // Sum over the workgroup, in a fixed order; every thread gets the result.
@@ -171,36 +192,51 @@ enum TileSum { kResidual, kTarget };
 
 // One pass over a node's rows: sTile[t] = sum over tile t of
 // max(0, p_k - q_k) (kResidual) or of p_k (kTarget); the thread's share of
-// the row's q mass is added to *qs. Tiles go to waves round-robin, kTilesInFlight at a
-// time with all their loads issued first. K >= 0: exactly K rejections so far,
-// the stage scalars in registers; K < 0: any number, read from LDS.
+// the row's q mass is added to *qs. Wave w takes tiles w, w + waves, ...
+// through a ring of kTilesInFlight tiles: a tile's slot is refilled with the
+// wave's next-but-(kTilesInFlight - 1) tile as soon as it is summed, so every
+// wave keeps that many tiles' loads in flight for the whole pass. K >= 0:
+// exactly K rejections so far, the stage scalars in registers; K < 0: any
+// number, read from LDS.
 template <TileSum WHAT, int K>
 __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
                                             const float* __restrict__ qrow, int V,
                                             const Stages& s, float* sTile, float* qs) {
+  constexpr int W = kTilesInFlight;
   const StageRegs<K < 0 ? 0 : K> r = stage_regs<K < 0 ? 0 : K>(s);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ntiles = (V + kTile - 1) / kTile;
+  const int mine = wave < ntiles ? (ntiles - 1 - wave) / kSampleWaves + 1 : 0;
   // p_0 needs no q: a draw with no rejection reads the target row alone
   constexpr bool need_q = WHAT == kResidual || K != 0;
-  for (int t0 = wave; t0 < ntiles; t0 += kSampleWaves * kTilesInFlight) {
-    float4 pv[kTilesInFlight], qv[kTilesInFlight];
+  // element offsets are clamped into the row (V >= 4), so that every load is
+  // issued unconditionally; tiles past the wave's last one are not summed
+  auto off = [&](int i) {
+    const int j = (wave + i * kSampleWaves) * kTile + 4 * lane;
+    return j < V - 4 ? j : V - 4;
+  };
+  float4 pv[W], qv[W];
 #pragma unroll
-    for (int u = 0; u < kTilesInFlight; ++u) {
-      const int j = (t0 + u * kSampleWaves) * kTile + 4 * lane;
-      pv[u] = qv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < V) {
-        pv[u] = *reinterpret_cast<const float4*>(prow + j);
-        if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + j);
-      }
-    }
+  for (int u = 0; u < W; ++u) {
+    pv[u] = *reinterpret_cast<const float4*>(prow + off(u));
+    qv[u] = need_q ? *reinterpret_cast<const float4*>(qrow + off(u))
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int i0 = 0; i0 < mine; i0 += W) {
 #pragma unroll
-    for (int u = 0; u < kTilesInFlight; ++u) {
-      const int t = t0 + u * kSampleWaves;
+    for (int u = 0; u < W; ++u) {
+      const int i = i0 + u;
+      const int t = wave + i * kSampleWaves;
       const int j = t * kTile + 4 * lane;
-      const float pe[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
-      const float qe[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+      const bool in_row = i < mine && j < V;
+      const float pe[4] = {in_row ? pv[u].x : 0.f, in_row ? pv[u].y : 0.f,
+                           in_row ? pv[u].z : 0.f, in_row ? pv[u].w : 0.f};
+      const float qe[4] = {in_row ? qv[u].x : 0.f, in_row ? qv[u].y : 0.f,
+                           in_row ? qv[u].z : 0.f, in_row ? qv[u].w : 0.f};
+      // the slot's next tile
+      pv[u] = *reinterpret_cast<const float4*>(prow + off(i + W));
+      if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + off(i + W));
       float m = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -209,8 +245,8 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
         m += WHAT == kResidual ? fmaxf(pq.x - pq.y, 0.f) : pq.x;
         *qs += qe[e];
       }
-      m = wave_sum(m);
-      if (lane == 0 && t < ntiles) sTile[t] = m;
+      m = wave_sum_lane63(m);
+      if (lane == 63 && i < mine) sTile[t] = m;
     }
   }
 }

@@ -230,7 +230,7 @@ constexpr int verify_lds_bytes() {
   constexpr int st1 = 16 * (2 * NP * (CPR + 1) + NP * CPV);
   constexpr int st2 = NP * DV * (4 + (int)sizeof(IO));
   constexpr int nqt = MT * (MT + 1) / 2;
-  constexpr int path = kFused ? kFusedPathRows * (16 * CPR + 4 * DV) : 0;
+  constexpr int path = kFused ? kFusedPathRows * (4 * DK + 4 * DV) : 0;
   return (st1 > st2 ? st1 : st2) + 4 * (NP * (NP + 1) / 2) + 4 * 256 * nqt +
          (int)sizeof(IO) * 256 * nqt + 16 * NP + path;
 }
@@ -245,6 +245,21 @@ template <class IO, int DK, int DV, int MT, bool kFused>
 constexpr int verify_waves_per_simd() {
   // (the fused kernel with 128-wide rows needs about 100 VGPRs: no cap)
   return verify_three_per_cu<IO, DK, DV, MT, kFused>() && !(kFused && DK == 128) ? 6 : 1;
+}
+
+// One 16-byte io chunk (8 bf16 or 4 fp32 values) widened to fp32 at dst.
+template <class IO>
+__device__ __forceinline__ void widen_chunk(const uint4& c, float* dst) {
+  if constexpr (std::is_same<IO, float>::value) {
+    *reinterpret_cast<float4*>(dst) = __builtin_bit_cast(float4, c);
+  } else {
+    *reinterpret_cast<float4*>(dst) =
+        make_float4(bf16_bits_to_float(c.x & 0xffffu), bf16_bits_to_float(c.x >> 16),
+                    bf16_bits_to_float(c.y & 0xffffu), bf16_bits_to_float(c.y >> 16));
+    *reinterpret_cast<float4*>(dst + 4) =
+        make_float4(bf16_bits_to_float(c.z & 0xffffu), bf16_bits_to_float(c.z >> 16),
+                    bf16_bits_to_float(c.w & 0xffffu), bf16_bits_to_float(c.w >> 16));
+  }
 }
 
 // Rank p (0 = the root) of a path given as a node bit set: its p-th lowest bit.
@@ -456,9 +471,10 @@ void wy_verify_kernel(const Args args) {
   __shared__ uint64_t sAnc[NP];
   __shared__ float sG2[NP];
   __shared__ float sBeta[NP];
-  // previous round's path (fused commit): k rows as io chunks, and the
-  // pseudo-values scaled by their path coefficients
-  __shared__ __align__(16) uint4 sPK[kFused ? PKC : 1];
+  // previous round's path (fused commit): k rows widened to fp32 once here
+  // (every lane reads 32 of them per path row), and the pseudo-values scaled
+  // by their path coefficients, or (replay) the v rows as io
+  __shared__ __align__(16) float sPK[kFused ? PCH * DK : 4];
   __shared__ __align__(16) float sPW[kFused ? PCH * DV : 4];
 
   const int tid = threadIdx.x;
@@ -709,7 +725,7 @@ void wy_verify_kernel(const Args args) {
   if constexpr (kFused) {
     if (pidx < P && tid < PKC + PUC) {
       if (tid < PKC) {
-        sPK[tid] = pld;
+        widen_chunk<IO>(pld, sPK + tid * EPC);
       } else if constexpr (kReplay) {
         reinterpret_cast<uint4*>(sPW)[tid - PKC] = pld;
       } else {
@@ -784,6 +800,10 @@ void wy_verify_kernel(const Args args) {
   // w = S k_j, S <- alpha_j S + beta_j (v_j - alpha_j w) k_j^T.
   if constexpr (kFused) {
     const float GA = pacc >= 0 ? exp2f(pgA) : 1.f;
+    // (replay) the fragment is carried as S = gam * Shat: a step is then one
+    // FMA per element, Shat += (c / gam') k^T with gam' = alpha gam, and gam
+    // is applied once at the end (or folded in early, before it underflows)
+    float gam = 1.f;
     if (owns && !kReplay) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -802,7 +822,9 @@ void wy_verify_kernel(const Args args) {
         if (pidx < pc && tid < PKC + PUC) {
           const size_t prow = (size_t)(plo + pnode) * H + h;
           if (tid < PKC) {
-            sPK[tid] = *reinterpret_cast<const uint4*>(pk + prow * DK + (tid - pidx * CPR) * EPC);
+            widen_chunk<IO>(
+                *reinterpret_cast<const uint4*>(pk + prow * DK + (tid - pidx * CPR) * EPC),
+                sPK + tid * EPC);
           } else if constexpr (kReplay) {
             reinterpret_cast<uint4*>(sPW)[tid - PKC] = *reinterpret_cast<const uint4*>(
                 pv + prow * DV + (tid - PKC - pidx * CPV) * EPC);
@@ -824,13 +846,13 @@ void wy_verify_kernel(const Args args) {
           const int node = nth_path_node(ppath, p0 + p);
           const float al = __shfl(palpha, node, kWave);
           const float be = __shfl(pbeta, node, kWave);
-          const IO* krow = reinterpret_cast<const IO*>(sPK) + p * DK + 8 * g;
+          const float* krow = sPK + p * DK + 8 * g;
           float4 kk[KS][2];
           float dot = 0.f;
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            kk[s][0] = io::load4(krow + 32 * s);
-            kk[s][1] = io::load4(krow + 32 * s + 4);
+            kk[s][0] = *reinterpret_cast<const float4*>(krow + 32 * s);
+            kk[s][1] = *reinterpret_cast<const float4*>(krow + 32 * s + 4);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
               dot += sraw[s][hh].x * kk[s][hh].x + sraw[s][hh].y * kk[s][hh].y +
@@ -840,16 +862,34 @@ void wy_verify_kernel(const Args args) {
           dot += __shfl_xor(dot, 16, kWave);
           dot += __shfl_xor(dot, 32, kWave);
           const float vr = io::load1(reinterpret_cast<const IO*>(sPW) + p * DV + r);
-          const float c = be * (vr - al * dot);
+          const float c = be * (vr - al * (gam * dot));
+          const float ng = al * gam;                 // wave-uniform
+          if (ng < 0x1p-30f) {
+            // fold the product into the fragment before it can underflow
 #pragma unroll
-          for (int s = 0; s < KS; ++s) {
+            for (int s = 0; s < KS; ++s) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              sraw[s][hh].x = al * sraw[s][hh].x + c * kk[s][hh].x;
-              sraw[s][hh].y = al * sraw[s][hh].y + c * kk[s][hh].y;
-              sraw[s][hh].z = al * sraw[s][hh].z + c * kk[s][hh].z;
-              sraw[s][hh].w = al * sraw[s][hh].w + c * kk[s][hh].w;
+              for (int hh = 0; hh < 2; ++hh) {
+                sraw[s][hh].x = ng * sraw[s][hh].x + c * kk[s][hh].x;
+                sraw[s][hh].y = ng * sraw[s][hh].y + c * kk[s][hh].y;
+                sraw[s][hh].z = ng * sraw[s][hh].z + c * kk[s][hh].z;
+                sraw[s][hh].w = ng * sraw[s][hh].w + c * kk[s][hh].w;
+              }
             }
+            gam = 1.f;
+          } else {
+            const float f = c * (1.f / ng);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                sraw[s][hh].x += f * kk[s][hh].x;
+                sraw[s][hh].y += f * kk[s][hh].y;
+                sraw[s][hh].z += f * kk[s][hh].z;
+                sraw[s][hh].w += f * kk[s][hh].w;
+              }
+            }
+            gam = ng;
           }
         }
       }
@@ -857,16 +897,28 @@ void wy_verify_kernel(const Args args) {
         const int r = 16 * jt + l16;
         for (int p = 0; p < pc; ++p) {
           const float w = sPW[p * DV + r];
-          const IO* krow = reinterpret_cast<const IO*>(sPK) + p * DK + 8 * g;
+          const float* krow = sPK + p * DK + 8 * g;
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            const float4 k0 = io::load4(krow + 32 * s);
-            const float4 k1 = io::load4(krow + 32 * s + 4);
+            const float4 k0 = *reinterpret_cast<const float4*>(krow + 32 * s);
+            const float4 k1 = *reinterpret_cast<const float4*>(krow + 32 * s + 4);
             sraw[s][0].x += w * k0.x; sraw[s][0].y += w * k0.y;
             sraw[s][0].z += w * k0.z; sraw[s][0].w += w * k0.w;
             sraw[s][1].x += w * k1.x; sraw[s][1].y += w * k1.y;
             sraw[s][1].z += w * k1.z; sraw[s][1].w += w * k1.w;
           }
+        }
+      }
+    }
+    if (owns && kReplay && gam != 1.f) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          sraw[s][hh].x *= gam;
+          sraw[s][hh].y *= gam;
+          sraw[s][hh].z *= gam;
+          sraw[s][hh].w *= gam;
         }
       }
     }

@@ -525,7 +525,7 @@ def _sampling_gpu(offsets, parents, draft, P, Q, U, max_nodes=64):
     return [o.cpu().numpy() for o in outs]
 
 
-@pytest.mark.parametrize("V", [1000, 5000])
+@pytest.mark.parametrize("V", [8, 1000, 5000])
 def test_accept_sampling_matches_oracle(V):
     _say("accept sampling, V", V)
     rng = np.random.default_rng(V)

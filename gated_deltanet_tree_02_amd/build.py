@@ -69,6 +69,50 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side C ABI sources (no device code): the code a sanitized build checks.
+HOST_SOURCES = ["gdn_tree_api.cpp", "tree_attn_api.cpp", "round_api.cpp"]
+SAN_BUILD = os.path.join(ROOT, "_build", "gdntree_san")
+SAN_LIB = os.path.join(SAN_BUILD, "libgdntree_san.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (each
+# option behind -Xarch_host; the device code is not instrumented)
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+             "-fno-omit-frame-pointer", "-g"]
+
+
+def build_host_sanitized() -> str:
+    """A copy of the library whose host-side C ABI code is built with ASan and
+    UBSan, linked with the kernel objects of the last regular build (made if
+    missing), at _build/gdntree_san/libgdntree_san.so. The sanitizer runtime
+    is not linked: load it first (LD_PRELOAD of clang's libclang_rt.asan)."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    dev_objs = [os.path.join(BUILD, f + ".o") for f in SOURCES if f.endswith(".hip")]
+    if not all(os.path.exists(o) for o in dev_objs):
+        build()
+    objs = []
+    for f in HOST_SOURCES:
+        obj = os.path.join(SAN_BUILD, f + ".o")
+        cmd = [hipcc()] + _flags() + SAN_FLAGS + ["-c", os.path.join(CSRC, f), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {f}:\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", SAN_LIB] + objs + dev_objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    return SAN_LIB
+
+
+def asan_runtime() -> str:
+    """clang's shared AddressSanitizer runtime (it carries UBSan's too)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True)
+    return r.stdout.strip()
+
+
 def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True

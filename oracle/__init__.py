@@ -23,7 +23,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "gdn_oracle.c"), os.path.join(_HERE, "attn_oracle.c")]
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_DEFAULT_PATH = os.path.join(_HERE, "liboracle.so")
+_LIB_PATH = _DEFAULT_PATH
 _lock = threading.Lock()
 _lib = None
 
@@ -33,21 +34,46 @@ STATUS_CACHE_FULL = 6
 
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc -O2 (no fast-math) and OpenMP."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    if force or not os.path.exists(_DEFAULT_PATH):
+        tmp = _DEFAULT_PATH + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC", "-std=c11",
                "-Wall", "-o", tmp] + _SRCS + ["-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, _DEFAULT_PATH)
+    return _DEFAULT_PATH
+
+
+_SAN_PATH = os.path.join(os.path.dirname(_HERE), "_build", "oracle_san", "liboracle_san.so")
+
+
+def build_sanitized() -> str:
+    """The oracle built by clang with AddressSanitizer and UBSan (no OpenMP),
+    for checking the oracle's own memory accesses; load the sanitizer runtime
+    first (LD_PRELOAD of clang's libclang_rt.asan) and select it with
+    use_library()."""
+    os.makedirs(os.path.dirname(_SAN_PATH), exist_ok=True)
+    clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+    cmd = [clang, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-shared", "-fPIC", "-std=c11", "-Wall",
+           "-Wno-unknown-pragmas", "-o", _SAN_PATH] + _SRCS + ["-lm"]
+    subprocess.run(cmd, check=True)
+    return _SAN_PATH
+
+
+def use_library(path: str) -> None:
+    """Load the oracle from `path` (a build of the same sources) from now on."""
+    global _LIB_PATH, _lib
+    with _lock:
+        _LIB_PATH, _lib = path, None
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
-                    os.path.getmtime(f) for f in _SRCS):
+            stale = not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+                os.path.getmtime(f) for f in _SRCS)
+            if stale and _LIB_PATH == _DEFAULT_PATH:
                 build(force=True)
             lib = ctypes.CDLL(_LIB_PATH)
             P = ctypes.c_void_p

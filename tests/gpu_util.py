@@ -39,6 +39,14 @@ def i32(x) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev())
 
 
+def nan_bytes(nbytes: int) -> torch.Tensor:
+    """A workspace of nbytes (at least 4) filled with fp32 NaN patterns, so
+    that any part a kernel reads without having written it shows up in the
+    results."""
+    n = max(4, (nbytes + 3) // 4 * 4)
+    return torch.full((n // 4,), float("nan"), device=dev()).view(torch.uint8)[:max(nbytes, 1)]
+
+
 class DeviceLayer:
     """One layer of a workload resident on the GPU, plus outputs/workspace."""
 
@@ -59,7 +67,7 @@ class DeviceLayer:
         self.S0 = f32(w.S0[layer])
         self.o = torch.full_like(self.v, float("nan"))
         nbytes = gt.gdn_tree_workspace_bytes(self.desc)
-        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev())
+        self.ws = nan_bytes(nbytes)
         self.status = torch.full((w.B,), -7, dtype=torch.int32, device=dev())
         self.S_out = torch.full_like(self.S0, float("nan"))
 
@@ -172,7 +180,7 @@ class DeviceAttn:
         self.vc = bits_to_dev(w.vc_bits)
         self.o = torch.full_like(self.q, float("nan"))
         nbytes = gt.gdn_tree_attn_workspace_bytes(self.desc)
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev()) if nbytes else None
+        self.ws = nan_bytes(nbytes) if nbytes else None
         self.status = torch.full((w.B,), -7, dtype=torch.int32, device=dev())
 
     def verify(self, scale=None):

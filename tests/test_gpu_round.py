@@ -25,7 +25,8 @@ if not torch.cuda.is_available():  # the -m gpu suite only runs on a GPU machine
     pytest.skip("no GPU", allow_module_level=True)
 
 from gpu_util import (TOL, bits_to_dev, dev_to_bits, f32, from_dev_io, i32,  # noqa: E402
-                      oracle_attn, oracle_layer, rel_err_rows, sub_workload, to_dev_io)
+                      nan_bytes, oracle_attn, oracle_layer, rel_err_rows, sub_workload,
+                      to_dev_io)
 
 
 def _say(*a):
@@ -214,7 +215,7 @@ def test_round_graph_replays_equal_eager_calls(mode):
     target = torch.zeros(w.T, dtype=torch.int32, device="cuda")
     E = _RoundState(w, aws, lens)          # eager calls
     G = _RoundState(w, aws, lens)          # graph replays
-    arena = torch.empty(max(1, layout.total_bytes), dtype=torch.uint8, device="cuda")
+    arena = nan_bytes(layout.total_bytes)
     gdn_io = [gt.make_layer_io(gdesc, q=ins[l]["q"], k=ins[l]["k"], v=ins[l]["v"],
                                alpha=ins[l]["alpha"], beta=ins[l]["beta"], S0=G.S[l], o=G.o[l],
                                S_out=G.S[l]) for l in range(n_gdn)]
@@ -227,9 +228,9 @@ def test_round_graph_replays_equal_eager_calls(mode):
                           stream=stream, keep=(ins, ains, G))
     # eager side: per-layer workspaces, the same calls in the same order
     wsb = gt.gdn_tree_workspace_bytes(gdesc)
-    ews = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(n_gdn)]
+    ews = [nan_bytes(wsb) for _ in range(n_gdn)]
     anb = gt.gdn_tree_attn_workspace_bytes(adesc)
-    aws_e = [torch.empty(anb, dtype=torch.uint8, device="cuda") if anb else None
+    aws_e = [nan_bytes(anb) if anb else None
              for _ in range(n_attn)]
     e_gdn_io = [gt.make_layer_io(gdesc, k=ins[l]["k"], S0=E.S[l], S_out=E.S[l], workspace=ews[l])
                 for l in range(n_gdn)]
@@ -312,7 +313,7 @@ def test_replay_round_graph_equals_eager_calls_and_the_oracle():
     G = _RoundState(w, aws, lens)
     for X in (E, G):                      # the states the previous round left
         X.S = [f32(wp.S0[l]) for l in range(n_gdn)]
-    arena = torch.empty(max(1, layout.total_bytes), dtype=torch.uint8, device="cuda")
+    arena = nan_bytes(layout.total_bytes)
     gdn_io = [gt.make_layer_io(gdesc, q=ins[l]["q"], k=ins[l]["k"], v=ins[l]["v"],
                                alpha=ins[l]["alpha"], beta=ins[l]["beta"], S0=G.S[l], o=G.o[l],
                                S_out=G.S[l]) for l in range(n_gdn)]
@@ -328,7 +329,7 @@ def test_replay_round_graph_equals_eager_calls_and_the_oracle():
                           prev=dict(desc=pdesc, offsets=p_off, parents=p_par, accepted=p_acc,
                                     gdn_layers=prev_io))
     anb = gt.gdn_tree_attn_workspace_bytes(adesc)
-    aws_e = [torch.empty(anb, dtype=torch.uint8, device="cuda") if anb else None
+    aws_e = [nan_bytes(anb) if anb else None
              for _ in range(n_attn)]
     e_attn_io = [gt.make_attn_layer_io(adesc, k=ains[l]["k"], v=ains[l]["v"], k_cache=E.kc[l],
                                        v_cache=E.vc[l]) for l in range(n_attn)]
@@ -421,7 +422,7 @@ def test_replay_round_keeps_the_first_failure_and_commits_what_it_can():
     G = _RoundState(w, [aw], lens)
     G.S = [f32(wp.S0[l]) for l in range(n_gdn)]
     kc0, vc0 = dev_to_bits(G.kc[0]), dev_to_bits(G.vc[0])
-    arena = torch.empty(max(1, layout.total_bytes), dtype=torch.uint8, device="cuda")
+    arena = nan_bytes(layout.total_bytes)
     gdn_io = [gt.make_layer_io(gdesc, q=ins[l]["q"], k=ins[l]["k"], v=ins[l]["v"],
                                alpha=ins[l]["alpha"], beta=ins[l]["beta"], S0=G.S[l], o=G.o[l],
                                S_out=G.S[l]) for l in range(n_gdn)]

@@ -50,7 +50,7 @@ METRIC = "tree-GDN verified draft nodes/s per layer (1 GPU) + % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "gated_deltanet_tree_02_amd", "csrc")
-TRAFFIC_FILES = [os.path.join(ROOT, "profiles", "gdn_wy_c4_hbm_traffic.md"),
+TRAFFIC_FILES = [os.path.join(ROOT, "profiles", "gdn_wy_c3_c4_c5_hbm_traffic.md"),
                  os.path.join(ROOT, "profiles", "tree_attn_fa_c4_hbm_traffic.md")]
 # sources whose hash ties a recorded counter measurement to the kernels it measured
 KERNEL_SOURCES = {"verify": ["wy_verify.hip", "device_common.h", "launch.h"],
@@ -84,6 +84,14 @@ def recorded_traffic(kind, config):
                 if m and m.group(1) == kernel_source_hash(kind):
                     return int(m.group(2))
     return None
+
+
+def traffic_fields(kind, config, alg_bytes):
+    """The recorded HBM bytes of one launch of this kernel on this workload
+    (None while unmeasured for the current sources) and their ratio to the
+    algorithmic bytes."""
+    t = recorded_traffic(kind, config)
+    return {"traffic_bytes": t, "traffic_over_alg": round(t / alg_bytes, 3) if t else None}
 
 
 def cpu_model():
@@ -131,7 +139,7 @@ def parse():
                         "or the separate verify and commit launches (WY, layer-batched)")
     p.add_argument("--secondary-steps", type=int, default=20,
                    help="timed steps of the schedule that is not the headline (0 = skip)")
-    p.add_argument("--per-layer-steps", type=int, default=5,
+    p.add_argument("--per-layer-steps", type=int, default=10,
                    help="after a layer-batched WY leg, timed steps with one launch per layer "
                         "(0 = skip)")
     p.add_argument("--round-steps", type=int, default=10,
@@ -680,7 +688,8 @@ def config_legs(args, gt, gi, dev):
         r.update({"alg_bytes": int(rb),
                   "achieved_GBs_median": round(rb / r["launch_us_median"] / 1e3, 1),
                   "frac_hbm_median": round(rb / r["launch_us_median"] / 1e3 / HBM_PEAK_GBS, 4),
-                  "nodes_per_s_per_layer": round(T / (r["launch_us_median"] * 1e-6), 1)})
+                  "nodes_per_s_per_layer": round(T / (r["launch_us_median"] * 1e-6), 1)},
+                 **traffic_fields("replay_verify", name, rb))
         rec["replay"] = r
         del replay_calls
         # the separate verify and commit launches (workspace per copy)
@@ -696,9 +705,11 @@ def config_legs(args, gt, gi, dev):
         v_med, c_med = sv["launch_us_median"], sc["launch_us_median"]
         rec["separate"] = {
             "verify": dict(sv, alg_bytes=int(vb),
-                           frac_hbm_median=round(vb / v_med / 1e3 / HBM_PEAK_GBS, 4)),
+                           frac_hbm_median=round(vb / v_med / 1e3 / HBM_PEAK_GBS, 4),
+                           **traffic_fields("verify", name, vb)),
             "commit": dict(sc, alg_bytes=int(cb),
-                           frac_hbm_median=round(cb / c_med / 1e3 / HBM_PEAK_GBS, 4)),
+                           frac_hbm_median=round(cb / c_med / 1e3 / HBM_PEAK_GBS, 4),
+                           **traffic_fields("commit", name, cb)),
             "nodes_per_s_per_layer": round(T / ((v_med + c_med) * 1e-6), 1)}
         rec["steps"] = steps
         log(f"config {name} ({time.time() - t0:.1f}s): {rec}")
@@ -1019,7 +1030,10 @@ def main():
             "nodes_per_s_per_layer": round(w.T * L * args.per_layer_steps / p_el, 1),
             # verify per layer (as a forward issues it), commit of all layers batched
             "model_order_nodes_per_s_per_layer": round(w.T / ((pv_us + c_us) * 1e-6), 1),
-            "steps": args.per_layer_steps}
+            "steps": args.per_layer_steps,
+            # HBM bytes of one single-layer launch (rocprofv3 counters)
+            "traffic_bytes": {k: recorded_traffic(k, args.config + "_per_layer")
+                              for k in ("verify", "commit", "commit_verify", "replay_verify")}}
         for ly in layers:
             ly.pop("o_wy"), ly.pop("ws_wy")
         pver = pcom = None

@@ -37,21 +37,20 @@ def tree_check(offsets, parents, b, max_nodes=64):
 
 
 def accept_one(parents, draft_tokens, target_tokens):
-    """The handbook's walk on one tree (local arrays): the accepted path (node
-    indices, root first)."""
-    n = len(parents)
-    path, node = [0], 0
+    """The greedy walk on one tree (local arrays): the accepted path (node
+    indices, root first). Children are listed per node in index order, so the
+    first listed child whose draft token equals the target's prediction at the
+    current node is the one taken."""
+    kids = [[] for _ in range(len(parents))]
+    for c in range(1, len(parents)):
+        kids[int(parents[c])].append(c)
+    walk = [0]
     while True:
-        pred = int(target_tokens[node])
-        child = None
-        for c in range(n):
-            if int(parents[c]) == node and int(draft_tokens[c]) == pred:
-                child = c
-                break
-        if child is None:
-            return path
-        path.append(child)
-        node = child
+        want = int(target_tokens[walk[-1]])
+        hits = [c for c in kids[walk[-1]] if int(draft_tokens[c]) == want]
+        if not hits:
+            return walk
+        walk.append(hits[0])
 
 
 def accept_greedy(offsets, parents, draft_tokens, target_tokens, max_nodes=64):

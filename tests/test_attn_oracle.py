@@ -27,14 +27,12 @@ def _dense_masked_attention(q, K, V, mask, scale):
 
 
 def _ancestor_mask(parents):
-    n = len(parents)
-    m = np.zeros((n, n), bool)
-    for i in range(n):
-        j = i
-        while j != -1:
-            m[i, j] = True
-            j = parents[j]
-    return m
+    """Row i marks i and its ancestors: row parents[i] (built first, since a
+    parent precedes its children) plus i itself."""
+    vis = np.eye(len(parents), dtype=bool)
+    for i in range(1, len(parents)):
+        vis[i] |= vis[parents[i]]
+    return vis
 
 
 def _random_case(rng, parents_list, Hq, Hkv, d, cap, lens):

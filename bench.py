@@ -518,8 +518,10 @@ def selective_fork_leg(args, gt, gi, w, layers, offsets, parents, accepted, stat
 
 
 def sampling_accept_leg(args, gt, gi, w, offsets, parents, dev, V=151936):
-    """Sampling-mode acceptance (gdn_tree_accept_sampling) on the GDN workload's
-    trees over a Qwen-sized vocabulary: per node a target and a draft
+    """Sampling-mode acceptance on the GDN workload's trees over a Qwen-sized
+    vocabulary, every row pass split over the workgroups the device fits per
+    sequence (gdn_tree_accept_sampling_split), and with one workgroup per
+    sequence (gdn_tree_accept_sampling) beside it: per node a target and a draft
     distribution from peaked logits (a few favoured tokens over a spread),
     the draft's logits the target's plus noise, children drawn from the
     parent's draft distribution without replacement; seeded, drawn on the GPU."""
@@ -555,33 +557,55 @@ def sampling_accept_leg(args, gt, gi, w, offsets, parents, dev, V=151936):
             draft[lo + torch.tensor(cs, device=dev)] = tok.to(torch.int32)
     U = torch.rand(T, 2, generator=g, device=dev)
     desc = gt.make_desc(B, 1, 128, 128, T, w.max_nodes)
-    acc, alen, nxt, status = (torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(4))
-    call = lambda: gt.gdn_tree_accept_sampling(desc, offsets, parents, draft, P, Q, U, acc, alen,
-                                               nxt, status)
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    steps = 20
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    outs = [[torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(4)] for _ in range(2)]
+    one = lambda: gt.gdn_tree_accept_sampling(desc, offsets, parents, draft, P, Q, U, *outs[0])
+    splits = gt.gdn_tree_accept_sampling_splits(desc)
+    ws = torch.empty(max(1, gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V)),
+                     dtype=torch.uint8, device=dev)
+    split = gt.prepare_accept_sampling_split(desc, offsets, parents, draft, P, Q, U, splits, ws,
+                                             *outs[1])
+    # the visited rows (about 276 MB) could sit in the 256 MB Infinity Cache
+    # from the previous call: a 1 GiB buffer is read between timed calls
+    flush = torch.ones(1 << 28, device=dev)
     stream = torch.cuda.current_stream(dev)
-    for s_ in range(steps):
-        ev[s_][0].record(stream)
-        call()
-        ev[s_][1].record(stream)
-    torch.cuda.synchronize()
-    if np.any(status.cpu().numpy() != 0):
+    steps = 20
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for s_ in range(steps):
+            flush.sum()
+            ev[s_][0].record(stream)
+            call()
+            ev[s_][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+
+    t_one = timed(one)
+    t_split = timed(split)
+    res = [[o.cpu().numpy() for o in x] for x in outs]
+    if np.any(res[0][3] != 0) or np.any(res[1][3] != 0):
         raise RuntimeError("nonzero status in the sampling acceptance")
-    times = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
-    lens = alen.cpu().numpy()
+    if not all(np.array_equal(a, b) for a, b in zip(res[0], res[1])):
+        raise RuntimeError("the split sampling acceptance disagrees with the one-workgroup call")
+    lens = res[0][1]
     # rows every walk must read: the two rows of each node it visits
     rows_bytes = int(lens.sum()) * 2 * V * 4
-    med = times[steps // 2]
-    out = {"vocab": V, "steps": steps, "us_per_call_median": round(med, 2),
+    med, med1 = t_split[steps // 2], t_one[steps // 2]
+    out = {"vocab": V, "steps": steps, "splits": int(splits),
+           "us_per_call_median": round(med, 2),
+           "us_per_call_p10_p90": [round(t_split[steps // 10], 2),
+                                   round(t_split[(9 * steps) // 10], 2)],
            "mean_accept_len": round(float(lens.mean()), 3),
            "visited_rows_bytes": rows_bytes,
-           "visited_rows_GBs": round(rows_bytes / med / 1e3, 1)}
+           "visited_rows_GBs": round(rows_bytes / med / 1e3, 1),
+           "cache_eviction": "1 GiB read between timed calls",
+           "one_workgroup_per_sequence": {"us_per_call_median": round(med1, 2),
+                                          "visited_rows_GBs": round(rows_bytes / med1 / 1e3, 1)}}
     log(f"sampling acceptance: {out}")
-    del P, Q
+    del P, Q, flush, ws, split
     torch.cuda.empty_cache()
     return out
 

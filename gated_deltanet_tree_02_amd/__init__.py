@@ -36,7 +36,9 @@ __all__ = [
     "prepare_fork_selective_commit",
     "GdnAttnLayerIO", "make_attn_layer_io", "gdn_tree_attn_commit_layers",
     "prepare_attn_commit_layers",
-    "gdn_tree_accept_greedy", "gdn_tree_accept_sampling", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
+    "gdn_tree_accept_greedy", "gdn_tree_accept_sampling",
+    "gdn_tree_accept_sampling_split_workspace_bytes", "gdn_tree_accept_sampling_splits",
+    "gdn_tree_accept_sampling_split", "prepare_accept_sampling_split", "GdnRoundDesc", "GdnRoundLayout", "make_round_desc",
     "gdn_round_plan", "gdn_round_tree_for_budget", "RoundGraph", "GdnRoundPrev",
 ]
 
@@ -192,6 +194,13 @@ def load_library() -> ctypes.CDLL:
             lib.gdn_tree_accept_sampling.argtypes = [D, P, P, P, P, P, ctypes.c_int32, P, P, P,
                                                      P, P, P]
             lib.gdn_tree_accept_sampling.restype = I
+            lib.gdn_tree_accept_sampling_split_workspace_bytes.argtypes = [D, ctypes.c_int32]
+            lib.gdn_tree_accept_sampling_split_workspace_bytes.restype = S
+            lib.gdn_tree_accept_sampling_splits.argtypes = [D]
+            lib.gdn_tree_accept_sampling_splits.restype = ctypes.c_int32
+            lib.gdn_tree_accept_sampling_split.argtypes = [D, P, P, P, P, P, ctypes.c_int32, P,
+                                                           ctypes.c_int32, P, S, P, P, P, P, P]
+            lib.gdn_tree_accept_sampling_split.restype = I
             R = ctypes.POINTER(GdnRoundDesc)
             lib.gdn_round_plan.argtypes = [R, ctypes.POINTER(GdnRoundLayout)]
             lib.gdn_round_plan.restype = I
@@ -1017,6 +1026,66 @@ def gdn_tree_accept_sampling(desc, offsets, parents, draft_tokens, target_probs,
         _check(load_library().gdn_tree_accept_sampling(ctypes.byref(desc), *args,
                                                        _stream(stream, dev)),
                "gdn_tree_accept_sampling")
+
+
+def gdn_tree_accept_sampling_split_workspace_bytes(desc, vocab: int) -> int:
+    return int(load_library().gdn_tree_accept_sampling_split_workspace_bytes(ctypes.byref(desc),
+                                                                            int(vocab)))
+
+
+def gdn_tree_accept_sampling_splits(desc) -> int:
+    """Workgroups per sequence that splits = 0 picks on the current device."""
+    return int(load_library().gdn_tree_accept_sampling_splits(ctypes.byref(desc)))
+
+
+def _sampling_split_args(desc, offsets, parents, draft_tokens, target_probs, draft_probs,
+                         uniforms, splits, workspace, accepted, accept_len, next_token,
+                         tree_status):
+    torch = _torch()
+    B, T = desc.num_seqs, desc.total_nodes
+    dev = offsets.device
+    i32, f32 = torch.int32, torch.float32
+    V = int(target_probs.shape[-1])
+    return [_ptr(offsets, "offsets", i32, (B + 1,), dev), _ptr(parents, "parents", i32, (T,), dev),
+            _ptr(draft_tokens, "draft_tokens", i32, (T,), dev),
+            _ptr(target_probs, "target_probs", f32, (T, V), dev),
+            _ptr(draft_probs, "draft_probs", f32, (T, V), dev), ctypes.c_int32(V),
+            _ptr(uniforms, "uniforms", f32, (T, 2), dev), ctypes.c_int32(int(splits))] + \
+        _ws_args(workspace, dev) + \
+        [_ptr(accepted, "accepted", i32, (B,), dev), _ptr(accept_len, "accept_len", i32, (B,), dev),
+         _ptr(next_token, "next_token", i32, (B,), dev),
+         _ptr(tree_status, "tree_status", i32, (B,), dev)]
+
+
+def gdn_tree_accept_sampling_split(desc, offsets, parents, draft_tokens, target_probs,
+                                   draft_probs, uniforms, splits, workspace, accepted, accept_len,
+                                   next_token, tree_status, stream=None):
+    """gdn_tree_accept_sampling with every row pass spread over `splits`
+    workgroups per sequence (0: the device's pick); workspace: uint8 of
+    gdn_tree_accept_sampling_split_workspace_bytes(desc, V) bytes (None with
+    splits = 1)."""
+    torch = _torch()
+    dev = offsets.device
+    args = _sampling_split_args(desc, offsets, parents, draft_tokens, target_probs, draft_probs,
+                                uniforms, splits, workspace, accepted, accept_len, next_token,
+                                tree_status)
+    with torch.cuda.device(dev):
+        _check(load_library().gdn_tree_accept_sampling_split(ctypes.byref(desc), *args,
+                                                             _stream(stream, dev)),
+               "gdn_tree_accept_sampling_split")
+
+
+def prepare_accept_sampling_split(desc, offsets, parents, draft_tokens, target_probs,
+                                  draft_probs, uniforms, splits, workspace, accepted, accept_len,
+                                  next_token, tree_status, stream=None, keep=()):
+    """Marshalled gdn_tree_accept_sampling_split."""
+    dev = offsets.device
+    args = _sampling_split_args(desc, offsets, parents, draft_tokens, target_probs, draft_probs,
+                                uniforms, splits, workspace, accepted, accept_len, next_token,
+                                tree_status)
+    return PreparedCall("gdn_tree_accept_sampling_split", desc, args, _stream(stream, dev),
+                        (offsets, parents, draft_tokens, target_probs, draft_probs, uniforms,
+                         workspace, accepted, accept_len, next_token, tree_status, tuple(keep)))
 
 
 def make_round_desc(gdn_desc=None, n_gdn_layers=0, attn_desc=None, n_attn_layers=0) -> GdnRoundDesc:

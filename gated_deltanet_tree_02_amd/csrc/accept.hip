@@ -8,6 +8,8 @@
 // node none of whose children match. Each step is one ballot over the lanes
 // (child of the current node and token equal to the prediction); a child has
 // a larger index than its parent, so the walk takes at most N_b - 1 steps.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -66,22 +68,29 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
 // rows; when no candidate is accepted, one token is drawn from p_k by inverse
 // CDF and the walk ends.
 //
-// One workgroup per sequence. p_k and q_k are never stored: for any token
-// they follow from p(j), q(j) and the per-stage scalars (1/Z_i, the rejected
-// tokens, the renormalisation of q). A rejection costs one pass over the
-// node's two rows, which yields the normaliser Z as a sum of per-tile sums of
-// max(0, p_k - q_k); those tile sums, scaled by 1/Z, are the tile sums of the
-// next p, so a final draw after a rejection needs no further pass (a draw
-// with no rejection at the node takes one pass over p). The draw then finds
-// the tile where the cumulative mass crosses the target and re-reads that
-// tile alone. Each wave works on whole 256-token tiles and keeps
-// kTilesInFlight tiles' loads in flight. Decisions are taken in fp32; sums
-// run in a fixed order.
+// One workgroup per sequence, or (split form) several, which divide every
+// pass over a node's rows by tiles and trade their tile sums after it. p_k and
+// q_k are never stored: for any token they follow from p(j), q(j) and the
+// per-stage scalars (1/Z_i, the rejected tokens, the renormalisation of q). A
+// rejection costs one pass over the node's two rows, which yields the
+// normaliser Z as a sum of per-tile sums of max(0, p_k - q_k) (the first one
+// at a node also the row's q mass, per tile); those tile sums, scaled by 1/Z,
+// are the tile sums of the next p, so a final draw after a rejection needs no
+// further pass (a draw with no rejection at the node takes one pass over p).
+// The draw then finds the tile where the cumulative mass crosses the target
+// and re-reads that tile alone. Each wave works on whole 256-token tiles and
+// keeps kTilesInFlight tiles' loads in flight. Decisions are taken in fp32;
+// totals run over the tile sums in a fixed order, so they do not depend on how
+// the tiles were divided.
 
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / 64;
-constexpr int kTile = 256;                       // tokens per tile (64 lanes x 4)
+constexpr int kTile = kSamplingTile;             // tokens per tile (64 lanes x 4)
+static_assert(kTile == 256, "a tile is 64 lanes x 4 tokens");
 constexpr int kTilesInFlight = 4;
+// (the split form takes fewer tiles per wave per pass, and more of them in
+// flight at once pays there)
+constexpr int kSplitTilesInFlight = 5;
 constexpr int kMaxTiles = (1 << 20) / kTile;     // vocabularies up to 2^20 tokens
 
 struct Stages {
@@ -174,46 +183,32 @@ __device__ __forceinline__ float wave_sum(float x) {
       float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_lane63(x)), 63));
 }
 
-// Sum over the workgroup, in a fixed order; every thread gets the result.
-__device__ __forceinline__ float block_sum(float x, float* red) {
-  x = wave_sum(x);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();                      // red is free
-  if ((threadIdx.x & 63) == 0) red[wave] = x;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int w = 0; w < kSampleWaves; ++w) t += red[w];
-  return t;
-}
-
 // What a tile pass sums per token.
 enum TileSum { kResidual, kTarget };
 
-// One pass over a node's rows: sTile[t] = sum over tile t of
-// max(0, p_k - q_k) (kResidual) or of p_k (kTarget); the thread's share of
-// the row's q mass is added to *qs. Wave w takes tiles w, w + waves, ...
-// through a ring of kTilesInFlight tiles: a tile's slot is refilled with the
-// wave's next-but-(kTilesInFlight - 1) tile as soon as it is summed, so every
-// wave keeps that many tiles' loads in flight for the whole pass. K >= 0:
-// exactly K rejections so far, the stage scalars in registers; K < 0: any
-// number, read from LDS.
-template <TileSum WHAT, int K>
+// One pass over tiles [tbeg, tend) of a node's rows: sTile[t] = sum over tile t
+// of max(0, p_k - q_k) (kResidual) or of p_k (kTarget), and with kQSum sQ[t] =
+// the tile's q mass. Wave w takes tiles tbeg + w, tbeg + w + waves, ... through
+// a ring of kTilesInFlight tiles: a tile's slot is refilled with the wave's
+// next-but-(kTilesInFlight - 1) tile as soon as it is summed, so every wave
+// keeps that many tiles' loads in flight for the whole pass. K >= 0: exactly
+// K rejections so far, the stage scalars in registers; K < 0: any number, read
+// from LDS. A tile's sums are the same whichever workgroup takes it.
+template <TileSum WHAT, int K, bool kQSum, int W>
 __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
-                                            const float* __restrict__ qrow, int V,
-                                            const Stages& s, float* sTile, float* qs) {
-  constexpr int W = kTilesInFlight;
+                                            const float* __restrict__ qrow, int V, int tbeg,
+                                            int tend, const Stages& s, float* sTile, float* sQ) {
   const StageRegs<K < 0 ? 0 : K> r = stage_regs<K < 0 ? 0 : K>(s);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int ntiles = (V + kTile - 1) / kTile;
-  const int mine = wave < ntiles ? (ntiles - 1 - wave) / kSampleWaves + 1 : 0;
+  const int span = tend - tbeg;
+  const int mine = wave < span ? (span - 1 - wave) / kSampleWaves + 1 : 0;
   // p_0 needs no q: a draw with no rejection reads the target row alone
-  constexpr bool need_q = WHAT == kResidual || K != 0;
+  constexpr bool need_q = WHAT == kResidual || K != 0 || kQSum;
   // element offsets are clamped into the row (V >= 4), so that every load is
   // issued unconditionally; tiles past the wave's last one are not summed
   auto off = [&](int i) {
-    const int j = (wave + i * kSampleWaves) * kTile + 4 * lane;
+    const int j = (tbeg + wave + i * kSampleWaves) * kTile + 4 * lane;
     return j < V - 4 ? j : V - 4;
   };
   float4 pv[W], qv[W];
@@ -227,7 +222,7 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
 #pragma unroll
     for (int u = 0; u < W; ++u) {
       const int i = i0 + u;
-      const int t = wave + i * kSampleWaves;
+      const int t = tbeg + wave + i * kSampleWaves;
       const int j = t * kTile + 4 * lane;
       const bool in_row = i < mine && j < V;
       const float pe[4] = {in_row ? pv[u].x : 0.f, in_row ? pv[u].y : 0.f,
@@ -237,46 +232,139 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
       // the slot's next tile
       pv[u] = *reinterpret_cast<const float4*>(prow + off(i + W));
       if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + off(i + W));
-      float m = 0.f;
+      float m = 0.f, qm = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float2 pq = K >= 0 ? stage_pq_reg<K < 0 ? 0 : K>(pe[e], qe[e], j + e, r)
                                  : stage_pq(pe[e], qe[e], j + e, s);
         m += WHAT == kResidual ? fmaxf(pq.x - pq.y, 0.f) : pq.x;
-        *qs += qe[e];
+        qm += qe[e];
       }
       m = wave_sum_lane63(m);
-      if (lane == 63 && i < mine) sTile[t] = m;
+      if (kQSum) qm = wave_sum_lane63(qm);
+      if (lane == 63 && i < mine) {
+        sTile[t] = m;
+        if (kQSum) sQ[t] = qm;
+      }
     }
   }
 }
 
-template <TileSum WHAT>
+template <TileSum WHAT, int W>
 __device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
-                                          const float* __restrict__ qrow, int V,
-                                          const Stages& s, float* sTile, float* qs) {
+                                          const float* __restrict__ qrow, int V, int tbeg,
+                                          int tend, const Stages& s, float* sTile, float* sQ) {
   switch (s.k) {
-    case 0: return tile_pass_t<WHAT, 0>(prow, qrow, V, s, sTile, qs);
-    case 1: return tile_pass_t<WHAT, 1>(prow, qrow, V, s, sTile, qs);
-    case 2: return tile_pass_t<WHAT, 2>(prow, qrow, V, s, sTile, qs);
-    case 3: return tile_pass_t<WHAT, 3>(prow, qrow, V, s, sTile, qs);
-    case 4: return tile_pass_t<WHAT, 4>(prow, qrow, V, s, sTile, qs);
-    default: return tile_pass_t<WHAT, -1>(prow, qrow, V, s, sTile, qs);
+    // the first rejection's pass also gives the q mass of the row, per tile
+    case 0:
+      if constexpr (WHAT == kResidual)
+        return tile_pass_t<WHAT, 0, true, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
+      else
+        return tile_pass_t<WHAT, 0, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
+    case 1: return tile_pass_t<WHAT, 1, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
+    case 2: return tile_pass_t<WHAT, 2, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
+    case 3: return tile_pass_t<WHAT, 3, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
+    case 4: return tile_pass_t<WHAT, 4, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
+    default: return tile_pass_t<WHAT, -1, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
   }
 }
 
+// A sum over tiles [0, ntiles) of `v` (times `scale`) in a fixed order, by wave
+// 0: lane l adds its block of ceil(ntiles / 64) tiles in order, then the lanes
+// are added in DPP steps. Every lane of wave 0 gets the total.
+__device__ __forceinline__ float tiles_total(const float* v, int ntiles, float scale) {
+  const int lane = threadIdx.x & 63;
+  const int per = (ntiles + 63) / 64;
+  const int t0 = min(lane * per, ntiles), t1 = min(t0 + per, ntiles);
+  float ls = 0.f;
+  for (int t = t0; t < t1; ++t) ls += v[t] * scale;
+  return wave_sum(ls);
+}
+
+// How long a workgroup of the split form waits for the others' tile sums
+// (polls, each after a short sleep; a poll takes about a microsecond) before
+// it sums every tile of the row itself. The sums are the same either way, so
+// the wait only costs time: with every workgroup resident it never runs out;
+// a workgroup that is not resident yet (the device busy with other work)
+// cannot hold the others up.
+constexpr unsigned kPatience = 256;
+
+// The split form's exchange after a pass over tiles [tbeg, tend). Every tile
+// sum travels as one 64-bit word, the value's bits in the low half and the
+// pass number (from 1) in the high half, written and read with single atomic
+// accesses at device scope (coherent across the XCDs' L2s): a reader that
+// sees the pass number sees the value, so no fence or counter is needed. Wave
+// 0 publishes this workgroup's tiles once the pass is done (stores issued
+// during the pass would share the load counter the pass waits on); then every
+// thread polls its share of all tiles of the row until each carries this
+// pass's number, and copies the values into sTile (and sQ). Each sequence has
+// two sets of words that alternate between passes. A word holds the value of
+// the pass its number names (every writer computes the same value), so a
+// workgroup that reads a word another one has already reused for a later pass
+// only sees a number that is not its pass's and keeps waiting, then sums the
+// tiles itself. The words are cleared before every call. Returns false if the
+// wait ran out.
+__device__ bool exchange_tiles(const AcceptSampleArgs& a, int b, int tbeg, int tend, int ntiles,
+                               bool with_q, unsigned& nsync, float* sTile, float* sQ) {
+  const int tid = threadIdx.x;
+  const unsigned long long tag = (unsigned long long)(nsync + 1u) << 32;
+  unsigned long long* words =
+      a.xch + ((size_t)b * 2 + (nsync & 1u)) * 2 * (size_t)a.xch_stride;
+  unsigned long long* qwords = words + a.xch_stride;
+  __syncthreads();                       // this workgroup's tiles are in LDS
+  if (tid < 64) {
+    for (int t = tbeg + tid; t < tend; t += 64) {
+      __hip_atomic_store(words + t, tag | __builtin_bit_cast(unsigned, sTile[t]),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (with_q)
+        __hip_atomic_store(qwords + t, tag | __builtin_bit_cast(unsigned, sQ[t]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  ++nsync;
+  for (unsigned polls = 0;; ++polls) {
+    int missing = 0;
+    for (int t = tid; t < ntiles; t += kSampleThreads) {
+      if (t >= tbeg && t < tend) continue;   // this workgroup's own
+      const unsigned long long w = __hip_atomic_load(words + t, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+      if ((w & ~0xffffffffull) == tag) sTile[t] = __builtin_bit_cast(float, (unsigned)w);
+      else missing = 1;
+      if (with_q) {
+        const unsigned long long u = __hip_atomic_load(qwords + t, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+        if ((u & ~0xffffffffull) == tag) sQ[t] = __builtin_bit_cast(float, (unsigned)u);
+        else missing = 1;
+      }
+    }
+    if (!__syncthreads_or(missing)) return true;
+    if (polls == kPatience) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// One workgroup per sequence (kSplit false), or a.splits workgroups per
+// sequence, workgroup i taking part i % splits of sequence i / splits: every
+// workgroup of a sequence takes the same decisions (from the same sums in the
+// same order), and a pass over a node's rows is divided among them by tiles.
+template <bool kSplit>
 __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const AcceptSampleArgs a) {
   __shared__ int sPar[64];
   __shared__ int sTok[64];
   __shared__ int sRem[64];
   __shared__ float sZinv[64];
   __shared__ float sQscale[65];
-  __shared__ float sRed[kSampleWaves];
+  __shared__ float sPX[64], sQX[64], sUX[64];   // candidates: p(x), q(x), uniform
   __shared__ float sTile[kMaxTiles];
+  __shared__ float sQ[kMaxTiles];
   __shared__ int sInfo[4];              // status, lo, n, decision / crossing tile
   __shared__ float sF[2];               // crossing: mass before the tile, draw target
 
-  const int b = blockIdx.x;
+  // (the divisions by runtime values go through vector registers: their
+  // uniform results are moved back to scalar ones)
+  const int S = kSplit ? a.splits : 1;
+  const int b = kSplit ? __builtin_amdgcn_readfirstlane((int)blockIdx.x / S) : (int)blockIdx.x;
+  const int part = kSplit ? (int)blockIdx.x - b * S : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -298,8 +386,8 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
   if (tid == 0) sQscale[0] = 1.f;
   __syncthreads();
   const int st = sInfo[0], lo = sInfo[1], n = sInfo[2];
-  if (st != GDN_TREE_OK) {
-    if (tid == 0) {
+  if (st != GDN_TREE_OK) {             // (the same for every workgroup of the sequence)
+    if (part == 0 && tid == 0) {
       a.status[b] = st;
       a.accepted[b] = -1;
       a.accept_len[b] = 0;
@@ -309,6 +397,27 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
   }
   const int V = a.V;
   const int ntiles = (V + kTile - 1) / kTile;
+  const int tbeg = __builtin_amdgcn_readfirstlane(part * ntiles / S);
+  const int tend = __builtin_amdgcn_readfirstlane((part + 1) * ntiles / S);
+  unsigned nsync = 0;                   // exchanges passed (split form)
+  // A pass over this workgroup's tiles, then every tile's sums in sTile (sQ):
+  // from the others' words, or, if they do not come, from a second pass here
+  // over all tiles (the same call site, so the pass is inlined once).
+  auto pass_all = [&](auto what, const float* prow, const float* qrow, const Stages& st,
+                      bool with_q) {
+    int tb = tbeg, te = tend;
+    for (;;) {
+      tile_pass<decltype(what)::value, kSplit ? kSplitTilesInFlight : kTilesInFlight>(
+          prow, qrow, V, tb, te, st, sTile, sQ);
+      if (!kSplit || (tb == 0 && te == ntiles)) {
+        __syncthreads();
+        return;
+      }
+      if (exchange_tiles(a, b, tbeg, tend, ntiles, with_q, nsync, sTile, sQ)) return;
+      tb = 0;
+      te = ntiles;
+    }
+  };
   int cur = 0, len = 1, token = V - 1;
   for (;;) {
     const float* __restrict__ prow = a.p + (size_t)(lo + cur) * V;
@@ -317,32 +426,32 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
     float qtot = 0.f, qrem = 0.f;
     bool tiles_ready = false;             // sTile holds the current p's tile sums / Z
     int next = -1;
+    // every candidate's p(x), q(x) and uniform, one lane per child, in one
+    // round trip when the walk enters the node
+    if (tid > cur && tid < n && sPar[tid] == cur) {
+      const int x = sTok[tid];
+      sPX[tid] = prow[x];
+      sQX[tid] = qrow[x];
+      sUX[tid] = a.u[2 * (size_t)(lo + tid)];
+    }
+    __syncthreads();
     for (int c = cur + 1; c < n; ++c) {   // children have larger indices, in node order
       if (sPar[c] != cur) continue;       // uniform
       const int x = sTok[c];
-      if (tid == 0) {
-        const float2 pq = stage_pq(prow[x], qrow[x], x, s);
-        sInfo[3] = a.u[2 * (size_t)(lo + c)] * pq.y < pq.x;
-      }
-      __syncthreads();
-      const bool take = sInfo[3] != 0;
-      __syncthreads();                    // sInfo[3] is read by all before reuse
+      // (every thread takes the decision alike, from the same values)
+      const float2 pq = stage_pq(sPX[c], sQX[c], x, s);
+      const bool take = sUX[c] * pq.y < pq.x;
       if (take) {
         next = c;
         break;
       }
       // rejected: tile sums of the residual max(0, p_k - q_k), and its mass Z
-      float qs = 0.f;
-      tile_pass<kResidual>(prow, qrow, V, s, sTile, &qs);
-      if (s.k == 0) qtot = block_sum(qs, sRed);     // (its barriers also publish sTile)
-      else __syncthreads();
+      // (the first pass at a node also sums the row's q mass)
+      pass_all(std::integral_constant<TileSum, kResidual>{}, prow, qrow, s, s.k == 0);
       if (wave == 0) {
-        const int per = (ntiles + 63) / 64;
-        const int t0 = min(lane * per, ntiles), t1 = min(t0 + per, ntiles);
-        float ls = 0.f;
-        for (int t = t0; t < t1; ++t) ls += sTile[t];
-        const float z = wave_sum(ls);
-        qrem += qrow[x];
+        const float z = tiles_total(sTile, ntiles, 1.f);
+        if (s.k == 0) qtot = tiles_total(sQ, ntiles, 1.f);
+        qrem += sQX[c];
         if (lane == 0) {
           sZinv[s.k] = z > 0.f ? 1.f / z : 0.f;
           sRem[s.k] = x;
@@ -365,9 +474,7 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
     if (tiles_ready) {
       scale = sZinv[s.k - 1];
     } else {
-      float unused = 0.f;
-      tile_pass<kTarget>(prow, qrow, V, s, sTile, &unused);
-      __syncthreads();
+      pass_all(std::integral_constant<TileSum, kTarget>{}, prow, qrow, s, false);
     }
     if (wave == 0) {
       // lane l owns tiles [l*per, (l+1)*per)
@@ -438,7 +545,7 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
     }
     break;
   }
-  if (tid == 0) {
+  if (part == 0 && tid == 0) {
     a.status[b] = GDN_TREE_OK;
     a.accepted[b] = cur;
     a.accept_len[b] = len;
@@ -446,11 +553,37 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
   }
 }
 
+// The split form's exchange words start every call at pass number 0 (none).
+__global__ __launch_bounds__(256) void sampling_xch_clear_kernel(const AcceptSampleArgs a) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (size_t)a.B * 4 * a.xch_stride) a.xch[i] = 0ull;
+}
+
 }  // namespace
 
 hipError_t launch_accept_sampling(const AcceptSampleArgs& a, hipStream_t s) {
-  return launch_kernel(reinterpret_cast<const void*>(&accept_sampling_kernel), (unsigned)a.B,
-                       (unsigned)kSampleThreads, s, a);
+  return launch_kernel(reinterpret_cast<const void*>(&accept_sampling_kernel<false>),
+                       (unsigned)a.B, (unsigned)kSampleThreads, s, a);
+}
+
+int accept_sampling_split_capacity() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&accept_sampling_kernel<true>),
+          kSampleThreads, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
+hipError_t launch_accept_sampling_split(const AcceptSampleArgs& a, hipStream_t s) {
+  const size_t words = (size_t)a.B * 4 * a.xch_stride;
+  const hipError_t e = launch_kernel(reinterpret_cast<const void*>(&sampling_xch_clear_kernel),
+                                     (unsigned)((words + 255) / 256), 256u, s, a);
+  if (e != hipSuccess) return e;
+  return launch_kernel(reinterpret_cast<const void*>(&accept_sampling_kernel<true>),
+                       (unsigned)(a.B * a.splits), (unsigned)kSampleThreads, s, a);
 }
 
 hipError_t launch_accept_greedy(const AcceptArgs& a, hipStream_t s) {

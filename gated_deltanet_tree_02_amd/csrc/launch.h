@@ -174,6 +174,12 @@ struct AcceptSampleArgs {
   int32_t* accept_len;
   int32_t* next_token;
   int32_t* status;
+  // split form: `splits` workgroups per sequence trade tile sums through
+  // xch (per sequence, two alternating sets of [tile sums | q tile sums],
+  // xch_stride 64-bit words each: the pass number above the value's bits)
+  int splits = 1;
+  unsigned long long* xch = nullptr;
+  int xch_stride = 0;
 };
 
 // Greedy acceptance of the verified trees.
@@ -343,6 +349,12 @@ hipError_t launch_fork_selective_commit(int io, int d, const SelectiveCommitArgs
                                         hipStream_t s);
 hipError_t launch_accept_greedy(const AcceptArgs& a, hipStream_t s);
 hipError_t launch_accept_sampling(const AcceptSampleArgs& a, hipStream_t s);
+// split form: clears the exchange words, then launches B * splits
+// workgroups
+hipError_t launch_accept_sampling_split(const AcceptSampleArgs& a, hipStream_t s);
+// workgroups of the split kernel that fit on the current device at once
+int accept_sampling_split_capacity();
+constexpr int kSamplingTile = 256;            // tokens per tile of a row pass
 
 // Kernel launch that reports its own error (no reliance on the sticky
 // last-error state, which other libraries in the process also use).

@@ -180,12 +180,15 @@ gdn_status gdn_tree_accept_greedy(const gdn_tree_desc* desc, const int32_t* offs
                             accept_len, next_token, tree_status, stream, 0);
 }
 
-gdn_status gdn_tree_accept_sampling(const gdn_tree_desc* desc, const int32_t* offsets,
-                                    const int32_t* parents, const int32_t* draft_tokens,
-                                    const float* target_probs, const float* draft_probs,
-                                    int32_t vocab, const float* uniforms, int32_t* accepted,
-                                    int32_t* accept_len, int32_t* next_token,
-                                    int32_t* tree_status, void* stream) {
+namespace {
+
+// Checks shared by the sampling calls (before anything is enqueued).
+gdn_status check_sampling(const gdn_tree_desc* desc, const int32_t* offsets,
+                          const int32_t* parents, const int32_t* draft_tokens,
+                          const float* target_probs, const float* draft_probs, int32_t vocab,
+                          const float* uniforms, const int32_t* accepted,
+                          const int32_t* accept_len, const int32_t* next_token,
+                          const int32_t* tree_status) {
   if (desc == nullptr) return GDN_ERR_NULL_PTR;
   if (desc->num_seqs < 0 || desc->total_nodes < 0 || desc->max_nodes < 1 ||
       desc->max_nodes > GDN_TREE_MAX_NODES)
@@ -197,10 +200,79 @@ gdn_status gdn_tree_accept_sampling(const gdn_tree_desc* desc, const int32_t* of
   if (desc->total_nodes > 0 &&
       (!parents || !draft_tokens || !target_probs || !draft_probs || !uniforms))
     return GDN_ERR_NULL_PTR;
+  return GDN_OK;
+}
+
+// Tiles of a row rounded up to 64, the floats of one exchange buffer.
+size_t sampling_xch_stride(int32_t vocab) {
+  const size_t tiles = ((size_t)vocab + gdn::kSamplingTile - 1) / gdn::kSamplingTile;
+  return (tiles + 63) / 64 * 64;
+}
+
+
+}  // namespace
+
+gdn_status gdn_tree_accept_sampling(const gdn_tree_desc* desc, const int32_t* offsets,
+                                    const int32_t* parents, const int32_t* draft_tokens,
+                                    const float* target_probs, const float* draft_probs,
+                                    int32_t vocab, const float* uniforms, int32_t* accepted,
+                                    int32_t* accept_len, int32_t* next_token,
+                                    int32_t* tree_status, void* stream) {
+  const gdn_status st = check_sampling(desc, offsets, parents, draft_tokens, target_probs,
+                                       draft_probs, vocab, uniforms, accepted, accept_len,
+                                       next_token, tree_status);
+  if (st != GDN_OK || desc->num_seqs == 0) return st;
   gdn::AcceptSampleArgs a{desc->num_seqs, desc->total_nodes, desc->max_nodes, vocab, offsets,
                           parents, draft_tokens, target_probs, draft_probs, uniforms,
                           accepted, accept_len, next_token, tree_status};
   return gdn::launch_accept_sampling(a, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? GDN_OK
+             : GDN_ERR_LAUNCH;
+}
+
+size_t gdn_tree_accept_sampling_split_workspace_bytes(const gdn_tree_desc* desc, int32_t vocab) {
+  if (desc == nullptr || desc->num_seqs <= 0 || vocab < 4 || vocab > (1 << 20)) return 0;
+  // per sequence two sets of [tile sums | q tile sums], one 64-bit word per tile
+  return round_up((size_t)desc->num_seqs * 4 * sampling_xch_stride(vocab) * 8);
+}
+
+int32_t gdn_tree_accept_sampling_splits(const gdn_tree_desc* desc) {
+  if (desc == nullptr || desc->num_seqs <= 0) return 1;
+  const int cap = gdn::accept_sampling_split_capacity();
+  int splits = cap / desc->num_seqs;
+  if (splits > GDN_SAMPLING_MAX_SPLITS) splits = GDN_SAMPLING_MAX_SPLITS;
+  return splits < 1 ? 1 : splits;
+}
+
+gdn_status gdn_tree_accept_sampling_split(const gdn_tree_desc* desc, const int32_t* offsets,
+                                          const int32_t* parents, const int32_t* draft_tokens,
+                                          const float* target_probs, const float* draft_probs,
+                                          int32_t vocab, const float* uniforms, int32_t splits,
+                                          void* workspace, size_t workspace_bytes,
+                                          int32_t* accepted, int32_t* accept_len,
+                                          int32_t* next_token, int32_t* tree_status,
+                                          void* stream) {
+  const gdn_status st = check_sampling(desc, offsets, parents, draft_tokens, target_probs,
+                                       draft_probs, vocab, uniforms, accepted, accept_len,
+                                       next_token, tree_status);
+  if (st != GDN_OK || desc->num_seqs == 0) return st;
+  if (splits < 0 || splits > GDN_SAMPLING_MAX_SPLITS) return GDN_ERR_UNSUPPORTED;
+  if (splits == 0) splits = gdn_tree_accept_sampling_splits(desc);
+  if (splits == 1)
+    return gdn_tree_accept_sampling(desc, offsets, parents, draft_tokens, target_probs,
+                                    draft_probs, vocab, uniforms, accepted, accept_len,
+                                    next_token, tree_status, stream);
+  if (workspace == nullptr) return GDN_ERR_NULL_PTR;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return GDN_ERR_BAD_SHAPE;
+  if (workspace_bytes < gdn_tree_accept_sampling_split_workspace_bytes(desc, vocab))
+    return GDN_ERR_WORKSPACE;
+  gdn::AcceptSampleArgs a{desc->num_seqs, desc->total_nodes, desc->max_nodes, vocab, offsets,
+                          parents, draft_tokens, target_probs, draft_probs, uniforms,
+                          accepted, accept_len, next_token, tree_status};
+  a.splits = splits;
+  a.xch = static_cast<unsigned long long*>(workspace);
+  a.xch_stride = (int)sampling_xch_stride(vocab);
+  return gdn::launch_accept_sampling_split(a, static_cast<hipStream_t>(stream)) == hipSuccess
              ? GDN_OK
              : GDN_ERR_LAUNCH;
 }

@@ -516,6 +516,19 @@ def _uniforms_clear_of_thresholds(rng, offsets, parents, draft, P, Q, tries=60):
     raise RuntimeError("no uniforms clear of the thresholds")
 
 
+def _uniforms_clear_per_sequence(rng, offsets, parents, draft, P, Q, tries=200):
+    """The same, drawn sequence by sequence (a long walk over a large
+    vocabulary lands a draw near a token boundary often enough that one
+    batch-wide draw rarely clears every decision)."""
+    U = np.zeros((len(parents), 2), np.float32)
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        o1 = np.array([0, hi - lo], np.int32)
+        U[lo:hi] = _uniforms_clear_of_thresholds(rng, o1, parents[lo:hi], draft[lo:hi],
+                                                 P[lo:hi], Q[lo:hi], tries)
+    return U
+
+
 def _sampling_gpu(offsets, parents, draft, P, Q, U, max_nodes=64):
     B, T = len(offsets) - 1, len(parents)
     desc = gt.make_desc(B, 1, 128, 128, T, max_nodes)
@@ -599,3 +612,111 @@ def test_accept_sampling_emits_the_target_distribution():
     sigma = np.sqrt(p * (1 - p) / N)
     _say("max |emp - p| / sigma", float(np.max(np.abs(emp - p) / sigma)))
     assert np.all(np.abs(emp - p) <= 5 * sigma + 1e-12)
+
+
+# ---------------------------------------------- sampling acceptance, passes split over workgroups
+
+
+def _sampling_split_gpu(offsets, parents, draft, P, Q, U, splits, ws=None, max_nodes=64):
+    B, T = len(offsets) - 1, len(parents)
+    desc = gt.make_desc(B, 1, 128, 128, T, max_nodes)
+    V = P.shape[1]
+    if ws is None:
+        ws = nan_bytes(gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V))
+    outs = [torch.full((B,), -9, dtype=torch.int32, device="cuda") for _ in range(4)]
+    gt.gdn_tree_accept_sampling_split(desc, i32(offsets), i32(parents), i32(draft), f32(P),
+                                      f32(Q), f32(U), splits, ws, *outs)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+def _max_splits(B):
+    return gt.gdn_tree_accept_sampling_splits(gt.make_desc(B, 1, 128, 128, B, 1))
+
+
+@pytest.mark.parametrize("V", [8, 1000, 5000, 151936])
+def test_accept_sampling_split_is_the_one_workgroup_call_bit_for_bit(V):
+    """Every split of the row passes (2 .. as many as fit, tile counts that do
+    not divide evenly, more parts than tiles at V = 8) gives the accepted
+    node, length, drawn token and status of the one-workgroup call exactly,
+    on uniforms drawn without regard to the decision margins."""
+    rng = np.random.default_rng(100 + V)
+    if V > 10000:
+        trees = [gi.kary_parents(3, 3)] * 5 + [gi.random_tree_parents(rng, 4, 24)] * 3
+    else:
+        trees = [gi.random_tree_parents(rng, 5, 30) for _ in range(18)] + \
+            [[-1], gi.chain_parents(7), gi.kary_parents(8, 1)]
+    offsets, parents, draft, P, Q = _sampling_case(rng, trees, V)
+    U = rng.random((len(parents), 2)).astype(np.float32)
+    one = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    top = _max_splits(len(trees))
+    assert top >= 2, top
+    for S in sorted({2, 3, 4, 7, top}):
+        if S > top:
+            continue
+        _say(f"split sampling V={V} splits={S}")
+        got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, S)
+        for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, one):
+            np.testing.assert_array_equal(g, r, err_msg=f"{name} splits={S}")
+    assert (one[3] == 0).all()
+
+
+def test_accept_sampling_split_full_size_against_the_oracle():
+    """16 k=3 d=3 trees at V = 151,936 with the device's own split count (16
+    on a 256-CU part), the workspace reused by a second, smaller call: both
+    against the oracle."""
+    V = 151936
+    rng = np.random.default_rng(78)
+    trees = [gi.kary_parents(3, 3)] * 16
+    offsets, parents, draft, P, Q = _sampling_case(rng, trees, V)
+    U = _uniforms_clear_per_sequence(rng, offsets, parents, draft, P, Q)
+    desc = gt.make_desc(16, 1, 128, 128, len(parents), 64)
+    ws = nan_bytes(gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V))
+    _say("split sampling full size, splits", gt.gdn_tree_accept_sampling_splits(desc))
+    got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, 0, ws=ws)
+    ref = oacc.accept_sampling(offsets, parents, draft, P, Q, U)
+    for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, ref):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+    # the first 9 sequences again, in the same workspace
+    n9 = int(offsets[9])
+    got9 = _sampling_split_gpu(offsets[:10], parents[:n9], draft[:n9], P[:n9], Q[:n9], U[:n9], 0,
+                               ws=ws)
+    for g, r in zip(got9, ref):
+        np.testing.assert_array_equal(g, r[:9])
+
+
+def test_accept_sampling_split_status_codes():
+    """Rejected trees leave every workgroup of their sequence before any
+    exchange; the others are unaffected."""
+    rng = np.random.default_rng(6)
+    trees = [[0, 0], [-1, 0, 1], [-1, 1], [-1], gi.kary_parents(2, 2)]
+    offsets, parents = _flat(trees)
+    V = 2048
+    T = len(parents)
+    P = _softmax(rng.standard_normal((T, V))).astype(np.float32)
+    Q = _softmax(rng.standard_normal((T, V))).astype(np.float32)
+    draft = rng.integers(0, V, T).astype(np.int32)
+    draft[offsets[1] + 2] = V
+    U = rng.random((T, 2)).astype(np.float32)
+    one = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, 4)
+    assert got[3].tolist() == [1, 7, 2, 0, 0]
+    for g, r in zip(got, one):
+        np.testing.assert_array_equal(g, r)
+
+
+def test_accept_sampling_split_grid_larger_than_the_device():
+    """More workgroups than the device holds at once (16 per sequence): some
+    wait for partners that are not resident yet, give up waiting and sum the
+    rows themselves; the results are still the one-workgroup call's."""
+    V = 5000
+    rng = np.random.default_rng(404)
+    trees = [gi.random_tree_parents(rng, 5, 30) for _ in range(40)]
+    offsets, parents, draft, P, Q = _sampling_case(rng, trees, V)
+    U = rng.random((len(parents), 2)).astype(np.float32)
+    # the device holds at most 16 * _max_splits(16) workgroups of this kernel
+    assert 16 * len(trees) > 16 * _max_splits(16), "the grid must exceed the device"
+    one = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, 16)
+    for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, one):
+        np.testing.assert_array_equal(g, r, err_msg=name)

@@ -38,6 +38,8 @@ def test_library_exports_every_declared_symbol():
                             "gdn_tree_fork_selective_workspace_bytes",
                             "gdn_tree_fork_selective_verify", "gdn_tree_fork_selective_commit",
                             "gdn_tree_accept_greedy", "gdn_tree_accept_sampling",
+                            "gdn_tree_accept_sampling_split_workspace_bytes",
+                            "gdn_tree_accept_sampling_splits", "gdn_tree_accept_sampling_split",
                             "gdn_round_plan",
                             "gdn_round_tree_for_budget", "gdn_round_capture",
                             "gdn_round_capture_replay",
@@ -45,6 +47,23 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_split_sampling_workspace_bytes():
+    """Per sequence two sets of [tile sums | q tile sums], one 64-bit word per
+    tile, the tiles of a row (256 tokens each) rounded up to 64; the total
+    rounded up to 256 bytes."""
+    lib = gt.load_library()
+    f = lambda B, V: lib.gdn_tree_accept_sampling_split_workspace_bytes(
+        ctypes.byref(gt.make_desc(B, 1, 128, 128, 4 * B, 8)), V)
+    up = lambda x: (x + 255) // 256 * 256
+    for B, V in ((1, 8), (64, 151936), (3, 1000), (128, 1 << 20)):
+        tiles = (V + 255) // 256
+        stride = (tiles + 63) // 64 * 64
+        assert f(B, V) == up(B * 4 * stride * 8), (B, V)
+    assert f(0, 1000) == 0 and f(4, 2) == 0
+    # with no GPU the device fits no split grid: one workgroup per sequence
+    assert lib.gdn_tree_accept_sampling_splits(ctypes.byref(gt.make_desc(64, 1, 128, 128, 64, 8))) >= 1
 
 
 def test_desc_layout_matches_header():
@@ -545,6 +564,17 @@ def test_accept_and_round_calls_check_before_launch():
     p[6] = None                                     # accepted
     assert samp(d3, 8, *p) == 1
     assert samp(gt.make_desc(0, 1, 128, 128, 0, 8), 8, *([None] * 10)) == 0
+    # the split form: the same checks, then the split count, before any launch
+    split = lambda desc, V, S, *p: lib.gdn_tree_accept_sampling_split(
+        ctypes.byref(desc), *p[:5], V, p[5], S, fake, ctypes.c_size_t(1 << 30), *p[6:], None)
+    for V in (0, 2, 6, (1 << 20) + 4):
+        assert split(d3, V, 2, *ok) == 3, V
+    p = list(ok)
+    p[4] = None                                     # draft_probs
+    assert split(d3, 8, 2, *p) == 1
+    for S in (-1, 17):
+        assert split(d3, 8, S, *ok) == 3, S
+    assert split(gt.make_desc(0, 1, 128, 128, 0, 8), 8, 4, *([None] * 10)) == 0
     # attention layer-batched commit
     ad = gt.make_attn_desc(2, 4, 2, 64, 10, 8, 32)
     assert lib.gdn_tree_attn_commit_layers(ctypes.byref(ad), 0, None, None, None, None, None,

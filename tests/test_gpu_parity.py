@@ -121,8 +121,11 @@ def test_c3_kary_tree():
 
 
 def test_c4_full_size_sampled():
-    """All 24 layers x 64 sequences on the GPU in the benchmark's launch
-    configuration; the oracle recomputes a sample of (layer, sequence) units."""
+    """Three sampled layers of the 24-layer, 64-sequence workload, each with
+    single-layer verify and commit calls on the full batch; the oracle
+    recomputes six sampled sequences of each. (The layer-batched launch the
+    benchmark times is checked in test_gpu_commit_verify.py and
+    test_gpu_layers.py.)"""
     w = gi.make_config("c4")
     rng = np.random.default_rng(40)
     layers = sorted(rng.choice(24, 3, replace=False).tolist())

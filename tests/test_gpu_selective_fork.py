@@ -192,3 +192,32 @@ def test_selective_fork_status_codes():
     x = [np.asarray(a[0], np.float64) for a in (sw.q, sw.k, sw.v, sw.alpha, sw.beta, sw.S0)]
     S_ref, _ = oracle.commit(sw.offsets, sw.parents, sw.accepted, *x[1:])
     assert rel_err_states(S_out.cpu().numpy()[keep], S_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d,io", [(32, "f32"), (64, "bf16"), (64, "f32"), (128, "f32")])
+def test_selective_fork_head_sizes_and_dtypes(d, io):
+    """The other head sizes and io dtypes, on ragged random trees and a deep
+    chain (depth 9), with a third of the confidences at or below the threshold:
+    outputs, saved checkpoints and commits against the oracle."""
+    rng = np.random.default_rng(200 + d + (1 if io == "f32" else 0))
+    trees = [gi.random_tree_parents(rng, 3, 40, max_depth=6) for _ in range(5)]
+    trees += [gi.chain_parents(10), [-1]]
+    w = gi.make_workload(trees, 3, d, d, io=io, seed=201 + d)
+    w.accepted[:] = [gi.pick_accepted(rng, t) for t in trees]
+    w.accepted[-1] = 0
+    conf = np.where(rng.random(w.T) < 1 / 3, rng.uniform(0.2, 0.95, w.T),
+                    rng.uniform(0.9501, 1.0, w.T)).astype(np.float32)
+    conf[w.offsets[:-1]] = 1.0
+    counts = _saved_counts(w, conf)
+    max_kept = max(max(counts), 1)
+    L = DeviceLayer(w, 0, max_nodes=64, max_depth=w.max_depth())
+    sel = Selective(L, conf, max_kept)
+    sel.verify()
+    S_out = torch.full_like(L.S0, float("nan"))
+    sel.commit(S_out)
+    torch.cuda.synchronize()
+    assert np.all(L.status.cpu().numpy() == 0)
+    e_o, e_ck, e_s = _check_against_oracle(w, conf, L, sel, S_out, list(range(w.B)), TOL[io])
+    _say(f"d={d} {io}: saved {sum(counts)} of {w.T}; o {e_o:.3e}, checkpoints {e_ck:.3e}, "
+         f"commit {e_s:.3e}")
+    assert e_o <= TOL[io] and e_ck <= TOL[io] and e_s <= TOL[io]

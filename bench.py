@@ -57,6 +57,7 @@ KERNEL_SOURCES = {"verify": ["wy_verify.hip", "device_common.h", "launch.h"],
                   "commit_verify": ["wy_verify.hip", "device_common.h", "launch.h"],
                   "replay_verify": ["wy_verify.hip", "device_common.h", "launch.h"],
                   "commit": ["wy_commit.hip", "device_common.h", "launch.h"],
+                  "replay_commit": ["wy_commit.hip", "device_common.h", "launch.h"],
                   "attn_verify": ["tree_attn.hip", "device_common.h", "launch.h",
                                   "tree_attn_api.cpp"]}
 
@@ -1019,7 +1020,36 @@ def main():
                    "achieved_GBs": round(cb / c_us / 1e3, 1),
                    "frac_hbm": round(cb / c_us / 1e3 / HBM_PEAK_GBS, 4)},
     }
-    for kind in ("verify", "commit"):
+    if batched and sep_steps > 0:
+        # the commit by replay alone (gdn_tree_replay_commit_layers, in place):
+        # the accepted path's gated delta rule steps from its own k, v,
+        # alpha, beta; no workspace
+        rc = gt.prepare_replay_commit_layers(
+            desc, offsets, parents, accepted,
+            [gt.make_layer_io(desc, k=ly["k"], v=ly["v"], alpha=ly["alpha"], beta=ly["beta"],
+                              S0=ly["S"], S_out=ly["S"]) for ly in layers], status, keep=(layers,))
+        for _ in range(args.warmup):
+            rc()
+        torch.cuda.synchronize()
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(sep_steps)]
+        for e0, e1 in rev:
+            e0.record()
+            rc()
+            e1.record()
+        torch.cuda.synchronize()
+        if np.any(status.cpu().numpy() != 0):
+            raise RuntimeError("nonzero status in the replay commit")
+        r_us = 1e3 * sum(a.elapsed_time(b) for a, b in rev) / sep_steps / L
+        path = sum(len(gi.path_to_root(p_, int(a_))) if a_ >= 0 else 0
+                   for p_, a_ in zip(w.parents_list, w.accepted))
+        rcb = (w.B * w.H * 2 * 4 * w.dv * w.dk + path * w.H * (io_bytes * (w.dk + w.dv) + 8)
+               + 4 * (2 * w.B + 1 + w.T))
+        kern["replay_commit"] = {"avg_us": round(r_us, 3), "alg_bytes": int(rcb),
+                                 "achieved_GBs": round(rcb / r_us / 1e3, 1),
+                                 "frac_hbm": round(rcb / r_us / 1e3 / HBM_PEAK_GBS, 4)}
+        del rc
+    for kind in [k_ for k_ in ("verify", "commit", "replay_commit") if k_ in kern]:
         t = recorded_traffic(kind, args.config) if args.mode == "wy" else None   # per layer
         k = kern[kind]
         k["layers_per_launch"] = lpl

@@ -510,24 +510,6 @@ void wy_verify_kernel(const Args args) {
   const int n = hi - lo;
   const int mt = (n + 15) >> 4;
 
-  // 1z. (fused commit) the previous round's node range and accepted node,
-  // and one lane per previous node: its parent and gate prefix.
-  PrevLane prv{0, 1, -1, GDN_TREE_OK, -1, 0.f, 1.f, 0.f};
-  const IO* __restrict__ pk = nullptr;
-  const IO* __restrict__ pv = nullptr;
-  const float* __restrict__ pU = nullptr;
-  float* __restrict__ S_out = nullptr;
-  if constexpr (kFused) {
-    const PendingLayer& pl = args.P[layer];
-    pk = static_cast<const IO*>(pl.k);
-    pv = static_cast<const IO*>(pl.v);
-    pU = pl.U;
-    S_out = pl.S_out;
-    prv = load_prev<kReplay>(args.prev, pl, b, h, H, lane);
-  }
-  const int plo = prv.lo, pacc = prv.acc;
-  const float pg2_raw = prv.g2_raw, palpha = prv.alpha, pbeta = prv.beta;
-
   // ---- 1. every global read of the workgroup, issued before any is used
   // (addresses clamped into the sequence, so the issue is unconditional).
   // 1a. parents and gates, one lane per node
@@ -553,6 +535,25 @@ void wy_verify_kernel(const Args args) {
     const int dd = mat == 2 ? DV : DK;
     stg[it] = *reinterpret_cast<const uint4*>(base + ((size_t)(lo + srow) * H + h) * dd + c * EPC);
   }
+  // 1c. (fused commit) the previous round's node range and accepted node,
+  // and one lane per previous node: its parent and gate prefix (or gates).
+  // Issued after the rows: nothing waits on these loads before the rows are
+  // in flight.
+  PrevLane prv{0, 1, -1, GDN_TREE_OK, -1, 0.f, 1.f, 0.f};
+  const IO* __restrict__ pk = nullptr;
+  const IO* __restrict__ pv = nullptr;
+  const float* __restrict__ pU = nullptr;
+  float* __restrict__ S_out = nullptr;
+  if constexpr (kFused) {
+    const PendingLayer& pl = args.P[layer];
+    pk = static_cast<const IO*>(pl.k);
+    pv = static_cast<const IO*>(pl.v);
+    pU = pl.U;
+    S_out = pl.S_out;
+    prv = load_prev<kReplay>(args.prev, pl, b, h, H, lane);
+  }
+  const int plo = prv.lo, pacc = prv.acc;
+  const float pg2_raw = prv.g2_raw, palpha = prv.alpha, pbeta = prv.beta;
   const bool owns = wave < DVT;                 // dv < 128: the last waves own no columns
   const int jt = owns ? wave : DVT - 1;
 

@@ -561,7 +561,8 @@ def sampling_accept_leg(args, gt, gi, w, offsets, parents, dev, V=151936):
     outs = [[torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(4)] for _ in range(2)]
     one = lambda: gt.gdn_tree_accept_sampling(desc, offsets, parents, draft, P, Q, U, *outs[0])
     splits = gt.gdn_tree_accept_sampling_splits(desc)
-    ws = torch.empty(max(1, gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V)),
+    # zero once: every call leaves the workspace zero
+    ws = torch.zeros(max(1, gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V)),
                      dtype=torch.uint8, device=dev)
     split = gt.prepare_accept_sampling_split(desc, offsets, parents, draft, P, Q, U, splits, ws,
                                              *outs[1])

@@ -1061,9 +1061,10 @@ def gdn_tree_accept_sampling_split(desc, offsets, parents, draft_tokens, target_
                                    draft_probs, uniforms, splits, workspace, accepted, accept_len,
                                    next_token, tree_status, stream=None):
     """gdn_tree_accept_sampling with every row pass spread over `splits`
-    workgroups per sequence (0: the device's pick); workspace: uint8 of
-    gdn_tree_accept_sampling_split_workspace_bytes(desc, V) bytes (None with
-    splits = 1)."""
+    workgroups per sequence (0: the device's pick; else 1, 2, 4, 8 or 16);
+    workspace: uint8 of gdn_tree_accept_sampling_split_workspace_bytes(desc, V)
+    bytes, all zero before its first use (every call leaves it zero), or
+    None with splits = 1."""
     torch = _torch()
     dev = offsets.device
     args = _sampling_split_args(desc, offsets, parents, draft_tokens, target_probs, draft_probs,

@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
 // CDF and the walk ends.
 //
 // One workgroup per sequence, or (split form) several, which divide every
-// pass over a node's rows by tiles and trade their tile sums after it. p_k and
+// pass over a node's rows by fixed groups of tiles and trade their group sums
+// after it. p_k and
 // q_k are never stored: for any token they follow from p(j), q(j) and the
 // per-stage scalars (1/Z_i, the rejected tokens, the renormalisation of q). A
 // rejection costs one pass over the node's two rows, which yields the
@@ -202,11 +203,14 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int span = tend - tbeg;
-  const int mine = wave < span ? (span - 1 - wave) / kSampleWaves + 1 : 0;
+  const int mine =
+      __builtin_amdgcn_readfirstlane(wave < span ? (span - 1 - wave) / kSampleWaves + 1 : 0);
   // p_0 needs no q: a draw with no rejection reads the target row alone
   constexpr bool need_q = WHAT == kResidual || K != 0 || kQSum;
-  // element offsets are clamped into the row (V >= 4), so that every load is
-  // issued unconditionally; tiles past the wave's last one are not summed
+  // element offsets are clamped into the row (V >= 4): the row's last tile
+  // may be partial; its tokens past the row are not summed. A slot is loaded
+  // only for a tile the wave has (a uniform branch): loads left in flight at
+  // the end of a pass would hold up the next wait on the load counter.
   auto off = [&](int i) {
     const int j = (tbeg + wave + i * kSampleWaves) * kTile + 4 * lane;
     return j < V - 4 ? j : V - 4;
@@ -214,24 +218,27 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
   float4 pv[W], qv[W];
 #pragma unroll
   for (int u = 0; u < W; ++u) {
-    pv[u] = *reinterpret_cast<const float4*>(prow + off(u));
-    qv[u] = need_q ? *reinterpret_cast<const float4*>(qrow + off(u))
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    pv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    qv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (u < mine) {
+      pv[u] = *reinterpret_cast<const float4*>(prow + off(u));
+      if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + off(u));
+    }
   }
   for (int i0 = 0; i0 < mine; i0 += W) {
 #pragma unroll
     for (int u = 0; u < W; ++u) {
       const int i = i0 + u;
+      if (i >= mine) break;             // the wave's tiles are done (uniform)
       const int t = tbeg + wave + i * kSampleWaves;
       const int j = t * kTile + 4 * lane;
-      const bool in_row = i < mine && j < V;
-      const float pe[4] = {in_row ? pv[u].x : 0.f, in_row ? pv[u].y : 0.f,
-                           in_row ? pv[u].z : 0.f, in_row ? pv[u].w : 0.f};
-      const float qe[4] = {in_row ? qv[u].x : 0.f, in_row ? qv[u].y : 0.f,
-                           in_row ? qv[u].z : 0.f, in_row ? qv[u].w : 0.f};
+      const float pe[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+      const float qe[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
       // the slot's next tile
-      pv[u] = *reinterpret_cast<const float4*>(prow + off(i + W));
-      if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + off(i + W));
+      if (i + W < mine) {
+        pv[u] = *reinterpret_cast<const float4*>(prow + off(i + W));
+        if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + off(i + W));
+      }
       float m = 0.f, qm = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -240,9 +247,15 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
         m += WHAT == kResidual ? fmaxf(pq.x - pq.y, 0.f) : pq.x;
         qm += qe[e];
       }
+      // a lane past the row's end (in its partial last tile) read clamped
+      // duplicates: it adds nothing (a lane's 4 tokens are all in or all out)
+      if (j >= V) {
+        m = 0.f;
+        qm = 0.f;
+      }
       m = wave_sum_lane63(m);
       if (kQSum) qm = wave_sum_lane63(qm);
-      if (lane == 63 && i < mine) {
+      if (lane == 63) {
         sTile[t] = m;
         if (kQSum) sQ[t] = qm;
       }
@@ -269,84 +282,148 @@ __device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
   }
 }
 
-// A sum over tiles [0, ntiles) of `v` (times `scale`) in a fixed order, by wave
-// 0: lane l adds its block of ceil(ntiles / 64) tiles in order, then the lanes
-// are added in DPP steps. Every lane of wave 0 gets the total.
-__device__ __forceinline__ float tiles_total(const float* v, int ntiles, float scale) {
+// The row's tiles fall into kGroups fixed groups, group g being tiles
+// [g * ntiles / kGroups, (g + 1) * ntiles / kGroups). Every total is taken over
+// the group sums in group order, and every group sum over its tiles in a fixed
+// order, so neither depends on how the tiles are divided among workgroups: a
+// workgroup of the split form takes whole groups.
+constexpr int kGroups = kSamplingGroups;
+static_assert(kGroups <= kSampleWaves, "one wave sums one group");
+
+__device__ __forceinline__ int group_begin(int g, int ntiles) { return g * ntiles / kGroups; }
+
+// Sum of v[t0, t1) by one wave in a fixed order: lane l adds its block of
+// ceil((t1 - t0) / 64) tiles in order, then the lanes are added in DPP steps.
+// Every lane gets the sum.
+__device__ __forceinline__ float wave_tiles_sum(const float* v, int t0, int t1) {
   const int lane = threadIdx.x & 63;
-  const int per = (ntiles + 63) / 64;
-  const int t0 = min(lane * per, ntiles), t1 = min(t0 + per, ntiles);
+  const int per = (t1 - t0 + 63) / 64;
+  const int lo = min(t0 + lane * per, t1), hi = min(lo + per, t1);
   float ls = 0.f;
-  for (int t = t0; t < t1; ++t) ls += v[t] * scale;
+  for (int t = lo; t < hi; ++t) ls += v[t];
   return wave_sum(ls);
 }
 
-// How long a workgroup of the split form waits for the others' tile sums
-// (polls, each after a short sleep; a poll takes about a microsecond) before
-// it sums every tile of the row itself. The sums are the same either way, so
-// the wait only costs time: with every workgroup resident it never runs out;
-// a workgroup that is not resident yet (the device busy with other work)
-// cannot hold the others up.
-constexpr unsigned kPatience = 256;
+// The total of the kGroups group sums, in group order.
+__device__ __forceinline__ float groups_total(const float* g) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kGroups; ++i) s += g[i];
+  return s;
+}
 
-// The split form's exchange after a pass over tiles [tbeg, tend). Every tile
-// sum travels as one 64-bit word, the value's bits in the low half and the
-// pass number (from 1) in the high half, written and read with single atomic
-// accesses at device scope (coherent across the XCDs' L2s): a reader that
-// sees the pass number sees the value, so no fence or counter is needed. Wave
-// 0 publishes this workgroup's tiles once the pass is done (stores issued
-// during the pass would share the load counter the pass waits on); then every
-// thread polls its share of all tiles of the row until each carries this
-// pass's number, and copies the values into sTile (and sQ). Each sequence has
-// two sets of words that alternate between passes. A word holds the value of
-// the pass its number names (every writer computes the same value), so a
-// workgroup that reads a word another one has already reused for a later pass
-// only sees a number that is not its pass's and keeps waiting, then sums the
-// tiles itself. The words are cleared before every call. Returns false if the
-// wait ran out.
-__device__ bool exchange_tiles(const AcceptSampleArgs& a, int b, int tbeg, int tend, int ntiles,
-                               bool with_q, unsigned& nsync, float* sTile, float* sQ) {
-  const int tid = threadIdx.x;
-  const unsigned long long tag = (unsigned long long)(nsync + 1u) << 32;
-  unsigned long long* words =
-      a.xch + ((size_t)b * 2 + (nsync & 1u)) * 2 * (size_t)a.xch_stride;
-  unsigned long long* qwords = words + a.xch_stride;
-  __syncthreads();                       // this workgroup's tiles are in LDS
-  if (tid < 64) {
-    for (int t = tbeg + tid; t < tend; t += 64) {
-      __hip_atomic_store(words + t, tag | __builtin_bit_cast(unsigned, sTile[t]),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (with_q)
-        __hip_atomic_store(qwords + t, tag | __builtin_bit_cast(unsigned, sQ[t]),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// How many of the other workgroups' words a workgroup of the split form reads
+// (four loads in flight per word, so one read ends about every quarter of a
+// memory round trip) before it sums every tile of the row itself. The sums are
+// the same either way, so the wait only costs time: with every workgroup
+// resident it never runs out; a workgroup that is not resident yet (the device
+// busy with other work) cannot hold the others up.
+constexpr unsigned kPatience = 1024;
+
+// The split form's exchange words of sequence b for pass number `pass` (from
+// 0): per sequence two sets of [group sums | q group sums] that alternate
+// between passes, one 64-bit word per group, the pass number (from 1) in the
+// high half and the value's bits in the low half. After every sequence's
+// words, one arrival count per sequence.
+constexpr int kSeqWords = 4 * kGroups;
+__device__ __forceinline__ unsigned long long* xch_words(const AcceptSampleArgs& a, int b,
+                                                         unsigned pass) {
+  return a.xch + (size_t)b * kSeqWords + (pass & 1u) * 2 * kGroups;
+}
+
+// The end of a split-form workgroup: it counts itself in, and the last of the
+// sequence's workgroups to arrive (all others are done reading and writing the
+// words) clears the words and the count, so that the next call finds them zero
+// without a clearing pass of its own. Before its workgroup counts in, every
+// wave waits until its own stores are acknowledged: the words are written
+// through to memory at device scope, so a word another workgroup published
+// cannot land after the clearing store. (A device-scope fence would also write
+// back and invalidate the L2 of the XCD, which the workgroups still walking
+// their rows there would pay for.)
+__device__ void seq_done(const AcceptSampleArgs& a, int b) {
+  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    unsigned long long* count = a.xch + (size_t)a.B * kSeqWords + b;
+    unsigned long long before = 0ull;
+    if (lane == 0)
+      before = __hip_atomic_fetch_add(count, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __shfl(before, 0, kWave);
+    if (before == (unsigned long long)(a.splits - 1)) {
+      static_assert(kSeqWords == 64, "one word per lane");
+      __hip_atomic_store(a.xch + (size_t)b * kSeqWords + lane, 0ull, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(count, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-  }
-  ++nsync;
-  for (unsigned polls = 0;; ++polls) {
-    int missing = 0;
-    for (int t = tid; t < ntiles; t += kSampleThreads) {
-      if (t >= tbeg && t < tend) continue;   // this workgroup's own
-      const unsigned long long w = __hip_atomic_load(words + t, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-      if ((w & ~0xffffffffull) == tag) sTile[t] = __builtin_bit_cast(float, (unsigned)w);
-      else missing = 1;
-      if (with_q) {
-        const unsigned long long u = __hip_atomic_load(qwords + t, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-        if ((u & ~0xffffffffull) == tag) sQ[t] = __builtin_bit_cast(float, (unsigned)u);
-        else missing = 1;
-      }
-    }
-    if (!__syncthreads_or(missing)) return true;
-    if (polls == kPatience) return false;
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 
+// The split form's exchange after a pass over groups [gbeg, gend), whose sums
+// this workgroup has published (each word written with a single atomic store
+// at device scope, coherent across the XCDs' L2s, by the wave that summed the
+// group). Wave 0 reads the other groups' words, one word per lane, keeping four
+// loads of each in flight until every word carries this pass's number: a
+// reader that sees the pass number sees the value, so no fence or counter is
+// needed. The values go to sG (and sGQ). A word holds the value of the pass
+// its number names (every writer computes the same value), so a workgroup that
+// reads a word another one has already reused for a later pass only sees a
+// number that is not its pass's and keeps waiting, then sums the row itself.
+// Every word is zero when a call starts: the last workgroup of a sequence to
+// finish clears the sequence's words (seq_done). Returns false (in every
+// thread) if the wait ran out.
+__device__ bool exchange_groups(const unsigned long long* words, unsigned long long tag,
+                                int gbeg, int gend, bool with_q, float* sG, float* sGQ) {
+  int missing = 0;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int g = lane & (kGroups - 1);
+    const bool isq = lane >= kGroups;
+    const bool wanted = lane < 2 * kGroups && (!isq || with_q) && (g < gbeg || g >= gend);
+    // every lane reads a word of the sequence (lanes that want none ignore it)
+    const unsigned long long* src = words + (isq ? kGroups : 0) + g;
+    auto load = [&]() {
+      return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    bool got = !wanted;
+    unsigned val = 0u;
+    unsigned long long w[4] = {load(), load(), load(), load()};
+    // one returned read: keep it if it is this pass's, and issue the next read
+    // into its register (the scheduling barrier keeps each read's wait and
+    // reissue in place, so four reads stay in flight); true once every lane
+    // has its word
+    auto take = [&](unsigned long long& x) {
+      const bool hit = !got && (x & ~0xffffffffull) == tag;
+      val = hit ? (unsigned)x : val;
+      got = got || hit;
+      x = load();
+      __builtin_amdgcn_sched_barrier(0);
+      return __ballot(!got) == 0ull;
+    };
+    // (sixteen reads per loop trip: only the first waits for all four)
+    bool done = false;
+    for (unsigned reads = 0; reads < kPatience && !done; reads += 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (take(w[i & 3])) {
+          done = true;
+          break;
+        }
+      }
+    }
+    if (wanted && got) (isq ? sGQ : sG)[g] = __builtin_bit_cast(float, val);
+    missing = !got;
+  }
+  return !__syncthreads_or(missing);
+}
+
 // One workgroup per sequence (kSplit false), or a.splits workgroups per
-// sequence, workgroup i taking part i % splits of sequence i / splits: every
-// workgroup of a sequence takes the same decisions (from the same sums in the
-// same order), and a pass over a node's rows is divided among them by tiles.
+// sequence (a divisor of kGroups), workgroup i taking part i % splits of
+// sequence i / splits and with it groups [part, part + 1) * kGroups / splits:
+// every workgroup of a sequence takes the same decisions (from the same sums in
+// the same order), and a pass over a node's rows is divided among them by
+// groups of tiles.
 template <bool kSplit>
 __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const AcceptSampleArgs a) {
   __shared__ int sPar[64];
@@ -357,8 +434,8 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
   __shared__ float sPX[64], sQX[64], sUX[64];   // candidates: p(x), q(x), uniform
   __shared__ float sTile[kMaxTiles];
   __shared__ float sQ[kMaxTiles];
-  __shared__ int sInfo[4];              // status, lo, n, decision / crossing tile
-  __shared__ float sF[2];               // crossing: mass before the tile, draw target
+  __shared__ float sG[kGroups], sGQ[kGroups];   // group sums of sTile, sQ
+  __shared__ int sInfo[3];              // status, lo, n
 
   // (the divisions by runtime values go through vector registers: their
   // uniform results are moved back to scalar ones)
@@ -397,34 +474,61 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
   }
   const int V = a.V;
   const int ntiles = (V + kTile - 1) / kTile;
-  const int tbeg = __builtin_amdgcn_readfirstlane(part * ntiles / S);
-  const int tend = __builtin_amdgcn_readfirstlane((part + 1) * ntiles / S);
-  unsigned nsync = 0;                   // exchanges passed (split form)
-  // A pass over this workgroup's tiles, then every tile's sums in sTile (sQ):
+  const int gbeg = part * (kGroups / S), gend = gbeg + kGroups / S;
+  unsigned nsync = 0;                   // passes exchanged (split form)
+  // The group sums of groups [g0, g1) from sTile (sQ) into sG (sGQ), one wave
+  // per group; with `words`, each is published as soon as it is summed.
+  auto group_sums = [&](int g0, int g1, bool with_q, unsigned long long* words,
+                        unsigned long long tag) {
+    if (wave < g1 - g0) {
+      const int g = g0 + wave;
+      const int t0 = group_begin(g, ntiles), t1 = group_begin(g + 1, ntiles);
+      const float gs = wave_tiles_sum(sTile, t0, t1);
+      const float gq = with_q ? wave_tiles_sum(sQ, t0, t1) : 0.f;
+      if (lane == 0) {
+        sG[g] = gs;
+        if (with_q) sGQ[g] = gq;
+        if (words != nullptr) {
+          __hip_atomic_store(words + g, tag | __builtin_bit_cast(unsigned, gs), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          if (with_q)
+            __hip_atomic_store(words + kGroups + g, tag | __builtin_bit_cast(unsigned, gq),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  };
+  // A pass over this workgroup's groups, then every group's sums in sG (sGQ):
   // from the others' words, or, if they do not come, from a second pass here
-  // over all tiles (the same call site, so the pass is inlined once).
+  // over every tile (the same call site, so the pass is inlined once).
   auto pass_all = [&](auto what, const float* prow, const float* qrow, const Stages& st,
                       bool with_q) {
-    int tb = tbeg, te = tend;
+    int g0 = gbeg, g1 = gend;
     for (;;) {
       tile_pass<decltype(what)::value, kSplit ? kSplitTilesInFlight : kTilesInFlight>(
-          prow, qrow, V, tb, te, st, sTile, sQ);
-      if (!kSplit || (tb == 0 && te == ntiles)) {
+          prow, qrow, V, group_begin(g0, ntiles), group_begin(g1, ntiles), st, sTile, sQ);
+      __syncthreads();                  // the pass's tile sums are in LDS
+      const bool whole = !kSplit || (g0 == 0 && g1 == kGroups);
+      unsigned long long* words = whole ? nullptr : xch_words(a, b, nsync);
+      const unsigned long long tag = (unsigned long long)(nsync + 1u) << 32;
+      group_sums(g0, g1, with_q, words, tag);
+      if (whole) {
         __syncthreads();
         return;
       }
-      if (exchange_tiles(a, b, tbeg, tend, ntiles, with_q, nsync, sTile, sQ)) return;
-      tb = 0;
-      te = ntiles;
+      ++nsync;
+      if (exchange_groups(words, tag, g0, g1, with_q, sG, sGQ)) return;
+      g0 = 0;
+      g1 = kGroups;
     }
   };
-  int cur = 0, len = 1, token = V - 1;
+  int cur = 0, len = 1;
   for (;;) {
     const float* __restrict__ prow = a.p + (size_t)(lo + cur) * V;
     const float* __restrict__ qrow = a.q + (size_t)(lo + cur) * V;
     Stages s{0, sRem, sZinv, sQscale};
     float qtot = 0.f, qrem = 0.f;
-    bool tiles_ready = false;             // sTile holds the current p's tile sums / Z
+    bool tiles_ready = false;             // sTile, sG hold the current p's sums / Z
     int next = -1;
     // every candidate's p(x), q(x) and uniform, one lane per child, in one
     // round trip when the walk enters the node
@@ -449,8 +553,8 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
       // (the first pass at a node also sums the row's q mass)
       pass_all(std::integral_constant<TileSum, kResidual>{}, prow, qrow, s, s.k == 0);
       if (wave == 0) {
-        const float z = tiles_total(sTile, ntiles, 1.f);
-        if (s.k == 0) qtot = tiles_total(sQ, ntiles, 1.f);
+        const float z = groups_total(sG);
+        if (s.k == 0) qtot = groups_total(sGQ);
         qrem += sQX[c];
         if (lane == 0) {
           sZinv[s.k] = z > 0.f ? 1.f / z : 0.f;
@@ -469,94 +573,103 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
       continue;
     }
     // final draw from p_k: tile sums (from the last rejection's pass, scaled,
-    // or from one pass over p), the crossing tile, then the token in it
+    // or from one pass over p); the group where the cumulative mass crosses u
+    // times the total, then (by the workgroup that summed that group, whose
+    // tile sums it holds) the tile, then the token in it
     float scale = 1.f;
     if (tiles_ready) {
       scale = sZinv[s.k - 1];
     } else {
       pass_all(std::integral_constant<TileSum, kTarget>{}, prow, qrow, s, false);
     }
-    if (wave == 0) {
-      // lane l owns tiles [l*per, (l+1)*per)
-      const int per = (ntiles + 63) / 64;
-      const int t0 = min(lane * per, ntiles), t1 = min(t0 + per, ntiles);
-      float ls = 0.f;
-      for (int t = t0; t < t1; ++t) ls += sTile[t] * scale;
-      float incl = ls;
+    if (wave != 0) break;
+    const float gv = lane < kGroups ? sG[lane] * scale : 0.f;
+    float gincl = gv;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += y;
-      }
-      const float total = __shfl(incl, 63, kWave);
-      const float target = a.u[2 * (size_t)(lo + cur) + 1] * total;
-      const uint64_t over = __ballot(incl > target && t1 > t0);
-      const int L = over ? __builtin_ctzll(over) : -1;
-      if (lane == (L < 0 ? 63 : L)) {
-        float run = incl - ls;
-        int tile = t1 > t0 ? t1 - 1 : ntiles - 1;
-        float before = run;
-        for (int t = t0; t < t1; ++t) {
-          if (run + sTile[t] * scale > target) {
-            tile = t;
-            before = run;
-            break;
-          }
-          run += sTile[t] * scale;
+    for (int off = 1; off < kGroups; off <<= 1) {
+      const float y = __shfl_up(gincl, off, kWave);
+      if (lane >= off) gincl += y;
+    }
+    const float total = __shfl(gincl, kGroups - 1, kWave);
+    const float target = a.u[2 * (size_t)(lo + cur) + 1] * total;
+    const uint64_t gover = __ballot(lane < kGroups && gincl > target);
+    const int G = gover ? __builtin_ctzll(gover) : kGroups - 1;
+    if (G < gbeg || G >= gend) break;     // another workgroup's group (uniform)
+    const float before_g = __shfl(gincl - gv, G, kWave);
+    // the tile: lane l owns the group's tiles [l*per, (l+1)*per)
+    const int gt0 = group_begin(G, ntiles), gt1 = group_begin(G + 1, ntiles);
+    const int per = (gt1 - gt0 + 63) / 64;
+    const int t0 = min(gt0 + lane * per, gt1), t1 = min(t0 + per, gt1);
+    float ls = 0.f;
+    for (int t = t0; t < t1; ++t) ls += sTile[t] * scale;
+    float incl = ls;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    incl += before_g;
+    const uint64_t over = __ballot(incl > target && t1 > t0);
+    const int L = over ? __builtin_ctzll(over) : 63;
+    // lane L walks its block: the crossing tile and the mass before it (with
+    // no crossing, the group's last tile and the mass through it)
+    int tile = gt1 - 1;
+    float before = incl;
+    if (lane == L) {
+      float run = incl - ls;
+      tile = t1 > t0 ? t1 - 1 : gt1 - 1;
+      before = run;
+      for (int t = t0; t < t1; ++t) {
+        if (run + sTile[t] * scale > target) {
+          tile = t;
           before = run;
+          break;
         }
-        sInfo[3] = tile;
-        sF[0] = before;
-        sF[1] = target;
+        run += sTile[t] * scale;
+        before = run;
       }
     }
-    __syncthreads();
-    if (wave == 0) {
-      const int tile = sInfo[3];
-      const float before = sF[0], target = sF[1];
-      const int j0 = tile * kTile + 4 * lane;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (j0 < V) {
-        const float4 p4 = *reinterpret_cast<const float4*>(prow + j0);
-        const float4 q4 = *reinterpret_cast<const float4*>(qrow + j0);
-        v[0] = stage_pq(p4.x, q4.x, j0, s).x;
-        v[1] = stage_pq(p4.y, q4.y, j0 + 1, s).x;
-        v[2] = stage_pq(p4.z, q4.z, j0 + 2, s).x;
-        v[3] = stage_pq(p4.w, q4.w, j0 + 3, s).x;
-      }
-      const float ls = v[0] + v[1] + v[2] + v[3];
-      float incl = ls;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += y;
-      }
-      float run = before + incl - ls;
-      int hit = -1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        run += v[e];
-        if (hit < 0 && j0 + e < V && run > target) hit = j0 + e;
-      }
-      const uint64_t any = __ballot(hit >= 0);
-      const int first = any ? __builtin_ctzll(any) : -1;
-      const int hit_first = __shfl(hit, first < 0 ? 0 : first, kWave);
-      if (lane == 0) token = first >= 0 ? hit_first : min(tile * kTile + kTile, V) - 1;
+    tile = __shfl(tile, L, kWave);
+    before = __shfl(before, L, kWave);
+    // the token: the first whose cumulative mass exceeds the target (with
+    // none, the tile's last token)
+    const int j0 = tile * kTile + 4 * lane;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (j0 < V) {
+      const float4 p4 = *reinterpret_cast<const float4*>(prow + j0);
+      const float4 q4 = *reinterpret_cast<const float4*>(qrow + j0);
+      v[0] = stage_pq(p4.x, q4.x, j0, s).x;
+      v[1] = stage_pq(p4.y, q4.y, j0 + 1, s).x;
+      v[2] = stage_pq(p4.z, q4.z, j0 + 2, s).x;
+      v[3] = stage_pq(p4.w, q4.w, j0 + 3, s).x;
     }
+    const float vs = v[0] + v[1] + v[2] + v[3];
+    float vincl = vs;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(vincl, off, kWave);
+      if (lane >= off) vincl += y;
+    }
+    float run = before + vincl - vs;
+    int hit = -1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      run += v[e];
+      if (hit < 0 && j0 + e < V && run > target) hit = j0 + e;
+    }
+    const uint64_t any = __ballot(hit >= 0);
+    const int first = any ? __builtin_ctzll(any) : -1;
+    const int hit_first = __shfl(hit, first < 0 ? 0 : first, kWave);
+    if (lane == 0) a.next_token[b] = first >= 0 ? hit_first : min(tile * kTile + kTile, V) - 1;
     break;
   }
+  // (next_token is written by the workgroup that drew it)
   if (part == 0 && tid == 0) {
     a.status[b] = GDN_TREE_OK;
     a.accepted[b] = cur;
     a.accept_len[b] = len;
-    a.next_token[b] = token;
   }
-}
-
-// The split form's exchange words start every call at pass number 0 (none).
-__global__ __launch_bounds__(256) void sampling_xch_clear_kernel(const AcceptSampleArgs a) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < (size_t)a.B * 4 * a.xch_stride) a.xch[i] = 0ull;
+  if constexpr (kSplit) seq_done(a, b);
 }
 
 }  // namespace
@@ -578,10 +691,6 @@ int accept_sampling_split_capacity() {
 }
 
 hipError_t launch_accept_sampling_split(const AcceptSampleArgs& a, hipStream_t s) {
-  const size_t words = (size_t)a.B * 4 * a.xch_stride;
-  const hipError_t e = launch_kernel(reinterpret_cast<const void*>(&sampling_xch_clear_kernel),
-                                     (unsigned)((words + 255) / 256), 256u, s, a);
-  if (e != hipSuccess) return e;
   return launch_kernel(reinterpret_cast<const void*>(&accept_sampling_kernel<true>),
                        (unsigned)(a.B * a.splits), (unsigned)kSampleThreads, s, a);
 }

@@ -174,12 +174,13 @@ struct AcceptSampleArgs {
   int32_t* accept_len;
   int32_t* next_token;
   int32_t* status;
-  // split form: `splits` workgroups per sequence trade tile sums through
-  // xch (per sequence, two alternating sets of [tile sums | q tile sums],
-  // xch_stride 64-bit words each: the pass number above the value's bits)
+  // split form: `splits` workgroups per sequence (a divisor of
+  // kSamplingGroups) trade group sums through xch (per sequence, two
+  // alternating sets of [group sums | q group sums], kSamplingGroups 64-bit
+  // words each: the pass number above the value's bits; then one arrival
+  // count per sequence), all zero between calls
   int splits = 1;
   unsigned long long* xch = nullptr;
-  int xch_stride = 0;
 };
 
 // Greedy acceptance of the verified trees.
@@ -355,6 +356,7 @@ hipError_t launch_accept_sampling_split(const AcceptSampleArgs& a, hipStream_t s
 // workgroups of the split kernel that fit on the current device at once
 int accept_sampling_split_capacity();
 constexpr int kSamplingTile = 256;            // tokens per tile of a row pass
+constexpr int kSamplingGroups = 16;           // fixed groups of tiles per row
 
 // Kernel launch that reports its own error (no reliance on the sticky
 // last-error state, which other libraries in the process also use).

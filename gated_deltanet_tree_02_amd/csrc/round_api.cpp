@@ -203,10 +203,13 @@ gdn_status check_sampling(const gdn_tree_desc* desc, const int32_t* offsets,
   return GDN_OK;
 }
 
-// Tiles of a row rounded up to 64, the floats of one exchange buffer.
-size_t sampling_xch_stride(int32_t vocab) {
-  const size_t tiles = ((size_t)vocab + gdn::kSamplingTile - 1) / gdn::kSamplingTile;
-  return (tiles + 63) / 64 * 64;
+static_assert(gdn::kSamplingGroups == GDN_SAMPLING_MAX_SPLITS,
+              "every workgroup of the split form takes whole groups of tiles");
+
+// A split count the group layout supports: a power of two dividing the group
+// count.
+bool valid_splits(int32_t splits) {
+  return splits >= 1 && splits <= gdn::kSamplingGroups && (splits & (splits - 1)) == 0;
 }
 
 
@@ -232,16 +235,19 @@ gdn_status gdn_tree_accept_sampling(const gdn_tree_desc* desc, const int32_t* of
 
 size_t gdn_tree_accept_sampling_split_workspace_bytes(const gdn_tree_desc* desc, int32_t vocab) {
   if (desc == nullptr || desc->num_seqs <= 0 || vocab < 4 || vocab > (1 << 20)) return 0;
-  // per sequence two sets of [tile sums | q tile sums], one 64-bit word per tile
-  return round_up((size_t)desc->num_seqs * 4 * sampling_xch_stride(vocab) * 8);
+  // per sequence two sets of [group sums | q group sums], one 64-bit word
+  // each, and an arrival count
+  return round_up((size_t)desc->num_seqs * (4 * gdn::kSamplingGroups + 1) * 8);
 }
 
 int32_t gdn_tree_accept_sampling_splits(const gdn_tree_desc* desc) {
   if (desc == nullptr || desc->num_seqs <= 0) return 1;
   const int cap = gdn::accept_sampling_split_capacity();
-  int splits = cap / desc->num_seqs;
-  if (splits > GDN_SAMPLING_MAX_SPLITS) splits = GDN_SAMPLING_MAX_SPLITS;
-  return splits < 1 ? 1 : splits;
+  // the largest power of two up to GDN_SAMPLING_MAX_SPLITS within cap / B
+  const int fit = cap / desc->num_seqs;
+  int splits = 1;
+  while (splits * 2 <= fit && splits * 2 <= GDN_SAMPLING_MAX_SPLITS) splits *= 2;
+  return splits;
 }
 
 gdn_status gdn_tree_accept_sampling_split(const gdn_tree_desc* desc, const int32_t* offsets,
@@ -256,7 +262,7 @@ gdn_status gdn_tree_accept_sampling_split(const gdn_tree_desc* desc, const int32
                                        draft_probs, vocab, uniforms, accepted, accept_len,
                                        next_token, tree_status);
   if (st != GDN_OK || desc->num_seqs == 0) return st;
-  if (splits < 0 || splits > GDN_SAMPLING_MAX_SPLITS) return GDN_ERR_UNSUPPORTED;
+  if (splits != 0 && !valid_splits(splits)) return GDN_ERR_UNSUPPORTED;
   if (splits == 0) splits = gdn_tree_accept_sampling_splits(desc);
   if (splits == 1)
     return gdn_tree_accept_sampling(desc, offsets, parents, draft_tokens, target_probs,
@@ -271,7 +277,6 @@ gdn_status gdn_tree_accept_sampling_split(const gdn_tree_desc* desc, const int32
                           accepted, accept_len, next_token, tree_status};
   a.splits = splits;
   a.xch = static_cast<unsigned long long*>(workspace);
-  a.xch_stride = (int)sampling_xch_stride(vocab);
   return gdn::launch_accept_sampling_split(a, static_cast<hipStream_t>(stream)) == hipSuccess
              ? GDN_OK
              : GDN_ERR_LAUNCH;

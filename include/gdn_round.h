@@ -95,27 +95,34 @@ gdn_status gdn_tree_accept_sampling(const gdn_tree_desc* desc, const int32_t* of
 /* The same acceptance with every pass over a node's rows spread over `splits`
  * workgroups per sequence, for batches too small to fill the device with one
  * workgroup per sequence. The decisions are the same, bit for bit, as
- * gdn_tree_accept_sampling's: the tile sums and their fixed-order totals do not
- * depend on how the tiles are divided. After each pass the workgroups of a
- * sequence trade their tile sums through `workspace`; a workgroup that waits
- * too long for the others (none is ever required to be resident at the same
- * time) sums the whole row itself, with the same result, so the call always
- * completes.
- *   splits     workgroups per sequence, 1..GDN_SAMPLING_MAX_SPLITS, or 0 for
+ * gdn_tree_accept_sampling's: both calls cut a row's 256-token tiles into
+ * GDN_SAMPLING_MAX_SPLITS fixed groups and take every total over the group
+ * sums in group order, each group sum over its tiles in a fixed order, so no
+ * sum depends on how the groups are divided. After each pass the workgroups
+ * of a sequence trade their group sums through `workspace`; a workgroup that
+ * waits too long for the others (none is ever required to be resident at the
+ * same time) sums the whole row itself, with the same result, so the call
+ * always completes.
+ *   splits     workgroups per sequence: 1, 2, 4, 8 or 16 (each takes whole
+ *              groups; GDN_ERR_UNSUPPORTED otherwise), or 0 for
  *              gdn_tree_accept_sampling_splits(desc) (the most whose grid
  *              the device holds at once; a larger grid is correct but slower)
  *   workspace  device memory of at least
- *              gdn_tree_accept_sampling_split_workspace_bytes(desc, vocab) bytes,
- *              256-byte aligned, owned by the caller; its contents need no
- *              preparation (the call clears what it uses with a kernel of its
- *              own, enqueued first), and two calls in flight at once must not
- *              share it
+ *              gdn_tree_accept_sampling_split_workspace_bytes(desc, vocab) bytes
+ *              (520 per sequence), 256-byte aligned, owned by the caller, all
+ *              zero before its first use (hipMemset once); every call that
+ *              runs leaves the part it used zero again (the last workgroup of
+ *              each sequence to finish clears it), so the workspace is reused
+ *              with no preparation and no clearing launch. Two calls in flight
+ *              at once must not share it, and a workspace with other contents
+ *              may give wrong results
  * Other arguments, checks and status codes as for gdn_tree_accept_sampling.
  * splits = 1 is that call (the workspace is not used and may be NULL). */
 #define GDN_SAMPLING_MAX_SPLITS 16
 size_t gdn_tree_accept_sampling_split_workspace_bytes(const gdn_tree_desc* desc, int32_t vocab);
-/* The splits that `splits = 0` picks on the current device: the most (up to
- * GDN_SAMPLING_MAX_SPLITS) whose grid is resident at once, at least 1. */
+/* The splits that `splits = 0` picks on the current device: the largest power
+ * of two up to GDN_SAMPLING_MAX_SPLITS whose grid is resident at once, at
+ * least 1. */
 int32_t gdn_tree_accept_sampling_splits(const gdn_tree_desc* desc);
 gdn_status gdn_tree_accept_sampling_split(const gdn_tree_desc* desc, const int32_t* offsets,
                                           const int32_t* parents, const int32_t* draft_tokens,

@@ -622,11 +622,14 @@ def _sampling_split_gpu(offsets, parents, draft, P, Q, U, splits, ws=None, max_n
     desc = gt.make_desc(B, 1, 128, 128, T, max_nodes)
     V = P.shape[1]
     if ws is None:
-        ws = nan_bytes(gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V))
+        ws = torch.zeros(gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V),
+                         dtype=torch.uint8, device="cuda")
     outs = [torch.full((B,), -9, dtype=torch.int32, device="cuda") for _ in range(4)]
     gt.gdn_tree_accept_sampling_split(desc, i32(offsets), i32(parents), i32(draft), f32(P),
                                       f32(Q), f32(U), splits, ws, *outs)
     torch.cuda.synchronize()
+    # the call leaves the workspace as it found it: all zero
+    assert int(torch.count_nonzero(ws)) == 0, "workspace not cleared"
     return [o.cpu().numpy() for o in outs]
 
 
@@ -636,10 +639,11 @@ def _max_splits(B):
 
 @pytest.mark.parametrize("V", [8, 1000, 5000, 151936])
 def test_accept_sampling_split_is_the_one_workgroup_call_bit_for_bit(V):
-    """Every split of the row passes (2 .. as many as fit, tile counts that do
-    not divide evenly, more parts than tiles at V = 8) gives the accepted
-    node, length, drawn token and status of the one-workgroup call exactly,
-    on uniforms drawn without regard to the decision margins."""
+    """Every split of the row passes (2 .. as many as fit; groups of tiles of
+    unequal sizes, and at V = 8 one tile, so that all but one workgroup own
+    only empty groups) gives the accepted node, length, drawn token and
+    status of the one-workgroup call exactly, on uniforms drawn without
+    regard to the decision margins."""
     rng = np.random.default_rng(100 + V)
     if V > 10000:
         trees = [gi.kary_parents(3, 3)] * 5 + [gi.random_tree_parents(rng, 4, 24)] * 3
@@ -651,11 +655,15 @@ def test_accept_sampling_split_is_the_one_workgroup_call_bit_for_bit(V):
     one = _sampling_gpu(offsets, parents, draft, P, Q, U)
     top = _max_splits(len(trees))
     assert top >= 2, top
-    for S in sorted({2, 3, 4, 7, top}):
+    # one workspace for every split count: each call leaves it zero
+    ws = torch.zeros(gt.gdn_tree_accept_sampling_split_workspace_bytes(
+        gt.make_desc(len(trees), 1, 128, 128, len(parents), 64), V), dtype=torch.uint8,
+        device="cuda")
+    for S in sorted({2, 4, 8, 16, top}):
         if S > top:
             continue
         _say(f"split sampling V={V} splits={S}")
-        got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, S)
+        got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, S, ws=ws)
         for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, one):
             np.testing.assert_array_equal(g, r, err_msg=f"{name} splits={S}")
     assert (one[3] == 0).all()
@@ -671,7 +679,8 @@ def test_accept_sampling_split_full_size_against_the_oracle():
     offsets, parents, draft, P, Q = _sampling_case(rng, trees, V)
     U = _uniforms_clear_per_sequence(rng, offsets, parents, draft, P, Q)
     desc = gt.make_desc(16, 1, 128, 128, len(parents), 64)
-    ws = nan_bytes(gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V))
+    ws = torch.zeros(gt.gdn_tree_accept_sampling_split_workspace_bytes(desc, V),
+                     dtype=torch.uint8, device="cuda")
     _say("split sampling full size, splits", gt.gdn_tree_accept_sampling_splits(desc))
     got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, 0, ws=ws)
     ref = oacc.accept_sampling(offsets, parents, draft, P, Q, U)

@@ -50,17 +50,15 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_split_sampling_workspace_bytes():
-    """Per sequence two sets of [tile sums | q tile sums], one 64-bit word per
-    tile, the tiles of a row (256 tokens each) rounded up to 64; the total
-    rounded up to 256 bytes."""
+    """Per sequence two sets of [group sums | q group sums], one 64-bit word
+    for each of the 16 groups of tiles, whatever the vocabulary, and a 64-bit
+    arrival count; the total rounded up to 256 bytes."""
     lib = gt.load_library()
     f = lambda B, V: lib.gdn_tree_accept_sampling_split_workspace_bytes(
         ctypes.byref(gt.make_desc(B, 1, 128, 128, 4 * B, 8)), V)
     up = lambda x: (x + 255) // 256 * 256
     for B, V in ((1, 8), (64, 151936), (3, 1000), (128, 1 << 20)):
-        tiles = (V + 255) // 256
-        stride = (tiles + 63) // 64 * 64
-        assert f(B, V) == up(B * 4 * stride * 8), (B, V)
+        assert f(B, V) == up(B * (4 * 16 + 1) * 8), (B, V)
     assert f(0, 1000) == 0 and f(4, 2) == 0
     # with no GPU the device fits no split grid: one workgroup per sequence
     assert lib.gdn_tree_accept_sampling_splits(ctypes.byref(gt.make_desc(64, 1, 128, 128, 64, 8))) >= 1
@@ -572,7 +570,8 @@ def test_accept_and_round_calls_check_before_launch():
     p = list(ok)
     p[4] = None                                     # draft_probs
     assert split(d3, 8, 2, *p) == 1
-    for S in (-1, 17):
+    # a split count must divide the 16 groups of tiles
+    for S in (-1, 3, 5, 6, 12, 17, 32):
         assert split(d3, 8, S, *ok) == 3, S
     assert split(gt.make_desc(0, 1, 128, 128, 0, 8), 8, 4, *([None] * 10)) == 0
     # attention layer-batched commit

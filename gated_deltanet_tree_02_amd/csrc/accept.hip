@@ -68,21 +68,32 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
 // rows; when no candidate is accepted, one token is drawn from p_k by inverse
 // CDF and the walk ends.
 //
+// p_k and q_k are never stored. After k rejections at a node they have a
+// closed form in the row values p(j), q(j) and a few per-stage scalars:
+//   p_k(j) = max(0, p(j) - L_k(j) q(j)) / U_k,   q_k(j) = s_k q(j) or 0,
+// with L_k(j) = lam_k and q_k(j) = s_k q(j) for a token not rejected yet, and
+// L_k(j) = lam_{m+1}, q_k(j) = 0 for the token x_m rejected at stage m; s_k
+// renormalises q over the tokens left, lam_0 = 0 and U_0 = 1. It follows by
+// induction from max(0, max(0, a) / c - b) = max(0, a - b c) / c (c > 0,
+// b >= 0): rejecting x_k leaves the residual max(0, p_k - q_k) =
+// max(0, p - lam' q) / U_k with lam' = lam_k + s_k U_k on the tokens not
+// rejected before (x_k among them), and p_k itself on the others; so
+// lam_{k+1} = lam' and U_{k+1} = U', the sum of the numerators, when U' > 0,
+// and nothing changes when the residual has no mass. A pass over a node's rows
+// therefore costs the same few operations per token at every stage: a
+// rejection sums the numerators max(0, p - lam' q) tile by tile (the first one
+// at a node also the row's q mass), and each tile holding an earlier rejected
+// token is then corrected for that token alone. Those tile sums are the
+// numerators of the next p, so a final draw after a rejection needs no further
+// pass (a draw with no rejection at the node takes one pass over p).
+//
 // One workgroup per sequence, or (split form) several, which divide every
 // pass over a node's rows by fixed groups of tiles and trade their group sums
-// after it. p_k and
-// q_k are never stored: for any token they follow from p(j), q(j) and the
-// per-stage scalars (1/Z_i, the rejected tokens, the renormalisation of q). A
-// rejection costs one pass over the node's two rows, which yields the
-// normaliser Z as a sum of per-tile sums of max(0, p_k - q_k) (the first one
-// at a node also the row's q mass, per tile); those tile sums, scaled by 1/Z,
-// are the tile sums of the next p, so a final draw after a rejection needs no
-// further pass (a draw with no rejection at the node takes one pass over p).
-// The draw then finds the tile where the cumulative mass crosses the target
-// and re-reads that tile alone. Each wave works on whole 256-token tiles and
-// keeps kTilesInFlight tiles' loads in flight. Decisions are taken in fp32;
-// totals run over the tile sums in a fixed order, so they do not depend on how
-// the tiles were divided.
+// after it. The draw finds the group, then the tile where the cumulative mass
+// crosses the target, and re-reads that tile alone. Each wave works on whole
+// 256-token tiles and keeps kTilesInFlight tiles' loads in flight. Decisions
+// are taken in fp32; totals run over group sums in a fixed order, so they do
+// not depend on how the tiles were divided.
 
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / 64;
@@ -94,68 +105,36 @@ constexpr int kTilesInFlight = 4;
 constexpr int kSplitTilesInFlight = 5;
 constexpr int kMaxTiles = (1 << 20) / kTile;     // vocabularies up to 2^20 tokens
 
+// The stage after k rejections at the current node (in LDS, but u).
 struct Stages {
   int k;                  // rejections so far at this node
   const int* rem;         // rejected tokens x_0 .. x_{k-1}
-  const float* zinv;      // 1 / Z_{i+1}, or 0 when that residual had no mass
-  const float* qscale;    // q_i = q restricted to tokens not in x_0..x_{i-1}, times qscale[i]
+  const float* lam;       // lam_0 .. lam_k
+  const float* qscale;    // s_0 .. s_k
+  float u;                // U_k
 };
 
-__device__ __forceinline__ bool removed(int j, const int* rem, int upto) {
-  bool r = false;
-  for (int i = 0; i < upto; ++i) r |= rem[i] == j;
-  return r;
-}
-
-// (p_k(j), q_k(j)) from the row values p(j), q(j)
-__device__ __forceinline__ float2 stage_pq(float pj, float qj, int j, const Stages& s) {
-  float pk = pj;
-  for (int i = 0; i < s.k; ++i) {
-    const float qi = removed(j, s.rem, i) ? 0.f : qj * s.qscale[i];
-    if (s.zinv[i] > 0.f) pk = fmaxf(pk - qi, 0.f) * s.zinv[i];
-  }
-  const float qk = removed(j, s.rem, s.k) ? 0.f : qj * s.qscale[s.k];
-  return make_float2(pk, qk);
-}
-
-// The same for exactly K stages, their scalars in scalar registers: a pass
-// evaluates it for every token of a row. A token is in the removed set of
-// stage i when it is one of x_0 .. x_{i-1}.
-template <int K>
-struct StageRegs {
-  int rem[K > 0 ? K : 1];
-  float zinv[K > 0 ? K : 1];
-  float qscale[K + 1];
-};
-
+// A value every lane holds alike, moved to a scalar register.
 __device__ __forceinline__ float uniform_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
-template <int K>
-__device__ __forceinline__ StageRegs<K> stage_regs(const Stages& s) {
-  StageRegs<K> r;
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    r.rem[i] = __builtin_amdgcn_readfirstlane(s.rem[i]);
-    r.zinv[i] = uniform_f(s.zinv[i]);
-  }
-#pragma unroll
-  for (int i = 0; i <= K; ++i) r.qscale[i] = uniform_f(s.qscale[i]);
-  return r;
+// Index of the first rejection of token j among x_0 .. x_{upto-1}, else -1.
+__device__ __forceinline__ int rejected_at(int j, const int* rem, int upto) {
+  int at = -1;
+  for (int i = upto - 1; i >= 0; --i)
+    if (rem[i] == j) at = i;
+  return at;
 }
 
-template <int K>
-__device__ __forceinline__ float2 stage_pq_reg(float pj, float qj, int j, const StageRegs<K>& r) {
-  float pk = pj;
-  bool gone = false;          // j in the removed set of the stage at hand
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    const float qi = gone ? 0.f : qj * r.qscale[i];
-    if (r.zinv[i] > 0.f) pk = fmaxf(pk - qi, 0.f) * r.zinv[i];
-    gone |= j == r.rem[i];
-  }
-  return make_float2(pk, gone ? 0.f : qj * r.qscale[K]);
+// (U_k p_k(j), q_k(j)) from the row values p(j), q(j). With lam = 0 the
+// target is p itself, whatever q holds (a leaf's draft row is never read as a
+// distribution).
+__device__ __forceinline__ float2 stage_pq(float pj, float qj, int j, const Stages& s) {
+  const int m = rejected_at(j, s.rem, s.k);
+  const float lam = m < 0 ? s.lam[s.k] : s.lam[m + 1];
+  return make_float2(lam != 0.f ? fmaxf(fmaf(-lam, qj, pj), 0.f) : pj,
+                     m < 0 ? qj * s.qscale[s.k] : 0.f);
 }
 
 // Sum over the 64 lanes of a wave in DPP steps, with no LDS traffic: an
@@ -184,29 +163,24 @@ __device__ __forceinline__ float wave_sum(float x) {
       float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_lane63(x)), 63));
 }
 
-// What a tile pass sums per token.
-enum TileSum { kResidual, kTarget };
-
-// One pass over tiles [tbeg, tend) of a node's rows: sTile[t] = sum over tile t
-// of max(0, p_k - q_k) (kResidual) or of p_k (kTarget), and with kQSum sQ[t] =
-// the tile's q mass. Wave w takes tiles tbeg + w, tbeg + w + waves, ... through
-// a ring of kTilesInFlight tiles: a tile's slot is refilled with the wave's
-// next-but-(kTilesInFlight - 1) tile as soon as it is summed, so every wave
-// keeps that many tiles' loads in flight for the whole pass. K >= 0: exactly
-// K rejections so far, the stage scalars in registers; K < 0: any number, read
-// from LDS. A tile's sums are the same whichever workgroup takes it.
-template <TileSum WHAT, int K, bool kQSum, int W>
-__device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
-                                            const float* __restrict__ qrow, int V, int tbeg,
-                                            int tend, const Stages& s, float* sTile, float* sQ) {
-  const StageRegs<K < 0 ? 0 : K> r = stage_regs<K < 0 ? 0 : K>(s);
+// One pass over tiles [tbeg, tend) of a node's rows: sTile[t] = sum over tile
+// t of max(0, p(j) - lam q(j)) (every token taken as not rejected), and with
+// kQSum sQ[t] = the tile's q mass; kNeedQ false reads the target row alone
+// (lam = 0). Wave w takes tiles tbeg + w, tbeg + w + waves, ... through a ring
+// of W tiles: a tile's slot is refilled with the wave's next-but-(W - 1) tile
+// as soon as it is summed, so every wave keeps that many tiles' loads in
+// flight for the whole pass. A tile's sums are the same whichever workgroup
+// takes it.
+template <bool kQSum, bool kNeedQ, int W>
+__device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
+                                          const float* __restrict__ qrow, int V, int tbeg,
+                                          int tend, float lam, float* sTile, float* sQ) {
+  static_assert(kNeedQ || !kQSum, "the q mass needs the q row");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int span = tend - tbeg;
   const int mine =
       __builtin_amdgcn_readfirstlane(wave < span ? (span - 1 - wave) / kSampleWaves + 1 : 0);
-  // p_0 needs no q: a draw with no rejection reads the target row alone
-  constexpr bool need_q = WHAT == kResidual || K != 0 || kQSum;
   // element offsets are clamped into the row (V >= 4): the row's last tile
   // may be partial; its tokens past the row are not summed. A slot is loaded
   // only for a tile the wave has (a uniform branch): loads left in flight at
@@ -222,7 +196,7 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
     qv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (u < mine) {
       pv[u] = *reinterpret_cast<const float4*>(prow + off(u));
-      if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + off(u));
+      if (kNeedQ) qv[u] = *reinterpret_cast<const float4*>(qrow + off(u));
     }
   }
   for (int i0 = 0; i0 < mine; i0 += W) {
@@ -237,14 +211,12 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
       // the slot's next tile
       if (i + W < mine) {
         pv[u] = *reinterpret_cast<const float4*>(prow + off(i + W));
-        if (need_q) qv[u] = *reinterpret_cast<const float4*>(qrow + off(i + W));
+        if (kNeedQ) qv[u] = *reinterpret_cast<const float4*>(qrow + off(i + W));
       }
       float m = 0.f, qm = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float2 pq = K >= 0 ? stage_pq_reg<K < 0 ? 0 : K>(pe[e], qe[e], j + e, r)
-                                 : stage_pq(pe[e], qe[e], j + e, s);
-        m += WHAT == kResidual ? fmaxf(pq.x - pq.y, 0.f) : pq.x;
+        m += kNeedQ ? fmaxf(fmaf(-lam, qe[e], pe[e]), 0.f) : pe[e];
         qm += qe[e];
       }
       // a lane past the row's end (in its partial last tile) read clamped
@@ -260,25 +232,6 @@ __device__ __forceinline__ void tile_pass_t(const float* __restrict__ prow,
         if (kQSum) sQ[t] = qm;
       }
     }
-  }
-}
-
-template <TileSum WHAT, int W>
-__device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
-                                          const float* __restrict__ qrow, int V, int tbeg,
-                                          int tend, const Stages& s, float* sTile, float* sQ) {
-  switch (s.k) {
-    // the first rejection's pass also gives the q mass of the row, per tile
-    case 0:
-      if constexpr (WHAT == kResidual)
-        return tile_pass_t<WHAT, 0, true, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
-      else
-        return tile_pass_t<WHAT, 0, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
-    case 1: return tile_pass_t<WHAT, 1, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
-    case 2: return tile_pass_t<WHAT, 2, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
-    case 3: return tile_pass_t<WHAT, 3, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
-    case 4: return tile_pass_t<WHAT, 4, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
-    default: return tile_pass_t<WHAT, -1, false, W>(prow, qrow, V, tbeg, tend, s, sTile, sQ);
   }
 }
 
@@ -428,9 +381,11 @@ template <bool kSplit>
 __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const AcceptSampleArgs a) {
   __shared__ int sPar[64];
   __shared__ int sTok[64];
-  __shared__ int sRem[64];
-  __shared__ float sZinv[64];
-  __shared__ float sQscale[65];
+  __shared__ int sRem[64];              // rejected tokens of the current node
+  __shared__ float sRemP[64], sRemQ[64];  // their p and q
+  __shared__ float sLam[65], sU[65];      // lam_k, U_k
+  __shared__ float sQscale[65];           // s_k
+  __shared__ int sReady;                  // the last pass's sums are p_k's numerators
   __shared__ float sPX[64], sQX[64], sUX[64];   // candidates: p(x), q(x), uniform
   __shared__ float sTile[kMaxTiles];
   __shared__ float sQ[kMaxTiles];
@@ -460,7 +415,11 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
       sInfo[2] = tl.n;
     }
   }
-  if (tid == 0) sQscale[0] = 1.f;
+  if (tid == 0) {
+    sLam[0] = 0.f;
+    sU[0] = 1.f;
+    sQscale[0] = 1.f;
+  }
   __syncthreads();
   const int st = sInfo[0], lo = sInfo[1], n = sInfo[2];
   if (st != GDN_TREE_OK) {             // (the same for every workgroup of the sequence)
@@ -498,16 +457,38 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
       }
     }
   };
-  // A pass over this workgroup's groups, then every group's sums in sG (sGQ):
+  // A pass over this workgroup's groups summing max(0, p - lam q) (with_q: and
+  // q; need_q false: p alone, lam = 0), each tile holding a token rejected
+  // earlier at the node corrected for it; then every group's sums in sG (sGQ):
   // from the others' words, or, if they do not come, from a second pass here
   // over every tile (the same call site, so the pass is inlined once).
-  auto pass_all = [&](auto what, const float* prow, const float* qrow, const Stages& st,
-                      bool with_q) {
+  constexpr int RW = kSplit ? kSplitTilesInFlight : kTilesInFlight;
+  auto pass_all = [&](const float* prow, const float* qrow, float lam, bool need_q, bool with_q,
+                      const Stages& st) {
     int g0 = gbeg, g1 = gend;
     for (;;) {
-      tile_pass<decltype(what)::value, kSplit ? kSplitTilesInFlight : kTilesInFlight>(
-          prow, qrow, V, group_begin(g0, ntiles), group_begin(g1, ntiles), st, sTile, sQ);
+      const int t0 = group_begin(g0, ntiles), t1 = group_begin(g1, ntiles);
+      if (with_q)
+        tile_pass<true, true, RW>(prow, qrow, V, t0, t1, lam, sTile, sQ);
+      else if (need_q)
+        tile_pass<false, true, RW>(prow, qrow, V, t0, t1, lam, sTile, sQ);
+      else
+        tile_pass<false, false, RW>(prow, qrow, V, t0, t1, 0.f, sTile, sQ);
       __syncthreads();                  // the pass's tile sums are in LDS
+      if (st.k > 0) {
+        // a token rejected at stage m keeps lam_{m+1}: its term in its tile
+        // is replaced (once, at its first rejection)
+        if (tid == 0) {
+          for (int m = 0; m < st.k; ++m) {
+            const int x = st.rem[m];
+            const int t = x / kTile;
+            if (t < t0 || t >= t1 || rejected_at(x, st.rem, m) >= 0) continue;
+            const float px = sRemP[m], qx = sRemQ[m];
+            sTile[t] += fmaxf(fmaf(-st.lam[m + 1], qx, px), 0.f) - fmaxf(fmaf(-lam, qx, px), 0.f);
+          }
+        }
+        __syncthreads();
+      }
       const bool whole = !kSplit || (g0 == 0 && g1 == kGroups);
       unsigned long long* words = whole ? nullptr : xch_words(a, b, nsync);
       const unsigned long long tag = (unsigned long long)(nsync + 1u) << 32;
@@ -526,9 +507,9 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
   for (;;) {
     const float* __restrict__ prow = a.p + (size_t)(lo + cur) * V;
     const float* __restrict__ qrow = a.q + (size_t)(lo + cur) * V;
-    Stages s{0, sRem, sZinv, sQscale};
+    Stages s{0, sRem, sLam, sQscale, 1.f};
     float qtot = 0.f, qrem = 0.f;
-    bool tiles_ready = false;             // sTile, sG hold the current p's sums / Z
+    bool tiles_ready = false;             // sTile, sG hold the numerators of the current p
     int next = -1;
     // every candidate's p(x), q(x) and uniform, one lane per child, in one
     // round trip when the walk enters the node
@@ -544,44 +525,52 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
       const int x = sTok[c];
       // (every thread takes the decision alike, from the same values)
       const float2 pq = stage_pq(sPX[c], sQX[c], x, s);
-      const bool take = sUX[c] * pq.y < pq.x;
+      const bool take = sUX[c] * pq.y < pq.x / s.u;
       if (take) {
         next = c;
         break;
       }
-      // rejected: tile sums of the residual max(0, p_k - q_k), and its mass Z
-      // (the first pass at a node also sums the row's q mass)
-      pass_all(std::integral_constant<TileSum, kResidual>{}, prow, qrow, s, s.k == 0);
+      // rejected: the residual's numerators max(0, p - lam' q), tile by tile,
+      // and their total U' (the first pass at a node also sums the row's q
+      // mass)
+      const float lam = uniform_f(s.lam[s.k] + s.qscale[s.k] * s.u);
+      pass_all(prow, qrow, lam, true, s.k == 0, s);
       if (wave == 0) {
-        const float z = groups_total(sG);
+        const float u2 = groups_total(sG);
         if (s.k == 0) qtot = groups_total(sGQ);
-        qrem += sQX[c];
+        // (a token drawn twice has left q already)
+        if (rejected_at(x, sRem, s.k) < 0) qrem += sQX[c];
         if (lane == 0) {
-          sZinv[s.k] = z > 0.f ? 1.f / z : 0.f;
           sRem[s.k] = x;
+          sRemP[s.k] = sPX[c];
+          sRemQ[s.k] = sQX[c];
+          sLam[s.k + 1] = u2 > 0.f ? lam : sLam[s.k];
+          sU[s.k + 1] = u2 > 0.f ? u2 : s.u;
+          sReady = u2 > 0.f;              // else p is unchanged and has no tile sums here
           const float left = qtot - qrem;
           sQscale[s.k + 1] = left > 0.f ? 1.f / left : 1.f;
         }
       }
       __syncthreads();
-      tiles_ready = sZinv[s.k] > 0.f;     // else p is unchanged and has no tile sums here
+      tiles_ready = sReady != 0;
       s.k += 1;
+      s.u = uniform_f(sU[s.k]);
     }
     if (next >= 0) {
       cur = next;
       ++len;
       continue;
     }
-    // final draw from p_k: tile sums (from the last rejection's pass, scaled,
-    // or from one pass over p); the group where the cumulative mass crosses u
-    // times the total, then (by the workgroup that summed that group, whose
-    // tile sums it holds) the tile, then the token in it
-    float scale = 1.f;
-    if (tiles_ready) {
-      scale = sZinv[s.k - 1];
-    } else {
-      pass_all(std::integral_constant<TileSum, kTarget>{}, prow, qrow, s, false);
+    // final draw from p_k: the tile sums of its numerators (from the last
+    // rejection's pass, or from one pass over the rows), scaled by 1 / U_k;
+    // the group where the cumulative mass crosses u times the total, then (by
+    // the workgroup that summed that group, whose tile sums it holds) the
+    // tile, then the token in it
+    if (!tiles_ready) {
+      const float lam = uniform_f(s.lam[s.k]);
+      pass_all(prow, qrow, lam, lam != 0.f, false, s);
     }
+    const float scale = 1.f / s.u;
     if (wave != 0) break;
     const float gv = lane < kGroups ? sG[lane] * scale : 0.f;
     float gincl = gv;
@@ -638,10 +627,10 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
     if (j0 < V) {
       const float4 p4 = *reinterpret_cast<const float4*>(prow + j0);
       const float4 q4 = *reinterpret_cast<const float4*>(qrow + j0);
-      v[0] = stage_pq(p4.x, q4.x, j0, s).x;
-      v[1] = stage_pq(p4.y, q4.y, j0 + 1, s).x;
-      v[2] = stage_pq(p4.z, q4.z, j0 + 2, s).x;
-      v[3] = stage_pq(p4.w, q4.w, j0 + 3, s).x;
+      v[0] = stage_pq(p4.x, q4.x, j0, s).x * scale;
+      v[1] = stage_pq(p4.y, q4.y, j0 + 1, s).x * scale;
+      v[2] = stage_pq(p4.z, q4.z, j0 + 2, s).x * scale;
+      v[3] = stage_pq(p4.w, q4.w, j0 + 3, s).x * scale;
     }
     const float vs = v[0] + v[1] + v[2] + v[3];
     float vincl = vs;

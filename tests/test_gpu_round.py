@@ -568,6 +568,44 @@ def test_accept_sampling_full_vocabulary():
         np.testing.assert_array_equal(g, r, err_msg=name)
 
 
+def test_accept_sampling_repeated_sibling_tokens():
+    """Siblings that repeat a token (not drawn without replacement): a token
+    rejected once has left q, so trying it again takes it iff the residual
+    holds mass there, and its q does not count twice in the renormalisation.
+    Against the oracle, one workgroup and split; the target rows made flat
+    enough (noise 3) that first candidates are often rejected, so that the
+    repeats are reached (at least 6 of them here)."""
+    _say("accept sampling, repeated sibling tokens")
+    rng = np.random.default_rng(31)
+    V = 1000
+    trees = [[-1, 0, 0, 0], [-1, 0, 0, 0, 1, 1, 1], gi.kary_parents(3, 2)] * 8
+    offsets, parents, draft, P, Q = _sampling_case(rng, trees, V, noise=3.0)
+    repeated = []                         # (sequence, node, its children)
+    for b, tr in enumerate(trees):
+        lo = int(offsets[b])
+        for u in range(len(tr)):
+            kids = [c for c in range(len(tr)) if tr[c] == u]
+            if len(kids) >= 2:            # the second sibling repeats the first
+                draft[lo + kids[1]] = draft[lo + kids[0]]
+                repeated.append((b, u, kids))
+    U = _uniforms_clear_of_thresholds(rng, offsets, parents, draft, P, Q)
+    ref = oacc.accept_sampling(offsets, parents, draft, P, Q, U)
+    reached = 0
+    for b, u, kids in repeated:
+        lo, path = int(offsets[b]), [int(ref[0][b])]
+        while path[-1] > 0:
+            path.append(trees[b][path[-1]])
+        acc, _ = oacc.node_plan(P[lo + u], Q[lo + u], [int(draft[lo + kids[0]])])
+        reached += u in path and U[lo + kids[0], 0] >= acc[0]
+    assert reached >= 6, reached
+    got = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, ref):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+    got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, 4)
+    for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, ref):
+        np.testing.assert_array_equal(g, r, err_msg="split " + name)
+
+
 def test_accept_sampling_status_codes():
     _say("accept sampling status")
     rng = np.random.default_rng(5)

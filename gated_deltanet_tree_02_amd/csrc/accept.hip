@@ -95,14 +95,17 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
 // are taken in fp32; totals run over group sums in a fixed order, so they do
 // not depend on how the tiles were divided.
 
-constexpr int kSampleThreads = 1024;
-constexpr int kSampleWaves = kSampleThreads / 64;
+constexpr int kSampleThreads = 1024;             // one workgroup per sequence
+// The split form's workgroups are smaller: a sequence's passes then spread
+// over more CUs (4 waves on each of 16 CUs, not 16 waves on each of 4), which
+// is what a sequence left to walk alone on an idle device can use.
+constexpr int kSplitThreads = 256;
 constexpr int kTile = kSamplingTile;             // tokens per tile (64 lanes x 4)
 static_assert(kTile == 256, "a tile is 64 lanes x 4 tokens");
 constexpr int kTilesInFlight = 4;
 // (the split form takes fewer tiles per wave per pass, and more of them in
 // flight at once pays there)
-constexpr int kSplitTilesInFlight = 5;
+constexpr int kSplitTilesInFlight = 6;
 constexpr int kMaxTiles = (1 << 20) / kTile;     // vocabularies up to 2^20 tokens
 
 // The stage after k rejections at the current node (in LDS, but u).
@@ -171,7 +174,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // as soon as it is summed, so every wave keeps that many tiles' loads in
 // flight for the whole pass. A tile's sums are the same whichever workgroup
 // takes it.
-template <bool kQSum, bool kNeedQ, int W>
+template <bool kQSum, bool kNeedQ, int W, int NWV>
 __device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
                                           const float* __restrict__ qrow, int V, int tbeg,
                                           int tend, float lam, float* sTile, float* sQ) {
@@ -180,13 +183,13 @@ __device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
   const int wave = threadIdx.x >> 6;
   const int span = tend - tbeg;
   const int mine =
-      __builtin_amdgcn_readfirstlane(wave < span ? (span - 1 - wave) / kSampleWaves + 1 : 0);
+      __builtin_amdgcn_readfirstlane(wave < span ? (span - 1 - wave) / NWV + 1 : 0);
   // element offsets are clamped into the row (V >= 4): the row's last tile
   // may be partial; its tokens past the row are not summed. A slot is loaded
   // only for a tile the wave has (a uniform branch): loads left in flight at
   // the end of a pass would hold up the next wait on the load counter.
   auto off = [&](int i) {
-    const int j = (tbeg + wave + i * kSampleWaves) * kTile + 4 * lane;
+    const int j = (tbeg + wave + i * NWV) * kTile + 4 * lane;
     return j < V - 4 ? j : V - 4;
   };
   float4 pv[W], qv[W];
@@ -204,7 +207,7 @@ __device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
     for (int u = 0; u < W; ++u) {
       const int i = i0 + u;
       if (i >= mine) break;             // the wave's tiles are done (uniform)
-      const int t = tbeg + wave + i * kSampleWaves;
+      const int t = tbeg + wave + i * NWV;
       const int j = t * kTile + 4 * lane;
       const float pe[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
       const float qe[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
@@ -241,7 +244,6 @@ __device__ __forceinline__ void tile_pass(const float* __restrict__ prow,
 // order, so neither depends on how the tiles are divided among workgroups: a
 // workgroup of the split form takes whole groups.
 constexpr int kGroups = kSamplingGroups;
-static_assert(kGroups <= kSampleWaves, "one wave sums one group");
 
 __device__ __forceinline__ int group_begin(int g, int ntiles) { return g * ntiles / kGroups; }
 
@@ -378,7 +380,9 @@ __device__ bool exchange_groups(const unsigned long long* words, unsigned long l
 // the same order), and a pass over a node's rows is divided among them by
 // groups of tiles.
 template <bool kSplit>
-__global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const AcceptSampleArgs a) {
+__global__ __launch_bounds__(kSplit ? kSplitThreads : kSampleThreads) void accept_sampling_kernel(
+    const AcceptSampleArgs a) {
+  constexpr int NWV = (kSplit ? kSplitThreads : kSampleThreads) / 64;   // waves
   __shared__ int sPar[64];
   __shared__ int sTok[64];
   __shared__ int sRem[64];              // rejected tokens of the current node
@@ -435,12 +439,12 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
   const int ntiles = (V + kTile - 1) / kTile;
   const int gbeg = part * (kGroups / S), gend = gbeg + kGroups / S;
   unsigned nsync = 0;                   // passes exchanged (split form)
-  // The group sums of groups [g0, g1) from sTile (sQ) into sG (sGQ), one wave
-  // per group; with `words`, each is published as soon as it is summed.
+  // The group sums of groups [g0, g1) from sTile (sQ) into sG (sGQ), wave w
+  // taking groups g0 + w, g0 + w + waves, ...; with `words`, each is published
+  // as soon as it is summed.
   auto group_sums = [&](int g0, int g1, bool with_q, unsigned long long* words,
                         unsigned long long tag) {
-    if (wave < g1 - g0) {
-      const int g = g0 + wave;
+    for (int g = g0 + wave; g < g1; g += NWV) {
       const int t0 = group_begin(g, ntiles), t1 = group_begin(g + 1, ntiles);
       const float gs = wave_tiles_sum(sTile, t0, t1);
       const float gq = with_q ? wave_tiles_sum(sQ, t0, t1) : 0.f;
@@ -469,11 +473,11 @@ __global__ __launch_bounds__(kSampleThreads) void accept_sampling_kernel(const A
     for (;;) {
       const int t0 = group_begin(g0, ntiles), t1 = group_begin(g1, ntiles);
       if (with_q)
-        tile_pass<true, true, RW>(prow, qrow, V, t0, t1, lam, sTile, sQ);
+        tile_pass<true, true, RW, NWV>(prow, qrow, V, t0, t1, lam, sTile, sQ);
       else if (need_q)
-        tile_pass<false, true, RW>(prow, qrow, V, t0, t1, lam, sTile, sQ);
+        tile_pass<false, true, RW, NWV>(prow, qrow, V, t0, t1, lam, sTile, sQ);
       else
-        tile_pass<false, false, RW>(prow, qrow, V, t0, t1, 0.f, sTile, sQ);
+        tile_pass<false, false, RW, NWV>(prow, qrow, V, t0, t1, 0.f, sTile, sQ);
       __syncthreads();                  // the pass's tile sums are in LDS
       if (st.k > 0) {
         // a token rejected at stage m keeps lam_{m+1}: its term in its tile
@@ -674,14 +678,14 @@ int accept_sampling_split_capacity() {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu, reinterpret_cast<const void*>(&accept_sampling_kernel<true>),
-          kSampleThreads, 0) != hipSuccess)
+          kSplitThreads, 0) != hipSuccess)
     return 0;
   return cus * per_cu;
 }
 
 hipError_t launch_accept_sampling_split(const AcceptSampleArgs& a, hipStream_t s) {
   return launch_kernel(reinterpret_cast<const void*>(&accept_sampling_kernel<true>),
-                       (unsigned)(a.B * a.splits), (unsigned)kSampleThreads, s, a);
+                       (unsigned)(a.B * a.splits), (unsigned)kSplitThreads, s, a);
 }
 
 hipError_t launch_accept_greedy(const AcceptArgs& a, hipStream_t s) {

@@ -758,11 +758,15 @@ def test_accept_sampling_split_grid_larger_than_the_device():
     rows themselves; the results are still the one-workgroup call's."""
     V = 5000
     rng = np.random.default_rng(404)
-    trees = [gi.random_tree_parents(rng, 5, 30) for _ in range(40)]
+    # the device holds fewer than 2 * 256 * splits(256) workgroups of this
+    # kernel (splits is the largest power of two within capacity / B)
+    cap_bound = 2 * 256 * max(1, _max_splits(256))
+    n_seq = cap_bound // 16 + 8
+    trees = [gi.random_tree_parents(rng, 5, 30) for _ in range(n_seq)]
     offsets, parents, draft, P, Q = _sampling_case(rng, trees, V)
     U = rng.random((len(parents), 2)).astype(np.float32)
-    # the device holds at most 16 * _max_splits(16) workgroups of this kernel
-    assert 16 * len(trees) > 16 * _max_splits(16), "the grid must exceed the device"
+    assert 16 * len(trees) > cap_bound, "the grid must exceed the device"
+    _say(f"split sampling grid: {16 * len(trees)} workgroups, device bound {cap_bound}")
     one = _sampling_gpu(offsets, parents, draft, P, Q, U)
     got = _sampling_split_gpu(offsets, parents, draft, P, Q, U, 16)
     for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, one):

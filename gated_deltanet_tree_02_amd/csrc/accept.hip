@@ -91,14 +91,15 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(const AcceptArgs a) 
 // pass over a node's rows by fixed groups of tiles and trade their group sums
 // after it. The draw finds the group, then the tile where the cumulative mass
 // crosses the target, and re-reads that tile alone. Each wave works on whole
-// 256-token tiles and keeps kTilesInFlight tiles' loads in flight. Decisions
+// 256-token tiles and keeps several tiles' loads in flight. Decisions
 // are taken in fp32; totals run over group sums in a fixed order, so they do
 // not depend on how the tiles were divided.
 
 constexpr int kSampleThreads = 1024;             // one workgroup per sequence
 // The split form's workgroups are smaller: a sequence's passes then spread
-// over more CUs (4 waves on each of 16 CUs, not 16 waves on each of 4), which
-// is what a sequence left to walk alone on an idle device can use.
+// over more CUs (with 64 sequences: 4 waves on each of 16 CUs, not 16 waves
+// on each of 4), which is what a sequence left to walk alone on an otherwise
+// idle device can use.
 constexpr int kSplitThreads = 256;
 constexpr int kTile = kSamplingTile;             // tokens per tile (64 lanes x 4)
 static_assert(kTile == 256, "a tile is 64 lanes x 4 tokens");

@@ -732,6 +732,29 @@ def test_accept_sampling_split_full_size_against_the_oracle():
         np.testing.assert_array_equal(g, r[:9])
 
 
+def test_accept_sampling_largest_vocabulary():
+    """The largest vocabulary the calls take (2^20 tokens: 4096 tiles, 256 per
+    group of the split form, 4 per lane in the group and crossing scans):
+    one workgroup against the oracle, and the split form at 2 and 16
+    workgroups per sequence against it bit for bit."""
+    V = 1 << 20
+    rng = np.random.default_rng(2020)
+    trees = [gi.kary_parents(2, 2), gi.chain_parents(4), [-1, 0, 0, 0], [-1]]
+    offsets, parents, draft, P, Q = _sampling_case(rng, trees, V)
+    # (sequence by sequence: over a million tokens a draw clears its margin
+    # only when it lands on one of the few likely tokens)
+    U = _uniforms_clear_per_sequence(rng, offsets, parents, draft, P, Q)
+    _say("accept sampling, V", V)
+    got = _sampling_gpu(offsets, parents, draft, P, Q, U)
+    ref = oacc.accept_sampling(offsets, parents, draft, P, Q, U)
+    for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), got, ref):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+    for S in (2, 16):
+        split = _sampling_split_gpu(offsets, parents, draft, P, Q, U, S)
+        for name, g, r in zip(("accepted", "accept_len", "next_token", "status"), split, got):
+            np.testing.assert_array_equal(g, r, err_msg=f"{name} splits={S}")
+
+
 def test_accept_sampling_split_status_codes():
     """Rejected trees leave every workgroup of their sequence before any
     exchange; the others are unaffected."""

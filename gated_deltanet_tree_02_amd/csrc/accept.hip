@@ -419,6 +419,15 @@ __global__ __launch_bounds__(kSplit ? kSplitThreads : kSampleThreads) void accep
       sInfo[1] = tl.lo;
       sInfo[2] = tl.n;
     }
+    // every candidate's p(x) and q(x) from its parent's rows, and its
+    // uniform, one lane per node, all in the walk's first round trip (a node
+    // has one parent, so this is each value the walk can ask for)
+    if (st == GDN_TREE_OK && lane >= 1 && lane < tl.n) {
+      const size_t at = (size_t)(tl.lo + tl.parent) * a.V + tok;
+      sPX[lane] = a.p[at];
+      sQX[lane] = a.q[at];
+      sUX[lane] = a.u[2 * (size_t)(tl.lo + lane)];
+    }
   }
   if (tid == 0) {
     sLam[0] = 0.f;
@@ -516,15 +525,6 @@ __global__ __launch_bounds__(kSplit ? kSplitThreads : kSampleThreads) void accep
     float qtot = 0.f, qrem = 0.f;
     bool tiles_ready = false;             // sTile, sG hold the numerators of the current p
     int next = -1;
-    // every candidate's p(x), q(x) and uniform, one lane per child, in one
-    // round trip when the walk enters the node
-    if (tid > cur && tid < n && sPar[tid] == cur) {
-      const int x = sTok[tid];
-      sPX[tid] = prow[x];
-      sQX[tid] = qrow[x];
-      sUX[tid] = a.u[2 * (size_t)(lo + tid)];
-    }
-    __syncthreads();
     for (int c = cur + 1; c < n; ++c) {   // children have larger indices, in node order
       if (sPar[c] != cur) continue;       // uniform
       const int x = sTok[c];

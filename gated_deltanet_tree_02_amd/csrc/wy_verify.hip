@@ -277,25 +277,30 @@ struct PrevLane {
   float g2_raw, alpha, beta;
 };
 
+// The previous round's node range and accepted node (scalar loads). Loaded
+// together with this round's node range, so that the previous tree's
+// per-node loads need no further round trip to memory.
+struct PrevHead {
+  int lo_r, hi_r, acc;
+};
+__device__ __forceinline__ PrevHead load_prev_head(const PendingTree& pt, int b) {
+  return PrevHead{pt.offsets[b], pt.offsets[b + 1], pt.accepted[b]};
+}
+
 template <bool kReplay>
 __device__ __forceinline__ PrevLane load_prev(const PendingTree& pt, const PendingLayer& pl,
-                                              int b, int h, int H, int lane) {
+                                              const PrevHead& ph, int h, int H, int lane) {
   PrevLane p;
-  p.lo = 0;
-  p.n = 1;
-  p.size_status = GDN_TREE_OK;
   p.g2_raw = 0.f;
   p.alpha = 1.f;
   p.beta = 0.f;
-  const int lo_r = pt.offsets[b];
-  const int hi_r = pt.offsets[b + 1];
-  p.acc = pt.accepted[b];
-  if (lo_r < 0 || hi_r > pt.T || hi_r - lo_r < 1 || hi_r - lo_r > pt.max_nodes) {
-    p.size_status = GDN_TREE_BAD_SIZE;
-  } else {
-    p.lo = lo_r;
-    p.n = hi_r - lo_r;
-  }
+  p.acc = ph.acc;
+  // (selects, not branches: the per-node loads below follow without a wait)
+  const bool bad = ph.lo_r < 0 || ph.hi_r > pt.T || ph.hi_r - ph.lo_r < 1 ||
+                   ph.hi_r - ph.lo_r > pt.max_nodes;
+  p.size_status = bad ? GDN_TREE_BAD_SIZE : GDN_TREE_OK;
+  p.lo = bad ? 0 : ph.lo_r;
+  p.n = bad ? 1 : ph.hi_r - ph.lo_r;
   const int nl = lane < p.n ? lane : 0;
   p.par_raw = pt.parents[p.lo + nl];
   const size_t gl = (size_t)(p.lo + nl) * H + h;
@@ -342,8 +347,8 @@ __device__ __forceinline__ int check_prev(const PrevLane& p, int lane, uint64_t&
 // elements per lane, 32 rows per pass; path rows are read straight from
 // memory. Returns the previous round's code.
 template <class IO, int DK, int DV, bool kReplay>
-__device__ int commit_prev_only(const CommitVerifyLayersArgs& args, int layer, int b, int h,
-                                int bh, const float* __restrict__ S0) {
+__device__ int commit_prev_only(const CommitVerifyLayersArgs& args, const PrevHead& ph, int layer,
+                                int h, int bh, const float* __restrict__ S0) {
   constexpr int NT = 64 * kVerifyWaves;
   constexpr int TPR = 16;                     // lanes per state row
   constexpr int CPT = DK / TPR;               // columns per lane
@@ -354,7 +359,7 @@ __device__ int commit_prev_only(const CommitVerifyLayersArgs& args, int layer, i
   const int lane = tid & 63;
   const int H = args.base.H;
   const PendingLayer& pl = args.P[layer];
-  const PrevLane p = load_prev<kReplay>(args.prev, pl, b, h, H, lane);
+  const PrevLane p = load_prev<kReplay>(args.prev, pl, ph, h, H, lane);
   uint64_t path0;
   const int ps = check_prev(p, lane, path0);
   float* __restrict__ S_out = pl.S_out;
@@ -482,7 +487,21 @@ void wy_verify_kernel(const Args args) {
   const int lane = tid & 63;
   const int g = lane >> 4;      // lane group of an MFMA operand / result
   const int l16 = lane & 15;
-  const int nbh = base_args(args).B * base_args(args).H;
+  // ---- 0. The prologue's scalar loads go out in two batches, each in full
+  // before its one wait (an empty asm statement takes the batch's values as
+  // operands; it has no side effects, so the loads stay scalar): the kernel
+  // arguments that locate the workgroup's sequence, then the layer's
+  // pointers together with the node ranges. Step 1 then issues every
+  // per-node load. Left alone, the compiler loads each field next to its
+  // first use: about eight dependent round trips before the first row is
+  // requested, each a memory latency when the scalar cache is cold.
+  int nB = base_args(args).B;
+  if constexpr (kFused)
+    asm("" : "+s"(nB) : "s"(base_args(args).H), "s"(base_args(args).offsets),
+        "s"(args.prev.offsets), "s"(args.prev.accepted));
+  else
+    asm("" : "+s"(nB) : "s"(base_args(args).H), "s"(base_args(args).offsets));
+  const int nbh = nB * base_args(args).H;
   const int layer = blockIdx.x / nbh;
   const VerifyArgs a = layer_args(args, layer);
   const int bh = blockIdx.x - layer * nbh;
@@ -494,14 +513,26 @@ void wy_verify_kernel(const Args args) {
   const IO* __restrict__ v = static_cast<const IO*>(a.v);
   IO* __restrict__ o = static_cast<IO*>(a.o);
 
-  // ---- node range (uniform, scalar loads)
-  const int lo = a.offsets[b];
+  // ---- node range, and (fused) the previous round's (uniform, scalar loads)
+  int lo = a.offsets[b];
   const int hi = a.offsets[b + 1];
+  PrevHead phd{0, 1, -1};
+  if constexpr (kFused) {
+    phd = load_prev_head(args.prev, b);
+    const PendingLayer& pl = args.P[layer];
+    asm("" : "+s"(lo) : "s"(hi), "s"(phd.lo_r), "s"(phd.hi_r), "s"(phd.acc), "s"(a.T),
+        "s"(a.max_nodes), "s"(a.parents), "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.alpha),
+        "s"(a.beta), "s"(args.prev.T), "s"(args.prev.max_nodes), "s"(args.prev.parents),
+        "s"(kReplay ? pl.alpha : pl.g2), "s"(pl.beta));
+  } else {
+    asm("" : "+s"(lo) : "s"(hi), "s"(a.T), "s"(a.max_nodes), "s"(a.parents), "s"(a.q),
+        "s"(a.k), "s"(a.v), "s"(a.alpha), "s"(a.beta));
+  }
   if (lo < 0 || hi > a.T || hi - lo < 1 || hi - lo > a.max_nodes) {
     // (fused) the previous round's commit is applied all the same
     int code = GDN_TREE_BAD_SIZE;
     if constexpr (kFused) {
-      const int pcode = commit_prev_only<IO, DK, DV, kReplay>(args, layer, b, h, bh, a.S0);
+      const int pcode = commit_prev_only<IO, DK, DV, kReplay>(args, phd, layer, h, bh, a.S0);
       code |= GDN_TREE_PREV(pcode);
     }
     if (h == 0 && tid == 0) put_status(a.status, b, code, a.merge);
@@ -550,7 +581,7 @@ void wy_verify_kernel(const Args args) {
     pv = static_cast<const IO*>(pl.v);
     pU = pl.U;
     S_out = pl.S_out;
-    prv = load_prev<kReplay>(args.prev, pl, b, h, H, lane);
+    prv = load_prev<kReplay>(args.prev, pl, phd, h, H, lane);
   }
   const int plo = prv.lo, pacc = prv.acc;
   const float pg2_raw = prv.g2_raw, palpha = prv.alpha, pbeta = prv.beta;
@@ -668,7 +699,7 @@ void wy_verify_kernel(const Args args) {
     int code = st;
     if constexpr (kFused) {
       if (st != GDN_TREE_OK && ps == GDN_TREE_OK)
-        ps = commit_prev_only<IO, DK, DV, kReplay>(args, layer, b, h, bh, a.S0);
+        ps = commit_prev_only<IO, DK, DV, kReplay>(args, phd, layer, h, bh, a.S0);
       code |= GDN_TREE_PREV(ps);
     }
     if (h == 0 && tid == 0) put_status(a.status, b, code, a.merge);

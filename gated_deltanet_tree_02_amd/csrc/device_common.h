@@ -161,7 +161,8 @@ __device__ __forceinline__ TreeLane load_tree(int b, int T, int max_nodes,
 
 // Pointer jumping over already-loaded parents (lane t holds parent(t), -1 for
 // the root, lanes >= n hold -1): visible set and the sum of x over the path
-// (x = 0 on lanes >= n). Six rounds cover depths below 64.
+// (x = 0 on lanes >= n). Six rounds cover depths below 64; the scan stops once
+// every lane has reached the root (after ceil(log2(depth + 1)) rounds).
 __device__ __forceinline__ void path_scan(int par, int lane, int n, float x, uint64_t& anc,
                                           float& sum) {
   anc = lane < n ? (1ull << lane) : 0ull;
@@ -169,6 +170,7 @@ __device__ __forceinline__ void path_scan(int par, int lane, int n, float x, uin
   int jmp = lane < n ? par : -1;
 #pragma unroll
   for (int it = 0; it < 6; ++it) {
+    if (__ballot(jmp >= 0) == 0ull) break;
     const int src = jmp < 0 ? lane : jmp;
     const uint64_t a2 = shfl_u64(anc, src);
     const float s2 = __shfl(sum, src, kWave);

@@ -314,11 +314,9 @@ __device__ __forceinline__ PrevLane load_prev(const PendingTree& pt, const Pendi
 }
 
 // Checks of the previous round before its commit (uniform result): nothing
-// is committed and nothing is checked for accepted == -1; otherwise the
-// previous tree (size, root, parents) and then the accepted index. `path`
-// receives the accepted node's path (root first, as a node set), or 0.
-__device__ __forceinline__ int check_prev(const PrevLane& p, int lane, uint64_t& path) {
-  path = 0ull;
+// is checked for accepted == -1; otherwise the previous tree (size, root,
+// parents) and then the accepted index.
+__device__ __forceinline__ int prev_status(const PrevLane& p, int lane) {
   if (p.acc == -1) return GDN_TREE_OK;
   int ps = p.size_status;
   const int par = lane < p.n ? p.par_raw : -1;
@@ -330,13 +328,20 @@ __device__ __forceinline__ int check_prev(const PrevLane& p, int lane, uint64_t&
     else if (p.acc < -1 || p.acc >= p.n)
       ps = GDN_TREE_BAD_ACCEPTED;
   }
-  ps = __builtin_amdgcn_readfirstlane(ps);
-  if (ps == GDN_TREE_OK) {
-    uint64_t anc;
-    float unused;
-    path_scan(par, lane, p.n, 0.f, anc, unused);
-    path = shfl_u64(anc, p.acc);
-  }
+  return __builtin_amdgcn_readfirstlane(ps);
+}
+// The accepted node's path (root first, as a node set) of a previous tree
+// that passed prev_status with accepted >= 0; one full wave.
+__device__ __forceinline__ uint64_t prev_path(const PrevLane& p, int lane) {
+  uint64_t anc;
+  float unused;
+  path_scan(lane < p.n ? p.par_raw : -1, lane, p.n, 0.f, anc, unused);
+  return shfl_u64(anc, p.acc);
+}
+// Both: the status, and in `path` the accepted path (0 if none is committed).
+__device__ __forceinline__ int check_prev(const PrevLane& p, int lane, uint64_t& path) {
+  const int ps = prev_status(p, lane);
+  path = (ps == GDN_TREE_OK && p.acc >= 0) ? prev_path(p, lane) : 0ull;
   return ps;
 }
 
@@ -474,6 +479,7 @@ void wy_verify_kernel(const Args args) {
   __shared__ __align__(16) float sT[NQT * TTS];
   __shared__ __align__(16) AqT sAqk[NQT * TTS];
   __shared__ uint64_t sAnc[NP];
+  __shared__ uint64_t sPath[1];   // (fused) the accepted path of the previous round
   __shared__ float sG2[NP];
   __shared__ float sBeta[NP];
   // previous round's path (fused commit): k rows widened to fp32 once here
@@ -622,8 +628,10 @@ void wy_verify_kernel(const Args args) {
       (mat == 0 ? sm.s1.k : sm.s1.q)[chunk_slot<CPR>(row, rel - row * CPR)] = stg[it];
     }
   }
-  // (every wave runs it: a branch around it would let the compiler sink the
-  // parent and gate loads into the branch, behind the staged-row waits)
+  // The tree checks run in every wave (a shuffle and a ballot each), the
+  // scans in wave 0 only: they are chains of LDS shuffles, and eight waves
+  // running the same ones slow each other down. (The checks also keep the
+  // parent and gate loads ahead of wave 0's branch.)
   const int par = lane < n ? par_raw : -1;
   int st = GDN_TREE_OK;
   if (__shfl(par, 0, kWave) != -1)
@@ -631,18 +639,36 @@ void wy_verify_kernel(const Args args) {
   else if (__ballot(lane >= 1 && lane < n && (par < 0 || par >= lane)) != 0ull)
     st = GDN_TREE_BAD_PARENT;
   st = __builtin_amdgcn_readfirstlane(st);
-  uint64_t anc;
-  float g2;
-  // (on a bad tree the scan still terminates; its results are not used)
-  path_scan(par, lane, n, lane < n ? gate_log2(alpha_l) : 0.f, anc, g2);
-  // (fused commit) the previous tree's checks, then the accepted node's path
-  // (root first), its gate prefix and the path coefficients 2^(gA - g2_i)
+  const float lg = lane < n ? gate_log2(alpha_l) : 0.f;
+  int ps = GDN_TREE_OK;   // the previous round's commit (fused)
+  if constexpr (kFused) ps = prev_status(prv, lane);
+  uint64_t anc = 0ull;
+  float g2 = 0.f;
+  if (wave == 0) {
+    // (on a bad tree the scan still terminates; its results are not used)
+    path_scan(par, lane, n, lg, anc, g2);
+    if constexpr (kFused) {
+      // the accepted node's path, root first (a rejected tree this round:
+      // committed on the cold path below)
+      const uint64_t pp =
+          (st == GDN_TREE_OK && ps == GDN_TREE_OK && pacc >= 0) ? prev_path(prv, lane) : 0ull;
+      if (lane == 0) sPath[0] = pp;
+    }
+    if (lane < NP) {
+      sAnc[lane] = anc;
+      sG2[lane] = g2;
+      sBeta[lane] = lane < n ? beta_raw : 0.f;
+    }
+  }
+  __syncthreads();
+  // (fused commit) the path, and its gate prefix and path coefficients
+  // 2^(gA - g2_i) (commit from pseudo-values)
   uint64_t ppath = 0ull;
   float pgA = 0.f, pcoef = 0.f;
-  int ps = GDN_TREE_OK;   // the previous round's commit (fused)
   if constexpr (kFused) {
-    ps = check_prev(prv, lane, ppath);
-    if (st != GDN_TREE_OK) ppath = 0ull;   // (committed on the cold path below)
+    const uint64_t pp = sPath[0];
+    ppath = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(pp >> 32)) << 32) |
+            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pp);
     if constexpr (!kReplay) {
       if (ppath) {
         pgA = __shfl(pg2_raw, pacc, kWave);
@@ -650,12 +676,6 @@ void wy_verify_kernel(const Args args) {
       }
     }
   }
-  if (wave == 0 && lane < NP) {
-    sAnc[lane] = anc;
-    sG2[lane] = g2;
-    sBeta[lane] = lane < n ? beta_raw : 0.f;
-  }
-  __syncthreads();
   // 1c. this wave's S0 rows 16w + lane%16, columns 32s + 8g .. +7. Issued only
   // now, once the q, k, v rows have arrived: when every resident workgroup
   // loads at once, the rows that the first phases need are not queued behind

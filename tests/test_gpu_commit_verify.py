@@ -270,6 +270,56 @@ def test_commit_verify_status_codes(mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+def test_commit_verify_bad_previous_node_range(mode):
+    """A previous round whose node range is malformed: too many nodes for its
+    descriptor, a range shifted onto another sequence's nodes (its first node
+    is no root), or a range past the node count. Each rejects that sequence's
+    previous commit (S_out unwritten, o rows zero) with the code above
+    gt.PREV_SHIFT; accepted = -1 checks nothing; the other sequences commit
+    and verify as the oracle does."""
+    prev_trees = [gi.kary_parents(2, 2)] * 6
+    cur_trees = [gi.kary_parents(2, 2)] * 6
+    wp = gi.make_workload(prev_trees, 2, 64, 64, io="bf16", seed=33)
+    wc = gi.make_workload(cur_trees, 2, 64, 64, io="bf16", seed=34)
+    wp.accepted[:] = [3, 5, 3, 4, 6, -1]
+    P, C = DeviceLayer(wp, 0), DeviceLayer(wc, 0)
+    P.verify()
+    torch.cuda.synchronize()
+    assert np.all(P.status.cpu().numpy() == 0)
+    offs = wp.offsets.copy()
+    offs[3] += 1          # seq 2: 8 nodes (> 7); seq 3: starts on its own second node
+    offs[5] = wp.T + 5    # seq 4 ends past the node count; seq 5 is empty (unchecked)
+    P.offsets.copy_(torch.from_numpy(offs.astype(np.int32)))
+    S0 = P.S0.clone()
+    S_out = torch.full_like(S0, float("nan"))
+    _fused(P, C, S0, S_out, mode)
+    torch.cuda.synchronize()
+    prev = gt.prev_code
+    assert C.status.cpu().numpy().tolist() == [0, 0, prev(3), prev(1), prev(3), 0]
+    o = C.o_np()
+    for b in (2, 3, 4):
+        assert torch.isnan(S_out[b]).all(), b
+        assert np.all(o[wc.offsets[b]:wc.offsets[b + 1]] == 0), b
+    assert torch.equal(S_out[5], S0[5])
+    done = [0, 1]
+    sp = sub_workload(wp, done)
+    S_ref, stc = oracle.commit(sp.offsets, sp.parents, sp.accepted, sp.k[0], sp.v[0],
+                               sp.alpha[0], sp.beta[0], sp.S0[0])
+    assert np.all(stc == 0)
+    e_s = rel_err_states(S_out.cpu().numpy()[done], S_ref)
+    keep = [0, 1, 5]
+    sc = sub_workload(wc, keep)
+    S_keep = np.stack([S_ref[0], S_ref[1], wp.S0[0][5]])
+    o_ref, st_ref = oracle.verify(sc.offsets, sc.parents, sc.q[0], sc.k[0], sc.v[0], sc.alpha[0],
+                                  sc.beta[0], S_keep)
+    assert np.all(st_ref == 0)
+    rows = np.concatenate([np.arange(wc.offsets[b], wc.offsets[b + 1]) for b in keep])
+    e_o = rel_err_rows(o[rows], o_ref)
+    _say(f"bad previous node range ({mode}): committed state err {e_s:.3e}, o err {e_o:.3e}")
+    assert e_s <= TOL["bf16"] and e_o <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_commit_verify_c4_full_size_sampled(mode):
     """Two consecutive rounds of the k=3 d=3, B=64, 16-head, 128x128 workload
     over all 24 GDN layers in one layer-batched launch (the benchmark's
